@@ -1,0 +1,166 @@
+"""fp64 CPU oracle for the selective scan and the SSD form -- TEST INFRASTRUCTURE.
+
+Only the tests, ``__graft_entry__.smoke()`` and the benchmark's ``cpu_baseline``
+leg may import this package.  The GPU library and its Python binding never
+import it, and it imports nothing of theirs.
+
+The arithmetic lives in ``oracle.c`` (plain C, double precision, sequential per
+slice; see the header comment there for the sources and the readings taken).
+This module only builds it with gcc, marshals numpy arrays, and splits
+independent (batch, channel) or (batch, head) slices over host threads.
+
+Parity pins: every function is pinned by CPU tests against closed forms, the
+convolution view, limits and invariants (tests/test_oracle_pins.py).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so with gcc (no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-ffp-contract=off",
+               "-fno-fast-math", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB):
+                build(force=False)
+            lib = ctypes.CDLL(_LIB)
+            P = ctypes.c_void_p
+            I64 = ctypes.c_int64
+            I = ctypes.c_int
+            lib.oracle_selective_scan.argtypes = [P] * 8 + [I, P, P, P] + [I64] * 6
+            lib.oracle_selective_scan.restype = None
+            lib.oracle_ssd_recurrent.argtypes = [P] * 8 + [I, P, P, P] + [I64] * 8
+            lib.oracle_ssd_recurrent.restype = None
+            lib.oracle_ssd_quadratic.argtypes = [P] * 8 + [I, P, P] + [I64] * 8
+            lib.oracle_ssd_quadratic.restype = None
+            lib.oracle_lti_conv.argtypes = [P, P, P, P, ctypes.c_double, ctypes.c_double, P, I64, I64]
+            lib.oracle_lti_conv.restype = None
+            _lib = lib
+    return _lib
+
+
+def _f64(a, shape=None):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+    if shape is not None and a.shape != tuple(shape):
+        raise ValueError("oracle: expected shape %s, got %s" % (tuple(shape), a.shape))
+    return a
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def default_threads() -> int:
+    return max(1, len(os.sched_getaffinity(0)))
+
+
+def _run_slices(fn, total: int, threads: int | None):
+    threads = threads or default_threads()
+    threads = max(1, min(threads, total))
+    if threads == 1 or total == 0:
+        fn(0, total)
+        return
+    bounds = [total * i // threads for i in range(threads + 1)]
+    with ThreadPoolExecutor(threads) as ex:   # ctypes releases the GIL during each call
+        list(ex.map(lambda i: fn(bounds[i], bounds[i + 1]), range(threads)))
+
+
+def selective_scan(x, delta, A, B, C, Dskip=None, z=None, delta_bias=None,
+                   delta_softplus=False, h0=None, want_y=True, threads=None):
+    """O1: y (batch, seqlen, dim) and h_final (batch, dim, dstate), both float64."""
+    x = _f64(x)
+    batch, seqlen, dim = x.shape
+    A = _f64(A)
+    dstate = A.shape[1]
+    delta = _f64(delta, x.shape)
+    B = _f64(B, (batch, seqlen, dstate))
+    C = _f64(C, (batch, seqlen, dstate))
+    Dskip = _f64(Dskip, (dim,))
+    z = _f64(z, x.shape)
+    delta_bias = _f64(delta_bias, (dim,))
+    h0 = _f64(h0, (batch, dim, dstate))
+    y = np.empty_like(x) if want_y else None
+    hf = np.empty((batch, dim, dstate), dtype=np.float64)
+    lib = _load()
+    _run_slices(lambda s0, s1: lib.oracle_selective_scan(
+        _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(z), _ptr(delta_bias),
+        int(bool(delta_softplus)), _ptr(h0), _ptr(y), _ptr(hf),
+        batch, seqlen, dim, dstate, s0, s1), batch * dim, threads)
+    return y, hf
+
+
+def _ssd_args(x, dt, A, B, C, Dskip, z, dt_bias, h0):
+    x = _f64(x)
+    batch, seqlen, nheads, headdim = x.shape
+    B = _f64(B)
+    ngroups, dstate = B.shape[2], B.shape[3]
+    if nheads % ngroups:
+        raise ValueError("oracle: nheads must be a multiple of ngroups")
+    return (x, _f64(dt, (batch, seqlen, nheads)), _f64(A, (nheads,)), _f64(B, (batch, seqlen, ngroups, dstate)),
+            _f64(C, (batch, seqlen, ngroups, dstate)), _f64(Dskip, (nheads,)), _f64(z, x.shape),
+            _f64(dt_bias, (nheads,)), _f64(h0, (batch, nheads, headdim, dstate)),
+            (batch, seqlen, nheads, headdim, ngroups, dstate))
+
+
+def ssd_recurrent(x, dt, A, B, C, Dskip=None, z=None, dt_bias=None, dt_softplus=False,
+                  h0=None, want_y=True, threads=None):
+    """O2: SSD by its recurrence; y (b, L, H, P) and h_final (b, H, P, N), float64."""
+    x, dt, A, B, C, Dskip, z, dt_bias, h0, dims = _ssd_args(x, dt, A, B, C, Dskip, z, dt_bias, h0)
+    batch, seqlen, nheads, headdim, ngroups, dstate = dims
+    y = np.empty_like(x) if want_y else None
+    hf = np.empty((batch, nheads, headdim, dstate), dtype=np.float64)
+    lib = _load()
+    _run_slices(lambda s0, s1: lib.oracle_ssd_recurrent(
+        _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(z), _ptr(dt_bias),
+        int(bool(dt_softplus)), _ptr(h0), _ptr(y), _ptr(hf), *dims, s0, s1), batch * nheads, threads)
+    return y, hf
+
+
+def ssd_quadratic(x, dt, A, B, C, Dskip=None, z=None, dt_bias=None, dt_softplus=False,
+                  h0=None, threads=None):
+    """O2': SSD by its O(L^2) matrix form; y (b, L, H, P), float64."""
+    x, dt, A, B, C, Dskip, z, dt_bias, h0, dims = _ssd_args(x, dt, A, B, C, Dskip, z, dt_bias, h0)
+    batch, seqlen, nheads, headdim, ngroups, dstate = dims
+    y = np.empty_like(x)
+    lib = _load()
+    _run_slices(lambda s0, s1: lib.oracle_ssd_quadratic(
+        _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(z), _ptr(dt_bias),
+        int(bool(dt_softplus)), _ptr(h0), _ptr(y), *dims, s0, s1), batch * nheads, threads)
+    return y
+
+
+def lti_conv(x, A, B, C, dt, Dskip=0.0):
+    """O3: one LTI channel as a causal convolution with K_i = C Abar^i Bbar; y (seqlen,)."""
+    x = _f64(x)
+    A = _f64(A)
+    B = _f64(B, A.shape)
+    C = _f64(C, A.shape)
+    y = np.empty_like(x)
+    _load().oracle_lti_conv(_ptr(x), _ptr(A), _ptr(B), _ptr(C), float(dt), float(Dskip), _ptr(y),
+                            x.shape[0], A.shape[0])
+    return y

@@ -1,0 +1,141 @@
+"""Seeded synthetic inputs for the selective scan and SSD workloads.
+
+This module only draws and rounds inputs; it holds none of the scan's
+arithmetic.  Both the fp64 oracle and the HIP library consume exactly the
+values drawn here (bf16 tensors are rounded to nearest even once, here, and
+the oracle reads those rounded values).
+
+Distributions follow the sources' parameterisation ("Mamba / SSM complete
+guide", sec. 5: A = -exp(log(1..N)) = -(n+1) per channel, dt drawn between
+dt_min = 1e-3 and dt_max = 1e-1, skip initialised from a normal range; "SSM &
+Mamba" experiment: seed 42) and the five workload shapes below.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+# The five workloads: four selective-scan layer shapes and one SSD shape.
+CONFIGS = [
+    dict(name="scan_f32_b1_d16_l256_n16", kind="scan", batch=1, dim=16, seqlen=256, dstate=16, dtype="f32",
+         delta_dtype="f32", dt="loguniform", dt_lo=1e-3, dt_hi=1e-1, gate=False, softplus=False, skip=True,
+         final_state=False),
+    dict(name="scan_bf16_b8_d1536_l2048_n16", kind="scan", batch=8, dim=1536, seqlen=2048, dstate=16, dtype="bf16",
+         delta_dtype="bf16", dt="softplus_bias", dt_lo=1e-3, dt_hi=1e-1, gate=True, softplus=True, skip=True,
+         final_state=False),
+    dict(name="scan_bf16_b4_d5120_l4096_n16", kind="scan", batch=4, dim=5120, seqlen=4096, dstate=16, dtype="bf16",
+         delta_dtype="bf16", dt="softplus_bias", dt_lo=1e-3, dt_hi=1e-1, gate=True, softplus=True, skip=True,
+         final_state=True),
+    dict(name="scan_bf16_b1_d2048_l131072_n16", kind="scan", batch=1, dim=2048, seqlen=131072, dstate=16,
+         dtype="bf16", delta_dtype="bf16", dt="loguniform", dt_lo=1e-4, dt_hi=1e-1, gate=False, softplus=False,
+         skip=True, final_state=True),
+    dict(name="ssd_bf16_b2_h64_p64_n128_l8192_q256", kind="ssd", batch=2, nheads=64, headdim=64, dstate=128,
+         seqlen=8192, ngroups=1, chunk=256, dtype="bf16", dt_dtype="f32", dt_lo=1e-3, dt_hi=1e-1,
+         a_lo=1.0, a_hi=16.0, gate=False, skip=False, final_state=True),
+]
+
+
+def round_to(arr: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float values to `dtype` ("f32" or "bf16", nearest even); returns float32 holding them."""
+    a = np.ascontiguousarray(arr, dtype=np.float32)
+    if dtype == "f32":
+        return a
+    if dtype == "bf16":
+        return torch.from_numpy(a).to(torch.bfloat16).to(torch.float32).numpy()
+    raise ValueError(dtype)
+
+
+def _loguniform(rng, lo, hi, size):
+    return np.exp(rng.uniform(np.log(lo), np.log(hi), size=size)).astype(np.float32)
+
+
+def scan_inputs(batch, seqlen, dim, dstate, dtype="bf16", delta_dtype=None, seed=0, dt="loguniform",
+                dt_lo=1e-3, dt_hi=1e-1, gate=False, softplus=False, skip=True, h0=False, **_):
+    """Inputs of the selective scan.  Returns a dict of float32 numpy arrays (values already
+    rounded to their storage dtype) plus "meta" (dtypes and flags)."""
+    delta_dtype = delta_dtype or dtype
+    rng = np.random.default_rng(seed)
+    out = {}
+    out["A"] = np.broadcast_to(-np.arange(1, dstate + 1, dtype=np.float32), (dim, dstate)).copy()
+    out["x"] = round_to(rng.standard_normal((batch, seqlen, dim), dtype=np.float32), dtype)
+    if dt == "loguniform":
+        out["delta"] = round_to(_loguniform(rng, dt_lo, dt_hi, (batch, seqlen, dim)), delta_dtype)
+        out["delta_bias"] = None
+    elif dt == "softplus_bias":
+        # per-channel bias placing softplus(0 + bias) log-uniformly in [dt_lo, dt_hi]
+        dt0 = _loguniform(rng, dt_lo, dt_hi, (dim,)).astype(np.float64)
+        out["delta_bias"] = np.log(np.expm1(dt0)).astype(np.float32)
+        out["delta"] = round_to(rng.standard_normal((batch, seqlen, dim), dtype=np.float32), delta_dtype)
+    else:
+        raise ValueError(dt)
+    out["B"] = round_to(rng.standard_normal((batch, seqlen, dstate), dtype=np.float32), dtype)
+    out["C"] = round_to(rng.standard_normal((batch, seqlen, dstate), dtype=np.float32), dtype)
+    out["D"] = rng.standard_normal(dim, dtype=np.float32) if skip else None
+    out["z"] = round_to(rng.standard_normal((batch, seqlen, dim), dtype=np.float32), dtype) if gate else None
+    out["h0"] = rng.standard_normal((batch, dim, dstate), dtype=np.float32) if h0 else None
+    out["meta"] = dict(kind="scan", dtype=dtype, delta_dtype=delta_dtype, softplus=bool(softplus))
+    return out
+
+
+def ssd_inputs(batch, seqlen, nheads, headdim, dstate, ngroups=1, dtype="bf16", dt_dtype="f32", seed=0,
+               dt_lo=1e-3, dt_hi=1e-1, a_lo=1.0, a_hi=16.0, gate=False, skip=False, h0=False, dt_softplus=False,
+               **_):
+    """Inputs of the SSD form: scalar A per head ~ -U[a_lo, a_hi], dt log-uniform per (b, t, h)."""
+    rng = np.random.default_rng(seed)
+    out = {}
+    out["x"] = round_to(rng.standard_normal((batch, seqlen, nheads, headdim), dtype=np.float32), dtype)
+    if dt_softplus:
+        dt0 = _loguniform(rng, dt_lo, dt_hi, (nheads,)).astype(np.float64)
+        out["dt_bias"] = np.log(np.expm1(dt0)).astype(np.float32)
+        out["dt"] = round_to(rng.standard_normal((batch, seqlen, nheads), dtype=np.float32), dt_dtype)
+    else:
+        out["dt_bias"] = None
+        out["dt"] = round_to(_loguniform(rng, dt_lo, dt_hi, (batch, seqlen, nheads)), dt_dtype)
+    out["A"] = (-rng.uniform(a_lo, a_hi, nheads)).astype(np.float32)
+    out["B"] = round_to(rng.standard_normal((batch, seqlen, ngroups, dstate), dtype=np.float32), dtype)
+    out["C"] = round_to(rng.standard_normal((batch, seqlen, ngroups, dstate), dtype=np.float32), dtype)
+    out["D"] = rng.standard_normal(nheads, dtype=np.float32) if skip else None
+    out["z"] = round_to(rng.standard_normal((batch, seqlen, nheads, headdim), dtype=np.float32), dtype) if gate else None
+    out["h0"] = rng.standard_normal((batch, nheads, headdim, dstate), dtype=np.float32) if h0 else None
+    out["meta"] = dict(kind="ssd", dtype=dtype, dt_dtype=dt_dtype, softplus=bool(dt_softplus))
+    return out
+
+
+def config_inputs(index: int, **overrides):
+    """Inputs of workload `index` (seed 42 + index), optionally with overridden sizes."""
+    cfg = dict(CONFIGS[index])
+    cfg.update(overrides)
+    seed = 42 + index
+    if cfg["kind"] == "scan":
+        return scan_inputs(seed=seed, **cfg), cfg
+    return ssd_inputs(seed=seed, **cfg), cfg
+
+
+_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def to_device(inp: dict, device) -> dict:
+    """Device tensors in their storage dtypes (exact: values are already rounded)."""
+    meta = inp["meta"]
+    act = _TORCH[meta["dtype"]]
+    fp32_keys = {"A", "D", "delta_bias", "dt_bias", "h0"}
+    out = {}
+    for k, v in inp.items():
+        if k == "meta" or v is None:
+            out[k] = None if k != "meta" else v
+            continue
+        if k in fp32_keys:
+            dt = torch.float32
+        elif k == "delta":
+            dt = _TORCH[meta["delta_dtype"]]
+        elif k == "dt":
+            dt = _TORCH[meta["dt_dtype"]]
+        else:
+            dt = act
+        out[k] = torch.from_numpy(np.ascontiguousarray(v)).to(device=device, dtype=dt)
+    return out
+
+
+def to_f64(inp: dict) -> dict:
+    return {k: (None if v is None else (v if k == "meta" else np.asarray(v, dtype=np.float64)))
+            for k, v in inp.items()}
