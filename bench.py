@@ -1,0 +1,231 @@
+"""Benchmark of the selective scan on one MI355X.
+
+One step = one full selective-scan forward (discretize + recurrence + readout
++ skip + gate) over the Mamba-130M-like layer workload: batch 8, 1536
+channels, 2048 tokens, 16 states, bf16 inputs/outputs, fp32 state, softplus dt
+with per-channel bias, silu(z) gate.  Inputs are resident in HBM before the
+timed region; each step reads one of four rotating input copies (> the 256 MB
+last-level cache) so no step reads another step's inputs from cache.
+
+Prints one JSON line with the headline throughput (token*channels/s), the
+roofline of the scan kernel measured with HIP events on the launch stream, the
+oracle timed on the host cores (rank 0, N=1 only), and the other workloads.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X figures used by the roofline (vendor-published).
+HBM_PEAK_GBS = 8000.0
+CUS, SIMDS_PER_CU, LANES_PER_SIMD, CLOCK_GHZ = 256, 4, 16, 2.4
+# VALU issue capacity in lane-slots/s: 256 CU x 4 SIMD x 16 lanes x 2.4 GHz.
+VALU_PEAK_TSLOTS = CUS * SIMDS_PER_CU * LANES_PER_SIMD * CLOCK_GHZ * 1e9 / 1e12
+# Algorithmic VALU slots per (token, channel, state) element: q = dt*a, the
+# ZOH gain fma, B*x, gain*(B*x), the state fma, the readout fma (6 full-rate
+# ops) plus one exp, which issues at half rate on gfx950 (2 slots).
+SLOTS_PER_ELEMENT = 8
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-others", action="store_true")
+    return p.parse_args()
+
+
+def scan_bytes(cfg):
+    """Algorithmic HBM bytes: every input read once, every output written once."""
+    b, L, D, N = cfg["batch"], cfg["seqlen"], cfg["dim"], cfg["dstate"]
+    e = 2 if cfg["dtype"] == "bf16" else 4
+    ed = 2 if cfg["delta_dtype"] == "bf16" else 4
+    per_tc = e * 2 + ed + (e if cfg["gate"] else 0)            # x, y, delta, z
+    total = b * L * D * per_tc + 2 * b * L * N * e + D * N * 4 + 3 * D * 4
+    if cfg.get("final_state"):
+        total += b * D * N * 4
+    return total
+
+
+def ssd_bytes(cfg):
+    b, L, H, P, N, G = cfg["batch"], cfg["seqlen"], cfg["nheads"], cfg["headdim"], cfg["dstate"], cfg["ngroups"]
+    total = b * L * H * P * 2 * 2 + 2 * b * L * G * N * 2 + b * L * H * 4 + H * 4
+    if cfg.get("final_state"):
+        total += b * H * P * N * 4
+    return total
+
+
+def ssd_flops(cfg):
+    """Algorithmic matrix FLOPs of the chunked form (causal half of each Q x Q block)."""
+    b, L, H, P, N, G, Q = (cfg["batch"], cfg["seqlen"], cfg["nheads"], cfg["headdim"], cfg["dstate"],
+                           cfg["ngroups"], cfg["chunk"])
+    chunks = L // Q
+    cb = b * chunks * G * Q * Q * N * 2 / 2          # C B^T, lower triangle, once per group
+    diag = b * H * chunks * Q * Q * P * 2 / 2        # (CB^T o L) X, lower triangle
+    states = b * H * chunks * Q * N * P * 2          # chunk states
+    off = b * H * chunks * Q * N * P * 2             # C H^T
+    return cb + diag + states + off
+
+
+def time_calls(fn, steps, warmup, torch):
+    """Run fn(i) warmup times, then `steps` times bracketed by events; returns (total_ms, [per-call ms])."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(st)
+    for i in range(steps):
+        evs[i].record(st)
+        fn(i)
+    evs[steps].record(st)
+    end.record(st)
+    torch.cuda.synchronize()
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    return start.elapsed_time(end), per
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (see DESIGN.md for how the scan "
+              "would shard); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import workloads
+    from selective_state_space_58_amd import _binding
+    if not os.path.exists(_binding.library_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    import selective_state_space_58_amd as ssm
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    steps, warmup = args.steps, args.warmup
+
+    # ---------------------------------------------------------------- headline workload
+    idx = 1
+    inp, cfg = workloads.config_inputs(idx)
+    copies = [workloads.to_device(inp, dev) for _ in range(4)]
+    ys = [torch.empty_like(c["x"]) for c in copies]
+
+    def step(i):
+        t = copies[i % 4]
+        ssm.ssm_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], delta_bias=t["delta_bias"],
+                         delta_softplus=True, y=ys[i % 4])
+
+    total_ms, per = time_calls(step, steps, warmup, torch)
+    ms = total_ms / steps
+    kern_ms = float(np.mean(per))
+    tc = cfg["batch"] * cfg["seqlen"] * cfg["dim"]
+    elems = tc * cfg["dstate"]
+    value = tc / (ms * 1e-3) / 1e9
+    nbytes = scan_bytes(cfg)
+    hbm_gbs = nbytes / (kern_ms * 1e-3) / 1e9
+    slots = elems * SLOTS_PER_ELEMENT / (kern_ms * 1e-3) / 1e12
+    out = {
+        "metric": "selective-scan Gtoken*channel/s at 1 MI355X + % of HBM roofline",
+        "value": round(value, 3),
+        "unit": "Gtoken*channel/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg["name"], "batch": cfg["batch"], "dim": cfg["dim"], "seqlen": cfg["seqlen"],
+                   "dstate": cfg["dstate"], "io_dtype": "bf16", "state_dtype": "f32", "softplus_dt": True,
+                   "gate": True, "skip": True},
+        "hbm": {"algorithmic_bytes": nbytes, "achieved_GBs": round(hbm_gbs, 1), "peak_GBs": HBM_PEAK_GBS,
+                "frac": round(hbm_gbs / HBM_PEAK_GBS, 4)},
+        "roofline": {"bound": "alu", "achieved": round(slots, 3), "peak": round(VALU_PEAK_TSLOTS, 3),
+                     "unit": "T VALU lane-slots/s (algorithmic: 8 per state element)",
+                     "frac": round(slots / VALU_PEAK_TSLOTS, 4), "traffic": None,
+                     "kernel_ms": round(kern_ms, 5)},
+    }
+
+    # ---------------------------------------------------------------- other workloads
+    others = {}
+    if not args.no_others:
+        del copies, ys
+        torch.cuda.empty_cache()
+        for oi in (2, 3, 4):
+            oinp, ocfg = workloads.config_inputs(oi)
+            t = workloads.to_device(oinp, dev)
+            if ocfg["kind"] == "scan":
+                y = torch.empty_like(t["x"])
+                hf = torch.empty((ocfg["batch"], ocfg["dim"], ocfg["dstate"]), dtype=torch.float32, device=dev)
+                nb = ssm.ssm_scan_workspace_bytes(ocfg["batch"], ocfg["seqlen"], ocfg["dim"], ocfg["dstate"])
+                ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+
+                def ostep(i, t=t, y=y, hf=hf, ws=ws, sp=oinp["meta"]["softplus"]):
+                    ssm.ssm_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                                     delta_bias=t["delta_bias"], delta_softplus=sp, y=y, h_final=hf, workspace=ws)
+                tot, _ = time_calls(ostep, 5, 2, torch)
+                oms = tot / 5
+                otc = ocfg["batch"] * ocfg["seqlen"] * ocfg["dim"]
+                ob = scan_bytes(ocfg)
+                others[ocfg["name"]] = {"ms": round(oms, 4), "Gtc_s": round(otc / (oms * 1e-3) / 1e9, 2),
+                                        "hbm_frac": round(ob / (oms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                        "valu_frac": round(otc * ocfg["dstate"] * SLOTS_PER_ELEMENT /
+                                                           (oms * 1e-3) / 1e12 / VALU_PEAK_TSLOTS, 4)}
+            else:
+                try:
+                    y = torch.empty_like(t["x"])
+                    hf = torch.empty((ocfg["batch"], ocfg["nheads"], ocfg["headdim"], ocfg["dstate"]),
+                                     dtype=torch.float32, device=dev)
+                    nb = ssm.ssd_workspace_bytes(ocfg["batch"], ocfg["seqlen"], ocfg["nheads"], ocfg["headdim"],
+                                                 ocfg["ngroups"], ocfg["dstate"], ocfg["chunk"])
+                    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+
+                    def sstep(i, t=t, y=y, hf=hf, ws=ws):
+                        ssm.ssd_chunk_scan_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], chunk_size=ocfg["chunk"],
+                                               y=y, h_final=hf, workspace=ws)
+                    tot, _ = time_calls(sstep, 5, 2, torch)
+                    oms = tot / 5
+                    otc = ocfg["batch"] * ocfg["seqlen"] * ocfg["nheads"] * ocfg["headdim"]
+                    others[ocfg["name"]] = {
+                        "ms": round(oms, 4), "Gtc_s": round(otc / (oms * 1e-3) / 1e9, 2),
+                        "hbm_frac": round(ssd_bytes(ocfg) / (oms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                        "mfma_frac": round(ssd_flops(ocfg) / (oms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+                except ssm.SSMError as e:
+                    others[ocfg["name"]] = {"error": str(e)}
+            del t
+            torch.cuda.empty_cache()
+        out["other_workloads"] = others
+
+    # ---------------------------------------------------------------- CPU baseline (oracle)
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = oracle.default_threads()
+        f = workloads.to_f64(inp)
+        t0 = time.perf_counter()
+        oracle.selective_scan(f["x"], f["delta"], f["A"], f["B"], f["C"], Dskip=f["D"], z=f["z"],
+                              delta_bias=f["delta_bias"], delta_softplus=True, threads=threads)
+        sec = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": round(tc / sec / 1e9, 5), "unit": "Gtoken*channel/s", "cores": threads,
+                               "kind": "oracle",
+                               "sample": "the whole workload (8 x 2048 x 1536 token-channels, 16 states), fp64, "
+                                         "%.1f s wall" % sec}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

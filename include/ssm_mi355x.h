@@ -1,0 +1,167 @@
+/*
+ * ssm_mi355x.h -- C ABI of the MI355X (gfx950) selective state-space scan library.
+ *
+ * The library computes the core of Mamba's selective SSM layer (S6) and its
+ * Mamba-2 SSD form.  Sources, cited by page title and section:
+ *   [guide]  "Mamba / State Space Models complete guide" (youngju.dev),
+ *            sec. 2 (continuous SSM, ZOH discretization, convolution kernel),
+ *            sec. 5 (selective scan listing, Mamba block), sec. 6 (Mamba 2).
+ *   [expl]   "Paper explainer: Mamba (2312.00752)" (0h-n0.github.io),
+ *            "Technical details": ZOH, selection mechanism, hardware-aware scan.
+ *   [ssm]    "SSM & Mamba" (disassemble-channel.com): "Discretization / ZOH",
+ *            "Equivalence with convolution", "Mamba: selective SSM".
+ *   [ssd]    "Mamba-2 / Structured State Space Duality" (abeam guide):
+ *            "Basic idea", "Linear and quadratic forms", block design.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensors are dense, contiguous, row-major, in the order written next
+ *    to each argument.  Every pointer is a DEVICE pointer on the current HIP
+ *    device, aligned to its element size.  The caller owns every buffer; the
+ *    library keeps no pointer after the call returns and never frees one.
+ *  - "act" tensors (x, B, C, z, y) use the dtype `act_dtype`; dt/delta uses
+ *    `delta_dtype`.  A, Dskip, biases, h0 and h_final are always fp32.  The
+ *    recurrent state is always fp32.  bf16 outputs are rounded to nearest even.
+ *  - Optional pointers may be NULL (stated per argument).
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *    null stream).  Results are valid once the stream has synchronised.
+ *  - Argument errors are detected on the host before anything is enqueued
+ *    and reported through the return value (an ssm_status); nothing is
+ *    launched then.  A HIP runtime failure returns SSM_ERR_HIP.  A message
+ *    with detail for the last failure of the calling thread is available from
+ *    ssm_last_error().
+ *  - Outputs must not alias inputs, except that h_final may equal h0 (the
+ *    state is read before it is overwritten, which gives an in-place
+ *    single-token decode step when seqlen == 1).
+ *  - workspace: device scratch of at least the size the matching
+ *    *_workspace_bytes() query returns for the same shapes, or NULL, in which
+ *    case the library takes stream-ordered memory (hipMallocAsync) for the
+ *    duration of the call.  Calls that share a workspace must be ordered on
+ *    one stream.
+ */
+#ifndef SSM_MI355X_H
+#define SSM_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types of act / delta tensors */
+enum ssm_dtype { SSM_F32 = 0, SSM_BF16 = 1 };
+
+/* return codes */
+enum ssm_status {
+  SSM_OK = 0,
+  SSM_ERR_NULL = 1,         /* a required pointer is NULL */
+  SSM_ERR_SHAPE = 2,        /* a size is negative, inconsistent or overflows 64-bit indexing */
+  SSM_ERR_DTYPE = 3,        /* unknown dtype code */
+  SSM_ERR_UNSUPPORTED = 4,  /* valid but not implemented here (e.g. dstate > 128) */
+  SSM_ERR_WORKSPACE = 5,    /* workspace given but smaller than required */
+  SSM_ERR_HIP = 6,          /* a HIP runtime call failed (see ssm_last_error) */
+  SSM_ERR_ALIGNMENT = 7     /* a pointer is not aligned to its element size */
+};
+
+/*
+ * Selective scan forward (S6).  For every batch b and channel d, with state
+ * h (dstate entries, fp32) starting at h0[b,d,:] (zeros if h0 == NULL):
+ *
+ *   v    = delta[b,t,d] + (delta_bias ? delta_bias[d] : 0)
+ *   dt   = delta_softplus ? log(1 + e^v) : v              ([expl] selection mechanism)
+ *   h_n  = exp(dt*A[d,n]) * h_n + (exp(dt*A[d,n]) - 1)/A[d,n] * B[b,t,n] * x[b,t,d]
+ *                                                         ([ssm] ZOH for diagonal A;
+ *                                                          the gain is dt when A[d,n] == 0)
+ *   y[b,t,d] = (sum_n C[b,t,n]*h_n + Dskip[d]*x[b,t,d]) * silu(z[b,t,d])
+ *                                                         ([guide] sec. 5: skip, then gate)
+ * for t = 0..seqlen-1, so y at token t includes token t's own input
+ * ([guide] sec. 2: y[0] = C Bbar u[0]).  h_final[b,d,:] = state after the
+ * last token.
+ *
+ *   x, delta, z, y : (batch, seqlen, dim)      act / delta / act / act dtype
+ *   A              : (dim, dstate) fp32        real diagonal entries (normally < 0)
+ *   B, C           : (batch, seqlen, dstate)   act dtype, shared by all channels
+ *   Dskip          : (dim) fp32 or NULL (no skip term)
+ *   z              : NULL for no gate
+ *   delta_bias     : (dim) fp32 or NULL
+ *   delta_softplus : 0 or 1
+ *   h0             : (batch, dim, dstate) fp32 or NULL (zeros)
+ *   y              : required output
+ *   h_final        : (batch, dim, dstate) fp32 output or NULL
+ *   dstate         : 1..128
+ * Long sequences with few (batch, channel) slices are split into time chunks
+ * whose carries are combined on the device (needs workspace).
+ */
+int ssm_scan_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                 const float* Dskip, const void* z, const float* delta_bias, int delta_softplus,
+                 const float* h0, void* y, float* h_final,
+                 int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                 int act_dtype, int delta_dtype,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Final state only: the same recurrence as ssm_scan_fwd, writing h_final
+ * (required) and no y; C, Dskip and z are not needed.  ([guide] sec. 2/4:
+ * recurrent inference keeps only the fixed-size state.)
+ */
+int ssm_scan_final_state(const void* x, const void* delta, const float* A, const void* B,
+                         const float* delta_bias, int delta_softplus, const float* h0,
+                         float* h_final,
+                         int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                         int act_dtype, int delta_dtype,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace needed by ssm_scan_fwd / ssm_scan_final_state for these shapes
+ * (0 when the unsplit path is taken).  Depends on the current device. */
+size_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                                int final_state_only);
+
+/*
+ * Mamba-2 SSD forward ([ssd] "Basic idea" and "Linear and quadratic forms";
+ * [guide] sec. 6: one scalar A per head, dt per head, B/C of width dstate
+ * shared by the heads of a group).  For batch b, head h (group
+ * g = h / (nheads/ngroups)), head channel p and state n, with state
+ * S[p][n] starting at h0[b,h,p,n] (zeros if NULL):
+ *
+ *   dt      = softplus?(dt[b,t,h] + dt_bias[h])
+ *   S[p][n] = exp(dt*A[h]) S[p][n] + (exp(dt*A[h]) - 1)/A[h] * B[b,t,g,n] * x[b,t,h,p]
+ *   y[b,t,h,p] = (sum_n C[b,t,g,n] S[p][n] + Dskip[h] x[b,t,h,p]) * silu(z[b,t,h,p])
+ *
+ * computed in chunks of `chunk_size` tokens: within a chunk as a causal,
+ * decayed matrix product on the matrix cores, across chunks by passing the
+ * state ([ssd] block decomposition).
+ *
+ *   x, z, y : (batch, seqlen, nheads, headdim)  act dtype (z NULL for no gate)
+ *   dt      : (batch, seqlen, nheads)           delta dtype
+ *   A       : (nheads) fp32, must be finite
+ *   B, C    : (batch, seqlen, ngroups, dstate)  act dtype
+ *   Dskip, dt_bias : (nheads) fp32 or NULL
+ *   h0, h_final    : (batch, nheads, headdim, dstate) fp32 or NULL
+ * Supported: act_dtype SSM_BF16, headdim == 64, dstate in {64, 128},
+ * chunk_size in {64, 128, 256}, nheads % ngroups == 0.  Other valid shapes
+ * return SSM_ERR_UNSUPPORTED.
+ */
+int ssd_chunk_scan_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C,
+                       const float* Dskip, const void* z, const float* dt_bias, int dt_softplus,
+                       const float* h0, void* y, float* h_final,
+                       int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                       int64_t ngroups, int64_t dstate, int64_t chunk_size,
+                       int act_dtype, int dt_dtype,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace needed by ssd_chunk_scan_fwd for these shapes. */
+size_t ssd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                           int64_t ngroups, int64_t dstate, int64_t chunk_size);
+
+/* Static text for a status code (never NULL). */
+const char* ssm_status_string(int status);
+
+/* Detail for the calling thread's most recent failure ("" if none). */
+const char* ssm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_MI355X_H */

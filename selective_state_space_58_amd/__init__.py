@@ -1,0 +1,18 @@
+"""MI355X-native selective state-space scan (Mamba S6) and its Mamba-2 SSD form.
+
+Thin Python binding over the C ABI in ``include/ssm_mi355x.h`` (library
+``libssm_mi355x.so`` built in-tree by ``build.py``).  The functions carry the
+C names, take torch tensors on the current ROCm device, allocate outputs with
+torch, and pass raw device pointers plus the current HIP stream.  All
+computation happens in the library's HIP kernels; there is no fallback.
+"""
+from ._binding import (  # noqa: F401
+    SSMError,
+    library_path,
+    load_library,
+    ssd_chunk_scan_fwd,
+    ssd_workspace_bytes,
+    ssm_scan_final_state,
+    ssm_scan_fwd,
+    ssm_scan_workspace_bytes,
+)

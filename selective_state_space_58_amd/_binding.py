@@ -1,0 +1,208 @@
+"""ctypes marshalling for libssm_mi355x.so (argument checks and pointers only)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libssm_mi355x.so")
+_lock = threading.Lock()
+_lib = None
+
+SSM_F32, SSM_BF16 = 0, 1
+_DT = {torch.float32: SSM_F32, torch.bfloat16: SSM_BF16}
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I = ctypes.c_int
+_SZ = ctypes.c_size_t
+
+
+class SSMError(RuntimeError):
+    """A non-zero status from the library (message includes its detail text)."""
+
+    def __init__(self, fn: str, status: int, detail: str):
+        self.status = status
+        super().__init__("%s failed: status %d (%s)" % (fn, status, detail))
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load the HIP library; raises if it has not been built (no fallback exists)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError("libssm_mi355x.so is not built; run __graft_entry__.build() or "
+                               "python selective_state_space_58_amd/build.py")
+        lib = ctypes.CDLL(_LIB_PATH)
+        lib.ssm_scan_fwd.argtypes = [_P] * 8 + [_I, _P, _P, _P] + [_I64] * 4 + [_I, _I, _P, _SZ, _P]
+        lib.ssm_scan_fwd.restype = _I
+        lib.ssm_scan_final_state.argtypes = [_P] * 5 + [_I, _P, _P] + [_I64] * 4 + [_I, _I, _P, _SZ, _P]
+        lib.ssm_scan_final_state.restype = _I
+        lib.ssd_chunk_scan_fwd.argtypes = [_P] * 8 + [_I, _P, _P, _P] + [_I64] * 7 + [_I, _I, _P, _SZ, _P]
+        lib.ssd_chunk_scan_fwd.restype = _I
+        lib.ssm_scan_workspace_bytes.argtypes = [_I64] * 4 + [_I]
+        lib.ssm_scan_workspace_bytes.restype = _SZ
+        lib.ssd_workspace_bytes.argtypes = [_I64] * 7
+        lib.ssd_workspace_bytes.restype = _SZ
+        lib.ssm_status_string.argtypes = [_I]
+        lib.ssm_status_string.restype = ctypes.c_char_p
+        lib.ssm_last_error.argtypes = []
+        lib.ssm_last_error.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+def _check(lib, fn, rc):
+    if rc != 0:
+        detail = lib.ssm_last_error().decode() or lib.ssm_status_string(rc).decode()
+        raise SSMError(fn, rc, detail)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, dtype=None, shape=None, device=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    return t
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _act_code(t, name):
+    if t.dtype not in _DT:
+        raise TypeError("%s must be float32 or bfloat16" % name)
+    return _DT[t.dtype]
+
+
+def ssm_scan_workspace_bytes(batch, seqlen, dim, dstate, final_state_only=False) -> int:
+    return int(load_library().ssm_scan_workspace_bytes(batch, seqlen, dim, dstate, int(final_state_only)))
+
+
+def ssd_workspace_bytes(batch, seqlen, nheads, headdim, ngroups, dstate, chunk_size) -> int:
+    return int(load_library().ssd_workspace_bytes(batch, seqlen, nheads, headdim, ngroups, dstate, chunk_size))
+
+
+def ssm_scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False, h0=None,
+                 return_final_state=False, y=None, h_final=None, workspace=None):
+    """Selective scan forward.  x, delta, z: (batch, seqlen, dim); A: (dim, dstate) fp32;
+    B, C: (batch, seqlen, dstate); D, delta_bias: (dim) fp32; h0: (batch, dim, dstate) fp32.
+    Returns y, or (y, h_final) with return_final_state."""
+    lib = load_library()
+    dev = x.device
+    _need(x, "x", device=dev)
+    batch, seqlen, dim = x.shape
+    act = _act_code(x, "x")
+    _need(delta, "delta", shape=x.shape, device=dev)
+    dcode = _act_code(delta, "delta")
+    _need(A, "A", torch.float32, device=dev)
+    if A.dim() != 2 or A.shape[0] != dim:
+        raise ValueError("A must be (dim, dstate)")
+    dstate = A.shape[1]
+    _need(B, "B", x.dtype, (batch, seqlen, dstate), dev)
+    _need(C, "C", x.dtype, (batch, seqlen, dstate), dev)
+    _need(D, "D", torch.float32, (dim,), dev)
+    _need(z, "z", x.dtype, x.shape, dev)
+    _need(delta_bias, "delta_bias", torch.float32, (dim,), dev)
+    _need(h0, "h0", torch.float32, (batch, dim, dstate), dev)
+    if y is None:
+        y = torch.empty_like(x)
+    _need(y, "y", x.dtype, x.shape, dev)
+    if return_final_state and h_final is None:
+        h_final = torch.empty((batch, dim, dstate), dtype=torch.float32, device=dev)
+    _need(h_final, "h_final", torch.float32, (batch, dim, dstate), dev)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib.ssm_scan_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                          int(bool(delta_softplus)), _ptr(h0), _ptr(y), _ptr(h_final),
+                          batch, seqlen, dim, dstate, act, dcode, _ptr(workspace), wsb, _stream(dev))
+    _check(lib, "ssm_scan_fwd", rc)
+    return (y, h_final) if (return_final_state or h_final is not None) else y
+
+
+def ssm_scan_final_state(x, delta, A, B, delta_bias=None, delta_softplus=False, h0=None, h_final=None,
+                         workspace=None):
+    """Final state h_L (batch, dim, dstate) fp32 of the selective scan, without y."""
+    lib = load_library()
+    dev = x.device
+    _need(x, "x", device=dev)
+    batch, seqlen, dim = x.shape
+    act = _act_code(x, "x")
+    _need(delta, "delta", shape=x.shape, device=dev)
+    dcode = _act_code(delta, "delta")
+    _need(A, "A", torch.float32, device=dev)
+    if A.dim() != 2 or A.shape[0] != dim:
+        raise ValueError("A must be (dim, dstate)")
+    dstate = A.shape[1]
+    _need(B, "B", x.dtype, (batch, seqlen, dstate), dev)
+    _need(delta_bias, "delta_bias", torch.float32, (dim,), dev)
+    _need(h0, "h0", torch.float32, (batch, dim, dstate), dev)
+    if h_final is None:
+        h_final = torch.empty((batch, dim, dstate), dtype=torch.float32, device=dev)
+    _need(h_final, "h_final", torch.float32, (batch, dim, dstate), dev)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib.ssm_scan_final_state(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(delta_bias),
+                                  int(bool(delta_softplus)), _ptr(h0), _ptr(h_final),
+                                  batch, seqlen, dim, dstate, act, dcode, _ptr(workspace), wsb, _stream(dev))
+    _check(lib, "ssm_scan_final_state", rc)
+    return h_final
+
+
+def ssd_chunk_scan_fwd(x, dt, A, B, C, chunk_size=256, D=None, z=None, dt_bias=None, dt_softplus=False,
+                       h0=None, return_final_state=False, y=None, h_final=None, workspace=None):
+    """Mamba-2 SSD forward.  x, z: (batch, seqlen, nheads, headdim); dt: (batch, seqlen, nheads);
+    A, D, dt_bias: (nheads) fp32; B, C: (batch, seqlen, ngroups, dstate);
+    h0: (batch, nheads, headdim, dstate) fp32.  Returns y, or (y, h_final)."""
+    lib = load_library()
+    dev = x.device
+    _need(x, "x", device=dev)
+    batch, seqlen, nheads, headdim = x.shape
+    act = _act_code(x, "x")
+    _need(dt, "dt", shape=(batch, seqlen, nheads), device=dev)
+    dcode = _act_code(dt, "dt")
+    _need(A, "A", torch.float32, (nheads,), dev)
+    _need(B, "B", x.dtype, device=dev)
+    if B.dim() != 4 or B.shape[:2] != (batch, seqlen):
+        raise ValueError("B must be (batch, seqlen, ngroups, dstate)")
+    ngroups, dstate = B.shape[2], B.shape[3]
+    _need(C, "C", x.dtype, B.shape, dev)
+    _need(D, "D", torch.float32, (nheads,), dev)
+    _need(z, "z", x.dtype, x.shape, dev)
+    _need(dt_bias, "dt_bias", torch.float32, (nheads,), dev)
+    _need(h0, "h0", torch.float32, (batch, nheads, headdim, dstate), dev)
+    if y is None:
+        y = torch.empty_like(x)
+    _need(y, "y", x.dtype, x.shape, dev)
+    if return_final_state and h_final is None:
+        h_final = torch.empty((batch, nheads, headdim, dstate), dtype=torch.float32, device=dev)
+    _need(h_final, "h_final", torch.float32, (batch, nheads, headdim, dstate), dev)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib.ssd_chunk_scan_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
+                                int(bool(dt_softplus)), _ptr(h0), _ptr(y), _ptr(h_final),
+                                batch, seqlen, nheads, headdim, ngroups, dstate, chunk_size, act, dcode,
+                                _ptr(workspace), wsb, _stream(dev))
+    _check(lib, "ssd_chunk_scan_fwd", rc)
+    return (y, h_final) if (return_final_state or h_final is not None) else y

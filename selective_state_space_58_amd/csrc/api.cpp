@@ -1,0 +1,247 @@
+// C ABI entry points of the MI355X selective-scan library: argument
+// validation (host only, before any HIP call), planning, workspace handling
+// and dispatch to the HIP kernels.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <limits>
+#include <string>
+
+#include "../../include/ssm_mi355x.h"
+#include "ssm_internal.h"
+
+namespace ssm {
+
+namespace {
+thread_local std::string g_last_error;
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > std::numeric_limits<int64_t>::max() / 4 / a) return false;  // keep byte offsets in range
+  *out = a * b;
+  return true;
+}
+
+bool elems_ok(std::initializer_list<int64_t> dims) {
+  int64_t acc = 1;
+  for (int64_t d : dims)
+    if (!mul_ok(acc, d, &acc)) return false;
+  return true;
+}
+
+bool aligned(const void* p, size_t a) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t dsize(int dt) { return dt == SSM_BF16 ? 2 : 4; }
+
+// Stream-ordered scratch for calls that pass no workspace.
+struct Scratch {
+  void* ptr = nullptr;
+  hipStream_t st = nullptr;
+  ~Scratch() {
+    if (ptr != nullptr) (void)hipFreeAsync(ptr, st);
+  }
+};
+
+int get_workspace(void* user, size_t user_bytes, size_t need, hipStream_t st, Scratch* own, void** out) {
+  *out = nullptr;
+  if (need == 0) return SSM_OK;
+  if (user != nullptr) {
+    if (user_bytes < need)
+      return fail(SSM_ERR_WORKSPACE, "workspace of " + std::to_string(user_bytes) + " bytes, need " +
+                                         std::to_string(need));
+    if (!aligned(user, 256)) return fail(SSM_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
+    *out = user;
+    return SSM_OK;
+  }
+  hipError_t e = hipMallocAsync(&own->ptr, need, st);
+  if (e != hipSuccess) return fail(SSM_ERR_HIP, std::string("hipMallocAsync: ") + hipGetErrorString(e));
+  own->st = st;
+  *out = own->ptr;
+  return SSM_OK;
+}
+
+int validate_scan(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                  const void* y_or_hf, bool final_only, const float* Dskip, const void* z, const float* bias,
+                  const float* h0, const float* hf, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                  int act_dtype, int delta_dtype, int softplus) {
+  if (batch < 0 || seqlen < 0 || dim < 0 || dstate < 0) return fail(SSM_ERR_SHAPE, "negative size");
+  // Tensors with no elements may be NULL (an empty framework tensor has no storage).
+  const bool has_tok = batch > 0 && seqlen > 0 && dim > 0;
+  const bool has_bc = batch > 0 && seqlen > 0;
+  if ((has_tok && (x == nullptr || delta == nullptr)) || (dim > 0 && A == nullptr) ||
+      (has_bc && (B == nullptr || (!final_only && C == nullptr))))
+    return fail(SSM_ERR_NULL, "x, delta, A, B and C (forward) are required");
+  if (final_only ? (batch > 0 && dim > 0 && y_or_hf == nullptr) : (has_tok && y_or_hf == nullptr))
+    return fail(SSM_ERR_NULL, final_only ? "h_final is required" : "y is required");
+  if (dstate == 0) return fail(SSM_ERR_SHAPE, "dstate must be >= 1");
+  if (act_dtype != SSM_F32 && act_dtype != SSM_BF16) return fail(SSM_ERR_DTYPE, "act_dtype must be SSM_F32 or SSM_BF16");
+  if (delta_dtype != SSM_F32 && delta_dtype != SSM_BF16)
+    return fail(SSM_ERR_DTYPE, "delta_dtype must be SSM_F32 or SSM_BF16");
+  if (softplus != 0 && softplus != 1) return fail(SSM_ERR_SHAPE, "delta_softplus must be 0 or 1");
+  if (!elems_ok({batch, seqlen, dim}) || !elems_ok({batch, seqlen, dstate}) || !elems_ok({batch, dim, dstate}) ||
+      !elems_ok({dim, dstate}))
+    return fail(SSM_ERR_SHAPE, "sizes overflow 64-bit indexing");
+  if (dstate > 128) return fail(SSM_ERR_UNSUPPORTED, "dstate > 128 is not supported");
+  const size_t as = dsize(act_dtype), ds = dsize(delta_dtype);
+  if (!aligned(x, as) || !aligned(B, as) || !aligned(C, as) || !aligned(z, as) || !aligned(y_or_hf, final_only ? 4 : as) ||
+      !aligned(delta, ds) || !aligned(A, 4) || !aligned(Dskip, 4) || !aligned(bias, 4) || !aligned(h0, 4) ||
+      !aligned(hf, 4))
+    return fail(SSM_ERR_ALIGNMENT, "a pointer is not aligned to its element size");
+  return SSM_OK;
+}
+
+int cached_cus = -1;
+
+}  // namespace
+
+int fail(int status, const std::string& msg) {
+  g_last_error = msg;
+  return status;
+}
+
+int device_cu_count() {
+  if (cached_cus > 0) return cached_cus;
+  int dev = 0;
+  hipDeviceProp_t prop;
+  if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess &&
+      prop.multiProcessorCount > 0) {
+    cached_cus = prop.multiProcessorCount;
+    return cached_cus;
+  }
+  (void)hipGetLastError();
+  return 256;  // MI355X
+}
+
+}  // namespace ssm
+
+using namespace ssm;
+
+extern "C" {
+
+const char* ssm_status_string(int status) {
+  switch (status) {
+    case SSM_OK: return "ok";
+    case SSM_ERR_NULL: return "required pointer is NULL";
+    case SSM_ERR_SHAPE: return "invalid or inconsistent size";
+    case SSM_ERR_DTYPE: return "unknown dtype";
+    case SSM_ERR_UNSUPPORTED: return "unsupported configuration";
+    case SSM_ERR_WORKSPACE: return "workspace too small";
+    case SSM_ERR_HIP: return "HIP runtime error";
+    case SSM_ERR_ALIGNMENT: return "misaligned pointer";
+    default: return "unknown status";
+  }
+}
+
+const char* ssm_last_error(void) { return g_last_error.c_str(); }
+
+size_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int final_state_only) {
+  if (batch <= 0 || seqlen <= 0 || dim <= 0 || dstate <= 0 || dstate > 128) return 0;
+  return plan_scan(batch, seqlen, dim, dstate, final_state_only != 0, device_cu_count()).ws_bytes;
+}
+
+static int scan_common(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                       const float* Dskip, const void* z, const float* delta_bias, int delta_softplus,
+                       const float* h0, void* y, float* h_final, int64_t batch, int64_t seqlen, int64_t dim,
+                       int64_t dstate, int act_dtype, int delta_dtype, void* workspace, size_t workspace_bytes,
+                       void* stream, bool final_only) {
+  g_last_error.clear();
+  int rc = validate_scan(x, delta, A, B, C, final_only ? (const void*)h_final : y, final_only, Dskip, z, delta_bias,
+                         h0, h_final, batch, seqlen, dim, dstate, act_dtype, delta_dtype, delta_softplus);
+  if (rc != SSM_OK) return rc;
+  if (batch == 0 || dim == 0) return SSM_OK;
+  ScanPlan p = plan_scan(batch, seqlen, dim, dstate, final_only, device_cu_count());
+  hipStream_t st = (hipStream_t)stream;
+  Scratch own;
+  void* ws = nullptr;
+  rc = get_workspace(workspace, workspace_bytes, seqlen > 0 ? p.ws_bytes : 0, st, &own, &ws);
+  if (rc != SSM_OK) return rc;
+  ScanArgs a{};
+  a.x = x; a.delta = delta; a.A = A; a.B = B; a.C = final_only ? nullptr : C;
+  a.Dskip = final_only ? nullptr : Dskip;
+  a.z = final_only ? nullptr : z;
+  a.delta_bias = delta_bias; a.h0 = h0;
+  a.y = final_only ? nullptr : y;
+  a.h_final = h_final;
+  a.batch = batch; a.seqlen = seqlen; a.dim = dim; a.dstate = dstate;
+  a.softplus = delta_softplus;
+  a.act_bf16 = act_dtype == SSM_BF16;
+  a.delta_bf16 = delta_dtype == SSM_BF16;
+  if (ws != nullptr) {
+    const size_t st_bytes = (size_t)p.nchunks * (size_t)(batch * dim * dstate) * sizeof(float);
+    a.ws_state = (float*)ws;
+    a.ws_dsum = (float*)((char*)ws + ((st_bytes + 255) / 256) * 256);
+  }
+  return launch_scan(a, p, final_only, stream);
+}
+
+int ssm_scan_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                 const float* Dskip, const void* z, const float* delta_bias, int delta_softplus,
+                 const float* h0, void* y, float* h_final, int64_t batch, int64_t seqlen, int64_t dim,
+                 int64_t dstate, int act_dtype, int delta_dtype, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  return scan_common(x, delta, A, B, C, Dskip, z, delta_bias, delta_softplus, h0, y, h_final, batch, seqlen, dim,
+                     dstate, act_dtype, delta_dtype, workspace, workspace_bytes, stream, false);
+}
+
+int ssm_scan_final_state(const void* x, const void* delta, const float* A, const void* B, const float* delta_bias,
+                         int delta_softplus, const float* h0, float* h_final, int64_t batch, int64_t seqlen,
+                         int64_t dim, int64_t dstate, int act_dtype, int delta_dtype, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return scan_common(x, delta, A, B, nullptr, nullptr, nullptr, delta_bias, delta_softplus, h0, nullptr, h_final,
+                     batch, seqlen, dim, dstate, act_dtype, delta_dtype, workspace, workspace_bytes, stream, true);
+}
+
+size_t ssd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t ngroups,
+                           int64_t dstate, int64_t chunk_size) {
+  if (batch <= 0 || seqlen <= 0 || nheads <= 0 || headdim <= 0 || ngroups <= 0 || dstate <= 0 || chunk_size <= 0)
+    return 0;
+  return ssd_ws_bytes(batch, seqlen, nheads, headdim, ngroups, dstate, chunk_size);
+}
+
+int ssd_chunk_scan_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C,
+                       const float* Dskip, const void* z, const float* dt_bias, int dt_softplus, const float* h0,
+                       void* y, float* h_final, int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                       int64_t ngroups, int64_t dstate, int64_t chunk_size, int act_dtype, int dt_dtype,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (x == nullptr || dt == nullptr || A == nullptr || B == nullptr || C == nullptr || y == nullptr)
+    return fail(SSM_ERR_NULL, "x, dt, A, B, C and y are required");
+  if (batch < 0 || seqlen < 0 || nheads < 0 || headdim < 0 || ngroups < 0 || dstate < 0 || chunk_size < 0)
+    return fail(SSM_ERR_SHAPE, "negative size");
+  if (nheads == 0 || headdim == 0 || ngroups == 0 || dstate == 0 || chunk_size == 0)
+    return fail(SSM_ERR_SHAPE, "nheads, headdim, ngroups, dstate and chunk_size must be >= 1");
+  if (nheads % ngroups != 0) return fail(SSM_ERR_SHAPE, "nheads must be a multiple of ngroups");
+  if (act_dtype != SSM_F32 && act_dtype != SSM_BF16) return fail(SSM_ERR_DTYPE, "act_dtype must be SSM_F32 or SSM_BF16");
+  if (dt_dtype != SSM_F32 && dt_dtype != SSM_BF16) return fail(SSM_ERR_DTYPE, "dt_dtype must be SSM_F32 or SSM_BF16");
+  if (dt_softplus != 0 && dt_softplus != 1) return fail(SSM_ERR_SHAPE, "dt_softplus must be 0 or 1");
+  if (!elems_ok({batch, seqlen, nheads, headdim}) || !elems_ok({batch, seqlen, ngroups, dstate}) ||
+      !elems_ok({batch, nheads, headdim, dstate}))
+    return fail(SSM_ERR_SHAPE, "sizes overflow 64-bit indexing");
+  if (act_dtype != SSM_BF16) return fail(SSM_ERR_UNSUPPORTED, "SSD supports bf16 activations only");
+  if (headdim != 64) return fail(SSM_ERR_UNSUPPORTED, "SSD supports headdim 64");
+  if (dstate != 64 && dstate != 128) return fail(SSM_ERR_UNSUPPORTED, "SSD supports dstate 64 or 128");
+  if (chunk_size != 64 && chunk_size != 128 && chunk_size != 256)
+    return fail(SSM_ERR_UNSUPPORTED, "SSD supports chunk_size 64, 128 or 256");
+  const size_t ds = dsize(dt_dtype);
+  if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(z, 16) || !aligned(y, 16) ||
+      !aligned(dt, ds) || !aligned(A, 4) || !aligned(Dskip, 4) || !aligned(dt_bias, 4) || !aligned(h0, 16) ||
+      !aligned(h_final, 16))
+    return fail(SSM_ERR_ALIGNMENT, "SSD needs 16-byte aligned x/B/C/z/y/h0/h_final and element-aligned dt");
+  if (batch == 0) return SSM_OK;
+  hipStream_t st = (hipStream_t)stream;
+  Scratch own;
+  void* ws = nullptr;
+  const size_t need = ssd_ws_bytes(batch, seqlen, nheads, headdim, ngroups, dstate, chunk_size);
+  int rc = get_workspace(workspace, workspace_bytes, seqlen > 0 ? need : 0, st, &own, &ws);
+  if (rc != SSM_OK) return rc;
+  SsdArgs a{};
+  a.x = x; a.dt = dt; a.A = A; a.B = B; a.C = C; a.Dskip = Dskip; a.z = z; a.dt_bias = dt_bias;
+  a.h0 = h0; a.y = y; a.h_final = h_final;
+  a.batch = batch; a.seqlen = seqlen; a.nheads = nheads; a.headdim = headdim; a.ngroups = ngroups;
+  a.dstate = dstate; a.chunk = chunk_size; a.softplus = dt_softplus; a.dt_bf16 = dt_dtype == SSM_BF16;
+  a.ws = ws;
+  return launch_ssd(a, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,123 @@
+// Selective scan: host-side planning and the phase sequence (chunk states,
+// carry, output pass), plus the two small helper kernels.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "ssm_internal.h"
+
+namespace ssm {
+
+hipError_t launch_scan_x0_d0(int S, int mode, const ScanArgs& a, dim3 grid, int64_t gpb, hipStream_t st);
+hipError_t launch_scan_x0_d1(int S, int mode, const ScanArgs& a, dim3 grid, int64_t gpb, hipStream_t st);
+hipError_t launch_scan_x1_d0(int S, int mode, const ScanArgs& a, dim3 grid, int64_t gpb, hipStream_t st);
+hipError_t launch_scan_x1_d1(int S, int mode, const ScanArgs& a, dim3 grid, int64_t gpb, hipStream_t st);
+
+namespace {
+
+// Combine chunk aggregates in order ("SSM & Mamba": the recurrence composes,
+// h_in(c+1) = exp(a * sum of dt over chunk c) * h_in(c) + h_loc(c)).
+// Slot c of ws_state receives the state entering chunk c.
+__global__ __launch_bounds__(256) void carry_kernel(ScanArgs a, int64_t nlocal, int write_final) {
+  const int64_t total = a.batch * a.dim * a.dstate;
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int64_t n = i % a.dstate, bd = i / a.dstate, d = bd % a.dim;
+  const float an = a.A[d * a.dstate + n];
+  float h = a.h0 != nullptr ? a.h0[i] : 0.f;
+  for (int64_t c = 0; c < nlocal; ++c) {
+    const float loc = a.ws_state[c * total + i];
+    a.ws_state[c * total + i] = h;
+    h = expf(an * a.ws_dsum[c * a.batch * a.dim + bd]) * h + loc;
+  }
+  if (nlocal < a.nchunks) a.ws_state[nlocal * total + i] = h;
+  if (write_final && a.h_final != nullptr) a.h_final[i] = h;
+}
+
+// seqlen == 0: the state passes through unchanged.
+__global__ __launch_bounds__(256) void copy_state_kernel(const float* h0, float* out, int64_t total) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i < total) out[i] = h0 != nullptr ? h0[i] : 0.f;
+}
+
+hipError_t launch_mode(int S, int mode, const ScanArgs& a, dim3 grid, int64_t gpb, hipStream_t st) {
+  if (a.act_bf16 && a.delta_bf16) return launch_scan_x1_d1(S, mode, a, grid, gpb, st);
+  if (a.act_bf16) return launch_scan_x1_d0(S, mode, a, grid, gpb, st);
+  if (a.delta_bf16) return launch_scan_x0_d1(S, mode, a, grid, gpb, st);
+  return launch_scan_x0_d0(S, mode, a, grid, gpb, st);
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+constexpr int kTile = 32;  // tokens per LDS tile (TileShape::T)
+
+}  // namespace
+
+ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, bool final_only, int num_cus) {
+  (void)final_only;
+  ScanPlan p{};
+  int S = 1;
+  while (S * kRows < dstate) S *= 2;
+  p.S = S;
+  p.T = kTile;
+  const int64_t waves = batch * ceil_div(dim, kChPerWave);
+  const int64_t simds = 4LL * (num_cus > 0 ? num_cus : 256);
+  int64_t nch = 1;
+  // Split time only when fewer than half of the SIMDs would get a wave: the
+  // split reruns the recurrence (pass 1), so it pays only when it fills the chip.
+  if (waves > 0 && waves * 2 < simds && seqlen > 0) {
+    nch = ceil_div(2 * simds, waves);
+    const int64_t min_len = 8LL * p.T;
+    const int64_t max_ch = std::max<int64_t>(1, seqlen / min_len);
+    nch = std::min(nch, max_ch);
+  }
+  const int64_t clen = ceil_div(ceil_div(std::max<int64_t>(seqlen, 1), nch), p.T) * p.T;
+  nch = ceil_div(std::max<int64_t>(seqlen, 1), clen);
+  p.nchunks = nch;
+  p.chunk_len = clen;
+  p.ws_bytes = 0;
+  if (nch > 1) {
+    const size_t st = (size_t)nch * (size_t)(batch * dim * dstate) * sizeof(float);
+    const size_t ds = (size_t)nch * (size_t)(batch * dim) * sizeof(float);
+    p.ws_bytes = ((st + 255) / 256) * 256 + ds;
+  }
+  return p;
+}
+
+int launch_scan(const ScanArgs& a0, const ScanPlan& p, bool final_only, void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  ScanArgs a = a0;
+  a.chunk_len = p.chunk_len;
+  a.nchunks = p.nchunks;
+  const int64_t total = a.batch * a.dim * a.dstate;
+  if (a.seqlen == 0) {
+    if (a.h_final != nullptr && total > 0) {
+      copy_state_kernel<<<dim3((unsigned)ceil_div(total, 256)), 256, 0, st>>>(a.h0, a.h_final, total);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return fail(6, std::string("copy_state_kernel launch: ") + hipGetErrorString(e));
+    }
+    return 0;
+  }
+  const int64_t gpb = ceil_div(a.dim, kChPerWave);
+  const int64_t nb = a.batch * gpb;
+  if (nb > 0x7fffffffLL || p.nchunks > 65535) return fail(4, "grid too large");
+  hipError_t e = hipSuccess;
+  if (p.nchunks == 1) {
+    e = launch_mode(p.S, final_only ? kModeState : kModeFull, a, dim3((unsigned)nb, 1), gpb, st);
+    if (e != hipSuccess) return fail(6, std::string("scan kernel launch: ") + hipGetErrorString(e));
+    return 0;
+  }
+  const int64_t nlocal = final_only ? p.nchunks : p.nchunks - 1;
+  e = launch_mode(p.S, kModeState, a, dim3((unsigned)nb, (unsigned)nlocal), gpb, st);
+  if (e != hipSuccess) return fail(6, std::string("chunk-state kernel launch: ") + hipGetErrorString(e));
+  carry_kernel<<<dim3((unsigned)ceil_div(total, 256)), 256, 0, st>>>(a, nlocal, final_only ? 1 : 0);
+  e = hipGetLastError();
+  if (e != hipSuccess) return fail(6, std::string("carry kernel launch: ") + hipGetErrorString(e));
+  if (!final_only) {
+    e = launch_mode(p.S, kModeFull, a, dim3((unsigned)nb, (unsigned)p.nchunks), gpb, st);
+    if (e != hipSuccess) return fail(6, std::string("scan kernel launch: ") + hipGetErrorString(e));
+  }
+  return 0;
+}
+
+}  // namespace ssm

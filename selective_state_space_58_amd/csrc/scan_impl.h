@@ -1,0 +1,377 @@
+// Selective scan (Mamba S6) kernel template for MI355X / gfx950.
+//
+// Computes, per (batch b, channel d) slice and per state n, with exact ZOH for a
+// diagonal A ("SSM & Mamba", Discretization/ZOH; "Paper explainer: Mamba",
+// Technical details):
+//   dt_t   = softplus(delta_t + bias_d)  (or delta_t + bias_d)
+//   h_t,n  = exp(dt_t a_dn) h_{t-1,n} + (exp(dt_t a_dn) - 1)/a_dn * B_t,n x_t
+//   y_t    = (sum_n C_t,n h_t,n + Dskip_d x_t) * silu(z_t)
+// ("Mamba / SSM complete guide", sec. 5, selective_scan and the block's gate).
+//
+// Mapping to CDNA4.  One wavefront per workgroup.  The 64 lanes are 4 rows of
+// 16: lane (row r, column c) holds states [r*S, r*S+S) of channel ch0+c in
+// VGPRs for the whole sequence, so the state never touches memory.  The work
+// per (t, d, n) element is 6 VALU ops plus one v_exp_f32; the per-(t, d) work
+// (softplus, silu, skip, bf16 conversion, stores) is done once, not per state.
+//   * Per time tile (T tokens) the wave stages (dt, x) and silu(z) per
+//     (token, channel) and B_t, C_t (fp32) per (token, row) in LDS; the global
+//     loads for the next tile are issued before the current tile is scanned.
+//   * The readout sum over n is split over the 4 rows; every 4 tokens a
+//     reduce-scatter with v_permlane32_swap / v_permlane16_swap (3 swaps + 3
+//     adds) leaves row r with the full sum for token 4k + r, and that lane
+//     applies the skip and gate and stores y for that token.
+//   * Lanes whose channel is past `dim` load from a clamped (valid) address
+//     and compute values that are never stored; a column never mixes with
+//     another column, so nothing leaks.  Tokens past the end of the slice get
+//     dt = 0, which leaves the state unchanged (exp(0) = 1, gain 0).
+//
+// ZOH gain accuracy: (exp(q) - 1)/a loses ~6e-8/|q| relative accuracy for small
+// q = dt*a.  fp32 activations (and any wave that holds an |a| < 1e-2) take an
+// accurate form dt * phi(q), phi(q) = expm1(q)/q by its Taylor series for
+// |q| < 1/4; bf16 activations take the short form, whose error is far below
+// bf16 resolution.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "ssm_internal.h"
+
+namespace ssm {
+namespace scan_dev {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float hw_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
+__device__ __forceinline__ float hw_log2(float v) { return __builtin_amdgcn_logf(v); }
+__device__ __forceinline__ float hw_rcp(float v) { return __builtin_amdgcn_rcpf(v); }
+
+template <bool BF16>
+struct Act;
+template <>
+struct Act<true> {
+  using T = __bf16;
+};
+template <>
+struct Act<false> {
+  using T = float;
+};
+
+// Raw storage bits held in the prefetch registers: bf16 stays 16-bit until it
+// is staged, so the loads of the next tile are not waited on early.
+template <bool BF16>
+struct Raw;
+template <>
+struct Raw<true> {
+  using T = unsigned short;
+  __device__ static float f32(T v) { return __builtin_bit_cast(float, (unsigned)v << 16); }
+};
+template <>
+struct Raw<false> {
+  using T = float;
+  __device__ static float f32(T v) { return v; }
+};
+
+// log(1 + e^v) without overflow.  Short form: log1p(e^-|v|) as log2(1 + e)*ln2,
+// whose absolute error (< 6e-8) is far below bf16 resolution of the output.
+__device__ __forceinline__ float softplus_short(float v) {
+  const float e = hw_exp2(-fabsf(v) * kLog2e);
+  const float r = fmaxf(v, 0.f) + hw_log2(1.f + e) * kLn2;
+  return v > 20.f ? v : r;
+}
+
+// Accurate form: log1p(e^-|v|) by its series when e^-|v| < 1/16.
+__device__ __forceinline__ float softplus_f(float v) {
+  const float e = hw_exp2(-fabsf(v) * kLog2e);
+  const float ser = e * fmaf(e, fmaf(e, fmaf(e, fmaf(e, fmaf(e, -1.f / 6.f, 0.2f), -0.25f), 1.f / 3.f), -0.5f), 1.f);
+  const float lg = hw_log2(1.f + e) * kLn2;
+  const float r = fmaxf(v, 0.f) + (e < 0.0625f ? ser : lg);
+  return v > 20.f ? v : r;
+}
+
+__device__ __forceinline__ float silu_f(float z) { return z * hw_rcp(1.f + hw_exp2(-z * kLog2e)); }
+
+// ZOH gain (e^q - 1)/a with q = dt*a, accurate for small |q| (a == 0 gives dt).
+__device__ __forceinline__ float zoh_gain_accurate(float E, float dt, float a, float ia) {
+  const float q = dt * a;
+  const float phi = fmaf(q, fmaf(q, fmaf(q, fmaf(q, fmaf(q, fmaf(q, 1.f / 5040.f, 1.f / 720.f), 1.f / 120.f),
+                                                 1.f / 24.f), 1.f / 6.f), 0.5f), 1.f);
+  const float g_long = fmaf(E, ia, -ia);
+  return fabsf(q) < 0.25f ? dt * phi : g_long;
+}
+
+__device__ __forceinline__ float bits_f(unsigned u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ unsigned f_bits(float f) { return __builtin_bit_cast(unsigned, f); }
+
+// Lanes are rows of 16 (row = lane / 16).  p_j holds, in every lane, a partial
+// sum for token j of a group of 4.  Returns, in row r, the sum over the 4 rows
+// of the same column of p_r.
+__device__ __forceinline__ float reduce_scatter_rows(float p0, float p1, float p2, float p3) {
+  // permlane32_swap(a, b): a' = [a.lo | b.lo], b' = [a.hi | b.hi]  (halves of 32 lanes)
+  const auto s02 = __builtin_amdgcn_permlane32_swap(f_bits(p0), f_bits(p2), false, false);
+  const float u0 = bits_f(s02[0]) + bits_f(s02[1]);  // rows 0,1: token 0 ; rows 2,3: token 2
+  const auto s13 = __builtin_amdgcn_permlane32_swap(f_bits(p1), f_bits(p3), false, false);
+  const float u1 = bits_f(s13[0]) + bits_f(s13[1]);  // rows 0,1: token 1 ; rows 2,3: token 3
+  // permlane16_swap(a, b): odd rows of a <-> even rows of b
+  const auto s = __builtin_amdgcn_permlane16_swap(f_bits(u0), f_bits(u1), false, false);
+  return bits_f(s[0]) + bits_f(s[1]);                // row r: token r
+}
+
+template <int S>
+struct TileShape {
+  static constexpr int R = kRows;
+  static constexpr int CH = kChPerWave;
+  static constexpr int NP = R * S;                 // padded state count of the wave
+  static constexpr int T = 32;                     // tokens per LDS tile
+  static constexpr int KX = T / R;                 // (token, channel) items per lane per tile
+  static constexpr int KB = T * NP / 64;           // B (and C) items per lane per tile
+};
+
+template <bool XB, bool DB, int S, int MODE, bool ACC>
+__device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t ch0, int64_t chunk,
+                                          const float (&a2)[S], const float (&ia)[S], const float (&av)[S],
+                                          float2* __restrict__ s_dx, float* __restrict__ s_gz,
+                                          float* __restrict__ s_bc) {
+  using TS = TileShape<S>;
+  using TX = typename Act<XB>::T;
+  using TD = typename Act<DB>::T;
+  constexpr int R = TS::R, CH = TS::CH, NP = TS::NP, T = TS::T, KX = TS::KX, KB = TS::KB;
+  constexpr bool FULL = (MODE == kModeFull);
+  const int lane = threadIdx.x;
+  const int r = lane >> 4, c = lane & 15;
+  const int64_t L = a.seqlen, dim = a.dim, N = a.dstate;
+  const int64_t ch = ch0 + c;
+  const bool ch_ok = ch < dim;
+  const int cl = ch_ok ? c : (int)(dim - 1 - ch0);   // clamped column for loads
+  const int64_t t_begin = chunk * a.chunk_len;
+  const int64_t t_stop = (t_begin + a.chunk_len < L) ? t_begin + a.chunk_len : L;
+  const int64_t slice_elems = a.batch * dim * N;
+  const uint32_t dim32 = (uint32_t)dim;
+  const uint32_t n32 = (uint32_t)N;
+
+  using RX = typename Raw<XB>::T;
+  using RD = typename Raw<DB>::T;
+  const RX* __restrict__ gx = (const RX*)a.x;
+  const RD* __restrict__ gd = (const RD*)a.delta;
+  const RX* __restrict__ gz = (const RX*)a.z;
+  const RX* __restrict__ gB = (const RX*)a.B;
+  const RX* __restrict__ gC = (const RX*)a.C;
+  TX* __restrict__ gy = (TX*)a.y;
+
+  // ---- initial state
+  const float* hin = nullptr;
+  if (FULL) hin = (a.nchunks > 1) ? a.ws_state + chunk * slice_elems : a.h0;
+  else hin = (a.nchunks == 1) ? a.h0 : nullptr;
+  float h[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int64_t n = r * S + s;
+    h[s] = (hin != nullptr && ch_ok && n < N) ? hin[(b * dim + ch) * N + n] : 0.f;
+  }
+  const float Dv = (FULL && a.Dskip != nullptr && ch_ok) ? a.Dskip[ch] : 0.f;
+  const float bias = (a.delta_bias != nullptr && ch_ok) ? a.delta_bias[ch] : 0.f;
+  const bool has_z = FULL && a.z != nullptr;
+  const bool dense_bc = (N == NP);
+
+  // ---- register prefetch of one tile.  Row offsets are 32-bit, relative to a
+  // wave-uniform 64-bit base, so loads use the scalar-base addressing form.
+  RX px[KX], pz[KX], pb[KB], pc[KB];
+  RD pd[KX];
+  auto fetch = [&](int64_t t0) {
+    const bool tail = t0 + T > t_stop;
+    const int64_t row0 = (b * L + t0) * dim + ch0;  // uniform
+    const RX* xb = gx + row0;
+    const RD* db = gd + row0;
+    const RX* zb = gz + row0;
+    const int64_t last = t_stop - 1 - t0;            // last valid local token (uniform)
+#pragma unroll
+    for (int k = 0; k < KX; ++k) {
+      int t = R * k + r;
+      if (tail) t = t < last ? t : (int)last;
+      const uint32_t off = (uint32_t)t * dim32 + (uint32_t)cl;
+      px[k] = xb[off];
+      pd[k] = db[off];
+      if (has_z) pz[k] = zb[off];
+    }
+    const int64_t bc0 = (b * L + t0) * N;            // uniform
+    const RX* bb = gB + bc0;
+    const RX* cb = gC + bc0;
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      const int e = lane + 64 * j;
+      int t = e / NP;
+      const int n = e % NP;
+      if (tail) t = t < last ? t : (int)last;
+      // entries with n >= N load a valid element and are zeroed when staged
+      const uint32_t off = (dense_bc && !tail) ? (uint32_t)e
+                                               : (uint32_t)t * n32 + ((uint32_t)n < n32 ? (uint32_t)n : 0u);
+      pb[j] = bb[off];
+      if (FULL) pc[j] = cb[off];
+    }
+  };
+  // ---- registers -> LDS: dt (softplus), x, silu(z); B and C as fp32
+  auto stage = [&](int64_t t0) {
+    const int64_t nvalid = t_stop - t0;             // uniform
+#pragma unroll
+    for (int k = 0; k < KX; ++k) {
+      const int t = R * k + r;
+      const float v = Raw<DB>::f32(pd[k]) + bias;
+      float dt = a.softplus ? (ACC ? softplus_f(v) : softplus_short(v)) : v;
+      dt = (t < nvalid) ? dt : 0.f;
+      s_dx[t * CH + c] = make_float2(dt, Raw<XB>::f32(px[k]));
+      if (FULL) s_gz[t * CH + c] = has_z ? silu_f(Raw<XB>::f32(pz[k])) : 1.f;
+    }
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      const int e = lane + 64 * j;
+      const int t = e / NP, n = e % NP;
+      const int base = ((t * R + n / S) * 2) * S + (n % S);
+      const bool ok = (uint32_t)n < n32;
+      s_bc[base] = ok ? Raw<XB>::f32(pb[j]) : 0.f;
+      if (FULL) s_bc[base + S] = ok ? Raw<XB>::f32(pc[j]) : 0.f;
+    }
+  };
+
+  float dsum = 0.f;
+  fetch(t_begin);
+  for (int64_t t0 = t_begin; t0 < t_stop; t0 += T) {
+    __syncthreads();
+    stage(t0);
+    __syncthreads();
+    if (t0 + T < t_stop) fetch(t0 + T);
+    const int64_t nvalid = t_stop - t0;
+    TX* yb = gy + (b * L + t0) * dim + ch0;          // uniform
+    // Operands of one group of R tokens: (dt, x) and this row's B/C slices.
+    // The next group's operands are read from LDS while the current group is
+    // computed, so LDS latency overlaps the VALU work.
+    struct Group {
+      float2 dx[R];
+      float b[R][S];
+      float c[R][S];
+    };
+    auto load_group = [&](int tb, Group& g) {
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        const int tt = tb + j;
+        g.dx[j] = s_dx[tt * CH + c];
+        const float* bc = s_bc + ((tt * R + r) * 2) * S;
+        if constexpr (S >= 4) {
+#pragma unroll
+          for (int q = 0; q < S / 4; ++q) {
+            const float4 vb = reinterpret_cast<const float4*>(bc)[q];
+            g.b[j][4 * q] = vb.x; g.b[j][4 * q + 1] = vb.y; g.b[j][4 * q + 2] = vb.z; g.b[j][4 * q + 3] = vb.w;
+            if (FULL) {
+              const float4 vc = reinterpret_cast<const float4*>(bc + S)[q];
+              g.c[j][4 * q] = vc.x; g.c[j][4 * q + 1] = vc.y; g.c[j][4 * q + 2] = vc.z; g.c[j][4 * q + 3] = vc.w;
+            }
+          }
+        } else {
+#pragma unroll
+          for (int s = 0; s < S; ++s) { g.b[j][s] = bc[s]; g.c[j][s] = FULL ? bc[S + s] : 0.f; }
+        }
+      }
+    };
+    Group cur, nxt;
+    load_group(0, cur);
+#pragma unroll
+    for (int tb = 0; tb < T; tb += R) {
+      if (tb + R < T) load_group(tb + R, nxt);
+      float pr[R];
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        const float2 dx = cur.dx[j];
+        float acc = 0.f;
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+          const float E = hw_exp2(dx.x * a2[s]);
+          const float g = ACC ? zoh_gain_accurate(E, dx.x, av[s], ia[s]) : fmaf(E, ia[s], -ia[s]);
+          h[s] = fmaf(E, h[s], g * (cur.b[j][s] * dx.y));
+          if (FULL) acc = fmaf(cur.c[j][s], h[s], acc);
+        }
+        pr[j] = acc;
+        if (!FULL) dsum += dx.x;
+      }
+      if (FULL) {
+        const float tot = reduce_scatter_rows(pr[0], pr[1], pr[2], pr[3]);
+        const int tl = tb + r;
+        const float xv = s_dx[tl * CH + c].y;
+        const float yv = fmaf(Dv, xv, tot) * s_gz[tl * CH + c];
+        if (ch_ok && tl < nvalid) yb[(uint32_t)tl * dim32 + (uint32_t)c] = (TX)yv;
+      }
+      if (tb + R < T) cur = nxt;
+    }
+  }
+
+  // ---- end state
+  float* hout = nullptr;
+  if (FULL) hout = (chunk == a.nchunks - 1) ? a.h_final : nullptr;
+  else hout = (a.nchunks == 1) ? a.h_final : a.ws_state + chunk * slice_elems;
+  if (hout != nullptr && ch_ok) {
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const int64_t n = r * S + s;
+      if (n < N) hout[(b * dim + ch) * N + n] = h[s];
+    }
+  }
+  if (!FULL && a.nchunks > 1 && r == 0 && ch_ok) a.ws_dsum[chunk * a.batch * dim + b * dim + ch] = dsum;
+}
+
+template <bool XB, bool DB, int S, int MODE>
+__global__ __launch_bounds__(64) void scan_kernel(ScanArgs a, int64_t groups_per_batch) {
+  using TS = TileShape<S>;
+  __shared__ float2 s_dx[TS::T * TS::CH];
+  __shared__ float s_gz[TS::T * TS::CH];
+  __shared__ __attribute__((aligned(16))) float s_bc[TS::T * TS::R * 2 * S];
+
+  // XCD-aware order: dispatch id i runs on XCD i % 8; give each XCD a contiguous
+  // range of (batch, channel-group) tiles so neighbouring channel groups share L2.
+  const int64_t nb = gridDim.x;
+  int64_t lin = blockIdx.x;
+  if ((nb & 7) == 0) lin = (lin & 7) * (nb >> 3) + (lin >> 3);
+  const int64_t b = lin / groups_per_batch;
+  const int64_t ch0 = (lin % groups_per_batch) * kChPerWave;
+  const int64_t chunk = blockIdx.y;
+
+  const int lane = threadIdx.x;
+  const int r = lane >> 4, c = lane & 15;
+  const int64_t ch = ch0 + c;
+  float a2[S], ia[S], av[S];
+  bool tiny = false;
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int64_t n = r * S + s;
+    const float an = (ch < a.dim && n < a.dstate) ? a.A[ch * a.dstate + n] : -1.f;
+    av[s] = an;
+    a2[s] = an * kLog2e;
+    ia[s] = 1.f / an;
+    tiny = tiny || !(fabsf(an) >= 1e-2f);
+  }
+  if (!XB || __builtin_amdgcn_ballot_w64(tiny) != 0)
+    scan_body<XB, DB, S, MODE, true>(a, b, ch0, chunk, a2, ia, av, s_dx, s_gz, s_bc);
+  else
+    scan_body<XB, DB, S, MODE, false>(a, b, ch0, chunk, a2, ia, av, s_dx, s_gz, s_bc);
+}
+
+// Launch one scan kernel variant for a given (act, delta) dtype pair.
+template <bool XB, bool DB>
+hipError_t launch_scan_variant(int S, int mode, const ScanArgs& a, dim3 grid, int64_t gpb, hipStream_t st) {
+#define SSM_LAUNCH_S(SV)                                                                   \
+  case SV:                                                                                 \
+    if (mode == kModeFull) scan_kernel<XB, DB, SV, kModeFull><<<grid, 64, 0, st>>>(a, gpb); \
+    else scan_kernel<XB, DB, SV, kModeState><<<grid, 64, 0, st>>>(a, gpb);                  \
+    break;
+  switch (S) {
+    SSM_LAUNCH_S(1)
+    SSM_LAUNCH_S(2)
+    SSM_LAUNCH_S(4)
+    SSM_LAUNCH_S(8)
+    SSM_LAUNCH_S(16)
+    SSM_LAUNCH_S(32)
+    default: return hipErrorInvalidValue;
+  }
+#undef SSM_LAUNCH_S
+  return hipGetLastError();
+}
+
+}  // namespace scan_dev
+}  // namespace ssm

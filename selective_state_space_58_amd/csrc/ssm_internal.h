@@ -1,0 +1,84 @@
+// Internal declarations shared by the host dispatch code and the HIP kernels
+// of the MI355X selective-scan library.  Not part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <string>
+
+namespace ssm {
+
+// Set the calling thread's error detail and return `status`.
+int fail(int status, const std::string& msg);
+
+// ---------------------------------------------------------------- selective scan
+// Kernel geometry: one wavefront (64 lanes) per workgroup.  The lanes form
+// kRows rows of 16; row r owns states [r*S, r*S + S) of the wave's 16
+// channels, so every (channel, state) pair lives in exactly one lane's VGPRs.
+constexpr int kRows = 4;
+constexpr int kChPerWave = 64 / kRows;
+
+enum ScanMode : int { kModeFull = 0, kModeState = 1 };
+
+struct ScanArgs {
+  const void* x;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* Dskip;
+  const void* z;
+  const float* delta_bias;
+  const float* h0;
+  void* y;
+  float* h_final;
+  float* ws_state;   // (nchunks, batch, dim, dstate) chunk-local end states / carries
+  float* ws_dsum;    // (nchunks, batch, dim) sum of dt over each chunk
+  int64_t batch, seqlen, dim, dstate;
+  int64_t chunk_len;  // tokens per time chunk (multiple of the time tile)
+  int64_t nchunks;    // number of time chunks (1 = unsplit)
+  int softplus;
+  int act_bf16, delta_bf16;
+};
+
+struct ScanPlan {
+  int S;              // states per lane (power of two, kRows*S >= dstate)
+  int T;              // time tile (tokens staged per LDS round)
+  int64_t nchunks;
+  int64_t chunk_len;
+  size_t ws_bytes;
+};
+
+ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, bool final_only,
+                   int num_cus);
+
+// Enqueue the whole selective scan (all phases).  Returns an ssm_status.
+int launch_scan(const ScanArgs& a, const ScanPlan& p, bool final_only, void* stream);
+
+// ---------------------------------------------------------------- SSD
+struct SsdArgs {
+  const void* x;
+  const void* dt;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* Dskip;
+  const void* z;
+  const float* dt_bias;
+  const float* h0;
+  void* y;
+  float* h_final;
+  int64_t batch, seqlen, nheads, headdim, ngroups, dstate, chunk;
+  int softplus;
+  int dt_bf16;
+  void* ws;
+};
+
+size_t ssd_ws_bytes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t ngroups,
+                    int64_t dstate, int64_t chunk);
+int launch_ssd(const SsdArgs& a, void* stream);
+
+int device_cu_count();
+
+}  // namespace ssm

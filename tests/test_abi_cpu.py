@@ -1,0 +1,110 @@
+"""CPU checks of the C ABI: the library loads, exports every declared symbol,
+and rejects bad arguments on the host before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssm_mi355x.h")
+
+
+def _lib():
+    from selective_state_space_58_amd import _binding
+    if not os.path.exists(_binding.library_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    return _binding.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssm_\w+|ssd_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = _lib()
+    names = declared_functions()
+    assert {"ssm_scan_fwd", "ssm_scan_final_state", "ssd_chunk_scan_fwd"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    lib = _lib()
+    for code in range(8):
+        s = lib.ssm_status_string(code)
+        assert s and isinstance(s, bytes)
+    assert lib.ssm_status_string(0) == b"ok"
+    assert lib.ssm_status_string(99) == b"unknown status"
+
+
+# fake but aligned device addresses: validation must reject before any dereference
+P = 0x10000
+
+
+def scan(lib, **kw):
+    a = dict(x=P, delta=P, A=P, B=P, C=P, D=None, z=None, bias=None, sp=0, h0=None, y=P, hf=None,
+             batch=1, seqlen=4, dim=4, dstate=4, act=1, ddt=1, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return lib.ssm_scan_fwd(a["x"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"], a["sp"], a["h0"],
+                            a["y"], a["hf"], a["batch"], a["seqlen"], a["dim"], a["dstate"], a["act"], a["ddt"],
+                            a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), 1), (dict(delta=None), 1), (dict(A=None), 1), (dict(B=None), 1), (dict(C=None), 1),
+    (dict(y=None), 1),
+    (dict(batch=-1), 2), (dict(seqlen=-1), 2), (dict(dim=-2), 2), (dict(dstate=0), 2), (dict(sp=2), 2),
+    (dict(batch=1 << 40, seqlen=1 << 20, dim=1 << 10), 2),
+    (dict(act=5), 3), (dict(ddt=-1), 3),
+    (dict(dstate=129), 4),
+    (dict(x=P + 1), 7), (dict(A=P + 2), 7), (dict(h0=P + 2), 7),
+])
+def test_scan_argument_errors(kw, code):
+    lib = _lib()
+    assert scan(lib, **kw) == code
+    assert lib.ssm_last_error() != b""
+
+
+def test_empty_batch_is_noop():
+    lib = _lib()
+    assert scan(lib, batch=0) == 0
+    assert scan(lib, dim=0) == 0
+
+
+def test_final_state_requires_output():
+    lib = _lib()
+    rc = lib.ssm_scan_final_state(P, P, P, P, None, 0, None, None, 1, 4, 4, 4, 1, 1, None, 0, None)
+    assert rc == 1
+
+
+def ssd(lib, **kw):
+    a = dict(x=P, dt=P, A=P, B=P, C=P, D=None, z=None, bias=None, sp=0, h0=None, y=P, hf=None,
+             batch=1, seqlen=256, nheads=2, headdim=64, ngroups=1, dstate=128, chunk=256, act=1, ddt=0,
+             ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return lib.ssd_chunk_scan_fwd(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"], a["sp"],
+                                  a["h0"], a["y"], a["hf"], a["batch"], a["seqlen"], a["nheads"], a["headdim"],
+                                  a["ngroups"], a["dstate"], a["chunk"], a["act"], a["ddt"], a["ws"], a["wsb"],
+                                  a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), 1), (dict(y=None), 1), (dict(nheads=3, ngroups=2), 2), (dict(headdim=-1), 2),
+    (dict(act=7), 3), (dict(act=0), 4), (dict(headdim=32), 4), (dict(dstate=96), 4), (dict(chunk=100), 4),
+    (dict(x=P + 2), 7),
+])
+def test_ssd_argument_errors(kw, code):
+    lib = _lib()
+    assert ssd(lib, **kw) == code
+
+
+def test_workspace_queries():
+    lib = _lib()
+    assert lib.ssm_scan_workspace_bytes(0, 10, 10, 16, 0) == 0
+    # few slices, long sequence: the time-split path needs workspace
+    assert lib.ssm_scan_workspace_bytes(1, 131072, 2048, 16, 0) > 0
+    assert lib.ssm_scan_workspace_bytes(8, 2048, 1536, 16, 0) == 0
