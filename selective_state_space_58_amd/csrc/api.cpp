@@ -205,10 +205,13 @@ int ssd_chunk_scan_fwd(const void* x, const void* dt, const float* A, const void
                        int64_t ngroups, int64_t dstate, int64_t chunk_size, int act_dtype, int dt_dtype,
                        void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error.clear();
-  if (x == nullptr || dt == nullptr || A == nullptr || B == nullptr || C == nullptr || y == nullptr)
-    return fail(SSM_ERR_NULL, "x, dt, A, B, C and y are required");
   if (batch < 0 || seqlen < 0 || nheads < 0 || headdim < 0 || ngroups < 0 || dstate < 0 || chunk_size < 0)
     return fail(SSM_ERR_SHAPE, "negative size");
+  // Tensors with no elements may be NULL (an empty framework tensor has no storage).
+  const bool has_tok = batch > 0 && seqlen > 0;
+  if ((has_tok && (x == nullptr || dt == nullptr || B == nullptr || C == nullptr || y == nullptr)) ||
+      (nheads > 0 && A == nullptr))
+    return fail(SSM_ERR_NULL, "x, dt, A, B, C and y are required");
   if (nheads == 0 || headdim == 0 || ngroups == 0 || dstate == 0 || chunk_size == 0)
     return fail(SSM_ERR_SHAPE, "nheads, headdim, ngroups, dstate and chunk_size must be >= 1");
   if (nheads % ngroups != 0) return fail(SSM_ERR_SHAPE, "nheads must be a multiple of ngroups");
