@@ -41,6 +41,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-others", action="store_true")
+    p.add_argument("--only", choices=["scan-2.8b", "scan-long", "ssd", "copy"], default=None,
+                   help="time only this other workload (for profiling); skips the headline JSON line")
     return p.parse_args()
 
 
@@ -97,6 +99,44 @@ def time_calls(fn, steps, warmup, torch):
     return start.elapsed_time(end), per
 
 
+def run_other(oi, steps, warmup, ssm, workloads, torch, dev):
+    """Time one of the non-headline workloads through the C ABI; returns a result dict."""
+    oinp, ocfg = workloads.config_inputs(oi)
+    t = workloads.to_device(oinp, dev)
+    if ocfg["kind"] == "scan":
+        y = torch.empty_like(t["x"])
+        hf = torch.empty((ocfg["batch"], ocfg["dim"], ocfg["dstate"]), dtype=torch.float32, device=dev)
+        nb = ssm.ssm_scan_workspace_bytes(ocfg["batch"], ocfg["seqlen"], ocfg["dim"], ocfg["dstate"])
+        ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+        sp = oinp["meta"]["softplus"]
+
+        def ostep(i):
+            ssm.ssm_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                             delta_bias=t["delta_bias"], delta_softplus=sp, y=y, h_final=hf, workspace=ws)
+        tot, _ = time_calls(ostep, steps, warmup, torch)
+        oms = tot / steps
+        otc = ocfg["batch"] * ocfg["seqlen"] * ocfg["dim"]
+        ob = scan_bytes(ocfg)
+        return {"name": ocfg["name"], "ms": round(oms, 4), "Gtc_s": round(otc / (oms * 1e-3) / 1e9, 2),
+                "hbm_frac": round(ob / (oms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "valu_frac": round(otc * ocfg["dstate"] * SLOTS_PER_ELEMENT / (oms * 1e-3) / 1e12 / VALU_PEAK_TSLOTS, 4)}
+    y = torch.empty_like(t["x"])
+    hf = torch.empty((ocfg["batch"], ocfg["nheads"], ocfg["headdim"], ocfg["dstate"]), dtype=torch.float32, device=dev)
+    nb = ssm.ssd_workspace_bytes(ocfg["batch"], ocfg["seqlen"], ocfg["nheads"], ocfg["headdim"], ocfg["ngroups"],
+                                 ocfg["dstate"], ocfg["chunk"])
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+
+    def sstep(i):
+        ssm.ssd_chunk_scan_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], chunk_size=ocfg["chunk"], y=y, h_final=hf,
+                               workspace=ws)
+    tot, _ = time_calls(sstep, steps, warmup, torch)
+    oms = tot / steps
+    otc = ocfg["batch"] * ocfg["seqlen"] * ocfg["nheads"] * ocfg["headdim"]
+    return {"name": ocfg["name"], "ms": round(oms, 4), "Gtc_s": round(otc / (oms * 1e-3) / 1e9, 2),
+            "hbm_frac": round(ssd_bytes(ocfg) / (oms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "mfma_frac_algorithmic": round(ssd_flops(ocfg) / (oms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -116,6 +156,20 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     steps, warmup = args.steps, args.warmup
+    if args.only == "copy":
+        # plain device copy of a known size: calibrates the HBM byte counters
+        nbytes = 1 << 30
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        tot, _ = time_calls(lambda i: dst.copy_(src), steps, warmup, torch)
+        print(json.dumps({"only": "copy", "bytes_read_per_call": nbytes, "bytes_written_per_call": nbytes,
+                          "ms": round(tot / steps, 4), "GBs_read_plus_write": round(2 * nbytes / (tot / steps * 1e-3) / 1e9, 1)}),
+              flush=True)
+        return
+    if args.only is not None:
+        oi = {"scan-2.8b": 2, "scan-long": 3, "ssd": 4}[args.only]
+        print(json.dumps({"only": args.only, **run_other(oi, steps, warmup, ssm, workloads, torch, dev)}), flush=True)
+        return
 
     # ---------------------------------------------------------------- headline workload
     idx = 1
@@ -167,47 +221,8 @@ def main():
         del copies, ys
         torch.cuda.empty_cache()
         for oi in (2, 3, 4):
-            oinp, ocfg = workloads.config_inputs(oi)
-            t = workloads.to_device(oinp, dev)
-            if ocfg["kind"] == "scan":
-                y = torch.empty_like(t["x"])
-                hf = torch.empty((ocfg["batch"], ocfg["dim"], ocfg["dstate"]), dtype=torch.float32, device=dev)
-                nb = ssm.ssm_scan_workspace_bytes(ocfg["batch"], ocfg["seqlen"], ocfg["dim"], ocfg["dstate"])
-                ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
-
-                def ostep(i, t=t, y=y, hf=hf, ws=ws, sp=oinp["meta"]["softplus"]):
-                    ssm.ssm_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
-                                     delta_bias=t["delta_bias"], delta_softplus=sp, y=y, h_final=hf, workspace=ws)
-                tot, _ = time_calls(ostep, 5, 2, torch)
-                oms = tot / 5
-                otc = ocfg["batch"] * ocfg["seqlen"] * ocfg["dim"]
-                ob = scan_bytes(ocfg)
-                others[ocfg["name"]] = {"ms": round(oms, 4), "Gtc_s": round(otc / (oms * 1e-3) / 1e9, 2),
-                                        "hbm_frac": round(ob / (oms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                                        "valu_frac": round(otc * ocfg["dstate"] * SLOTS_PER_ELEMENT /
-                                                           (oms * 1e-3) / 1e12 / VALU_PEAK_TSLOTS, 4)}
-            else:
-                try:
-                    y = torch.empty_like(t["x"])
-                    hf = torch.empty((ocfg["batch"], ocfg["nheads"], ocfg["headdim"], ocfg["dstate"]),
-                                     dtype=torch.float32, device=dev)
-                    nb = ssm.ssd_workspace_bytes(ocfg["batch"], ocfg["seqlen"], ocfg["nheads"], ocfg["headdim"],
-                                                 ocfg["ngroups"], ocfg["dstate"], ocfg["chunk"])
-                    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
-
-                    def sstep(i, t=t, y=y, hf=hf, ws=ws):
-                        ssm.ssd_chunk_scan_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], chunk_size=ocfg["chunk"],
-                                               y=y, h_final=hf, workspace=ws)
-                    tot, _ = time_calls(sstep, 5, 2, torch)
-                    oms = tot / 5
-                    otc = ocfg["batch"] * ocfg["seqlen"] * ocfg["nheads"] * ocfg["headdim"]
-                    others[ocfg["name"]] = {
-                        "ms": round(oms, 4), "Gtc_s": round(otc / (oms * 1e-3) / 1e9, 2),
-                        "hbm_frac": round(ssd_bytes(ocfg) / (oms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                        "mfma_frac": round(ssd_flops(ocfg) / (oms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
-                except ssm.SSMError as e:
-                    others[ocfg["name"]] = {"error": str(e)}
-            del t
+            res = run_other(oi, 5, 2, ssm, workloads, torch, dev)
+            others[res.pop("name")] = res
             torch.cuda.empty_cache()
         out["other_workloads"] = others
 

@@ -15,7 +15,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libssm_mi355x.so")
 SOURCES = [("api.cpp", []), ("scan_host.hip", []), ("ssd_kernels.hip", [])] + [
-    ("scan_inst.hip", ["-DSSM_XB=%d" % xb, "-DSSM_DB=%d" % db]) for xb in (0, 1) for db in (0, 1)]
+    ("scan_inst.hip", ["-DSSM_XB=%d" % xb, "-DSSM_DB=%d" % db, "-DSSM_S=%d" % sv])
+    for sv in (32, 16, 8, 4, 2, 1) for xb in (1, 0) for db in (1, 0)]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-Wall", "-Wno-unused-command-line-argument",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-ffp-contract=fast"]
@@ -23,7 +24,7 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-Wall", "-Wno-u
 
 def _compile(item) -> str:
     src, defs = item
-    tag = "".join(d.split("=")[-1] for d in defs)
+    tag = "_".join(d.split("=")[-1] for d in defs)
     out = os.path.join(BUILD, os.path.basename(src) + tag + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
     cmd = [HIPCC] + FLAGS + defs + lang + ["-c", os.path.join(CSRC, src), "-o", out]
@@ -36,7 +37,7 @@ def _compile(item) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(len(SOURCES)) as ex:
+    with ThreadPoolExecutor(min(len(SOURCES), os.cpu_count() or 8, 16)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp] + objs

@@ -31,6 +31,7 @@ bool elems_ok(std::initializer_list<int64_t> dims) {
 }
 
 bool aligned(const void* p, size_t a) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+bool aligned16(const void* p) { return aligned(p, 16); }
 
 size_t dsize(int dt) { return dt == SSM_BF16 ? 2 : 4; }
 
@@ -167,6 +168,8 @@ static int scan_common(const void* x, const void* delta, const float* A, const v
   a.softplus = delta_softplus;
   a.act_bf16 = act_dtype == SSM_BF16;
   a.delta_bf16 = delta_dtype == SSM_BF16;
+  a.vec_io = (dim % kChPerWave == 0) && act_dtype == delta_dtype && aligned16(x) && aligned16(delta) &&
+             aligned16(B) && (final_only || aligned16(C)) && (final_only || aligned16(z));
   if (ws != nullptr) {
     const size_t st_bytes = (size_t)p.nchunks * (size_t)(batch * dim * dstate) * sizeof(float);
     a.ws_state = (float*)ws;

@@ -8,10 +8,13 @@
 
 namespace ssm {
 
-hipError_t launch_scan_x0_d0(int S, int mode, const ScanArgs& a, dim3 grid, int64_t gpb, hipStream_t st);
-hipError_t launch_scan_x0_d1(int S, int mode, const ScanArgs& a, dim3 grid, int64_t gpb, hipStream_t st);
-hipError_t launch_scan_x1_d0(int S, int mode, const ScanArgs& a, dim3 grid, int64_t gpb, hipStream_t st);
-hipError_t launch_scan_x1_d1(int S, int mode, const ScanArgs& a, dim3 grid, int64_t gpb, hipStream_t st);
+#define SSM_DECL(XB, DB, S) \
+  hipError_t launch_scan_x##XB##_d##DB##_s##S(int mode, const ScanArgs& a, dim3 grid, int64_t gpb, hipStream_t st);
+#define SSM_DECL_ALL_S(XB, DB) SSM_DECL(XB, DB, 1) SSM_DECL(XB, DB, 2) SSM_DECL(XB, DB, 4) SSM_DECL(XB, DB, 8) SSM_DECL(XB, DB, 16) SSM_DECL(XB, DB, 32)
+SSM_DECL_ALL_S(0, 0)
+SSM_DECL_ALL_S(0, 1)
+SSM_DECL_ALL_S(1, 0)
+SSM_DECL_ALL_S(1, 1)
 
 namespace {
 
@@ -40,11 +43,32 @@ __global__ __launch_bounds__(256) void copy_state_kernel(const float* h0, float*
   if (i < total) out[i] = h0 != nullptr ? h0[i] : 0.f;
 }
 
+template <int XB, int DB>
+hipError_t launch_s(int S, int mode, const ScanArgs& a, dim3 grid, int64_t gpb, hipStream_t st);
+
+#define SSM_LAUNCH_S(XB, DB)                                                                        \
+  template <>                                                                                       \
+  hipError_t launch_s<XB, DB>(int S, int mode, const ScanArgs& a, dim3 grid, int64_t gpb, hipStream_t st) { \
+    switch (S) {                                                                                    \
+      case 1: return launch_scan_x##XB##_d##DB##_s1(mode, a, grid, gpb, st);                        \
+      case 2: return launch_scan_x##XB##_d##DB##_s2(mode, a, grid, gpb, st);                        \
+      case 4: return launch_scan_x##XB##_d##DB##_s4(mode, a, grid, gpb, st);                        \
+      case 8: return launch_scan_x##XB##_d##DB##_s8(mode, a, grid, gpb, st);                        \
+      case 16: return launch_scan_x##XB##_d##DB##_s16(mode, a, grid, gpb, st);                      \
+      case 32: return launch_scan_x##XB##_d##DB##_s32(mode, a, grid, gpb, st);                      \
+      default: return hipErrorInvalidValue;                                                         \
+    }                                                                                               \
+  }
+SSM_LAUNCH_S(0, 0)
+SSM_LAUNCH_S(0, 1)
+SSM_LAUNCH_S(1, 0)
+SSM_LAUNCH_S(1, 1)
+
 hipError_t launch_mode(int S, int mode, const ScanArgs& a, dim3 grid, int64_t gpb, hipStream_t st) {
-  if (a.act_bf16 && a.delta_bf16) return launch_scan_x1_d1(S, mode, a, grid, gpb, st);
-  if (a.act_bf16) return launch_scan_x1_d0(S, mode, a, grid, gpb, st);
-  if (a.delta_bf16) return launch_scan_x0_d1(S, mode, a, grid, gpb, st);
-  return launch_scan_x0_d0(S, mode, a, grid, gpb, st);
+  if (a.act_bf16 && a.delta_bf16) return launch_s<1, 1>(S, mode, a, grid, gpb, st);
+  if (a.act_bf16) return launch_s<1, 0>(S, mode, a, grid, gpb, st);
+  if (a.delta_bf16) return launch_s<0, 1>(S, mode, a, grid, gpb, st);
+  return launch_s<0, 0>(S, mode, a, grid, gpb, st);
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -117,6 +117,8 @@ __device__ __forceinline__ float reduce_scatter_rows(float p0, float p1, float p
   return bits_f(s[0]) + bits_f(s[1]);                // row r: token r
 }
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
 template <int S>
 struct TileShape {
   static constexpr int R = kRows;
@@ -127,7 +129,7 @@ struct TileShape {
   static constexpr int KB = T * NP / 64;           // B (and C) items per lane per tile
 };
 
-template <bool XB, bool DB, int S, int MODE, bool ACC>
+template <bool XB, bool DB, int S, int MODE, bool ACC, bool VEC>
 __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t ch0, int64_t chunk,
                                           const float (&a2)[S], const float (&ia)[S], const float (&av)[S],
                                           float2* __restrict__ s_dx, float* __restrict__ s_gz,
@@ -177,7 +179,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
   // wave-uniform 64-bit base, so loads use the scalar-base addressing form.
   RX px[KX], pz[KX], pb[KB], pc[KB];
   RD pd[KX];
-  auto fetch = [&](int64_t t0) {
+  auto fetch_scalar = [&](int64_t t0) {
     const bool tail = t0 + T > t_stop;
     const int64_t row0 = (b * L + t0) * dim + ch0;  // uniform
     const RX* xb = gx + row0;
@@ -210,7 +212,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
     }
   };
   // ---- registers -> LDS: dt (softplus), x, silu(z); B and C as fp32
-  auto stage = [&](int64_t t0) {
+  auto stage_scalar = [&](int64_t t0) {
     const int64_t nvalid = t_stop - t0;             // uniform
 #pragma unroll
     for (int k = 0; k < KX; ++k) {
@@ -230,6 +232,115 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
       s_bc[base] = ok ? Raw<XB>::f32(pb[j]) : 0.f;
       if (FULL) s_bc[base + S] = ok ? Raw<XB>::f32(pc[j]) : 0.f;
     }
+  };
+
+
+  // ---- vectorised tile I/O (every channel group full, pointers 16-byte
+  // aligned, N == NP, delta stored like x): each lane moves whole 16-byte
+  // chunks.  Chunk k of a tile covers token k / XROW, channels
+  // (k % XROW) * EX .. + EX of x, delta and z, and elements k*EX .. + EX of
+  // the (token, state)-contiguous B and C tiles.
+  constexpr int EX = 16 / (int)sizeof(RX);                 // elements per chunk
+  constexpr int XROW = CH / EX;                             // chunks per token row
+  constexpr int CXN = (T * CH) / (64 * EX);                 // x chunks per lane
+  constexpr int CBN = (T * NP) / (64 * EX) > 0 ? (T * NP) / (64 * EX) : 1;  // B chunks per lane
+  constexpr int GW = S < EX ? S : EX;                       // floats per LDS write of B/C
+  u32x4 vx[CXN], vd[CXN], vz[CXN], vb[CBN], vc[CBN];
+  const int vc0 = (lane % XROW) * EX;                       // this lane's first channel in a row
+  float vbias[EX];
+#pragma unroll
+  for (int e = 0; e < EX; ++e) vbias[e] = (VEC && a.delta_bias != nullptr) ? a.delta_bias[ch0 + vc0 + e] : 0.f;
+  // (the element is copied to a scalar first: bit-casting a vector-element
+  // lvalue directly reads element 0 with this compiler)
+  auto raw_elem = [](const u32x4& v, int e) -> float {
+    if constexpr (sizeof(RX) == 2) {
+      const unsigned u = (v[e >> 1] >> (16 * (e & 1))) << 16;
+      return __builtin_bit_cast(float, u);
+    } else {
+      const unsigned u = v[e];
+      return __builtin_bit_cast(float, u);
+    }
+  };
+  auto fetch_vec = [&](int64_t t0) {
+    const bool tail = t0 + T > t_stop;
+    const int64_t last = t_stop - 1 - t0;
+    const int64_t row0 = (b * L + t0) * dim + ch0;          // uniform
+    const char* xb = (const char*)(gx + row0);
+    const char* db = (const char*)(gd + row0);
+    const char* zb = (const char*)(gz + row0);
+    const uint32_t rowb = dim32 * (uint32_t)sizeof(RX);
+#pragma unroll
+    for (int q = 0; q < CXN; ++q) {
+      const int k = lane + 64 * q;
+      int tl = k / XROW;
+      if (tail) tl = tl < last ? tl : (int)last;
+      const uint32_t off = (uint32_t)tl * rowb + (uint32_t)(k % XROW) * 16u;
+      vx[q] = *reinterpret_cast<const u32x4*>(xb + off);
+      vd[q] = *reinterpret_cast<const u32x4*>(db + off);
+      if (has_z) vz[q] = *reinterpret_cast<const u32x4*>(zb + off);
+    }
+    const RX* bb = gB + (b * L + t0) * N;                   // uniform
+    const RX* cb = gC + (b * L + t0) * N;
+#pragma unroll
+    for (int q = 0; q < CBN; ++q) {
+      const int e0 = (lane + 64 * q) * EX;
+      int t = e0 / NP;
+      if (tail) t = t < last ? t : (int)last;
+      const uint32_t off = (uint32_t)t * (uint32_t)NP + (uint32_t)(e0 % NP);
+      vb[q] = *reinterpret_cast<const u32x4*>(bb + off);
+      if (FULL) vc[q] = *reinterpret_cast<const u32x4*>(cb + off);
+    }
+  };
+  auto stage_vec = [&](int64_t t0) {
+    const int64_t nvalid = t_stop - t0;
+#pragma unroll
+    for (int q = 0; q < CXN; ++q) {
+      const int k = lane + 64 * q;
+      const int tl = k / XROW;
+      const bool ok = tl < nvalid;
+      float dxv[2 * EX];
+#pragma unroll
+      for (int e = 0; e < EX; ++e) {
+        const float v = raw_elem(vd[q], e) + vbias[e];
+        float dt = a.softplus ? (ACC ? softplus_f(v) : softplus_short(v)) : v;
+        dxv[2 * e] = ok ? dt : 0.f;
+        dxv[2 * e + 1] = raw_elem(vx[q], e);
+      }
+      float4* dst = reinterpret_cast<float4*>(s_dx + tl * CH + vc0);
+#pragma unroll
+      for (int e = 0; e < EX / 2; ++e) dst[e] = make_float4(dxv[4 * e], dxv[4 * e + 1], dxv[4 * e + 2], dxv[4 * e + 3]);
+      if (FULL) {
+        float gzv[EX];
+#pragma unroll
+        for (int e = 0; e < EX; ++e) gzv[e] = has_z ? silu_f(raw_elem(vz[q], e)) : 1.f;
+        float4* gd4 = reinterpret_cast<float4*>(s_gz + tl * CH + vc0);
+#pragma unroll
+        for (int e = 0; e < EX / 4; ++e) gd4[e] = make_float4(gzv[4 * e], gzv[4 * e + 1], gzv[4 * e + 2], gzv[4 * e + 3]);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < CBN; ++q) {
+      const int e0 = (lane + 64 * q) * EX;
+      const int t = e0 / NP, n0 = e0 % NP;
+#pragma unroll
+      for (int g = 0; g < EX / GW; ++g) {
+        const int n = n0 + g * GW;
+        const int base = ((t * R + n / S) * 2) * S + (n % S);
+#pragma unroll
+        for (int e = 0; e < GW; ++e) {
+          s_bc[base + e] = raw_elem(vb[q], g * GW + e);
+          if (FULL) s_bc[base + S + e] = raw_elem(vc[q], g * GW + e);
+        }
+      }
+    }
+  };
+  auto fetch = [&](int64_t t0) {
+    if constexpr (VEC) fetch_vec(t0);
+    else fetch_scalar(t0);
+  };
+  auto stage = [&](int64_t t0) {
+    if constexpr (VEC) stage_vec(t0);
+    else stage_scalar(t0);
   };
 
   float dsum = 0.f;
@@ -273,9 +384,26 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
     };
     Group cur, nxt;
     load_group(0, cur);
+    // exp(dt*a) of a group is computed one group ahead, so the transcendental
+    // latency overlaps the previous group's state updates
+    float Ecur[R][S], Enxt[R][S];
+    auto group_exp = [&](const Group& g, float (&E)[R][S]) {
 #pragma unroll
+      for (int j = 0; j < R; ++j)
+#pragma unroll
+        for (int s = 0; s < S; ++s) E[j][s] = hw_exp2(g.dx[j].x * a2[s]);
+    };
+    group_exp(cur, Ecur);
+    const bool full_tile = ch_ok && nvalid >= T;       // uniform on the vector path
+    const int nval32 = nvalid < T ? (int)nvalid : T;
+    // full unroll for small S; wide S (N > 32) keeps the loop to bound code size
+    constexpr int kGroupUnroll = (S <= 8) ? T / R : 2;
+#pragma unroll kGroupUnroll
     for (int tb = 0; tb < T; tb += R) {
-      if (tb + R < T) load_group(tb + R, nxt);
+      if (tb + R < T) {
+        load_group(tb + R, nxt);
+        group_exp(nxt, Enxt);
+      }
       float pr[R];
 #pragma unroll
       for (int j = 0; j < R; ++j) {
@@ -283,7 +411,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
         float acc = 0.f;
 #pragma unroll
         for (int s = 0; s < S; ++s) {
-          const float E = hw_exp2(dx.x * a2[s]);
+          const float E = Ecur[j][s];
           const float g = ACC ? zoh_gain_accurate(E, dx.x, av[s], ia[s]) : fmaf(E, ia[s], -ia[s]);
           h[s] = fmaf(E, h[s], g * (cur.b[j][s] * dx.y));
           if (FULL) acc = fmaf(cur.c[j][s], h[s], acc);
@@ -296,9 +424,15 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
         const int tl = tb + r;
         const float xv = s_dx[tl * CH + c].y;
         const float yv = fmaf(Dv, xv, tot) * s_gz[tl * CH + c];
-        if (ch_ok && tl < nvalid) yb[(uint32_t)tl * dim32 + (uint32_t)c] = (TX)yv;
+        if (full_tile || (ch_ok && tl < nval32)) yb[(uint32_t)tl * dim32 + (uint32_t)c] = (TX)yv;
       }
-      if (tb + R < T) cur = nxt;
+      if (tb + R < T) {
+        cur = nxt;
+#pragma unroll
+        for (int j = 0; j < R; ++j)
+#pragma unroll
+          for (int s = 0; s < S; ++s) Ecur[j][s] = Enxt[j][s];
+      }
     }
   }
 
@@ -316,7 +450,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
   if (!FULL && a.nchunks > 1 && r == 0 && ch_ok) a.ws_dsum[chunk * a.batch * dim + b * dim + ch] = dsum;
 }
 
-template <bool XB, bool DB, int S, int MODE>
+template <bool XB, bool DB, int S, int MODE, bool VEC>
 __global__ __launch_bounds__(64) void scan_kernel(ScanArgs a, int64_t groups_per_batch) {
   using TS = TileShape<S>;
   __shared__ float2 s_dx[TS::T * TS::CH];
@@ -347,29 +481,35 @@ __global__ __launch_bounds__(64) void scan_kernel(ScanArgs a, int64_t groups_per
     tiny = tiny || !(fabsf(an) >= 1e-2f);
   }
   if (!XB || __builtin_amdgcn_ballot_w64(tiny) != 0)
-    scan_body<XB, DB, S, MODE, true>(a, b, ch0, chunk, a2, ia, av, s_dx, s_gz, s_bc);
+    scan_body<XB, DB, S, MODE, true, VEC>(a, b, ch0, chunk, a2, ia, av, s_dx, s_gz, s_bc);
   else
-    scan_body<XB, DB, S, MODE, false>(a, b, ch0, chunk, a2, ia, av, s_dx, s_gz, s_bc);
+    scan_body<XB, DB, S, MODE, false, VEC>(a, b, ch0, chunk, a2, ia, av, s_dx, s_gz, s_bc);
 }
 
-// Launch one scan kernel variant for a given (act, delta) dtype pair.
-template <bool XB, bool DB>
-hipError_t launch_scan_variant(int S, int mode, const ScanArgs& a, dim3 grid, int64_t gpb, hipStream_t st) {
-#define SSM_LAUNCH_S(SV)                                                                   \
-  case SV:                                                                                 \
-    if (mode == kModeFull) scan_kernel<XB, DB, SV, kModeFull><<<grid, 64, 0, st>>>(a, gpb); \
-    else scan_kernel<XB, DB, SV, kModeState><<<grid, 64, 0, st>>>(a, gpb);                  \
-    break;
-  switch (S) {
-    SSM_LAUNCH_S(1)
-    SSM_LAUNCH_S(2)
-    SSM_LAUNCH_S(4)
-    SSM_LAUNCH_S(8)
-    SSM_LAUNCH_S(16)
-    SSM_LAUNCH_S(32)
-    default: return hipErrorInvalidValue;
+// The vectorised tile path needs whole 16-byte chunks of the B/C tile per lane.
+template <bool XB, int S>
+constexpr bool vec_shape_ok() {
+  return (TileShape<S>::T * TileShape<S>::NP) / (64 * (16 / (XB ? 2 : 4))) >= 1;
+}
+template <bool XB, int S>
+bool vec_ok(const ScanArgs& a) {
+  return vec_shape_ok<XB, S>() && a.dstate == TileShape<S>::NP;
+}
+
+// Launch the scan kernel for one (act dtype, delta dtype, states-per-lane) triple.
+template <bool XB, bool DB, int SV>
+hipError_t launch_scan_variant(int mode, const ScanArgs& a, dim3 grid, int64_t gpb, hipStream_t st) {
+  bool vec = false;
+  if constexpr (vec_shape_ok<XB, SV>()) vec = a.vec_io && vec_ok<XB, SV>(a);
+  if constexpr (vec_shape_ok<XB, SV>()) {
+    if (vec) {
+      if (mode == kModeFull) scan_kernel<XB, DB, SV, kModeFull, true><<<grid, 64, 0, st>>>(a, gpb);
+      else scan_kernel<XB, DB, SV, kModeState, true><<<grid, 64, 0, st>>>(a, gpb);
+      return hipGetLastError();
+    }
   }
-#undef SSM_LAUNCH_S
+  if (mode == kModeFull) scan_kernel<XB, DB, SV, kModeFull, false><<<grid, 64, 0, st>>>(a, gpb);
+  else scan_kernel<XB, DB, SV, kModeState, false><<<grid, 64, 0, st>>>(a, gpb);
   return hipGetLastError();
 }
 

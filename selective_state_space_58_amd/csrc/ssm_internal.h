@@ -40,6 +40,7 @@ struct ScanArgs {
   int64_t nchunks;    // number of time chunks (1 = unsplit)
   int softplus;
   int act_bf16, delta_bf16;
+  int vec_io;          // 16-byte tile I/O allowed (dim % 16 == 0, aligned, delta stored like x)
 };
 
 struct ScanPlan {
