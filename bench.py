@@ -14,8 +14,10 @@ oracle timed on the host cores (rank 0, N=1 only), and the other workloads.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -41,9 +43,41 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-others", action="store_true")
-    p.add_argument("--only", choices=["scan-2.8b", "scan-long", "ssd", "copy"], default=None,
+    p.add_argument("--only", choices=["scan-2.8b", "scan-long", "ssd", "step", "ssd-step", "copy"], default=None,
                    help="time only this other workload (for profiling); skips the headline JSON line")
     return p.parse_args()
+
+
+# Sources that determine the headline scan kernel's code and launch plan, and the
+# committed rocprofv3 counter summary of that kernel on the headline workload.
+SCAN_KERNEL_SOURCES = ["selective_state_space_58_amd/csrc/scan_impl.h",
+                       "selective_state_space_58_amd/csrc/scan_inst.hip",
+                       "selective_state_space_58_amd/csrc/scan_host.hip"]
+SCAN_COUNTER_SUMMARY = "profiles/scan_bf16_b8_d1536_l2048_n16_hbm_counters.md"
+
+
+def scan_kernel_digest():
+    h = hashlib.sha256()
+    for f in SCAN_KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the headline scan kernel, from the committed counter summary
+    (FETCH_SIZE and WRITE_SIZE scaled by a copy-kernel calibration); None when the summary is
+    missing or the kernel sources changed since the counters were taken."""
+    try:
+        with open(os.path.join(ROOT, SCAN_COUNTER_SUMMARY)) as fh:
+            text = fh.read()
+    except OSError:
+        return None
+    d = re.search(r"kernel_sources_sha256_16:\s*([0-9a-f]{16})", text)
+    t = re.search(r"traffic_bytes_per_launch:\s*(\d+)", text)
+    if d is None or t is None or d.group(1) != scan_kernel_digest():
+        return None
+    return int(t.group(1))
 
 
 def scan_bytes(cfg):
@@ -76,6 +110,22 @@ def ssd_flops(cfg):
     states = b * H * chunks * Q * N * P * 2          # chunk states
     off = b * H * chunks * Q * N * P * 2             # C H^T
     return cb + diag + states + off
+
+
+def step_bytes(cfg):
+    """Algorithmic HBM bytes of one decode step: the fp32 state read and written once, the per-channel
+    (and per-head) inputs read once, y written once."""
+    e = 2 if cfg["dtype"] == "bf16" else 4
+    b, N = cfg["batch"], cfg["dstate"]
+    if cfg["kind"] == "step":
+        D = cfg["dim"]
+        ed = 2 if cfg.get("delta_dtype", cfg["dtype"]) == "bf16" else 4
+        return (8 * b * D * N + 4 * D * N + b * D * (e * (3 if cfg["gate"] else 2) + ed) + 2 * b * N * e
+                + 8 * D)
+    H, P, G = cfg["nheads"], cfg["headdim"], cfg["ngroups"]
+    edt = 2 if cfg["dt_dtype"] == "bf16" else 4
+    return (8 * b * H * P * N + b * H * P * e * (3 if cfg["gate"] else 2) + b * H * edt + 2 * b * G * N * e
+            + 12 * H)
 
 
 def time_calls(fn, steps, warmup, torch):
@@ -137,6 +187,29 @@ def run_other(oi, steps, warmup, ssm, workloads, torch, dev):
             "mfma_frac_algorithmic": round(ssd_flops(ocfg) / (oms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
 
 
+def run_step(si, steps, warmup, ssm, workloads, torch, dev):
+    """Time one decode-step workload (state updated in place on every call)."""
+    inp, cfg = workloads.step_config_inputs(si)
+    t = workloads.to_device(inp, dev)
+    y = torch.empty_like(t["x"])
+    sp = inp["meta"]["softplus"]
+    if cfg["kind"] == "step":
+        def fn(i):
+            ssm.ssm_state_update(t["x"], t["delta"], t["A"], t["B"], t["C"], t["state"], D=t["D"], z=t["z"],
+                                 delta_bias=t["delta_bias"], delta_softplus=sp, y=y)
+        chans = cfg["batch"] * cfg["dim"]
+    else:
+        def fn(i):
+            ssm.ssd_state_update(t["x"], t["dt"], t["A"], t["B"], t["C"], t["state"], D=t["D"], z=t["z"],
+                                 dt_bias=t["dt_bias"], dt_softplus=sp, y=y)
+        chans = cfg["batch"] * cfg["nheads"] * cfg["headdim"]
+    tot, _ = time_calls(fn, steps, warmup, torch)
+    ms = tot / steps
+    nb = step_bytes(cfg)
+    return {"name": cfg["name"], "us": round(ms * 1e3, 2), "Gchannel_steps_s": round(chans / (ms * 1e-3) / 1e9, 2),
+            "hbm_GBs": round(nb / (ms * 1e-3) / 1e9, 1), "hbm_frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -165,6 +238,10 @@ def main():
         print(json.dumps({"only": "copy", "bytes_read_per_call": nbytes, "bytes_written_per_call": nbytes,
                           "ms": round(tot / steps, 4), "GBs_read_plus_write": round(2 * nbytes / (tot / steps * 1e-3) / 1e9, 1)}),
               flush=True)
+        return
+    if args.only in ("step", "ssd-step"):
+        si = {"step": 0, "ssd-step": 1}[args.only]
+        print(json.dumps({"only": args.only, **run_step(si, steps, warmup, ssm, workloads, torch, dev)}), flush=True)
         return
     if args.only is not None:
         oi = {"scan-2.8b": 2, "scan-long": 3, "ssd": 4}[args.only]
@@ -211,7 +288,7 @@ def main():
                 "frac": round(hbm_gbs / HBM_PEAK_GBS, 4)},
         "roofline": {"bound": "alu", "achieved": round(slots, 3), "peak": round(VALU_PEAK_TSLOTS, 3),
                      "unit": "T VALU lane-slots/s (algorithmic: 8 per state element)",
-                     "frac": round(slots / VALU_PEAK_TSLOTS, 4), "traffic": None,
+                     "frac": round(slots / VALU_PEAK_TSLOTS, 4), "traffic": measured_traffic(),
                      "kernel_ms": round(kern_ms, 5)},
     }
 
@@ -222,6 +299,10 @@ def main():
         torch.cuda.empty_cache()
         for oi in (2, 3, 4):
             res = run_other(oi, 5, 2, ssm, workloads, torch, dev)
+            others[res.pop("name")] = res
+            torch.cuda.empty_cache()
+        for si in range(len(workloads.STEP_CONFIGS)):
+            res = run_step(si, 20, 5, ssm, workloads, torch, dev)
             others[res.pop("name")] = res
             torch.cuda.empty_cache()
         out["other_workloads"] = others

@@ -154,6 +154,56 @@ int ssd_chunk_scan_fwd(const void* x, const void* dt, const float* A, const void
 size_t ssd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                            int64_t ngroups, int64_t dstate, int64_t chunk_size);
 
+/*
+ * Single-token state update (recurrent inference, [guide] sec. 2 recurrent
+ * view and sec. 4 inference; [ssd] inference: the past lives in a fixed-size
+ * state).  Advances every (batch, channel) state by one token, in place, and
+ * writes that token's output:
+ *
+ *   dt  = softplus?(delta[b,d] + delta_bias[d])
+ *   state[b,d,n] = exp(dt*A[d,n]) state[b,d,n] + (exp(dt*A[d,n]) - 1)/A[d,n] * B[b,n] * x[b,d]
+ *   y[b,d]  = (sum_n C[b,n] state[b,d,n] + Dskip[d] x[b,d]) * silu(z[b,d])
+ *
+ * i.e. ssm_scan_fwd with seqlen == 1 and h_final == h0 == state.
+ *
+ *   x, delta, z, y : (batch, dim)          act / delta / act / act dtype
+ *   A              : (dim, dstate) fp32
+ *   B, C           : (batch, dstate)       act dtype
+ *   Dskip, delta_bias : (dim) fp32 or NULL; z NULL for no gate
+ *   state          : (batch, dim, dstate) fp32, read and overwritten (required)
+ *   y              : required output; must not alias state
+ *   dstate         : 1..256
+ * No workspace.  Enqueued on `stream`.
+ */
+int ssm_state_update(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                     const float* Dskip, const void* z, const float* delta_bias, int delta_softplus,
+                     float* state, void* y,
+                     int64_t batch, int64_t dim, int64_t dstate,
+                     int act_dtype, int delta_dtype, void* stream);
+
+/*
+ * Mamba-2 single-token state update ([ssd] inference; the recurrent form of
+ * ssd_chunk_scan_fwd).  For head h (group g = h / (nheads/ngroups)) and head
+ * channel p:
+ *
+ *   dt  = softplus?(dt[b,h] + dt_bias[h])
+ *   state[b,h,p,n] = exp(dt*A[h]) state[b,h,p,n] + (exp(dt*A[h]) - 1)/A[h] * B[b,g,n] * x[b,h,p]
+ *   y[b,h,p] = (sum_n C[b,g,n] state[b,h,p,n] + Dskip[h] x[b,h,p]) * silu(z[b,h,p])
+ *
+ *   x, z, y : (batch, nheads, headdim)   act dtype (z NULL for no gate)
+ *   dt      : (batch, nheads)            dt dtype
+ *   A       : (nheads) fp32
+ *   B, C    : (batch, ngroups, dstate)   act dtype
+ *   Dskip, dt_bias : (nheads) fp32 or NULL
+ *   state   : (batch, nheads, headdim, dstate) fp32, read and overwritten (required)
+ *   dstate 1..256, any headdim >= 1, nheads % ngroups == 0.  No workspace.
+ */
+int ssd_state_update(const void* x, const void* dt, const float* A, const void* B, const void* C,
+                     const float* Dskip, const void* z, const float* dt_bias, int dt_softplus,
+                     float* state, void* y,
+                     int64_t batch, int64_t nheads, int64_t headdim, int64_t ngroups, int64_t dstate,
+                     int act_dtype, int dt_dtype, void* stream);
+
 /* Static text for a status code (never NULL). */
 const char* ssm_status_string(int status);
 

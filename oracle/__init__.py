@@ -154,6 +154,29 @@ def ssd_quadratic(x, dt, A, B, C, Dskip=None, z=None, dt_bias=None, dt_softplus=
     return y
 
 
+def state_update(x, delta, A, B, C, state, Dskip=None, z=None, delta_bias=None, delta_softplus=False,
+                 threads=None):
+    """One recurrent step (O1 over a single token, starting from `state`).
+    x, delta, z: (batch, dim); B, C: (batch, dstate); state: (batch, dim, dstate).
+    Returns (y (batch, dim), new state (batch, dim, dstate)), float64."""
+    x = _f64(x)
+    one = lambda a: None if a is None else _f64(a)[:, None]
+    y, hf = selective_scan(x[:, None], one(delta), A, one(B), one(C), Dskip=Dskip, z=one(z), delta_bias=delta_bias,
+                           delta_softplus=delta_softplus, h0=state, threads=threads)
+    return y[:, 0], hf
+
+
+def ssd_state_update(x, dt, A, B, C, state, Dskip=None, z=None, dt_bias=None, dt_softplus=False, threads=None):
+    """One recurrent Mamba-2 step (O2 over a single token, starting from `state`).
+    x, z: (batch, nheads, headdim); dt: (batch, nheads); B, C: (batch, ngroups, dstate);
+    state: (batch, nheads, headdim, dstate).  Returns (y, new state), float64."""
+    x = _f64(x)
+    one = lambda a: None if a is None else _f64(a)[:, None]
+    y, hf = ssd_recurrent(x[:, None], one(dt), A, one(B), one(C), Dskip=Dskip, z=one(z), dt_bias=dt_bias,
+                          dt_softplus=dt_softplus, h0=state, threads=threads)
+    return y[:, 0], hf
+
+
 def lti_conv(x, A, B, C, dt, Dskip=0.0):
     """O3: one LTI channel as a causal convolution with K_i = C Abar^i Bbar; y (seqlen,)."""
     x = _f64(x)

@@ -11,8 +11,10 @@ from ._binding import (  # noqa: F401
     library_path,
     load_library,
     ssd_chunk_scan_fwd,
+    ssd_state_update,
     ssd_workspace_bytes,
     ssm_scan_final_state,
     ssm_scan_fwd,
+    ssm_state_update,
     ssm_scan_workspace_bytes,
 )

@@ -53,6 +53,10 @@ def load_library():
         lib.ssm_scan_workspace_bytes.restype = _SZ
         lib.ssd_workspace_bytes.argtypes = [_I64] * 7
         lib.ssd_workspace_bytes.restype = _SZ
+        lib.ssm_state_update.argtypes = [_P] * 8 + [_I, _P, _P] + [_I64] * 3 + [_I, _I, _P]
+        lib.ssm_state_update.restype = _I
+        lib.ssd_state_update.argtypes = [_P] * 8 + [_I, _P, _P] + [_I64] * 5 + [_I, _I, _P]
+        lib.ssd_state_update.restype = _I
         lib.ssm_status_string.argtypes = [_I]
         lib.ssm_status_string.restype = ctypes.c_char_p
         lib.ssm_last_error.argtypes = []
@@ -206,3 +210,68 @@ def ssd_chunk_scan_fwd(x, dt, A, B, C, chunk_size=256, D=None, z=None, dt_bias=N
                                 _ptr(workspace), wsb, _stream(dev))
     _check(lib, "ssd_chunk_scan_fwd", rc)
     return (y, h_final) if (return_final_state or h_final is not None) else y
+
+
+def ssm_state_update(x, delta, A, B, C, state, D=None, z=None, delta_bias=None, delta_softplus=False, y=None):
+    """One recurrent step.  x, delta, z: (batch, dim); A: (dim, dstate) fp32; B, C: (batch, dstate);
+    state: (batch, dim, dstate) fp32, updated in place.  Returns y (batch, dim)."""
+    lib = load_library()
+    dev = x.device
+    _need(x, "x", device=dev)
+    if x.dim() != 2:
+        raise ValueError("x must be (batch, dim)")
+    batch, dim = x.shape
+    act = _act_code(x, "x")
+    _need(delta, "delta", shape=x.shape, device=dev)
+    dcode = _act_code(delta, "delta")
+    _need(A, "A", torch.float32, device=dev)
+    if A.dim() != 2 or A.shape[0] != dim:
+        raise ValueError("A must be (dim, dstate)")
+    dstate = A.shape[1]
+    _need(B, "B", x.dtype, (batch, dstate), dev)
+    _need(C, "C", x.dtype, (batch, dstate), dev)
+    _need(state, "state", torch.float32, (batch, dim, dstate), dev)
+    _need(D, "D", torch.float32, (dim,), dev)
+    _need(z, "z", x.dtype, x.shape, dev)
+    _need(delta_bias, "delta_bias", torch.float32, (dim,), dev)
+    if y is None:
+        y = torch.empty_like(x)
+    _need(y, "y", x.dtype, x.shape, dev)
+    rc = lib.ssm_state_update(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                              int(bool(delta_softplus)), _ptr(state), _ptr(y), batch, dim, dstate, act, dcode,
+                              _stream(dev))
+    _check(lib, "ssm_state_update", rc)
+    return y
+
+
+def ssd_state_update(x, dt, A, B, C, state, D=None, z=None, dt_bias=None, dt_softplus=False, y=None):
+    """One recurrent Mamba-2 step.  x, z: (batch, nheads, headdim); dt: (batch, nheads);
+    A, D, dt_bias: (nheads) fp32; B, C: (batch, ngroups, dstate);
+    state: (batch, nheads, headdim, dstate) fp32, updated in place.  Returns y."""
+    lib = load_library()
+    dev = x.device
+    _need(x, "x", device=dev)
+    if x.dim() != 3:
+        raise ValueError("x must be (batch, nheads, headdim)")
+    batch, nheads, headdim = x.shape
+    act = _act_code(x, "x")
+    _need(dt, "dt", shape=(batch, nheads), device=dev)
+    dcode = _act_code(dt, "dt")
+    _need(A, "A", torch.float32, (nheads,), dev)
+    _need(B, "B", x.dtype, device=dev)
+    if B.dim() != 3 or B.shape[0] != batch:
+        raise ValueError("B must be (batch, ngroups, dstate)")
+    ngroups, dstate = B.shape[1], B.shape[2]
+    _need(C, "C", x.dtype, B.shape, dev)
+    _need(state, "state", torch.float32, (batch, nheads, headdim, dstate), dev)
+    _need(D, "D", torch.float32, (nheads,), dev)
+    _need(z, "z", x.dtype, x.shape, dev)
+    _need(dt_bias, "dt_bias", torch.float32, (nheads,), dev)
+    if y is None:
+        y = torch.empty_like(x)
+    _need(y, "y", x.dtype, x.shape, dev)
+    rc = lib.ssd_state_update(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
+                              int(bool(dt_softplus)), _ptr(state), _ptr(y), batch, nheads, headdim, ngroups, dstate,
+                              act, dcode, _stream(dev))
+    _check(lib, "ssd_state_update", rc)
+    return y

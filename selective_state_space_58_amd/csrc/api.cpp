@@ -250,4 +250,73 @@ int ssd_chunk_scan_fwd(const void* x, const void* dt, const float* A, const void
   return launch_ssd(a, stream);
 }
 
+static int step_common(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                       const float* Dskip, const void* z, const float* bias, int softplus, float* state, void* y,
+                       int64_t batch, int64_t dim, int64_t dstate, int64_t headdim, int64_t ngroups,
+                       bool per_head, int act_dtype, int delta_dtype, void* stream) {
+  g_last_error.clear();
+  if (batch < 0 || dim < 0 || dstate < 0 || headdim < 0 || ngroups < 0) return fail(SSM_ERR_SHAPE, "negative size");
+  if (dstate == 0 || headdim == 0 || ngroups == 0) return fail(SSM_ERR_SHAPE, "dstate, headdim and ngroups must be >= 1");
+  if (dim % headdim != 0) return fail(SSM_ERR_SHAPE, "channels must be a whole number of heads");
+  const int64_t nheads = dim / headdim;
+  if (nheads % ngroups != 0) return fail(SSM_ERR_SHAPE, "nheads must be a multiple of ngroups");
+  const bool has = batch > 0 && dim > 0;
+  if ((has && (x == nullptr || delta == nullptr || B == nullptr || C == nullptr || state == nullptr ||
+               y == nullptr)) ||
+      (dim > 0 && A == nullptr))
+    return fail(SSM_ERR_NULL, "x, delta/dt, A, B, C, state and y are required");
+  if (act_dtype != SSM_F32 && act_dtype != SSM_BF16) return fail(SSM_ERR_DTYPE, "act_dtype must be SSM_F32 or SSM_BF16");
+  if (delta_dtype != SSM_F32 && delta_dtype != SSM_BF16)
+    return fail(SSM_ERR_DTYPE, "delta dtype must be SSM_F32 or SSM_BF16");
+  if (softplus != 0 && softplus != 1) return fail(SSM_ERR_SHAPE, "softplus flag must be 0 or 1");
+  if (!elems_ok({batch, dim, dstate}) || !elems_ok({dim, dstate}) || !elems_ok({batch, ngroups, dstate}))
+    return fail(SSM_ERR_SHAPE, "sizes overflow 64-bit indexing");
+  if (dstate > 256) return fail(SSM_ERR_UNSUPPORTED, "dstate > 256 is not supported");
+  const size_t as = dsize(act_dtype), ds = dsize(delta_dtype);
+  if (!aligned(x, as) || !aligned(B, as) || !aligned(C, as) || !aligned(z, as) || !aligned(y, as) ||
+      !aligned(delta, ds) || !aligned(A, 4) || !aligned(Dskip, 4) || !aligned(bias, 4) || !aligned(state, 4))
+    return fail(SSM_ERR_ALIGNMENT, "a pointer is not aligned to its element size");
+  if (!has) return SSM_OK;
+  // the state is overwritten while y is written: they must not overlap
+  const char* s0 = (const char*)state;
+  const char* s1 = s0 + (size_t)(batch * dim * dstate) * sizeof(float);
+  const char* y0 = (const char*)y;
+  const char* y1 = y0 + (size_t)(batch * dim) * as;
+  if (y0 < s1 && s0 < y1) return fail(SSM_ERR_SHAPE, "y must not overlap the state");
+  StepArgs a{};
+  a.x = x; a.delta = delta; a.A = A; a.B = B; a.C = C; a.Dskip = Dskip; a.z = z; a.delta_bias = bias;
+  a.state = state; a.y = y;
+  a.batch = batch; a.dim = dim; a.dstate = dstate; a.headdim = headdim; a.ngroups = ngroups;
+  a.a_per_head = per_head ? 1 : 0;
+  a.softplus = softplus;
+  a.act_bf16 = act_dtype == SSM_BF16;
+  a.delta_bf16 = delta_dtype == SSM_BF16;
+  const size_t bc_align = act_dtype == SSM_BF16 ? 8 : 16;
+  a.vec = dstate % 4 == 0 && aligned16(state) && (per_head || aligned16(A)) && aligned(B, bc_align) &&
+          aligned(C, bc_align);
+  return launch_state_update(a, stream);
+}
+
+int ssm_state_update(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                     const float* Dskip, const void* z, const float* delta_bias, int delta_softplus, float* state,
+                     void* y, int64_t batch, int64_t dim, int64_t dstate, int act_dtype, int delta_dtype,
+                     void* stream) {
+  return step_common(x, delta, A, B, C, Dskip, z, delta_bias, delta_softplus, state, y, batch, dim, dstate, 1, 1,
+                     false, act_dtype, delta_dtype, stream);
+}
+
+int ssd_state_update(const void* x, const void* dt, const float* A, const void* B, const void* C,
+                     const float* Dskip, const void* z, const float* dt_bias, int dt_softplus, float* state, void* y,
+                     int64_t batch, int64_t nheads, int64_t headdim, int64_t ngroups, int64_t dstate, int act_dtype,
+                     int dt_dtype, void* stream) {
+  if (nheads < 0 || headdim < 0) {
+    g_last_error.clear();
+    return fail(SSM_ERR_SHAPE, "negative size");
+  }
+  int64_t dim = 0;
+  if (!mul_ok(nheads, headdim, &dim)) return fail(SSM_ERR_SHAPE, "sizes overflow 64-bit indexing");
+  return step_common(x, dt, A, B, C, Dskip, z, dt_bias, dt_softplus, state, y, batch, dim, dstate, headdim, ngroups,
+                     true, act_dtype, dt_dtype, stream);
+}
+
 }  // extern "C"

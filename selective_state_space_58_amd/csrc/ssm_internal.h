@@ -80,6 +80,31 @@ size_t ssd_ws_bytes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headd
                     int64_t dstate, int64_t chunk);
 int launch_ssd(const SsdArgs& a, void* stream);
 
+// ---------------------------------------------------------------- single-token state update
+// Channel d of batch b belongs to head d / headdim (headdim 1: every channel is
+// its own head, the Mamba layout); dt, delta_bias and Dskip are indexed by head,
+// A by (d, n) (a_per_head 0) or by head (a_per_head 1), B and C by
+// (b, head / (nheads / ngroups), n).
+struct StepArgs {
+  const void* x;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* Dskip;
+  const void* z;
+  const float* delta_bias;
+  float* state;       // (batch, dim, dstate) fp32, updated in place
+  void* y;
+  int64_t batch, dim, dstate, headdim, ngroups;
+  int a_per_head;
+  int softplus;
+  int act_bf16, delta_bf16;
+  int vec;            // 16-byte state/A and 8/16-byte B/C accesses allowed
+};
+
+int launch_state_update(const StepArgs& a, void* stream);
+
 int device_cu_count();
 
 }  // namespace ssm

@@ -108,3 +108,48 @@ def test_workspace_queries():
     # few slices, long sequence: the time-split path needs workspace
     assert lib.ssm_scan_workspace_bytes(1, 131072, 2048, 16, 0) > 0
     assert lib.ssm_scan_workspace_bytes(8, 2048, 1536, 16, 0) == 0
+
+
+def step(lib, **kw):
+    a = dict(x=P, delta=P, A=P, B=P, C=P, D=None, z=None, bias=None, sp=0, state=P + 0x100000, y=P,
+             batch=2, dim=8, dstate=16, act=1, ddt=1, stream=None)
+    a.update(kw)
+    return lib.ssm_state_update(a["x"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"], a["sp"],
+                                a["state"], a["y"], a["batch"], a["dim"], a["dstate"], a["act"], a["ddt"],
+                                a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), 1), (dict(state=None), 1), (dict(y=None), 1), (dict(C=None), 1), (dict(A=None), 1),
+    (dict(batch=-1), 2), (dict(dstate=0), 2), (dict(sp=3), 2), (dict(y=P + 0x100000), 2),
+    (dict(act=2), 3), (dict(dstate=257), 4), (dict(state=P + 0x100002), 7), (dict(x=P + 1), 7),
+])
+def test_state_update_argument_errors(kw, code):
+    lib = _lib()
+    assert step(lib, **kw) == code
+    assert lib.ssm_last_error() != b""
+
+
+def ssd_step(lib, **kw):
+    a = dict(x=P, dt=P, A=P, B=P, C=P, D=None, z=None, bias=None, sp=0, state=P + 0x100000, y=P,
+             batch=2, nheads=4, headdim=64, ngroups=2, dstate=128, act=1, ddt=0, stream=None)
+    a.update(kw)
+    return lib.ssd_state_update(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"], a["sp"],
+                                a["state"], a["y"], a["batch"], a["nheads"], a["headdim"], a["ngroups"], a["dstate"],
+                                a["act"], a["ddt"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=None), 1), (dict(state=None), 1), (dict(nheads=3), 2), (dict(headdim=0), 2), (dict(nheads=-4), 2),
+    (dict(ddt=9), 3), (dict(dstate=300), 4), (dict(A=P + 1), 7),
+])
+def test_ssd_state_update_argument_errors(kw, code):
+    lib = _lib()
+    assert ssd_step(lib, **kw) == code
+
+
+def test_state_update_empty_is_noop():
+    lib = _lib()
+    assert step(lib, batch=0) == 0
+    assert step(lib, dim=0) == 0
+    assert ssd_step(lib, nheads=0) == 0

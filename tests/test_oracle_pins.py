@@ -208,3 +208,42 @@ def test_empty_and_single_step(oracle_mod):
     y, hf = oracle_mod.selective_scan(x, dt, A, B, C, h0=h0)
     h = np.exp(dt[0, 0, :, None] * A) * h0[0] + np.expm1(dt[0, 0, :, None] * A) / A * B[0, 0] * x[0, 0, :, None]
     assert rel(hf[0], h) < 1e-14 and rel(y[0, 0], h @ C[0, 0]) < 1e-14
+
+
+def test_state_update_step_closed_form_and_composition(oracle_mod):
+    # one decode step written out: dt = softplus(u + bias); h = e^{dt a} h0 + expm1(dt a)/a B x;
+    # y = (C.h + D x) silu(z)
+    rng = np.random.default_rng(50)
+    b, D, N, T = 3, 5, 6, 9
+    A = -rng.uniform(0.3, 5, (D, N)); bias = rng.standard_normal(D); Ds = rng.standard_normal(D)
+    x = rng.standard_normal((b, T, D)); u = rng.standard_normal((b, T, D)); z = rng.standard_normal((b, T, D))
+    B = rng.standard_normal((b, T, N)); C = rng.standard_normal((b, T, N)); h0 = rng.standard_normal((b, D, N))
+    y1, h1 = oracle_mod.state_update(x[:, 0], u[:, 0], A, B[:, 0], C[:, 0], h0, Dskip=Ds, z=z[:, 0],
+                                     delta_bias=bias, delta_softplus=True)
+    dt = np.logaddexp(0.0, u[:, 0] + bias)[:, :, None]
+    h = np.exp(dt * A) * h0 + np.expm1(dt * A) / A * B[:, 0, None, :] * x[:, 0, :, None]
+    yr = (np.einsum("bdn,bn->bd", h, C[:, 0]) + Ds * x[:, 0]) * z[:, 0] * expit(z[:, 0])
+    assert rel(h1, h) < 1e-14 and rel(y1, yr) < 1e-13
+    # T steps, each from the previous state, equal the scan over the T tokens
+    y_seq, h_seq = oracle_mod.selective_scan(x, u, A, B, C, Dskip=Ds, z=z, delta_bias=bias, delta_softplus=True,
+                                             h0=h0)
+    st = h0
+    for t in range(T):
+        yt, st = oracle_mod.state_update(x[:, t], u[:, t], A, B[:, t], C[:, t], st, Dskip=Ds, z=z[:, t],
+                                         delta_bias=bias, delta_softplus=True)
+        assert rel(yt, y_seq[:, t]) < 1e-13
+    assert rel(st, h_seq) < 1e-14
+
+
+@pytest.mark.parametrize("G", [1, 2])
+def test_ssd_state_update_steps_equal_quadratic_form(oracle_mod, G):
+    # successive Mamba-2 decode steps reproduce the matrix (quadratic) form over the same tokens
+    rng = np.random.default_rng(60 + G)
+    inp = _ssd_inputs(rng, 2, 11, 4, 3, G, 5)
+    y_quad = oracle_mod.ssd_quadratic(dt_softplus=True, **inp)
+    st = inp["h0"]
+    for t in range(11):
+        yt, st = oracle_mod.ssd_state_update(inp["x"][:, t], inp["dt"][:, t], inp["A"], inp["B"][:, t],
+                                             inp["C"][:, t], st, Dskip=inp["Dskip"], z=inp["z"][:, t],
+                                             dt_bias=inp["dt_bias"], dt_softplus=True)
+        assert rel(yt, y_quad[:, t]) < 1e-12

@@ -34,6 +34,17 @@ CONFIGS = [
          a_lo=1.0, a_hi=16.0, gate=False, skip=False, final_state=True),
 ]
 
+# Single-token decode steps (recurrent inference) at serving batch sizes: the
+# 2.8B-like Mamba layer (5120 channels, 16 states) and a Mamba-2 2.7B-like
+# layer (80 heads of 64 channels, 128 states, one group).
+STEP_CONFIGS = [
+    dict(name="step_bf16_b128_d5120_n16", kind="step", batch=128, dim=5120, dstate=16, dtype="bf16",
+         delta_dtype="bf16", dt_lo=1e-3, dt_hi=1e-1, gate=True, softplus=True, skip=True),
+    dict(name="ssd_step_bf16_b128_h80_p64_n128", kind="ssd_step", batch=128, nheads=80, headdim=64, ngroups=1,
+         dstate=128, dtype="bf16", dt_dtype="f32", dt_lo=1e-3, dt_hi=1e-1, a_lo=1.0, a_hi=16.0, gate=True,
+         skip=True, dt_softplus=True),
+]
+
 
 def round_to(arr: np.ndarray, dtype: str) -> np.ndarray:
     """Round float values to `dtype` ("f32" or "bf16", nearest even); returns float32 holding them."""
@@ -101,6 +112,66 @@ def ssd_inputs(batch, seqlen, nheads, headdim, dstate, ngroups=1, dtype="bf16", 
     return out
 
 
+def step_inputs(batch, dim, dstate, dtype="bf16", delta_dtype=None, seed=0, dt_lo=1e-3, dt_hi=1e-1, gate=True,
+                softplus=True, skip=True, **_):
+    """Inputs of one selective-scan decode step: x, delta, z (batch, dim); B, C (batch, dstate);
+    state (batch, dim, dstate) ~ N(0, 1) fp32.  With softplus, delta ~ N(0, 1) plus a per-channel bias
+    placing softplus(bias) log-uniformly in [dt_lo, dt_hi]; otherwise delta is log-uniform itself."""
+    delta_dtype = delta_dtype or dtype
+    rng = np.random.default_rng(seed)
+    out = {}
+    out["A"] = np.broadcast_to(-np.arange(1, dstate + 1, dtype=np.float32), (dim, dstate)).copy()
+    out["x"] = round_to(rng.standard_normal((batch, dim), dtype=np.float32), dtype)
+    if softplus:
+        dt0 = _loguniform(rng, dt_lo, dt_hi, (dim,)).astype(np.float64)
+        out["delta_bias"] = np.log(np.expm1(dt0)).astype(np.float32)
+        out["delta"] = round_to(rng.standard_normal((batch, dim), dtype=np.float32), delta_dtype)
+    else:
+        out["delta_bias"] = None
+        out["delta"] = round_to(_loguniform(rng, dt_lo, dt_hi, (batch, dim)), delta_dtype)
+    out["B"] = round_to(rng.standard_normal((batch, dstate), dtype=np.float32), dtype)
+    out["C"] = round_to(rng.standard_normal((batch, dstate), dtype=np.float32), dtype)
+    out["D"] = rng.standard_normal(dim, dtype=np.float32) if skip else None
+    out["z"] = round_to(rng.standard_normal((batch, dim), dtype=np.float32), dtype) if gate else None
+    out["state"] = rng.standard_normal((batch, dim, dstate), dtype=np.float32)
+    out["meta"] = dict(kind="step", dtype=dtype, delta_dtype=delta_dtype, softplus=bool(softplus))
+    return out
+
+
+def ssd_step_inputs(batch, nheads, headdim, dstate, ngroups=1, dtype="bf16", dt_dtype="f32", seed=0, dt_lo=1e-3,
+                    dt_hi=1e-1, a_lo=1.0, a_hi=16.0, gate=True, skip=True, dt_softplus=True, **_):
+    """Inputs of one Mamba-2 decode step: x, z (batch, nheads, headdim); dt (batch, nheads);
+    A ~ -U[a_lo, a_hi] per head; B, C (batch, ngroups, dstate); state ~ N(0, 1) fp32."""
+    rng = np.random.default_rng(seed)
+    out = {}
+    out["x"] = round_to(rng.standard_normal((batch, nheads, headdim), dtype=np.float32), dtype)
+    if dt_softplus:
+        dt0 = _loguniform(rng, dt_lo, dt_hi, (nheads,)).astype(np.float64)
+        out["dt_bias"] = np.log(np.expm1(dt0)).astype(np.float32)
+        out["dt"] = round_to(rng.standard_normal((batch, nheads), dtype=np.float32), dt_dtype)
+    else:
+        out["dt_bias"] = None
+        out["dt"] = round_to(_loguniform(rng, dt_lo, dt_hi, (batch, nheads)), dt_dtype)
+    out["A"] = (-rng.uniform(a_lo, a_hi, nheads)).astype(np.float32)
+    out["B"] = round_to(rng.standard_normal((batch, ngroups, dstate), dtype=np.float32), dtype)
+    out["C"] = round_to(rng.standard_normal((batch, ngroups, dstate), dtype=np.float32), dtype)
+    out["D"] = rng.standard_normal(nheads, dtype=np.float32) if skip else None
+    out["z"] = round_to(rng.standard_normal((batch, nheads, headdim), dtype=np.float32), dtype) if gate else None
+    out["state"] = rng.standard_normal((batch, nheads, headdim, dstate), dtype=np.float32)
+    out["meta"] = dict(kind="ssd_step", dtype=dtype, dt_dtype=dt_dtype, softplus=bool(dt_softplus))
+    return out
+
+
+def step_config_inputs(index: int, **overrides):
+    """Inputs of decode workload `index` of STEP_CONFIGS (seed 142 + index)."""
+    cfg = dict(STEP_CONFIGS[index])
+    cfg.update(overrides)
+    seed = 142 + index
+    if cfg["kind"] == "step":
+        return step_inputs(seed=seed, **cfg), cfg
+    return ssd_step_inputs(seed=seed, **cfg), cfg
+
+
 def config_inputs(index: int, **overrides):
     """Inputs of workload `index` (seed 42 + index), optionally with overridden sizes."""
     cfg = dict(CONFIGS[index])
@@ -118,7 +189,7 @@ def to_device(inp: dict, device) -> dict:
     """Device tensors in their storage dtypes (exact: values are already rounded)."""
     meta = inp["meta"]
     act = _TORCH[meta["dtype"]]
-    fp32_keys = {"A", "D", "delta_bias", "dt_bias", "h0"}
+    fp32_keys = {"A", "D", "delta_bias", "dt_bias", "h0", "state"}
     out = {}
     for k, v in inp.items():
         if k == "meta" or v is None:
