@@ -43,7 +43,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-others", action="store_true")
-    p.add_argument("--only", choices=["scan-2.8b", "scan-long", "ssd", "step", "ssd-step", "copy"], default=None,
+    p.add_argument("--only", choices=["scan-2.8b", "scan-long", "ssd", "step", "ssd-step", "conv", "copy"],
+                   default=None,
                    help="time only this other workload (for profiling); skips the headline JSON line")
     return p.parse_args()
 
@@ -210,6 +211,24 @@ def run_step(si, steps, warmup, ssm, workloads, torch, dev):
             "hbm_GBs": round(nb / (ms * 1e-3) / 1e9, 1), "hbm_frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def run_conv(ci, steps, warmup, ssm, workloads, torch, dev):
+    """Time the causal conv1d + SiLU on its workload (x read once, out written once)."""
+    cfg = workloads.CONV_CONFIGS[ci]
+    inp = workloads.conv_inputs(seed=242 + ci, **cfg)
+    t = workloads.to_device(inp, dev)
+    out = torch.empty_like(t["x"])
+
+    def fn(i):
+        ssm.ssm_causal_conv1d_fwd(t["x"], t["weight"], t["bias"], out=out)
+    tot, _ = time_calls(fn, steps, warmup, torch)
+    ms = tot / steps
+    e = 2 if cfg["dtype"] == "bf16" else 4
+    tc = cfg["batch"] * cfg["seqlen"] * cfg["dim"]
+    nb = 2 * tc * e + cfg["dim"] * (cfg["width"] + 1) * 4
+    return {"name": cfg["name"], "us": round(ms * 1e3, 2), "Gtc_s": round(tc / (ms * 1e-3) / 1e9, 2),
+            "hbm_GBs": round(nb / (ms * 1e-3) / 1e9, 1), "hbm_frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -238,6 +257,9 @@ def main():
         print(json.dumps({"only": "copy", "bytes_read_per_call": nbytes, "bytes_written_per_call": nbytes,
                           "ms": round(tot / steps, 4), "GBs_read_plus_write": round(2 * nbytes / (tot / steps * 1e-3) / 1e9, 1)}),
               flush=True)
+        return
+    if args.only == "conv":
+        print(json.dumps({"only": "conv", **run_conv(0, steps, warmup, ssm, workloads, torch, dev)}), flush=True)
         return
     if args.only in ("step", "ssd-step"):
         si = {"step": 0, "ssd-step": 1}[args.only]
@@ -303,6 +325,10 @@ def main():
             torch.cuda.empty_cache()
         for si in range(len(workloads.STEP_CONFIGS)):
             res = run_step(si, 20, 5, ssm, workloads, torch, dev)
+            others[res.pop("name")] = res
+            torch.cuda.empty_cache()
+        for ci in range(len(workloads.CONV_CONFIGS)):
+            res = run_conv(ci, 20, 5, ssm, workloads, torch, dev)
             others[res.pop("name")] = res
             torch.cuda.empty_cache()
         out["other_workloads"] = others

@@ -204,6 +204,32 @@ int ssd_state_update(const void* x, const void* dt, const float* A, const void* 
                      int64_t batch, int64_t nheads, int64_t headdim, int64_t ngroups, int64_t dstate,
                      int act_dtype, int dt_dtype, void* stream);
 
+/*
+ * Causal depthwise 1-D convolution + SiLU, the step of the Mamba block that
+ * produces the scan's input ([guide] sec. 5, the Mamba block: Conv1d with one
+ * group per channel, padding width-1, output trimmed to seqlen, then silu):
+ *
+ *   out[b,t,d] = silu( bias[d] + sum_{k<width} weight[d,k] * xx[b, t-(width-1)+k, d] )
+ *
+ * where xx[b,i,d] = x[b,i,d] for i >= 0 and, for i < 0, the inputs carried in
+ * from a previous segment, state_in[b, d, (width-1)+i] (oldest first; zeros
+ * when state_in is NULL, i.e. the block's zero padding).  state_out receives
+ * the last width-1 inputs of that extended sequence, so a later segment, or
+ * a single decode token (seqlen 1), continues the same convolution.
+ *
+ *   x, out              : (batch, seqlen, dim)  act dtype; out must not overlap x
+ *   weight              : (dim, width) fp32;  bias : (dim) fp32 or NULL
+ *   state_in, state_out : (batch, dim, width-1) act dtype or NULL; state_out
+ *                         may be the same buffer as state_in (in-place update)
+ *   silu                : 1 applies silu, 0 returns the convolution alone
+ *   width               : 1..8
+ * No workspace.  Enqueued on `stream`.
+ */
+int ssm_causal_conv1d_fwd(const void* x, const float* weight, const float* bias, const void* state_in,
+                          int silu, void* out, void* state_out,
+                          int64_t batch, int64_t seqlen, int64_t dim, int64_t width,
+                          int act_dtype, void* stream);
+
 /* Static text for a status code (never NULL). */
 const char* ssm_status_string(int status);
 

@@ -44,8 +44,8 @@ def _load():
     global _lib
     with _lock:
         if _lib is None:
-            if not os.path.exists(_LIB):
-                build(force=False)
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build(force=True)
             lib = ctypes.CDLL(_LIB)
             P = ctypes.c_void_p
             I64 = ctypes.c_int64
@@ -58,6 +58,8 @@ def _load():
             lib.oracle_ssd_quadratic.restype = None
             lib.oracle_lti_conv.argtypes = [P, P, P, P, ctypes.c_double, ctypes.c_double, P, I64, I64]
             lib.oracle_lti_conv.restype = None
+            lib.oracle_causal_conv1d.argtypes = [P] * 4 + [I, P, P] + [I64] * 6
+            lib.oracle_causal_conv1d.restype = None
             _lib = lib
     return _lib
 
@@ -187,3 +189,24 @@ def lti_conv(x, A, B, C, dt, Dskip=0.0):
     _load().oracle_lti_conv(_ptr(x), _ptr(A), _ptr(B), _ptr(C), float(dt), float(Dskip), _ptr(y),
                             x.shape[0], A.shape[0])
     return y
+
+
+def causal_conv1d(x, weight, bias=None, state_in=None, silu=True, want_state=False, threads=None):
+    """O4: causal depthwise conv1d (+ SiLU) of x (batch, seqlen, dim) with weight (dim, width).
+    state_in: (batch, dim, width-1) inputs carried in from a previous segment (zeros if None).
+    Returns out (batch, seqlen, dim) and, with want_state, state_out (batch, dim, width-1); float64."""
+    x = _f64(x)
+    batch, seqlen, dim = x.shape
+    weight = _f64(weight)
+    if weight.ndim != 2 or weight.shape[0] != dim:
+        raise ValueError("oracle: weight must be (dim, width)")
+    width = weight.shape[1]
+    bias = _f64(bias, (dim,))
+    state_in = _f64(state_in, (batch, dim, width - 1))
+    out = np.empty_like(x)
+    st = np.empty((batch, dim, width - 1), dtype=np.float64) if want_state else None
+    lib = _load()
+    _run_slices(lambda s0, s1: lib.oracle_causal_conv1d(
+        _ptr(x), _ptr(weight), _ptr(bias), _ptr(state_in), int(bool(silu)), _ptr(out), _ptr(st),
+        batch, seqlen, dim, width, s0, s1), batch * dim, threads)
+    return (out, st) if want_state else out

@@ -249,3 +249,57 @@ void oracle_lti_conv(const double* x, const double* A, const double* B, const do
   free(pw);
   free(K);
 }
+
+/*
+ * O4. Causal depthwise 1-D convolution of the Mamba block's x branch, then
+ * SiLU (P1 sec. 5, the Mamba block: Conv1d with one group per channel,
+ * padding width-1 and the output trimmed to the first seqlen positions,
+ * then silu).  Per batch b and channel d, with weights w[d][0..W-1]:
+ *
+ *   out[t] = silu( bias_d + sum_{k=0..W-1} w[d][k] * xx[t - (W-1) + k] )
+ *
+ * where xx[i] = x[b, i, d] for i >= 0, and for -(W-1) <= i < 0 the inputs
+ * carried in from a previous segment, state_in[b, d, (W-1) + i] (oldest
+ * first; zeros when state_in is NULL, which is the padding of the block).
+ * state_out[b, d, j] = xx[seqlen - (W-1) + j], the last W-1 inputs of the
+ * extended sequence, so that a later segment (or a single decode token)
+ * continues the same convolution.  silu_on = 0 leaves out the SiLU.
+ *
+ *   x, out : (batch, seqlen, dim); w : (dim, width); bias : (dim) or NULL
+ *   state_in, state_out : (batch, dim, width-1) or NULL
+ * Slices s = b*dim + d in [s_begin, s_end).
+ */
+static double conv_ext(const double* x, const double* state_in, int64_t b, int64_t d, int64_t i,
+                       int64_t seqlen, int64_t dim, int64_t width) {
+  if (i >= 0) return x[(b * seqlen + i) * dim + d];
+  if (!state_in) return 0.0;
+  return state_in[(b * dim + d) * (width - 1) + (width - 1) + i];
+}
+
+void oracle_causal_conv1d(const double* x, const double* w, const double* bias, const double* state_in,
+                          int silu_on, double* out, double* state_out, int64_t batch, int64_t seqlen,
+                          int64_t dim, int64_t width, int64_t s_begin, int64_t s_end) {
+  (void)batch;
+  for (int64_t s = s_begin; s < s_end; ++s) {
+    const int64_t b = s / dim, d = s % dim;
+    double* keep = NULL;
+    if (state_out && width > 1) {
+      /* read the carried-in values first: state_out may be the same buffer */
+      keep = (double*)malloc(sizeof(double) * (size_t)(width - 1));
+      for (int64_t j = 0; j < width - 1; ++j)
+        keep[j] = conv_ext(x, state_in, b, d, seqlen - (width - 1) + j, seqlen, dim, width);
+    }
+    if (out) {
+      for (int64_t t = 0; t < seqlen; ++t) {
+        double acc = bias ? bias[d] : 0.0;
+        for (int64_t k = 0; k < width; ++k)
+          acc += w[d * width + k] * conv_ext(x, state_in, b, d, t - (width - 1) + k, seqlen, dim, width);
+        out[(b * seqlen + t) * dim + d] = silu_on ? silu(acc) : acc;
+      }
+    }
+    if (keep) {
+      for (int64_t j = 0; j < width - 1; ++j) state_out[(b * dim + d) * (width - 1) + j] = keep[j];
+      free(keep);
+    }
+  }
+}

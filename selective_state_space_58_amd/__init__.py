@@ -10,6 +10,7 @@ from ._binding import (  # noqa: F401
     SSMError,
     library_path,
     load_library,
+    ssm_causal_conv1d_fwd,
     ssd_chunk_scan_fwd,
     ssd_state_update,
     ssd_workspace_bytes,

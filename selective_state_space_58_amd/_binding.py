@@ -57,6 +57,8 @@ def load_library():
         lib.ssm_state_update.restype = _I
         lib.ssd_state_update.argtypes = [_P] * 8 + [_I, _P, _P] + [_I64] * 5 + [_I, _I, _P]
         lib.ssd_state_update.restype = _I
+        lib.ssm_causal_conv1d_fwd.argtypes = [_P] * 4 + [_I, _P, _P] + [_I64] * 4 + [_I, _P]
+        lib.ssm_causal_conv1d_fwd.restype = _I
         lib.ssm_status_string.argtypes = [_I]
         lib.ssm_status_string.restype = ctypes.c_char_p
         lib.ssm_last_error.argtypes = []
@@ -275,3 +277,33 @@ def ssd_state_update(x, dt, A, B, C, state, D=None, z=None, dt_bias=None, dt_sof
                               act, dcode, _stream(dev))
     _check(lib, "ssd_state_update", rc)
     return y
+
+
+def ssm_causal_conv1d_fwd(x, weight, bias=None, state_in=None, silu=True, out=None, state_out=None,
+                          return_state=False):
+    """Causal depthwise conv1d (+ SiLU).  x: (batch, seqlen, dim); weight: (dim, width) fp32;
+    bias: (dim) fp32; state_in/state_out: (batch, dim, width-1) in x's dtype (state_out may be
+    state_in for an in-place update).  Returns out, or (out, state_out) with return_state."""
+    lib = load_library()
+    dev = x.device
+    _need(x, "x", device=dev)
+    if x.dim() != 3:
+        raise ValueError("x must be (batch, seqlen, dim)")
+    batch, seqlen, dim = x.shape
+    act = _act_code(x, "x")
+    _need(weight, "weight", torch.float32, device=dev)
+    if weight.dim() != 2 or weight.shape[0] != dim:
+        raise ValueError("weight must be (dim, width)")
+    width = weight.shape[1]
+    _need(bias, "bias", torch.float32, (dim,), dev)
+    _need(state_in, "state_in", x.dtype, (batch, dim, width - 1), dev)
+    if out is None:
+        out = torch.empty_like(x)
+    _need(out, "out", x.dtype, x.shape, dev)
+    if return_state and state_out is None:
+        state_out = torch.empty((batch, dim, width - 1), dtype=x.dtype, device=dev)
+    _need(state_out, "state_out", x.dtype, (batch, dim, width - 1), dev)
+    rc = lib.ssm_causal_conv1d_fwd(_ptr(x), _ptr(weight), _ptr(bias), _ptr(state_in), int(bool(silu)), _ptr(out),
+                                   _ptr(state_out), batch, seqlen, dim, width, act, _stream(dev))
+    _check(lib, "ssm_causal_conv1d_fwd", rc)
+    return (out, state_out) if (return_state or state_out is not None) else out

@@ -319,4 +319,38 @@ int ssd_state_update(const void* x, const void* dt, const float* A, const void* 
                      true, act_dtype, dt_dtype, stream);
 }
 
+int ssm_causal_conv1d_fwd(const void* x, const float* weight, const float* bias, const void* state_in, int silu,
+                          void* out, void* state_out, int64_t batch, int64_t seqlen, int64_t dim, int64_t width,
+                          int act_dtype, void* stream) {
+  g_last_error.clear();
+  if (batch < 0 || seqlen < 0 || dim < 0 || width < 0) return fail(SSM_ERR_SHAPE, "negative size");
+  if (width == 0) return fail(SSM_ERR_SHAPE, "width must be >= 1");
+  if (silu != 0 && silu != 1) return fail(SSM_ERR_SHAPE, "silu must be 0 or 1");
+  if (act_dtype != SSM_F32 && act_dtype != SSM_BF16) return fail(SSM_ERR_DTYPE, "act_dtype must be SSM_F32 or SSM_BF16");
+  const bool has_tok = batch > 0 && seqlen > 0 && dim > 0;
+  if ((has_tok && (x == nullptr || out == nullptr)) || (dim > 0 && weight == nullptr))
+    return fail(SSM_ERR_NULL, "x, weight and out are required");
+  if (!elems_ok({batch, seqlen, dim}) || !elems_ok({dim, width}) || !elems_ok({batch, dim, width}))
+    return fail(SSM_ERR_SHAPE, "sizes overflow 64-bit indexing");
+  if (width > 8) return fail(SSM_ERR_UNSUPPORTED, "conv width > 8 is not supported");
+  const size_t as = dsize(act_dtype);
+  if (!aligned(x, as) || !aligned(out, as) || !aligned(state_in, as) || !aligned(state_out, as) ||
+      !aligned(weight, 4) || !aligned(bias, 4))
+    return fail(SSM_ERR_ALIGNMENT, "a pointer is not aligned to its element size");
+  if (batch == 0 || dim == 0) return SSM_OK;
+  if (has_tok) {
+    const char* x0 = (const char*)x;
+    const char* x1 = x0 + (size_t)(batch * seqlen * dim) * as;
+    const char* o0 = (const char*)out;
+    const char* o1 = o0 + (size_t)(batch * seqlen * dim) * as;
+    if (o0 < x1 && x0 < o1) return fail(SSM_ERR_SHAPE, "out must not overlap x");
+  }
+  ConvArgs a{};
+  a.x = x; a.w = weight; a.bias = bias; a.state_in = state_in; a.out = out; a.state_out = state_out;
+  a.batch = batch; a.seqlen = seqlen; a.dim = dim; a.width = width; a.silu = silu;
+  a.act_bf16 = act_dtype == SSM_BF16;
+  a.vec = dim % 8 == 0 && aligned16(x) && aligned16(out);
+  return launch_conv(a, stream);
+}
+
 }  // extern "C"

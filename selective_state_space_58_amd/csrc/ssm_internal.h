@@ -105,6 +105,22 @@ struct StepArgs {
 
 int launch_state_update(const StepArgs& a, void* stream);
 
+// ---------------------------------------------------------------- causal conv1d (+ SiLU)
+struct ConvArgs {
+  const void* x;          // (batch, seqlen, dim) act dtype
+  const float* w;         // (dim, width)
+  const float* bias;      // (dim) or null
+  const void* state_in;   // (batch, dim, width-1) act dtype or null (zeros)
+  void* out;              // (batch, seqlen, dim) act dtype
+  void* state_out;        // (batch, dim, width-1) act dtype or null; may alias state_in
+  int64_t batch, seqlen, dim, width;
+  int silu;
+  int act_bf16;
+  int vec;                // 8 channels per thread with 16/32-byte accesses
+};
+
+int launch_conv(const ConvArgs& a, void* stream);
+
 int device_cu_count();
 
 }  // namespace ssm

@@ -153,3 +153,28 @@ def test_state_update_empty_is_noop():
     assert step(lib, batch=0) == 0
     assert step(lib, dim=0) == 0
     assert ssd_step(lib, nheads=0) == 0
+
+
+def conv(lib, **kw):
+    a = dict(x=P, w=P, bias=None, sin=None, silu=1, out=P + 0x100000, sout=None, batch=2, seqlen=8, dim=16, width=4,
+             act=1, stream=None)
+    a.update(kw)
+    return lib.ssm_causal_conv1d_fwd(a["x"], a["w"], a["bias"], a["sin"], a["silu"], a["out"], a["sout"], a["batch"],
+                                     a["seqlen"], a["dim"], a["width"], a["act"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), 1), (dict(w=None), 1), (dict(out=None), 1), (dict(width=0), 2), (dict(silu=2), 2),
+    (dict(seqlen=-1), 2), (dict(out=P + 8), 2), (dict(act=4), 3), (dict(width=9), 4), (dict(x=P + 1), 7),
+    (dict(w=P + 2), 7),
+])
+def test_conv_argument_errors(kw, code):
+    lib = _lib()
+    assert conv(lib, **kw) == code
+    assert lib.ssm_last_error() != b""
+
+
+def test_conv_empty_is_noop():
+    lib = _lib()
+    assert conv(lib, batch=0) == 0
+    assert conv(lib, dim=0) == 0

@@ -247,3 +247,41 @@ def test_ssd_state_update_steps_equal_quadratic_form(oracle_mod, G):
                                              inp["C"][:, t], st, Dskip=inp["Dskip"], z=inp["z"][:, t],
                                              dt_bias=inp["dt_bias"], dt_softplus=True)
         assert rel(yt, y_quad[:, t]) < 1e-12
+
+
+def test_causal_conv1d_against_numpy_and_torch(oracle_mod):
+    # the block's depthwise causal conv: numpy's full convolution with the reversed taps, first L
+    # outputs; and torch's Conv1d formulation (padding W-1, one group per channel, trimmed to L)
+    import torch
+    rng = np.random.default_rng(70)
+    b, L, D, W = 2, 23, 5, 4
+    x = rng.standard_normal((b, L, D)); w = rng.standard_normal((D, W)); bias = rng.standard_normal(D)
+    out = oracle_mod.causal_conv1d(x, w, bias, silu=False)
+    for bi in range(b):
+        for d in range(D):
+            ref = np.convolve(x[bi, :, d], w[d, ::-1])[:L] + bias[d]
+            assert rel(out[bi, :, d], ref) < 1e-14
+    conv = torch.nn.functional.conv1d(torch.from_numpy(x).transpose(1, 2), torch.from_numpy(w)[:, None, :],
+                                      torch.from_numpy(bias), padding=W - 1, groups=D)[:, :, :L]
+    ref = torch.nn.functional.silu(conv).transpose(1, 2).numpy()
+    assert rel(oracle_mod.causal_conv1d(x, w, bias, silu=True), ref) < 1e-14
+
+
+def test_causal_conv1d_impulse_and_state_handoff(oracle_mod):
+    rng = np.random.default_rng(71)
+    D, W, L = 3, 4, 17
+    w = rng.standard_normal((D, W))
+    x = np.zeros((1, L, D)); x[0, 0, :] = 1.0
+    out = oracle_mod.causal_conv1d(x, w, silu=False)
+    for t in range(L):                       # impulse response: the taps, newest first
+        assert np.allclose(out[0, t], w[:, W - 1 - t] if t < W else 0.0, rtol=0, atol=1e-15)
+    # a sequence split anywhere, the second part carrying the first part's state, equals the whole
+    b = 2
+    x = rng.standard_normal((b, L, D)); bias = rng.standard_normal(D); s0 = rng.standard_normal((b, D, W - 1))
+    full, st_full = oracle_mod.causal_conv1d(x, w, bias, state_in=s0, want_state=True)
+    for m in (0, 1, 2, 3, 9):
+        o1, st1 = oracle_mod.causal_conv1d(x[:, :m], w, bias, state_in=s0, want_state=True)
+        o2, st2 = oracle_mod.causal_conv1d(x[:, m:], w, bias, state_in=st1, want_state=True)
+        assert rel(np.concatenate([o1, o2], 1), full) < 1e-14 and np.array_equal(st2, st_full)
+    # the carried state is the last W-1 inputs, oldest first
+    assert np.array_equal(st_full, np.transpose(x[:, L - (W - 1):, :], (0, 2, 1)))

@@ -172,6 +172,29 @@ def step_config_inputs(index: int, **overrides):
     return ssd_step_inputs(seed=seed, **cfg), cfg
 
 
+# Causal conv1d + SiLU feeding the scan, on the headline layer's shape (d_conv 4).
+CONV_CONFIGS = [
+    dict(name="conv1d_silu_bf16_b8_l2048_d1536_w4", kind="conv", batch=8, seqlen=2048, dim=1536, width=4,
+         dtype="bf16"),
+]
+
+
+def conv_inputs(batch, seqlen, dim, width, dtype="bf16", seed=0, bias=True, state=False, **_):
+    """Inputs of the causal depthwise conv1d: x ~ N(0,1) (batch, seqlen, dim); weight and bias
+    ~ U(-1/sqrt(width), 1/sqrt(width)) (the Conv1d default range for one input channel per group);
+    optional carried-in state (batch, dim, width-1) ~ N(0,1) in x's dtype."""
+    rng = np.random.default_rng(seed)
+    k = 1.0 / np.sqrt(width)
+    out = {}
+    out["x"] = round_to(rng.standard_normal((batch, seqlen, dim), dtype=np.float32), dtype)
+    out["weight"] = rng.uniform(-k, k, (dim, width)).astype(np.float32)
+    out["bias"] = rng.uniform(-k, k, dim).astype(np.float32) if bias else None
+    out["state_in"] = (round_to(rng.standard_normal((batch, dim, width - 1), dtype=np.float32), dtype)
+                       if state else None)
+    out["meta"] = dict(kind="conv", dtype=dtype)
+    return out
+
+
 def config_inputs(index: int, **overrides):
     """Inputs of workload `index` (seed 42 + index), optionally with overridden sizes."""
     cfg = dict(CONFIGS[index])
@@ -189,7 +212,7 @@ def to_device(inp: dict, device) -> dict:
     """Device tensors in their storage dtypes (exact: values are already rounded)."""
     meta = inp["meta"]
     act = _TORCH[meta["dtype"]]
-    fp32_keys = {"A", "D", "delta_bias", "dt_bias", "h0", "state"}
+    fp32_keys = {"A", "D", "delta_bias", "dt_bias", "h0", "state", "weight", "bias"}
     out = {}
     for k, v in inp.items():
         if k == "meta" or v is None:
