@@ -168,7 +168,7 @@ static int scan_common(const void* x, const void* delta, const float* A, const v
   a.softplus = delta_softplus;
   a.act_bf16 = act_dtype == SSM_BF16;
   a.delta_bf16 = delta_dtype == SSM_BF16;
-  a.vec_io = (dim % kChPerWave == 0) && act_dtype == delta_dtype && aligned16(x) && aligned16(delta) &&
+  a.vec_io = act_dtype == delta_dtype && aligned16(x) && aligned16(delta) &&
              aligned16(B) && (final_only || aligned16(C)) && (final_only || aligned16(z));
   if (ws != nullptr) {
     const size_t st_bytes = (size_t)p.nchunks * (size_t)(batch * dim * dstate) * sizeof(float);

@@ -8,13 +8,16 @@
 
 namespace ssm {
 
-#define SSM_DECL(XB, DB, S) \
-  hipError_t launch_scan_x##XB##_d##DB##_s##S(int mode, const ScanArgs& a, dim3 grid, int64_t gpb, hipStream_t st);
-#define SSM_DECL_ALL_S(XB, DB) SSM_DECL(XB, DB, 1) SSM_DECL(XB, DB, 2) SSM_DECL(XB, DB, 4) SSM_DECL(XB, DB, 8) SSM_DECL(XB, DB, 16) SSM_DECL(XB, DB, 32)
-SSM_DECL_ALL_S(0, 0)
-SSM_DECL_ALL_S(0, 1)
-SSM_DECL_ALL_S(1, 0)
-SSM_DECL_ALL_S(1, 1)
+#define SSM_DECL(R, XB, DB, S)                                                                         \
+  hipError_t launch_scan_r##R##_x##XB##_d##DB##_s##S(int mode, const ScanArgs& a, dim3 grid, int64_t gpb, \
+                                                     hipStream_t st);
+#define SSM_DECL_ALL(XB, DB)                                                                             \
+  SSM_DECL(4, XB, DB, 1) SSM_DECL(4, XB, DB, 2) SSM_DECL(4, XB, DB, 4) SSM_DECL(4, XB, DB, 8)            \
+  SSM_DECL(4, XB, DB, 16) SSM_DECL(4, XB, DB, 32) SSM_DECL(8, XB, DB, 2) SSM_DECL(16, XB, DB, 1)
+SSM_DECL_ALL(0, 0)
+SSM_DECL_ALL(0, 1)
+SSM_DECL_ALL(1, 0)
+SSM_DECL_ALL(1, 1)
 
 namespace {
 
@@ -44,48 +47,65 @@ __global__ __launch_bounds__(256) void copy_state_kernel(const float* h0, float*
 }
 
 template <int XB, int DB>
-hipError_t launch_s(int S, int mode, const ScanArgs& a, dim3 grid, int64_t gpb, hipStream_t st);
+hipError_t launch_s(int R, int S, int mode, const ScanArgs& a, dim3 grid, int64_t gpb, hipStream_t st);
 
-#define SSM_LAUNCH_S(XB, DB)                                                                        \
-  template <>                                                                                       \
-  hipError_t launch_s<XB, DB>(int S, int mode, const ScanArgs& a, dim3 grid, int64_t gpb, hipStream_t st) { \
-    switch (S) {                                                                                    \
-      case 1: return launch_scan_x##XB##_d##DB##_s1(mode, a, grid, gpb, st);                        \
-      case 2: return launch_scan_x##XB##_d##DB##_s2(mode, a, grid, gpb, st);                        \
-      case 4: return launch_scan_x##XB##_d##DB##_s4(mode, a, grid, gpb, st);                        \
-      case 8: return launch_scan_x##XB##_d##DB##_s8(mode, a, grid, gpb, st);                        \
-      case 16: return launch_scan_x##XB##_d##DB##_s16(mode, a, grid, gpb, st);                      \
-      case 32: return launch_scan_x##XB##_d##DB##_s32(mode, a, grid, gpb, st);                      \
-      default: return hipErrorInvalidValue;                                                         \
-    }                                                                                               \
+#define SSM_LAUNCH_S(XB, DB)                                                                              \
+  template <>                                                                                             \
+  hipError_t launch_s<XB, DB>(int R, int S, int mode, const ScanArgs& a, dim3 grid, int64_t gpb,          \
+                              hipStream_t st) {                                                           \
+    if (R == 8 && S == 2) return launch_scan_r8_x##XB##_d##DB##_s2(mode, a, grid, gpb, st);               \
+    if (R == 16 && S == 1) return launch_scan_r16_x##XB##_d##DB##_s1(mode, a, grid, gpb, st);             \
+    if (R != 4) return hipErrorInvalidValue;                                                              \
+    switch (S) {                                                                                          \
+      case 1: return launch_scan_r4_x##XB##_d##DB##_s1(mode, a, grid, gpb, st);                           \
+      case 2: return launch_scan_r4_x##XB##_d##DB##_s2(mode, a, grid, gpb, st);                           \
+      case 4: return launch_scan_r4_x##XB##_d##DB##_s4(mode, a, grid, gpb, st);                           \
+      case 8: return launch_scan_r4_x##XB##_d##DB##_s8(mode, a, grid, gpb, st);                           \
+      case 16: return launch_scan_r4_x##XB##_d##DB##_s16(mode, a, grid, gpb, st);                         \
+      case 32: return launch_scan_r4_x##XB##_d##DB##_s32(mode, a, grid, gpb, st);                         \
+      default: return hipErrorInvalidValue;                                                               \
+    }                                                                                                     \
   }
 SSM_LAUNCH_S(0, 0)
 SSM_LAUNCH_S(0, 1)
 SSM_LAUNCH_S(1, 0)
 SSM_LAUNCH_S(1, 1)
 
-hipError_t launch_mode(int S, int mode, const ScanArgs& a, dim3 grid, int64_t gpb, hipStream_t st) {
-  if (a.act_bf16 && a.delta_bf16) return launch_s<1, 1>(S, mode, a, grid, gpb, st);
-  if (a.act_bf16) return launch_s<1, 0>(S, mode, a, grid, gpb, st);
-  if (a.delta_bf16) return launch_s<0, 1>(S, mode, a, grid, gpb, st);
-  return launch_s<0, 0>(S, mode, a, grid, gpb, st);
+hipError_t launch_mode(const ScanPlan& p, int mode, const ScanArgs& a, dim3 grid, int64_t gpb, hipStream_t st) {
+  if (a.act_bf16 && a.delta_bf16) return launch_s<1, 1>(p.R, p.S, mode, a, grid, gpb, st);
+  if (a.act_bf16) return launch_s<1, 0>(p.R, p.S, mode, a, grid, gpb, st);
+  if (a.delta_bf16) return launch_s<0, 1>(p.R, p.S, mode, a, grid, gpb, st);
+  return launch_s<0, 0>(p.R, p.S, mode, a, grid, gpb, st);
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-constexpr int kTile = 32;  // tokens per LDS tile (TileShape::T)
 
 }  // namespace
 
 ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, bool final_only, int num_cus) {
   (void)final_only;
   ScanPlan p{};
-  int S = 1;
-  while (S * kRows < dstate) S *= 2;
-  p.S = S;
-  p.T = kTile;
-  const int64_t waves = batch * ceil_div(dim, kChPerWave);
   const int64_t simds = 4LL * (num_cus > 0 ? num_cus : 256);
+  // Rows per wave.  Four rows of 16 channels run one wave per SIMD at best;
+  // when that leaves SIMDs idle or single-waved and the states fit, 16 rows of
+  // 4 channels (one state per lane) or 8 rows of 8 give 4x or 2x the waves,
+  // so every SIMD interleaves several.  Layers with so few (batch, channel)
+  // slices that even that cannot fill the chip are split in time instead
+  // (below), where 4 rows measured fastest.
+  int S = 1;
+  while (S * 4 < dstate) S *= 2;
+  p.R = 4;
+  const int64_t waves4 = batch * ceil_div(dim, 16);
+  const bool time_split = waves4 > 0 && waves4 * 2 < simds && seqlen >= 16LL * 32;
+  if (dstate <= 16 && !time_split) {
+    if (waves4 < simds) p.R = 16;
+    else if (waves4 < 2 * simds) p.R = 8;
+  }
+  if (p.R != 4) S = 16 / p.R;
+  p.S = S;
+  p.T = p.R == 4 ? 32 : 64;
+  const int64_t waves = batch * ceil_div(dim, 64 / p.R);
   int64_t nch = 1;
   // Split time only when fewer than half of the SIMDs would get a wave: the
   // split reruns the recurrence (pass 1), so it pays only when it fills the chip.
@@ -122,23 +142,23 @@ int launch_scan(const ScanArgs& a0, const ScanPlan& p, bool final_only, void* st
     }
     return 0;
   }
-  const int64_t gpb = ceil_div(a.dim, kChPerWave);
+  const int64_t gpb = ceil_div(a.dim, 64 / p.R);
   const int64_t nb = a.batch * gpb;
   if (nb > 0x7fffffffLL || p.nchunks > 65535) return fail(4, "grid too large");
   hipError_t e = hipSuccess;
   if (p.nchunks == 1) {
-    e = launch_mode(p.S, final_only ? kModeState : kModeFull, a, dim3((unsigned)nb, 1), gpb, st);
+    e = launch_mode(p, final_only ? kModeState : kModeFull, a, dim3((unsigned)nb, 1), gpb, st);
     if (e != hipSuccess) return fail(6, std::string("scan kernel launch: ") + hipGetErrorString(e));
     return 0;
   }
   const int64_t nlocal = final_only ? p.nchunks : p.nchunks - 1;
-  e = launch_mode(p.S, kModeState, a, dim3((unsigned)nb, (unsigned)nlocal), gpb, st);
+  e = launch_mode(p, kModeState, a, dim3((unsigned)nb, (unsigned)nlocal), gpb, st);
   if (e != hipSuccess) return fail(6, std::string("chunk-state kernel launch: ") + hipGetErrorString(e));
   carry_kernel<<<dim3((unsigned)ceil_div(total, 256)), 256, 0, st>>>(a, nlocal, final_only ? 1 : 0);
   e = hipGetLastError();
   if (e != hipSuccess) return fail(6, std::string("carry kernel launch: ") + hipGetErrorString(e));
   if (!final_only) {
-    e = launch_mode(p.S, kModeFull, a, dim3((unsigned)nb, (unsigned)p.nchunks), gpb, st);
+    e = launch_mode(p, kModeFull, a, dim3((unsigned)nb, (unsigned)p.nchunks), gpb, st);
     if (e != hipSuccess) return fail(6, std::string("scan kernel launch: ") + hipGetErrorString(e));
   }
   return 0;

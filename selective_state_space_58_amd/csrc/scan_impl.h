@@ -8,18 +8,22 @@
 //   y_t    = (sum_n C_t,n h_t,n + Dskip_d x_t) * silu(z_t)
 // ("Mamba / SSM complete guide", sec. 5, selective_scan and the block's gate).
 //
-// Mapping to CDNA4.  One wavefront per workgroup.  The 64 lanes are 4 rows of
-// 16: lane (row r, column c) holds states [r*S, r*S+S) of channel ch0+c in
-// VGPRs for the whole sequence, so the state never touches memory.  The work
-// per (t, d, n) element is 6 VALU ops plus one v_exp_f32; the per-(t, d) work
-// (softplus, silu, skip, bf16 conversion, stores) is done once, not per state.
+// Mapping to CDNA4.  One wavefront per workgroup.  The 64 lanes are R rows of
+// 64/R columns (R = 4, 8 or 16): lane (row r, column c) holds states
+// [r*S, r*S+S) of channel ch0+c in VGPRs for the whole sequence, so the state
+// never touches memory.  More rows give fewer channels per wave and so more
+// waves for a given layer: the host picks R so that every SIMD gets waves to
+// interleave.  The work per (t, d, n) element is 6 VALU ops plus one
+// v_exp_f32; the per-(t, d) work (softplus, silu, skip, bf16 conversion,
+// stores) is done once, not per state.
 //   * Per time tile (T tokens) the wave stages (dt, x) and silu(z) per
 //     (token, channel) and B_t, C_t (fp32) per (token, row) in LDS; the global
 //     loads for the next tile are issued before the current tile is scanned.
-//   * The readout sum over n is split over the 4 rows; every 4 tokens a
-//     reduce-scatter with v_permlane32_swap / v_permlane16_swap (3 swaps + 3
-//     adds) leaves row r with the full sum for token 4k + r, and that lane
-//     applies the skip and gate and stores y for that token.
+//   * The readout sum over n is split over the R rows; every R tokens a
+//     reduce-scatter over the rows (v_permlane32_swap / v_permlane16_swap for
+//     lanes 32 and 16 apart, a DPP row rotation or a swizzle for 8 and 4)
+//     leaves row r with the full sum for token Rk + r, and that lane applies
+//     the skip and gate and stores y for that token.
 //   * Lanes whose channel is past `dim` load from a clamped (valid) address
 //     and compute values that are never stored; a column never mixes with
 //     another column, so nothing leaks.  Tokens past the end of the slice get
@@ -103,44 +107,92 @@ __device__ __forceinline__ float zoh_gain_accurate(float E, float dt, float a, f
 __device__ __forceinline__ float bits_f(unsigned u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ unsigned f_bits(float f) { return __builtin_bit_cast(unsigned, f); }
 
-// Lanes are rows of 16 (row = lane / 16).  p_j holds, in every lane, a partial
-// sum for token j of a group of 4.  Returns, in row r, the sum over the 4 rows
-// of the same column of p_r.
-__device__ __forceinline__ float reduce_scatter_rows(float p0, float p1, float p2, float p3) {
-  // permlane32_swap(a, b): a' = [a.lo | b.lo], b' = [a.hi | b.hi]  (halves of 32 lanes)
-  const auto s02 = __builtin_amdgcn_permlane32_swap(f_bits(p0), f_bits(p2), false, false);
-  const float u0 = bits_f(s02[0]) + bits_f(s02[1]);  // rows 0,1: token 0 ; rows 2,3: token 2
-  const auto s13 = __builtin_amdgcn_permlane32_swap(f_bits(p1), f_bits(p3), false, false);
-  const float u1 = bits_f(s13[0]) + bits_f(s13[1]);  // rows 0,1: token 1 ; rows 2,3: token 3
-  // permlane16_swap(a, b): odd rows of a <-> even rows of b
-  const auto s = __builtin_amdgcn_permlane16_swap(f_bits(u0), f_bits(u1), false, false);
-  return bits_f(s[0]) + bits_f(s[1]);                // row r: token r
+// One level of the row reduce-scatter: lanes whose bit `D` (a lane distance
+// of 32, 16, 8 or 4) is clear end with a + a(lane ^ D), the others with
+// b + b(lane ^ D).
+template <int D>
+__device__ __forceinline__ float pair_sum(float a, float b) {
+  if constexpr (D == 32) {
+    // permlane32_swap(a, b): a' = [a.lo | b.lo], b' = [a.hi | b.hi]  (halves of 32 lanes)
+    const auto sw = __builtin_amdgcn_permlane32_swap(f_bits(a), f_bits(b), false, false);
+    return bits_f(sw[0]) + bits_f(sw[1]);
+  } else if constexpr (D == 16) {
+    // permlane16_swap(a, b): odd 16-lane rows of a <-> even 16-lane rows of b
+    const auto sw = __builtin_amdgcn_permlane16_swap(f_bits(a), f_bits(b), false, false);
+    return bits_f(sw[0]) + bits_f(sw[1]);
+  } else {
+    const bool up = (__lane_id() & D) != 0;
+    const float keep = up ? b : a, send = up ? a : b;
+    int other;
+    if constexpr (D == 8) {
+      other = __builtin_amdgcn_update_dpp(0, (int)f_bits(send), 0x128, 0xf, 0xf, false);  // row_ror:8 = lane ^ 8
+    } else {
+      static_assert(D == 4, "row distance");
+      other = __builtin_amdgcn_ds_swizzle((int)f_bits(send), 0x101f);  // bit mode: xor 4 within 32 lanes
+    }
+    return keep + bits_f((unsigned)other);
+  }
+}
+
+// Lanes are R rows of 64/R (row = lane / (64/R)).  p[j] holds, in every lane,
+// a partial sum for token j of a group of R.  Returns, in row r, the sum over
+// the R rows of the same column of p[r]: each level pairs value i with value
+// i + K/2 across the highest remaining lane bit, so the token index ends up
+// equal to the row index.
+template <int R>
+__device__ __forceinline__ float reduce_scatter_rows(const float (&p)[R]) {
+  float v[R];
+#pragma unroll
+  for (int j = 0; j < R; ++j) v[j] = p[j];
+  // lane bits 5, 4, ... down to log2(64 / R)
+#pragma unroll
+  for (int K = R, D = 32; K > 1; K /= 2, D /= 2) {
+#pragma unroll
+    for (int i = 0; i < K / 2; ++i) {
+      if (D == 32) v[i] = pair_sum<32>(v[i], v[i + K / 2]);
+      else if (D == 16) v[i] = pair_sum<16>(v[i], v[i + K / 2]);
+      else if (D == 8) v[i] = pair_sum<8>(v[i], v[i + K / 2]);
+      else v[i] = pair_sum<4>(v[i], v[i + K / 2]);
+    }
+  }
+  return v[0];
 }
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+template <int NW>
+struct VecOf;
+template <>
+struct VecOf<4> {
+  using T = u32x4;
+};
+template <>
+struct VecOf<2> {
+  using T = u32x2;
+};
 
-template <int S>
+template <int R_, int S>
 struct TileShape {
-  static constexpr int R = kRows;
-  static constexpr int CH = kChPerWave;
+  static constexpr int R = R_;
+  static constexpr int CH = 64 / R;                // channels per wave
   static constexpr int NP = R * S;                 // padded state count of the wave
-  static constexpr int T = 32;                     // tokens per LDS tile
+  static constexpr int T = R == 4 ? 32 : 64;       // tokens per LDS tile
   static constexpr int KX = T / R;                 // (token, channel) items per lane per tile
   static constexpr int KB = T * NP / 64;           // B (and C) items per lane per tile
 };
 
-template <bool XB, bool DB, int S, int MODE, bool ACC, bool VEC>
+template <int RR, bool XB, bool DB, int S, int MODE, bool ACC, bool VEC>
 __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t ch0, int64_t chunk,
                                           const float (&a2)[S], const float (&ia)[S], const float (&av)[S],
                                           float2* __restrict__ s_dx, float* __restrict__ s_gz,
                                           float* __restrict__ s_bc) {
-  using TS = TileShape<S>;
+  using TS = TileShape<RR, S>;
   using TX = typename Act<XB>::T;
   using TD = typename Act<DB>::T;
   constexpr int R = TS::R, CH = TS::CH, NP = TS::NP, T = TS::T, KX = TS::KX, KB = TS::KB;
   constexpr bool FULL = (MODE == kModeFull);
   const int lane = threadIdx.x;
-  const int r = lane >> 4, c = lane & 15;
+  const int r = lane / CH, c = lane % CH;
   const int64_t L = a.seqlen, dim = a.dim, N = a.dstate;
   const int64_t ch = ch0 + c;
   const bool ch_ok = ch < dim;
@@ -240,19 +292,22 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
   // chunks.  Chunk k of a tile covers token k / XROW, channels
   // (k % XROW) * EX .. + EX of x, delta and z, and elements k*EX .. + EX of
   // the (token, state)-contiguous B and C tiles.
-  constexpr int EX = 16 / (int)sizeof(RX);                 // elements per chunk
+  constexpr int VB = CH * (int)sizeof(RX) < 16 ? CH * (int)sizeof(RX) : 16;  // bytes per chunk
+  constexpr int NW = VB / 4;                                // dwords per chunk
+  using VT = typename VecOf<NW>::T;
+  constexpr int EX = VB / (int)sizeof(RX);                  // elements per chunk
   constexpr int XROW = CH / EX;                             // chunks per token row
   constexpr int CXN = (T * CH) / (64 * EX);                 // x chunks per lane
   constexpr int CBN = (T * NP) / (64 * EX) > 0 ? (T * NP) / (64 * EX) : 1;  // B chunks per lane
   constexpr int GW = S < EX ? S : EX;                       // floats per LDS write of B/C
-  u32x4 vx[CXN], vd[CXN], vz[CXN], vb[CBN], vc[CBN];
+  VT vx[CXN], vd[CXN], vz[CXN], vb[CBN], vc[CBN];
   const int vc0 = (lane % XROW) * EX;                       // this lane's first channel in a row
   float vbias[EX];
 #pragma unroll
   for (int e = 0; e < EX; ++e) vbias[e] = (VEC && a.delta_bias != nullptr) ? a.delta_bias[ch0 + vc0 + e] : 0.f;
   // (the element is copied to a scalar first: bit-casting a vector-element
   // lvalue directly reads element 0 with this compiler)
-  auto raw_elem = [](const u32x4& v, int e) -> float {
+  auto raw_elem = [](const VT& v, int e) -> float {
     if constexpr (sizeof(RX) == 2) {
       const unsigned u = (v[e >> 1] >> (16 * (e & 1))) << 16;
       return __builtin_bit_cast(float, u);
@@ -274,10 +329,10 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
       const int k = lane + 64 * q;
       int tl = k / XROW;
       if (tail) tl = tl < last ? tl : (int)last;
-      const uint32_t off = (uint32_t)tl * rowb + (uint32_t)(k % XROW) * 16u;
-      vx[q] = *reinterpret_cast<const u32x4*>(xb + off);
-      vd[q] = *reinterpret_cast<const u32x4*>(db + off);
-      if (has_z) vz[q] = *reinterpret_cast<const u32x4*>(zb + off);
+      const uint32_t off = (uint32_t)tl * rowb + (uint32_t)(k % XROW) * (uint32_t)VB;
+      vx[q] = *reinterpret_cast<const VT*>(xb + off);
+      vd[q] = *reinterpret_cast<const VT*>(db + off);
+      if (has_z) vz[q] = *reinterpret_cast<const VT*>(zb + off);
     }
     const RX* bb = gB + (b * L + t0) * N;                   // uniform
     const RX* cb = gC + (b * L + t0) * N;
@@ -287,8 +342,8 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
       int t = e0 / NP;
       if (tail) t = t < last ? t : (int)last;
       const uint32_t off = (uint32_t)t * (uint32_t)NP + (uint32_t)(e0 % NP);
-      vb[q] = *reinterpret_cast<const u32x4*>(bb + off);
-      if (FULL) vc[q] = *reinterpret_cast<const u32x4*>(cb + off);
+      vb[q] = *reinterpret_cast<const VT*>(bb + off);
+      if (FULL) vc[q] = *reinterpret_cast<const VT*>(cb + off);
     }
   };
   auto stage_vec = [&](int64_t t0) {
@@ -352,17 +407,19 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
     if (t0 + T < t_stop) fetch(t0 + T);
     const int64_t nvalid = t_stop - t0;
     TX* yb = gy + (b * L + t0) * dim + ch0;          // uniform
-    // Operands of one group of R tokens: (dt, x) and this row's B/C slices.
-    // The next group's operands are read from LDS while the current group is
-    // computed, so LDS latency overlaps the VALU work.
-    struct Group {
-      float2 dx[R];
-      float b[R][S];
-      float c[R][S];
+    // Operands of one step of U = 4 tokens: (dt, x) and this row's B/C
+    // slices.  The next step's operands are read from LDS while the current
+    // step is computed, so LDS latency overlaps the VALU work; a group of R
+    // tokens (R / U steps) ends with the row reduce-scatter and the stores.
+    constexpr int U = 4;
+    struct Step {
+      float2 dx[U];
+      float b[U][S];
+      float c[U][S];
     };
-    auto load_group = [&](int tb, Group& g) {
+    auto load_step = [&](int tb, Step& g) {
 #pragma unroll
-      for (int j = 0; j < R; ++j) {
+      for (int j = 0; j < U; ++j) {
         const int tt = tb + j;
         g.dx[j] = s_dx[tt * CH + c];
         const float* bc = s_bc + ((tt * R + r) * 2) * S;
@@ -382,31 +439,32 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
         }
       }
     };
-    Group cur, nxt;
-    load_group(0, cur);
-    // exp(dt*a) of a group is computed one group ahead, so the transcendental
-    // latency overlaps the previous group's state updates
-    float Ecur[R][S], Enxt[R][S];
-    auto group_exp = [&](const Group& g, float (&E)[R][S]) {
+    Step cur, nxt;
+    load_step(0, cur);
+    // exp(dt*a) of a step is computed one step ahead, so the transcendental
+    // latency overlaps the previous step's state updates
+    float Ecur[U][S], Enxt[U][S];
+    auto step_exp = [&](const Step& g, float (&E)[U][S]) {
 #pragma unroll
-      for (int j = 0; j < R; ++j)
+      for (int j = 0; j < U; ++j)
 #pragma unroll
         for (int s = 0; s < S; ++s) E[j][s] = hw_exp2(g.dx[j].x * a2[s]);
     };
-    group_exp(cur, Ecur);
+    step_exp(cur, Ecur);
     const bool full_tile = ch_ok && nvalid >= T;       // uniform on the vector path
     const int nval32 = nvalid < T ? (int)nvalid : T;
+    float pr[R];
     // full unroll for small S; wide S (N > 32) keeps the loop to bound code size
-    constexpr int kGroupUnroll = (S <= 8) ? T / R : 2;
-#pragma unroll kGroupUnroll
-    for (int tb = 0; tb < T; tb += R) {
-      if (tb + R < T) {
-        load_group(tb + R, nxt);
-        group_exp(nxt, Enxt);
+    constexpr int kStepUnroll = (S <= 8) ? T / U : 2;
+    static_assert(R == U || kStepUnroll == T / U, "rows beyond one step need the fully unrolled loop");
+#pragma unroll kStepUnroll
+    for (int tb = 0; tb < T; tb += U) {
+      if (tb + U < T) {
+        load_step(tb + U, nxt);
+        step_exp(nxt, Enxt);
       }
-      float pr[R];
 #pragma unroll
-      for (int j = 0; j < R; ++j) {
+      for (int j = 0; j < U; ++j) {
         const float2 dx = cur.dx[j];
         float acc = 0.f;
 #pragma unroll
@@ -416,20 +474,20 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
           h[s] = fmaf(E, h[s], g * (cur.b[j][s] * dx.y));
           if (FULL) acc = fmaf(cur.c[j][s], h[s], acc);
         }
-        pr[j] = acc;
+        pr[R == U ? j : (tb + j) % R] = acc;   // static index: R == U, or the loop is fully unrolled
         if (!FULL) dsum += dx.x;
       }
-      if (FULL) {
-        const float tot = reduce_scatter_rows(pr[0], pr[1], pr[2], pr[3]);
-        const int tl = tb + r;
+      if (FULL && (R == U || (tb + U) % R == 0)) {
+        const float tot = reduce_scatter_rows<R>(pr);
+        const int tl = tb + U - R + r;
         const float xv = s_dx[tl * CH + c].y;
         const float yv = fmaf(Dv, xv, tot) * s_gz[tl * CH + c];
         if (full_tile || (ch_ok && tl < nval32)) yb[(uint32_t)tl * dim32 + (uint32_t)c] = (TX)yv;
       }
-      if (tb + R < T) {
+      if (tb + U < T) {
         cur = nxt;
 #pragma unroll
-        for (int j = 0; j < R; ++j)
+        for (int j = 0; j < U; ++j)
 #pragma unroll
           for (int s = 0; s < S; ++s) Ecur[j][s] = Enxt[j][s];
       }
@@ -450,11 +508,19 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
   if (!FULL && a.nchunks > 1 && r == 0 && ch_ok) a.ws_dsum[chunk * a.batch * dim + b * dim + ch] = dsum;
 }
 
-template <bool XB, bool DB, int S, int MODE, bool VEC>
-__global__ __launch_bounds__(64) void scan_kernel(ScanArgs a, int64_t groups_per_batch) {
-  using TS = TileShape<S>;
-  __shared__ float2 s_dx[TS::T * TS::CH];
-  __shared__ float s_gz[TS::T * TS::CH];
+// Waves per SIMD the register budget is sized for: the 4-row layout runs one
+// wave per SIMD on its target shapes, the 8- and 16-row layouts two and three.
+template <int RR>
+constexpr int scan_waves_per_simd() {
+  return RR == 4 ? 1 : RR == 8 ? 2 : 3;
+}
+
+template <int RR, bool XB, bool DB, int S, int MODE, bool VEC>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(scan_waves_per_simd<RR>())))
+void scan_kernel(ScanArgs a, int64_t groups_per_batch) {
+  using TS = TileShape<RR, S>;
+  __shared__ __attribute__((aligned(16))) float2 s_dx[TS::T * TS::CH];
+  __shared__ __attribute__((aligned(16))) float s_gz[TS::T * TS::CH];
   __shared__ __attribute__((aligned(16))) float s_bc[TS::T * TS::R * 2 * S];
 
   // XCD-aware order: dispatch id i runs on XCD i % 8; give each XCD a contiguous
@@ -463,11 +529,11 @@ __global__ __launch_bounds__(64) void scan_kernel(ScanArgs a, int64_t groups_per
   int64_t lin = blockIdx.x;
   if ((nb & 7) == 0) lin = (lin & 7) * (nb >> 3) + (lin >> 3);
   const int64_t b = lin / groups_per_batch;
-  const int64_t ch0 = (lin % groups_per_batch) * kChPerWave;
+  const int64_t ch0 = (lin % groups_per_batch) * TS::CH;
   const int64_t chunk = blockIdx.y;
 
   const int lane = threadIdx.x;
-  const int r = lane >> 4, c = lane & 15;
+  const int r = lane / TS::CH, c = lane % TS::CH;
   const int64_t ch = ch0 + c;
   float a2[S], ia[S], av[S];
   bool tiny = false;
@@ -481,35 +547,39 @@ __global__ __launch_bounds__(64) void scan_kernel(ScanArgs a, int64_t groups_per
     tiny = tiny || !(fabsf(an) >= 1e-2f);
   }
   if (!XB || __builtin_amdgcn_ballot_w64(tiny) != 0)
-    scan_body<XB, DB, S, MODE, true, VEC>(a, b, ch0, chunk, a2, ia, av, s_dx, s_gz, s_bc);
+    scan_body<RR, XB, DB, S, MODE, true, VEC>(a, b, ch0, chunk, a2, ia, av, s_dx, s_gz, s_bc);
   else
-    scan_body<XB, DB, S, MODE, false, VEC>(a, b, ch0, chunk, a2, ia, av, s_dx, s_gz, s_bc);
+    scan_body<RR, XB, DB, S, MODE, false, VEC>(a, b, ch0, chunk, a2, ia, av, s_dx, s_gz, s_bc);
 }
 
-// The vectorised tile path needs whole 16-byte chunks of the B/C tile per lane.
-template <bool XB, int S>
+// The vectorised tile path needs whole chunks of the x and B/C tiles per lane.
+template <int RR, bool XB, int S>
 constexpr bool vec_shape_ok() {
-  return (TileShape<S>::T * TileShape<S>::NP) / (64 * (16 / (XB ? 2 : 4))) >= 1;
+  using TS = TileShape<RR, S>;
+  constexpr int sz = XB ? 2 : 4;
+  constexpr int VB = TS::CH * sz < 16 ? TS::CH * sz : 16;
+  constexpr int EX = VB / sz;
+  return (TS::T * TS::NP) % (64 * EX) == 0 && (TS::T * TS::CH) % (64 * EX) == 0 && TS::CH % EX == 0;
 }
-template <bool XB, int S>
+template <int RR, bool XB, int S>
 bool vec_ok(const ScanArgs& a) {
-  return vec_shape_ok<XB, S>() && a.dstate == TileShape<S>::NP;
+  return vec_shape_ok<RR, XB, S>() && a.dstate == TileShape<RR, S>::NP && a.dim % TileShape<RR, S>::CH == 0;
 }
 
-// Launch the scan kernel for one (act dtype, delta dtype, states-per-lane) triple.
-template <bool XB, bool DB, int SV>
+// Launch the scan kernel for one (rows, act dtype, delta dtype, states-per-lane) combination.
+template <int RR, bool XB, bool DB, int SV>
 hipError_t launch_scan_variant(int mode, const ScanArgs& a, dim3 grid, int64_t gpb, hipStream_t st) {
   bool vec = false;
-  if constexpr (vec_shape_ok<XB, SV>()) vec = a.vec_io && vec_ok<XB, SV>(a);
-  if constexpr (vec_shape_ok<XB, SV>()) {
+  if constexpr (vec_shape_ok<RR, XB, SV>()) vec = a.vec_io && vec_ok<RR, XB, SV>(a);
+  if constexpr (vec_shape_ok<RR, XB, SV>()) {
     if (vec) {
-      if (mode == kModeFull) scan_kernel<XB, DB, SV, kModeFull, true><<<grid, 64, 0, st>>>(a, gpb);
-      else scan_kernel<XB, DB, SV, kModeState, true><<<grid, 64, 0, st>>>(a, gpb);
+      if (mode == kModeFull) scan_kernel<RR, XB, DB, SV, kModeFull, true><<<grid, 64, 0, st>>>(a, gpb);
+      else scan_kernel<RR, XB, DB, SV, kModeState, true><<<grid, 64, 0, st>>>(a, gpb);
       return hipGetLastError();
     }
   }
-  if (mode == kModeFull) scan_kernel<XB, DB, SV, kModeFull, false><<<grid, 64, 0, st>>>(a, gpb);
-  else scan_kernel<XB, DB, SV, kModeState, false><<<grid, 64, 0, st>>>(a, gpb);
+  if (mode == kModeFull) scan_kernel<RR, XB, DB, SV, kModeFull, false><<<grid, 64, 0, st>>>(a, gpb);
+  else scan_kernel<RR, XB, DB, SV, kModeState, false><<<grid, 64, 0, st>>>(a, gpb);
   return hipGetLastError();
 }
 

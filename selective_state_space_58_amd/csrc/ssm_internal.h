@@ -13,11 +13,11 @@ namespace ssm {
 int fail(int status, const std::string& msg);
 
 // ---------------------------------------------------------------- selective scan
-// Kernel geometry: one wavefront (64 lanes) per workgroup.  The lanes form
-// kRows rows of 16; row r owns states [r*S, r*S + S) of the wave's 16
+// Kernel geometry: one wavefront (64 lanes) per workgroup.  The lanes form R
+// rows of 64/R channels; row r owns states [r*S, r*S + S) of the wave's
 // channels, so every (channel, state) pair lives in exactly one lane's VGPRs.
-constexpr int kRows = 4;
-constexpr int kChPerWave = 64 / kRows;
+// R is 4 in general, 8 or 16 for layers with dstate <= 16 and too few
+// (batch, channel) slices to give every SIMD several waves at R = 4.
 
 enum ScanMode : int { kModeFull = 0, kModeState = 1 };
 
@@ -40,11 +40,12 @@ struct ScanArgs {
   int64_t nchunks;    // number of time chunks (1 = unsplit)
   int softplus;
   int act_bf16, delta_bf16;
-  int vec_io;          // 16-byte tile I/O allowed (dim % 16 == 0, aligned, delta stored like x)
+  int vec_io;          // vector tile I/O allowed (16-byte aligned, delta stored like x)
 };
 
 struct ScanPlan {
-  int S;              // states per lane (power of two, kRows*S >= dstate)
+  int R;              // rows of lanes per wave (4, 8 or 16); 64/R channels per wave
+  int S;              // states per lane (power of two, R*S >= dstate)
   int T;              // time tile (tokens staged per LDS round)
   int64_t nchunks;
   int64_t chunk_len;
