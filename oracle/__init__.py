@@ -58,6 +58,8 @@ def _load():
             lib.oracle_ssd_quadratic.restype = None
             lib.oracle_lti_conv.argtypes = [P, P, P, P, ctypes.c_double, ctypes.c_double, P, I64, I64]
             lib.oracle_lti_conv.restype = None
+            lib.oracle_selective_scan_bwd.argtypes = [P] * 8 + [I] + [P] * 12 + [I64] * 6
+            lib.oracle_selective_scan_bwd.restype = None
             lib.oracle_causal_conv1d.argtypes = [P] * 4 + [I, P, P] + [I64] * 6
             lib.oracle_causal_conv1d.restype = None
             _lib = lib
@@ -114,6 +116,61 @@ def selective_scan(x, delta, A, B, C, Dskip=None, z=None, delta_bias=None,
         int(bool(delta_softplus)), _ptr(h0), _ptr(y), _ptr(hf),
         batch, seqlen, dim, dstate, s0, s1), batch * dim, threads)
     return y, hf
+
+
+def selective_scan_bwd(x, delta, A, B, C, dout, Dskip=None, z=None, delta_bias=None, delta_softplus=False,
+                       h0=None, dh_final=None, threads=None):
+    """O5: gradients of sum(dout * y) + sum(dh_final * h_final) for O1, float64.  Returns a dict with
+    dx, ddelta, dA, dB, dC and, for the optional inputs given, dDskip, dz, ddelta_bias, dh0.
+    Threads accumulate the shared gradients (dA, dB, dC, dDskip, ddelta_bias) in private buffers."""
+    x = _f64(x)
+    batch, seqlen, dim = x.shape
+    A = _f64(A)
+    dstate = A.shape[1]
+    delta = _f64(delta, x.shape)
+    B = _f64(B, (batch, seqlen, dstate))
+    C = _f64(C, (batch, seqlen, dstate))
+    dout = _f64(dout, x.shape)
+    Dskip = _f64(Dskip, (dim,))
+    z = _f64(z, x.shape)
+    delta_bias = _f64(delta_bias, (dim,))
+    h0 = _f64(h0, (batch, dim, dstate))
+    dh_final = _f64(dh_final, (batch, dim, dstate))
+    dx = np.empty_like(x)
+    ddelta = np.empty_like(x)
+    dz = np.empty_like(x) if z is not None else None
+    dh0 = np.empty((batch, dim, dstate)) if h0 is not None else None
+    total = batch * dim
+    threads = max(1, min(threads or default_threads(), total))
+    bounds = [total * i // threads for i in range(threads + 1)]
+    acc = [dict(dA=np.zeros((dim, dstate)), dB=np.zeros((batch, seqlen, dstate)), dC=np.zeros((batch, seqlen, dstate)),
+                dD=np.zeros(dim), dbias=np.zeros(dim)) for _ in range(threads)]
+    lib = _load()
+
+    def run(i):
+        a = acc[i]
+        lib.oracle_selective_scan_bwd(
+            _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(z), _ptr(delta_bias),
+            int(bool(delta_softplus)), _ptr(h0), _ptr(dout), _ptr(dh_final), _ptr(dx), _ptr(ddelta), _ptr(a["dA"]),
+            _ptr(a["dB"]), _ptr(a["dC"]), _ptr(a["dD"]) if Dskip is not None else None, _ptr(dz),
+            _ptr(a["dbias"]) if delta_bias is not None else None, _ptr(dh0),
+            batch, seqlen, dim, dstate, bounds[i], bounds[i + 1])
+    if threads == 1:
+        run(0)
+    else:
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(run, range(threads)))
+    out = dict(dx=dx, ddelta=ddelta, dA=sum(a["dA"] for a in acc), dB=sum(a["dB"] for a in acc),
+               dC=sum(a["dC"] for a in acc))
+    if Dskip is not None:
+        out["dDskip"] = sum(a["dD"] for a in acc)
+    if z is not None:
+        out["dz"] = dz
+    if delta_bias is not None:
+        out["ddelta_bias"] = sum(a["dbias"] for a in acc)
+    if h0 is not None:
+        out["dh0"] = dh0
+    return out
 
 
 def _ssd_args(x, dt, A, B, C, Dskip, z, dt_bias, h0):

@@ -303,3 +303,116 @@ void oracle_causal_conv1d(const double* x, const double* w, const double* bias, 
     }
   }
 }
+
+/* d/da of the ZOH gain expm1(dt a)/a: (dt e^{dt a} - g)/a, written as
+ * dt^2 * psi(q), psi(q) = sum_{k>=2} (k-1) q^{k-2} / k!, q = dt a, by its
+ * series for small |q| (where the quotient cancels) and directly otherwise;
+ * dt^2/2 at a = 0. */
+static double zoh_gain_da(double dt, double a) {
+  double q = dt * a;
+  if (fabs(q) < 0.1) {
+    double psi = 0.0, term = 0.5; /* term = q^{k-2} / k!, from k = 2 */
+    for (int k = 2; k < 20; ++k) {
+      psi += (double)(k - 1) * term;
+      term *= q / (double)(k + 1);
+    }
+    return dt * dt * psi;
+  }
+  return (dt * exp(q) - expm1(q) / a) / a;
+}
+
+/*
+ * O5. Gradient of the selective scan O1 (reverse-mode, exact in fp64).  The
+ * pages give no backward pass; this is the adjoint of the recurrence as O1
+ * writes it, pinned against central finite differences of O1.  For the scalar
+ *   loss = sum_{b,t,d} dout[b,t,d] * out[b,t,d] + sum dh_final * h_final
+ * it returns, per slice s = b*dim + d in [s_begin, s_end):
+ *   dx, ddelta, dz (batch, seqlen, dim) and dh0 (batch, dim, dstate)   -- written;
+ *   dA (dim, dstate), dB, dC (batch, seqlen, dstate), dDskip, ddelta_bias (dim)
+ *                                                                     -- ADDED to;
+ * (ddelta is the gradient with respect to the delta input, i.e. through the
+ * bias and the softplus when they are used).  The caller gives each thread
+ * its own accumulation buffers.  Optional inputs as in O1; dh_final, dz,
+ * dh0, dDskip and ddelta_bias may be NULL.
+ *
+ * Adjoint of one step (lam = dloss/dh_t, then carried to h_{t-1}):
+ *   dy = dout * silu(z);  dz = dout * y * silu'(z)
+ *   lam_n += C_n dy;      dC_n += h_n dy
+ *   dE = lam_n h_{t-1,n}; dg = lam_n B_n x
+ *   dB_n += lam_n g x;    dx += lam_n g B_n  (+ Dskip dy)
+ *   ddt += dE E a + dg E;           (d g/d dt = e^{dt a} = E)
+ *   dA_n += dE E dt + dg dg/da;
+ *   lam_n *= E
+ */
+void oracle_selective_scan_bwd(const double* x, const double* delta, const double* A,
+                               const double* B, const double* C, const double* Dskip,
+                               const double* z, const double* delta_bias, int delta_softplus,
+                               const double* h0, const double* dout, const double* dh_final,
+                               double* dx, double* ddelta, double* dA, double* dB, double* dC,
+                               double* dDskip, double* dz, double* ddelta_bias, double* dh0,
+                               int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                               int64_t s_begin, int64_t s_end) {
+  (void)batch;
+  size_t nh = (size_t)((seqlen + 1) * dstate > 0 ? (seqlen + 1) * dstate : 1);
+  double* hs = (double*)malloc(sizeof(double) * nh);       /* h_t for t = -1 .. L-1 */
+  double* dts = (double*)malloc(sizeof(double) * (size_t)(seqlen > 0 ? seqlen : 1));
+  double* ys = (double*)malloc(sizeof(double) * (size_t)(seqlen > 0 ? seqlen : 1));
+  double* lam = (double*)malloc(sizeof(double) * (size_t)(dstate > 0 ? dstate : 1));
+  for (int64_t s = s_begin; s < s_end; ++s) {
+    int64_t b = s / dim, d = s % dim;
+    /* forward, keeping every state */
+    for (int64_t n = 0; n < dstate; ++n) hs[n] = h0 ? h0[(b * dim + d) * dstate + n] : 0.0;
+    for (int64_t t = 0; t < seqlen; ++t) {
+      int64_t i = (b * seqlen + t) * dim + d, r = (b * seqlen + t) * dstate;
+      double v = delta[i] + (delta_bias ? delta_bias[d] : 0.0);
+      double dt = delta_softplus ? softplus(v) : v;
+      dts[t] = dt;
+      double acc = 0.0;
+      for (int64_t n = 0; n < dstate; ++n) {
+        double a = A[d * dstate + n];
+        double h = exp(dt * a) * hs[t * dstate + n] + zoh_gain(dt, a) * B[r + n] * x[i];
+        hs[(t + 1) * dstate + n] = h;
+        acc += C[r + n] * h;
+      }
+      ys[t] = acc + (Dskip ? Dskip[d] * x[i] : 0.0);
+    }
+    /* reverse */
+    for (int64_t n = 0; n < dstate; ++n) lam[n] = dh_final ? dh_final[(b * dim + d) * dstate + n] : 0.0;
+    for (int64_t t = seqlen - 1; t >= 0; --t) {
+      int64_t i = (b * seqlen + t) * dim + d, r = (b * seqlen + t) * dstate;
+      double dy = dout[i];
+      if (z) {
+        double sg = 1.0 / (1.0 + exp(-z[i]));
+        if (dz) dz[i] = dout[i] * ys[t] * (sg + z[i] * sg * (1.0 - sg));
+        dy = dout[i] * z[i] * sg;
+      }
+      double dxi = Dskip ? Dskip[d] * dy : 0.0;
+      if (dDskip) dDskip[d] += dy * x[i];
+      double dt = dts[t], ddt = 0.0;
+      for (int64_t n = 0; n < dstate; ++n) {
+        double a = A[d * dstate + n];
+        double E = exp(dt * a), g = zoh_gain(dt, a);
+        lam[n] += C[r + n] * dy;
+        dC[r + n] += hs[(t + 1) * dstate + n] * dy;
+        double dE = lam[n] * hs[t * dstate + n];
+        double dg = lam[n] * B[r + n] * x[i];
+        dB[r + n] += lam[n] * g * x[i];
+        dxi += lam[n] * g * B[r + n];
+        ddt += dE * E * a + dg * E;
+        dA[d * dstate + n] += dE * E * dt + dg * zoh_gain_da(dt, a);
+        lam[n] *= E;
+      }
+      dx[i] = dxi;
+      double v = delta[i] + (delta_bias ? delta_bias[d] : 0.0);
+      double dv = delta_softplus ? ddt / (1.0 + exp(-v)) : ddt;   /* softplus' = sigmoid */
+      ddelta[i] = dv;
+      if (ddelta_bias) ddelta_bias[d] += dv;
+    }
+    if (dh0)
+      for (int64_t n = 0; n < dstate; ++n) dh0[(b * dim + d) * dstate + n] = lam[n];
+  }
+  free(hs);
+  free(dts);
+  free(ys);
+  free(lam);
+}

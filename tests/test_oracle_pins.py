@@ -285,3 +285,46 @@ def test_causal_conv1d_impulse_and_state_handoff(oracle_mod):
         assert rel(np.concatenate([o1, o2], 1), full) < 1e-14 and np.array_equal(st2, st_full)
     # the carried state is the last W-1 inputs, oldest first
     assert np.array_equal(st_full, np.transpose(x[:, L - (W - 1):, :], (0, 2, 1)))
+
+
+def _scan_loss(oracle_mod, p, dout, dh_final, softplus):
+    y, hf = oracle_mod.selective_scan(p["x"], p["delta"], p["A"], p["B"], p["C"], Dskip=p.get("Dskip"), z=p.get("z"),
+                                      delta_bias=p.get("delta_bias"), delta_softplus=softplus, h0=p.get("h0"))
+    return float(np.sum(dout * y) + np.sum(dh_final * hf))
+
+
+@pytest.mark.parametrize("softplus,full", [(True, True), (False, True), (False, False)])
+def test_scan_backward_against_finite_differences(oracle_mod, softplus, full):
+    # every gradient of O5 against central differences of the forward O1 (which is pinned above)
+    rng = np.random.default_rng(80 + 2 * softplus + full)
+    b, L, D, N = 2, 6, 3, 4
+    p = dict(x=rng.standard_normal((b, L, D)),
+             delta=(rng.standard_normal((b, L, D)) if softplus else rng.uniform(0.05, 0.8, (b, L, D))),
+             A=-rng.uniform(0.2, 3.0, (D, N)), B=rng.standard_normal((b, L, N)), C=rng.standard_normal((b, L, N)))
+    p["A"][0, 0] = 0.0                       # the a = 0 limit of the gain and its derivative
+    p["A"][1, 1] = -1e-7                     # |dt a| far below the series threshold
+    if full:
+        p.update(Dskip=rng.standard_normal(D), z=rng.standard_normal((b, L, D)), delta_bias=rng.standard_normal(D) * 0.3,
+                 h0=rng.standard_normal((b, D, N)))
+    dout = rng.standard_normal((b, L, D))
+    dh_final = rng.standard_normal((b, D, N))
+    g = oracle_mod.selective_scan_bwd(p["x"], p["delta"], p["A"], p["B"], p["C"], dout, Dskip=p.get("Dskip"),
+                                      z=p.get("z"), delta_bias=p.get("delta_bias"), delta_softplus=softplus,
+                                      h0=p.get("h0"), dh_final=dh_final, threads=1)
+    names = dict(x="dx", delta="ddelta", A="dA", B="dB", C="dC", Dskip="dDskip", z="dz", delta_bias="ddelta_bias",
+                 h0="dh0")
+    for k, gk in names.items():
+        if k not in p:
+            continue
+        num = np.zeros_like(p[k])
+        for idx in np.ndindex(p[k].shape):
+            v0 = p[k][idx]
+            eps = 1e-6 * max(1.0, abs(v0))
+            p[k][idx] = v0 + eps
+            lp = _scan_loss(oracle_mod, p, dout, dh_final, softplus)
+            p[k][idx] = v0 - eps
+            lm = _scan_loss(oracle_mod, p, dout, dh_final, softplus)
+            p[k][idx] = v0
+            num[idx] = (lp - lm) / (2 * eps)
+        err = np.max(np.abs(g[gk] - num)) / max(np.max(np.abs(num)), 1e-12)
+        assert err < 2e-7, (k, err)
