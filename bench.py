@@ -43,7 +43,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-others", action="store_true")
-    p.add_argument("--only", choices=["scan-2.8b", "scan-long", "ssd", "step", "ssd-step", "conv", "copy"],
+    p.add_argument("--only", choices=["scan-2.8b", "scan-long", "ssd", "step", "ssd-step", "conv", "bwd", "copy"],
                    default=None,
                    help="time only this other workload (for profiling); skips the headline JSON line")
     return p.parse_args()
@@ -229,6 +229,26 @@ def run_conv(ci, steps, warmup, ssm, workloads, torch, dev):
             "hbm_GBs": round(nb / (ms * 1e-3) / 1e9, 1), "hbm_frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def run_bwd(steps, warmup, ssm, workloads, torch, dev, np):
+    """Time the selective-scan backward on the headline layer (all gradients)."""
+    inp, cfg = workloads.config_inputs(1)
+    t = workloads.to_device(inp, dev)
+    rng = np.random.default_rng(7)
+    dout = torch.from_numpy(workloads.round_to(rng.standard_normal(inp["x"].shape, dtype=np.float32), "bf16")).to(
+        dev, torch.bfloat16)
+    nb = ssm.ssm_scan_bwd_workspace_bytes(cfg["batch"], cfg["seqlen"], cfg["dim"], cfg["dstate"])
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+
+    def fn(i):
+        ssm.ssm_scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], dout, D=t["D"], z=t["z"],
+                         delta_bias=t["delta_bias"], delta_softplus=True, workspace=ws)
+    tot, _ = time_calls(fn, steps, warmup, torch)
+    ms = tot / steps
+    tc = cfg["batch"] * cfg["seqlen"] * cfg["dim"]
+    return {"name": "scan_bwd_" + cfg["name"][len("scan_"):], "ms": round(ms, 4),
+            "Gtc_s": round(tc / (ms * 1e-3) / 1e9, 2)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -257,6 +277,9 @@ def main():
         print(json.dumps({"only": "copy", "bytes_read_per_call": nbytes, "bytes_written_per_call": nbytes,
                           "ms": round(tot / steps, 4), "GBs_read_plus_write": round(2 * nbytes / (tot / steps * 1e-3) / 1e9, 1)}),
               flush=True)
+        return
+    if args.only == "bwd":
+        print(json.dumps({"only": "bwd", **run_bwd(steps, warmup, ssm, workloads, torch, dev, np)}), flush=True)
         return
     if args.only == "conv":
         print(json.dumps({"only": "conv", **run_conv(0, steps, warmup, ssm, workloads, torch, dev)}), flush=True)
@@ -331,6 +354,9 @@ def main():
             res = run_conv(ci, 20, 5, ssm, workloads, torch, dev)
             others[res.pop("name")] = res
             torch.cuda.empty_cache()
+        res = run_bwd(5, 2, ssm, workloads, torch, dev, np)
+        others[res.pop("name")] = res
+        torch.cuda.empty_cache()
         out["other_workloads"] = others
 
     # ---------------------------------------------------------------- CPU baseline (oracle)

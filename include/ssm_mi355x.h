@@ -230,6 +230,44 @@ int ssm_causal_conv1d_fwd(const void* x, const float* weight, const float* bias,
                           int64_t batch, int64_t seqlen, int64_t dim, int64_t width,
                           int act_dtype, void* stream);
 
+/*
+ * Backward pass of ssm_scan_fwd (training).  Given dout = dloss/dy and
+ * optionally dh_final = dloss/dh_final, computes the gradients of
+ *   loss = sum dout * y + sum dh_final * h_final
+ * with respect to every input of ssm_scan_fwd.  The pages give no backward
+ * pass; this is the exact adjoint of the forward recurrence (reverse-time
+ * scan of lam = dloss/dh with the same ZOH factors).
+ *
+ *   inputs as ssm_scan_fwd (x, delta, A, B, C, Dskip, z, delta_bias,
+ *   delta_softplus, h0), plus
+ *   dout        : (batch, seqlen, dim) act dtype (required)
+ *   dh_final    : (batch, dim, dstate) fp32 or NULL (zeros)
+ * outputs (all overwritten):
+ *   dx          : (batch, seqlen, dim) act dtype (required)
+ *   ddelta      : (batch, seqlen, dim) delta dtype (required): gradient with
+ *                 respect to the delta input, through bias and softplus
+ *   dA          : (dim, dstate) fp32 (required)
+ *   dB, dC      : (batch, seqlen, dstate) fp32 (required; summed over channels)
+ *   dDskip      : (dim) fp32, required when Dskip is given, else ignored
+ *   dz          : (batch, seqlen, dim) act dtype, required when z is given
+ *   ddelta_bias : (dim) fp32, required when delta_bias is given
+ *   dh0         : (batch, dim, dstate) fp32 or NULL
+ * dstate 1..16.  The sums over channels and batch use fp32 atomics, so the
+ * last bits of dA, dB, dC, dDskip and ddelta_bias vary from run to run.
+ * Workspace: ssm_scan_bwd_workspace_bytes() (the states at every 16-token
+ * tile start), or NULL for stream-ordered scratch.
+ */
+int ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                 const float* Dskip, const void* z, const float* delta_bias, int delta_softplus,
+                 const float* h0, const void* dout, const float* dh_final,
+                 void* dx, void* ddelta, float* dA, float* dB, float* dC, float* dDskip, void* dz,
+                 float* ddelta_bias, float* dh0,
+                 int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                 int act_dtype, int delta_dtype,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
+
 /* Static text for a status code (never NULL). */
 const char* ssm_status_string(int status);
 

@@ -11,6 +11,8 @@ from ._binding import (  # noqa: F401
     library_path,
     load_library,
     ssm_causal_conv1d_fwd,
+    ssm_scan_bwd,
+    ssm_scan_bwd_workspace_bytes,
     ssd_chunk_scan_fwd,
     ssd_state_update,
     ssd_workspace_bytes,

@@ -59,6 +59,10 @@ def load_library():
         lib.ssd_state_update.restype = _I
         lib.ssm_causal_conv1d_fwd.argtypes = [_P] * 4 + [_I, _P, _P] + [_I64] * 4 + [_I, _P]
         lib.ssm_causal_conv1d_fwd.restype = _I
+        lib.ssm_scan_bwd.argtypes = [_P] * 8 + [_I] + [_P] * 12 + [_I64] * 4 + [_I, _I, _P, _SZ, _P]
+        lib.ssm_scan_bwd.restype = _I
+        lib.ssm_scan_bwd_workspace_bytes.argtypes = [_I64] * 4
+        lib.ssm_scan_bwd_workspace_bytes.restype = _SZ
         lib.ssm_status_string.argtypes = [_I]
         lib.ssm_status_string.restype = ctypes.c_char_p
         lib.ssm_last_error.argtypes = []
@@ -307,3 +311,52 @@ def ssm_causal_conv1d_fwd(x, weight, bias=None, state_in=None, silu=True, out=No
                                    _ptr(state_out), batch, seqlen, dim, width, act, _stream(dev))
     _check(lib, "ssm_causal_conv1d_fwd", rc)
     return (out, state_out) if (return_state or state_out is not None) else out
+
+
+def ssm_scan_bwd_workspace_bytes(batch, seqlen, dim, dstate) -> int:
+    return int(load_library().ssm_scan_bwd_workspace_bytes(batch, seqlen, dim, dstate))
+
+
+def ssm_scan_bwd(x, delta, A, B, C, dout, D=None, z=None, delta_bias=None, delta_softplus=False, h0=None,
+                 dh_final=None, want_dh0=False, workspace=None):
+    """Gradients of sum(dout * y) + sum(dh_final * h_final) for ssm_scan_fwd with the same inputs.
+    Returns a dict: dx, ddelta (input dtypes), dA, dB, dC (fp32) and, for the optional inputs given,
+    dD, dz, ddelta_bias, and dh0 (with h0 or want_dh0)."""
+    lib = load_library()
+    dev = x.device
+    _need(x, "x", device=dev)
+    batch, seqlen, dim = x.shape
+    act = _act_code(x, "x")
+    _need(delta, "delta", shape=x.shape, device=dev)
+    dcode = _act_code(delta, "delta")
+    _need(A, "A", torch.float32, device=dev)
+    if A.dim() != 2 or A.shape[0] != dim:
+        raise ValueError("A must be (dim, dstate)")
+    dstate = A.shape[1]
+    _need(B, "B", x.dtype, (batch, seqlen, dstate), dev)
+    _need(C, "C", x.dtype, (batch, seqlen, dstate), dev)
+    _need(dout, "dout", x.dtype, x.shape, dev)
+    _need(D, "D", torch.float32, (dim,), dev)
+    _need(z, "z", x.dtype, x.shape, dev)
+    _need(delta_bias, "delta_bias", torch.float32, (dim,), dev)
+    _need(h0, "h0", torch.float32, (batch, dim, dstate), dev)
+    _need(dh_final, "dh_final", torch.float32, (batch, dim, dstate), dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = dict(dx=torch.empty_like(x), ddelta=torch.empty_like(delta), dA=torch.empty((dim, dstate), **f32),
+             dB=torch.empty((batch, seqlen, dstate), **f32), dC=torch.empty((batch, seqlen, dstate), **f32))
+    if D is not None:
+        g["dD"] = torch.empty((dim,), **f32)
+    if z is not None:
+        g["dz"] = torch.empty_like(x)
+    if delta_bias is not None:
+        g["ddelta_bias"] = torch.empty((dim,), **f32)
+    if h0 is not None or want_dh0:
+        g["dh0"] = torch.empty((batch, dim, dstate), **f32)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib.ssm_scan_bwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                          int(bool(delta_softplus)), _ptr(h0), _ptr(dout), _ptr(dh_final), _ptr(g["dx"]),
+                          _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g.get("dD")),
+                          _ptr(g.get("dz")), _ptr(g.get("ddelta_bias")), _ptr(g.get("dh0")),
+                          batch, seqlen, dim, dstate, act, dcode, _ptr(workspace), wsb, _stream(dev))
+    _check(lib, "ssm_scan_bwd", rc)
+    return g

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libssm_mi355x.so")
-SOURCES = [("api.cpp", []), ("scan_host.hip", []), ("ssd_kernels.hip", []), ("step_kernels.hip", []), ("conv_kernels.hip", [])] + [
+SOURCES = [("api.cpp", []), ("scan_host.hip", []), ("ssd_kernels.hip", []), ("step_kernels.hip", []), ("conv_kernels.hip", []), ("scan_bwd.hip", [])] + [
     ("scan_inst.hip", ["-DSSM_R=%d" % rr, "-DSSM_XB=%d" % xb, "-DSSM_DB=%d" % db, "-DSSM_S=%d" % sv])
     for rr, sv in ((4, 32), (4, 16), (4, 8), (4, 4), (4, 2), (4, 1), (8, 2), (16, 1))
     for xb in (1, 0) for db in (1, 0)]

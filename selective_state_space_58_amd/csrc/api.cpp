@@ -353,4 +353,51 @@ int ssm_causal_conv1d_fwd(const void* x, const float* weight, const float* bias,
   return launch_conv(a, stream);
 }
 
+size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
+  if (batch <= 0 || seqlen <= 0 || dim <= 0 || dstate <= 0 || dstate > 16) return 0;
+  if (!elems_ok({batch, seqlen, dim, dstate})) return 0;
+  return scan_bwd_ws_bytes(batch, seqlen, dim, dstate);
+}
+
+int ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* Dskip,
+                 const void* z, const float* delta_bias, int delta_softplus, const float* h0, const void* dout,
+                 const float* dh_final, void* dx, void* ddelta, float* dA, float* dB, float* dC, float* dDskip,
+                 void* dz, float* ddelta_bias, float* dh0, int64_t batch, int64_t seqlen, int64_t dim,
+                 int64_t dstate, int act_dtype, int delta_dtype, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  g_last_error.clear();
+  int rc = validate_scan(x, delta, A, B, C, dx, false, Dskip, z, delta_bias, h0, dh0, batch, seqlen, dim, dstate,
+                         act_dtype, delta_dtype, delta_softplus);
+  if (rc != SSM_OK) return rc;
+  const bool has_tok = batch > 0 && seqlen > 0 && dim > 0;
+  if ((has_tok && (dout == nullptr || ddelta == nullptr || dB == nullptr || dC == nullptr)) ||
+      (dim > 0 && dA == nullptr) || (has_tok && z != nullptr && dz == nullptr) ||
+      (dim > 0 && Dskip != nullptr && dDskip == nullptr) || (dim > 0 && delta_bias != nullptr && ddelta_bias == nullptr))
+    return fail(SSM_ERR_NULL, "dout, dx, ddelta, dA, dB, dC and the gradients of the optional inputs given are required");
+  if (dstate > 16) return fail(SSM_ERR_UNSUPPORTED, "the backward pass supports dstate <= 16");
+  const size_t as = dsize(act_dtype), ds = dsize(delta_dtype);
+  if (!aligned(dout, as) || !aligned(dx, as) || !aligned(dz, as) || !aligned(ddelta, ds) || !aligned(dA, 4) ||
+      !aligned(dB, 4) || !aligned(dC, 4) || !aligned(dDskip, 4) || !aligned(ddelta_bias, 4) ||
+      !aligned(dh_final, 4))
+    return fail(SSM_ERR_ALIGNMENT, "a pointer is not aligned to its element size");
+  if (batch == 0 || dim == 0) return SSM_OK;
+  hipStream_t st = (hipStream_t)stream;
+  Scratch own;
+  void* ws = nullptr;
+  rc = get_workspace(workspace, workspace_bytes, seqlen > 0 ? scan_bwd_ws_bytes(batch, seqlen, dim, dstate) : 0, st,
+                     &own, &ws);
+  if (rc != SSM_OK) return rc;
+  BwdArgs a{};
+  a.x = x; a.delta = delta; a.A = A; a.B = B; a.C = C; a.Dskip = Dskip; a.z = z; a.delta_bias = delta_bias;
+  a.h0 = h0; a.dout = dout; a.dh_final = dh_final;
+  a.dx = dx; a.ddelta = ddelta; a.dA = dA; a.dB = dB; a.dC = dC;
+  a.dDskip = Dskip != nullptr ? dDskip : nullptr;
+  a.dz = z != nullptr ? dz : nullptr;
+  a.ddelta_bias = delta_bias != nullptr ? ddelta_bias : nullptr;
+  a.dh0 = dh0; a.ws_ckpt = (float*)ws;
+  a.batch = batch; a.seqlen = seqlen; a.dim = dim; a.dstate = dstate;
+  a.softplus = delta_softplus; a.act_bf16 = act_dtype == SSM_BF16; a.delta_bf16 = delta_dtype == SSM_BF16;
+  return launch_scan_bwd(a, stream);
+}
+
 }  // extern "C"

@@ -58,6 +58,37 @@ ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, b
 // Enqueue the whole selective scan (all phases).  Returns an ssm_status.
 int launch_scan(const ScanArgs& a, const ScanPlan& p, bool final_only, void* stream);
 
+// ---------------------------------------------------------------- selective scan backward
+struct BwdArgs {
+  const void* x;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* Dskip;
+  const void* z;
+  const float* delta_bias;
+  const float* h0;
+  const void* dout;        // act dtype, like y
+  const float* dh_final;   // or null
+  void* dx;                // act dtype
+  void* ddelta;            // delta dtype
+  float* dA;               // (dim, dstate)
+  float* dB;               // (batch, seqlen, dstate) fp32
+  float* dC;
+  float* dDskip;           // (dim) or null
+  void* dz;                // act dtype; required when z is given
+  float* ddelta_bias;      // (dim) or null
+  float* dh0;              // (batch, dim, dstate) or null
+  float* ws_ckpt;          // (ntiles, batch, dim, dstate) states at tile starts
+  int64_t batch, seqlen, dim, dstate;
+  int softplus;
+  int act_bf16, delta_bf16;
+};
+
+size_t scan_bwd_ws_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
+int launch_scan_bwd(const BwdArgs& a, void* stream);
+
 // ---------------------------------------------------------------- SSD
 struct SsdArgs {
   const void* x;

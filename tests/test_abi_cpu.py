@@ -178,3 +178,33 @@ def test_conv_empty_is_noop():
     lib = _lib()
     assert conv(lib, batch=0) == 0
     assert conv(lib, dim=0) == 0
+
+
+def bwd(lib, **kw):
+    Q = P + 0x100000
+    a = dict(x=P, delta=P, A=P, B=P, C=P, D=None, z=None, bias=None, sp=0, h0=None, dout=P, dhf=None,
+             dx=Q, ddelta=Q + 0x10000, dA=Q + 0x20000, dB=Q + 0x30000, dC=Q + 0x40000, dD=None, dz=None, dbias=None,
+             dh0=None, batch=1, seqlen=4, dim=4, dstate=4, act=1, ddt=1, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return lib.ssm_scan_bwd(a["x"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"], a["sp"], a["h0"],
+                            a["dout"], a["dhf"], a["dx"], a["ddelta"], a["dA"], a["dB"], a["dC"], a["dD"], a["dz"],
+                            a["dbias"], a["dh0"], a["batch"], a["seqlen"], a["dim"], a["dstate"], a["act"], a["ddt"],
+                            a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dout=None), 1), (dict(dx=None), 1), (dict(ddelta=None), 1), (dict(dA=None), 1), (dict(dB=None), 1),
+    (dict(z=P), 1), (dict(D=P), 1), (dict(bias=P), 1), (dict(seqlen=-1), 2), (dict(act=3), 3),
+    (dict(dstate=17), 4), (dict(dx=P + 0x100001), 7), (dict(dA=P + 0x100002), 7),
+])
+def test_scan_bwd_argument_errors(kw, code):
+    lib = _lib()
+    assert bwd(lib, **kw) == code
+    assert lib.ssm_last_error() != b""
+
+
+def test_scan_bwd_workspace_query():
+    lib = _lib()
+    assert lib.ssm_scan_bwd_workspace_bytes(2, 100, 40, 16) == 7 * 2 * 40 * 16 * 4
+    assert lib.ssm_scan_bwd_workspace_bytes(2, 100, 40, 17) == 0
+    assert bwd(lib, batch=0) == 0
