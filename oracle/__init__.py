@@ -51,6 +51,8 @@ def _load():
             I64 = ctypes.c_int64
             I = ctypes.c_int
             lib.oracle_selective_scan.argtypes = [P] * 8 + [I, P, P, P] + [I64] * 6
+            lib.oracle_selective_scan_euler.argtypes = [P] * 8 + [I, P, P, P] + [I64] * 6
+            lib.oracle_selective_scan_euler.restype = None
             lib.oracle_selective_scan.restype = None
             lib.oracle_ssd_recurrent.argtypes = [P] * 8 + [I, P, P, P] + [I64] * 8
             lib.oracle_ssd_recurrent.restype = None
@@ -95,8 +97,17 @@ def _run_slices(fn, total: int, threads: int | None):
 
 
 def selective_scan(x, delta, A, B, C, Dskip=None, z=None, delta_bias=None,
-                   delta_softplus=False, h0=None, want_y=True, threads=None):
-    """O1: y (batch, seqlen, dim) and h_final (batch, dim, dstate), both float64."""
+                   delta_softplus=False, h0=None, want_y=True, threads=None, euler=False, reverse=False):
+    """O1: y (batch, seqlen, dim) and h_final (batch, dim, dstate), both float64.
+    euler: the Euler input discretization Bbar = dt * B (O1e).  reverse: the scan run over the
+    time-reversed sequence, by definition flip(scan(flip(inputs))): h0 is the state before the last
+    token, h_final the state after token 0, and y_t depends on tokens t .. L-1."""
+    if reverse:
+        flip = lambda a: None if a is None else np.ascontiguousarray(np.flip(np.asarray(a, dtype=np.float64), 1))
+        y, hf = selective_scan(flip(x), flip(delta), A, flip(B), flip(C), Dskip=Dskip, z=flip(z),
+                               delta_bias=delta_bias, delta_softplus=delta_softplus, h0=h0, want_y=want_y,
+                               threads=threads, euler=euler)
+        return (flip(y) if y is not None else None), hf
     x = _f64(x)
     batch, seqlen, dim = x.shape
     A = _f64(A)
@@ -111,7 +122,8 @@ def selective_scan(x, delta, A, B, C, Dskip=None, z=None, delta_bias=None,
     y = np.empty_like(x) if want_y else None
     hf = np.empty((batch, dim, dstate), dtype=np.float64)
     lib = _load()
-    _run_slices(lambda s0, s1: lib.oracle_selective_scan(
+    fn = lib.oracle_selective_scan_euler if euler else lib.oracle_selective_scan
+    _run_slices(lambda s0, s1: fn(
         _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(z), _ptr(delta_bias),
         int(bool(delta_softplus)), _ptr(h0), _ptr(y), _ptr(hf),
         batch, seqlen, dim, dstate, s0, s1), batch * dim, threads)

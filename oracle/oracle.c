@@ -73,12 +73,12 @@ static double zoh_gain(double dt, double a) {
  *         P1 sec. 2 "x[t] = A_bar x[t-1] + B_bar u[t]")
  *   y_t = sum_n C_t,n h_t,n + Dskip x_t, then * silu(z_t)         (P1 sec. 5)
  */
-void oracle_selective_scan(const double* x, const double* delta, const double* A,
-                           const double* B, const double* C, const double* Dskip,
-                           const double* z, const double* delta_bias, int delta_softplus,
-                           const double* h0, double* y, double* h_final,
-                           int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
-                           int64_t s_begin, int64_t s_end) {
+static void selective_scan_impl(const double* x, const double* delta, const double* A,
+                                const double* B, const double* C, const double* Dskip,
+                                const double* z, const double* delta_bias, int delta_softplus,
+                                const double* h0, double* y, double* h_final,
+                                int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                                int64_t s_begin, int64_t s_end, int euler) {
   double* h = (double*)malloc(sizeof(double) * (size_t)(dstate > 0 ? dstate : 1));
   for (int64_t s = s_begin; s < s_end; ++s) {
     int64_t b = s / dim, d = s % dim;
@@ -93,7 +93,7 @@ void oracle_selective_scan(const double* x, const double* delta, const double* A
       for (int64_t n = 0; n < dstate; ++n) {
         double a = A[d * dstate + n];
         double abar = exp(dt * a);
-        double g = zoh_gain(dt, a);
+        double g = euler ? dt : zoh_gain(dt, a);
         h[n] = abar * h[n] + g * B[r + n] * x[i];
         acc += C[r + n] * h[n];
       }
@@ -105,6 +105,31 @@ void oracle_selective_scan(const double* x, const double* delta, const double* A
       for (int64_t n = 0; n < dstate; ++n) h_final[(b * dim + d) * dstate + n] = h[n];
   }
   free(h);
+}
+
+void oracle_selective_scan(const double* x, const double* delta, const double* A,
+                           const double* B, const double* C, const double* Dskip,
+                           const double* z, const double* delta_bias, int delta_softplus,
+                           const double* h0, double* y, double* h_final,
+                           int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                           int64_t s_begin, int64_t s_end) {
+  selective_scan_impl(x, delta, A, B, C, Dskip, z, delta_bias, delta_softplus, h0, y, h_final, batch, seqlen, dim,
+                      dstate, s_begin, s_end, 0);
+}
+
+/*
+ * O1e. The same scan with the Euler input discretization of the pages'
+ * listings, Bbar = dt * B (P1 sec. 5 selective_scan: deltaB_u = delta * B * u;
+ * P2 listing), keeping Abar = exp(dt a).
+ */
+void oracle_selective_scan_euler(const double* x, const double* delta, const double* A,
+                                 const double* B, const double* C, const double* Dskip,
+                                 const double* z, const double* delta_bias, int delta_softplus,
+                                 const double* h0, double* y, double* h_final,
+                                 int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                                 int64_t s_begin, int64_t s_end) {
+  selective_scan_impl(x, delta, A, B, C, Dskip, z, delta_bias, delta_softplus, h0, y, h_final, batch, seqlen, dim,
+                      dstate, s_begin, s_end, 1);
 }
 
 /*

@@ -328,3 +328,33 @@ def test_scan_backward_against_finite_differences(oracle_mod, softplus, full):
             num[idx] = (lp - lm) / (2 * eps)
         err = np.max(np.abs(g[gk] - num)) / max(np.max(np.abs(num)), 1e-12)
         assert err < 2e-7, (k, err)
+
+
+def test_euler_closed_form(oracle_mod):
+    # constant dt, a, B, C, x with Bbar = dt B: h_t = dt B x (1 - e^{a dt (t+1)}) / (1 - e^{a dt})
+    L = 200
+    for a, dt, Bv, Cv, xv in [(-0.7, 0.05, 1.3, -0.4, 2.0), (-3.0, 0.2, -0.5, 1.1, -1.5)]:
+        y, hf = oracle_mod.selective_scan(np.full((1, L, 1), xv), np.full((1, L, 1), dt), np.array([[a]]),
+                                          np.full((1, L, 1), Bv), np.full((1, L, 1), Cv), euler=True)
+        E = np.exp(a * dt)
+        h = dt * Bv * xv * (1.0 - E ** (np.arange(L) + 1)) / (1.0 - E)
+        assert rel(y[0, :, 0], Cv * h) < 1e-13 and abs(hf[0, 0, 0] - h[-1]) <= 1e-13 * abs(h[-1])
+    # a = 0: Euler and ZOH coincide (both gains are dt)
+    rng = np.random.default_rng(90)
+    x = rng.standard_normal((1, 20, 2)); dt = rng.uniform(0.1, 0.5, (1, 20, 2))
+    B = rng.standard_normal((1, 20, 3)); C = rng.standard_normal((1, 20, 3))
+    A = np.zeros((2, 3))
+    assert rel(oracle_mod.selective_scan(x, dt, A, B, C, euler=True)[0], oracle_mod.selective_scan(x, dt, A, B, C)[0]) < 1e-15
+
+
+def test_reverse_scan_is_anticausal_convolution(oracle_mod):
+    # time-invariant parameters: the reverse scan is y_t = sum_{j >= t} K_{j-t} x_j with the same kernel
+    rng = np.random.default_rng(91)
+    L, N = 40, 5
+    A = -rng.uniform(0.2, 2.0, N); B = rng.standard_normal(N); C = rng.standard_normal(N); dt = 0.07
+    x = rng.standard_normal(L)
+    y, _ = oracle_mod.selective_scan(x[None, :, None], np.full((1, L, 1), dt), A[None, :],
+                                     np.broadcast_to(B, (1, L, N)), np.broadcast_to(C, (1, L, N)), reverse=True)
+    K = oracle_mod.lti_conv(np.eye(L)[0], A, B, C, dt)     # impulse response = the kernel K_0 .. K_{L-1}
+    ref = np.array([sum(K[j - t] * x[j] for j in range(t, L)) for t in range(L)])
+    assert rel(y[0, :, 0], ref) < 1e-13
