@@ -100,6 +100,42 @@ int ssm_scan_fwd(const void* x, const void* delta, const float* A, const void* B
                  int act_dtype, int delta_dtype,
                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* flag bits of ssm_scan_fwd_ex */
+enum ssm_scan_flag {
+  SSM_SCAN_REVERSE = 1,         /* run the recurrence from the last token to the first */
+  SSM_SCAN_EULER = 2,           /* Euler input discretization: gain dt instead of ZOH */
+  SSM_SCAN_DELTA_PER_TOKEN = 4  /* delta is (batch, seqlen): one dt per token for all channels */
+};
+
+/*
+ * Variants of ssm_scan_fwd selected by flags (any combination; 0 is
+ * ssm_scan_fwd itself).  Arguments, layouts, ownership and errors are those
+ * of ssm_scan_fwd, plus:
+ *   SSM_SCAN_REVERSE : the scan of the time-reversed sequence, i.e.
+ *       flip_t(scan(flip_t(inputs))) with flip_t reversing the token axis of
+ *       x, delta, B, C and z.  y[b,t,d] then depends on tokens t..seqlen-1,
+ *       h0 is the state entering at token seqlen-1 and h_final the state
+ *       after token 0.  This is the backward branch of a bidirectional or
+ *       multi-direction scan ([guide] sec. 9, VMamba: an image's patch sequence
+ *       scanned in four orders, each a flip or transpose of the same S6
+ *       scan); layouts stay in natural token order, nothing is copied.
+ *   SSM_SCAN_EULER : Bbar = dt * B, i.e. h_n = exp(dt*A[d,n]) h_n +
+ *       dt * B[b,t,n] * x[b,t,d], the simplified discretization of the
+ *       code listings ([guide] sec. 5 naive selective scan; [ssm] the numpy
+ *       selective SSM implementation) in place of exact ZOH.
+ *   SSM_SCAN_DELTA_PER_TOKEN : delta holds batch * seqlen values (row-major
+ *       (batch, seqlen), delta dtype); every channel of token t reads
+ *       delta[b,t] (plus its own delta_bias[d] when given), as in [ssm]'s numpy
+ *       selective SSM, which projects one step size per token.
+ * Unknown bits return SSM_ERR_UNSUPPORTED.
+ */
+int ssm_scan_fwd_ex(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                    const float* Dskip, const void* z, const float* delta_bias, int delta_softplus,
+                    const float* h0, void* y, float* h_final,
+                    int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                    int act_dtype, int delta_dtype, int flags,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * Final state only: the same recurrence as ssm_scan_fwd, writing h_final
  * (required) and no y; C, Dskip and z are not needed.  ([guide] sec. 2/4:

@@ -7,6 +7,9 @@ torch, and pass raw device pointers plus the current HIP stream.  All
 computation happens in the library's HIP kernels; there is no fallback.
 """
 from ._binding import (  # noqa: F401
+    SSM_SCAN_DELTA_PER_TOKEN,
+    SSM_SCAN_EULER,
+    SSM_SCAN_REVERSE,
     SSMError,
     library_path,
     load_library,
@@ -18,6 +21,7 @@ from ._binding import (  # noqa: F401
     ssd_workspace_bytes,
     ssm_scan_final_state,
     ssm_scan_fwd,
+    ssm_scan_fwd_ex,
     ssm_state_update,
     ssm_scan_workspace_bytes,
 )

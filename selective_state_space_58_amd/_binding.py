@@ -45,6 +45,8 @@ def load_library():
         lib = ctypes.CDLL(_LIB_PATH)
         lib.ssm_scan_fwd.argtypes = [_P] * 8 + [_I, _P, _P, _P] + [_I64] * 4 + [_I, _I, _P, _SZ, _P]
         lib.ssm_scan_fwd.restype = _I
+        lib.ssm_scan_fwd_ex.argtypes = [_P] * 8 + [_I, _P, _P, _P] + [_I64] * 4 + [_I, _I, _I, _P, _SZ, _P]
+        lib.ssm_scan_fwd_ex.restype = _I
         lib.ssm_scan_final_state.argtypes = [_P] * 5 + [_I, _P, _P] + [_I64] * 4 + [_I, _I, _P, _SZ, _P]
         lib.ssm_scan_final_state.restype = _I
         lib.ssd_chunk_scan_fwd.argtypes = [_P] * 8 + [_I, _P, _P, _P] + [_I64] * 7 + [_I, _I, _P, _SZ, _P]
@@ -117,17 +119,41 @@ def ssd_workspace_bytes(batch, seqlen, nheads, headdim, ngroups, dstate, chunk_s
     return int(load_library().ssd_workspace_bytes(batch, seqlen, nheads, headdim, ngroups, dstate, chunk_size))
 
 
+# flag bits of ssm_scan_fwd_ex (enum ssm_scan_flag)
+SSM_SCAN_REVERSE = 1
+SSM_SCAN_EULER = 2
+SSM_SCAN_DELTA_PER_TOKEN = 4
+
+
 def ssm_scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False, h0=None,
                  return_final_state=False, y=None, h_final=None, workspace=None):
     """Selective scan forward.  x, delta, z: (batch, seqlen, dim); A: (dim, dstate) fp32;
     B, C: (batch, seqlen, dstate); D, delta_bias: (dim) fp32; h0: (batch, dim, dstate) fp32.
     Returns y, or (y, h_final) with return_final_state."""
+    return _scan_fwd(x, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, return_final_state, y, h_final,
+                     workspace, None)
+
+
+def ssm_scan_fwd_ex(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False, h0=None,
+                    return_final_state=False, y=None, h_final=None, workspace=None, reverse=False, euler=False):
+    """ssm_scan_fwd with the variant flags: reverse (scan from the last token to the first),
+    euler (Bbar = dt * B).  delta may be (batch, seqlen), one step size per token for all channels."""
+    flags = (SSM_SCAN_REVERSE if reverse else 0) | (SSM_SCAN_EULER if euler else 0)
+    if isinstance(delta, torch.Tensor) and delta.dim() == 2:
+        flags |= SSM_SCAN_DELTA_PER_TOKEN
+    return _scan_fwd(x, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, return_final_state, y, h_final,
+                     workspace, flags)
+
+
+def _scan_fwd(x, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, return_final_state, y, h_final, workspace,
+              flags):
     lib = load_library()
     dev = x.device
     _need(x, "x", device=dev)
     batch, seqlen, dim = x.shape
     act = _act_code(x, "x")
-    _need(delta, "delta", shape=x.shape, device=dev)
+    per_token = flags is not None and (flags & SSM_SCAN_DELTA_PER_TOKEN) != 0
+    _need(delta, "delta", shape=(batch, seqlen) if per_token else x.shape, device=dev)
     dcode = _act_code(delta, "delta")
     _need(A, "A", torch.float32, device=dev)
     if A.dim() != 2 or A.shape[0] != dim:
@@ -146,10 +172,14 @@ def ssm_scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softp
         h_final = torch.empty((batch, dim, dstate), dtype=torch.float32, device=dev)
     _need(h_final, "h_final", torch.float32, (batch, dim, dstate), dev)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    rc = lib.ssm_scan_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
-                          int(bool(delta_softplus)), _ptr(h0), _ptr(y), _ptr(h_final),
-                          batch, seqlen, dim, dstate, act, dcode, _ptr(workspace), wsb, _stream(dev))
-    _check(lib, "ssm_scan_fwd", rc)
+    args = (_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+            int(bool(delta_softplus)), _ptr(h0), _ptr(y), _ptr(h_final), batch, seqlen, dim, dstate, act, dcode)
+    if flags is None:
+        rc = lib.ssm_scan_fwd(*args, _ptr(workspace), wsb, _stream(dev))
+        _check(lib, "ssm_scan_fwd", rc)
+    else:
+        rc = lib.ssm_scan_fwd_ex(*args, int(flags), _ptr(workspace), wsb, _stream(dev))
+        _check(lib, "ssm_scan_fwd_ex", rc)
     return (y, h_final) if (return_final_state or h_final is not None) else y
 
 

@@ -145,8 +145,10 @@ static int scan_common(const void* x, const void* delta, const float* A, const v
                        const float* Dskip, const void* z, const float* delta_bias, int delta_softplus,
                        const float* h0, void* y, float* h_final, int64_t batch, int64_t seqlen, int64_t dim,
                        int64_t dstate, int act_dtype, int delta_dtype, void* workspace, size_t workspace_bytes,
-                       void* stream, bool final_only) {
+                       void* stream, bool final_only, int flags = 0) {
   g_last_error.clear();
+  if ((flags & ~(SSM_SCAN_REVERSE | SSM_SCAN_EULER | SSM_SCAN_DELTA_PER_TOKEN)) != 0)
+    return fail(SSM_ERR_UNSUPPORTED, "unknown scan flag bits");
   int rc = validate_scan(x, delta, A, B, C, final_only ? (const void*)h_final : y, final_only, Dskip, z, delta_bias,
                          h0, h_final, batch, seqlen, dim, dstate, act_dtype, delta_dtype, delta_softplus);
   if (rc != SSM_OK) return rc;
@@ -168,7 +170,10 @@ static int scan_common(const void* x, const void* delta, const float* A, const v
   a.softplus = delta_softplus;
   a.act_bf16 = act_dtype == SSM_BF16;
   a.delta_bf16 = delta_dtype == SSM_BF16;
-  a.vec_io = act_dtype == delta_dtype && aligned16(x) && aligned16(delta) &&
+  a.reverse = (flags & SSM_SCAN_REVERSE) != 0;
+  a.euler = (flags & SSM_SCAN_EULER) != 0;
+  a.delta_per_token = (flags & SSM_SCAN_DELTA_PER_TOKEN) != 0;
+  a.vec_io = act_dtype == delta_dtype && !a.delta_per_token && aligned16(x) && aligned16(delta) &&
              aligned16(B) && (final_only || aligned16(C)) && (final_only || aligned16(z));
   if (ws != nullptr) {
     const size_t st_bytes = (size_t)p.nchunks * (size_t)(batch * dim * dstate) * sizeof(float);
@@ -185,6 +190,15 @@ int ssm_scan_fwd(const void* x, const void* delta, const float* A, const void* B
                  void* stream) {
   return scan_common(x, delta, A, B, C, Dskip, z, delta_bias, delta_softplus, h0, y, h_final, batch, seqlen, dim,
                      dstate, act_dtype, delta_dtype, workspace, workspace_bytes, stream, false);
+}
+
+int ssm_scan_fwd_ex(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                    const float* Dskip, const void* z, const float* delta_bias, int delta_softplus,
+                    const float* h0, void* y, float* h_final, int64_t batch, int64_t seqlen, int64_t dim,
+                    int64_t dstate, int act_dtype, int delta_dtype, int flags, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return scan_common(x, delta, A, B, C, Dskip, z, delta_bias, delta_softplus, h0, y, h_final, batch, seqlen, dim,
+                     dstate, act_dtype, delta_dtype, workspace, workspace_bytes, stream, false, flags);
 }
 
 int ssm_scan_final_state(const void* x, const void* delta, const float* A, const void* B, const float* delta_bias,

@@ -181,7 +181,10 @@ struct TileShape {
   static constexpr int KB = T * NP / 64;           // B (and C) items per lane per tile
 };
 
-template <int RR, bool XB, bool DB, int S, int MODE, bool ACC, bool VEC>
+// GAIN: kGainShort (e^q - 1)/a, kGainAccurate (series near q = 0), kGainEuler dt.
+enum GainMode : int { kGainShort = 0, kGainAccurate = 1, kGainEuler = 2 };
+
+template <int RR, bool XB, bool DB, int S, int MODE, int GAIN, bool VEC>
 __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t ch0, int64_t chunk,
                                           const float (&a2)[S], const float (&ia)[S], const float (&av)[S],
                                           float2* __restrict__ s_dx, float* __restrict__ s_gz,
@@ -191,6 +194,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
   using TD = typename Act<DB>::T;
   constexpr int R = TS::R, CH = TS::CH, NP = TS::NP, T = TS::T, KX = TS::KX, KB = TS::KB;
   constexpr bool FULL = (MODE == kModeFull);
+  constexpr bool ACC = GAIN != kGainShort;   // accurate softplus as well
   const int lane = threadIdx.x;
   const int r = lane / CH, c = lane % CH;
   const int64_t L = a.seqlen, dim = a.dim, N = a.dstate;
@@ -227,27 +231,37 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
   const bool has_z = FULL && a.z != nullptr;
   const bool dense_bc = (N == NP);
 
+  // Time direction.  Token t (processing order) of the tile starting at t0 is
+  // global row grow0(t0) + u(t): u(t) = t forward; reversed, the tile covers
+  // rows L - t0 - T .. L - 1 - t0 and u(t) = T - 1 - t, so row offsets stay
+  // non-negative.
+  const bool rev = a.reverse != 0;
+  auto grow0 = [&](int64_t t0) -> int64_t { return rev ? L - t0 - T : t0; };
+  auto urow = [&](int t) -> uint32_t { return (uint32_t)(rev ? T - 1 - t : t); };
+  const bool tok_delta = !VEC && a.delta_per_token != 0;
+
   // ---- register prefetch of one tile.  Row offsets are 32-bit, relative to a
   // wave-uniform 64-bit base, so loads use the scalar-base addressing form.
   RX px[KX], pz[KX], pb[KB], pc[KB];
   RD pd[KX];
   auto fetch_scalar = [&](int64_t t0) {
     const bool tail = t0 + T > t_stop;
-    const int64_t row0 = (b * L + t0) * dim + ch0;  // uniform
+    const int64_t row0 = (b * L + grow0(t0)) * dim + ch0;  // uniform
     const RX* xb = gx + row0;
-    const RD* db = gd + row0;
+    // delta shared by every channel of a token: one value per (batch, token)
+    const RD* db = tok_delta ? gd + (b * L + grow0(t0)) : gd + row0;
     const RX* zb = gz + row0;
     const int64_t last = t_stop - 1 - t0;            // last valid local token (uniform)
 #pragma unroll
     for (int k = 0; k < KX; ++k) {
       int t = R * k + r;
       if (tail) t = t < last ? t : (int)last;
-      const uint32_t off = (uint32_t)t * dim32 + (uint32_t)cl;
+      const uint32_t off = urow(t) * dim32 + (uint32_t)cl;
       px[k] = xb[off];
-      pd[k] = db[off];
+      pd[k] = db[tok_delta ? urow(t) : off];
       if (has_z) pz[k] = zb[off];
     }
-    const int64_t bc0 = (b * L + t0) * N;            // uniform
+    const int64_t bc0 = (b * L + grow0(t0)) * N;     // uniform
     const RX* bb = gB + bc0;
     const RX* cb = gC + bc0;
 #pragma unroll
@@ -257,8 +271,8 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
       const int n = e % NP;
       if (tail) t = t < last ? t : (int)last;
       // entries with n >= N load a valid element and are zeroed when staged
-      const uint32_t off = (dense_bc && !tail) ? (uint32_t)e
-                                               : (uint32_t)t * n32 + ((uint32_t)n < n32 ? (uint32_t)n : 0u);
+      const uint32_t off = (dense_bc && !tail && !rev) ? (uint32_t)e
+                                                       : urow(t) * n32 + ((uint32_t)n < n32 ? (uint32_t)n : 0u);
       pb[j] = bb[off];
       if (FULL) pc[j] = cb[off];
     }
@@ -319,7 +333,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
   auto fetch_vec = [&](int64_t t0) {
     const bool tail = t0 + T > t_stop;
     const int64_t last = t_stop - 1 - t0;
-    const int64_t row0 = (b * L + t0) * dim + ch0;          // uniform
+    const int64_t row0 = (b * L + grow0(t0)) * dim + ch0;   // uniform
     const char* xb = (const char*)(gx + row0);
     const char* db = (const char*)(gd + row0);
     const char* zb = (const char*)(gz + row0);
@@ -329,19 +343,19 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
       const int k = lane + 64 * q;
       int tl = k / XROW;
       if (tail) tl = tl < last ? tl : (int)last;
-      const uint32_t off = (uint32_t)tl * rowb + (uint32_t)(k % XROW) * (uint32_t)VB;
+      const uint32_t off = urow(tl) * rowb + (uint32_t)(k % XROW) * (uint32_t)VB;
       vx[q] = *reinterpret_cast<const VT*>(xb + off);
       vd[q] = *reinterpret_cast<const VT*>(db + off);
       if (has_z) vz[q] = *reinterpret_cast<const VT*>(zb + off);
     }
-    const RX* bb = gB + (b * L + t0) * N;                   // uniform
-    const RX* cb = gC + (b * L + t0) * N;
+    const RX* bb = gB + (b * L + grow0(t0)) * N;            // uniform
+    const RX* cb = gC + (b * L + grow0(t0)) * N;
 #pragma unroll
     for (int q = 0; q < CBN; ++q) {
       const int e0 = (lane + 64 * q) * EX;
       int t = e0 / NP;
       if (tail) t = t < last ? t : (int)last;
-      const uint32_t off = (uint32_t)t * (uint32_t)NP + (uint32_t)(e0 % NP);
+      const uint32_t off = urow(t) * (uint32_t)NP + (uint32_t)(e0 % NP);
       vb[q] = *reinterpret_cast<const VT*>(bb + off);
       if (FULL) vc[q] = *reinterpret_cast<const VT*>(cb + off);
     }
@@ -406,7 +420,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
     __syncthreads();
     if (t0 + T < t_stop) fetch(t0 + T);
     const int64_t nvalid = t_stop - t0;
-    TX* yb = gy + (b * L + t0) * dim + ch0;          // uniform
+    TX* yb = gy + (b * L + grow0(t0)) * dim + ch0;   // uniform
     // Operands of one step of U = 4 tokens: (dt, x) and this row's B/C
     // slices.  The next step's operands are read from LDS while the current
     // step is computed, so LDS latency overlaps the VALU work; a group of R
@@ -470,7 +484,9 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
 #pragma unroll
         for (int s = 0; s < S; ++s) {
           const float E = Ecur[j][s];
-          const float g = ACC ? zoh_gain_accurate(E, dx.x, av[s], ia[s]) : fmaf(E, ia[s], -ia[s]);
+          const float g = GAIN == kGainEuler      ? dx.x
+                          : GAIN == kGainAccurate ? zoh_gain_accurate(E, dx.x, av[s], ia[s])
+                                                  : fmaf(E, ia[s], -ia[s]);
           h[s] = fmaf(E, h[s], g * (cur.b[j][s] * dx.y));
           if (FULL) acc = fmaf(cur.c[j][s], h[s], acc);
         }
@@ -482,7 +498,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
         const int tl = tb + U - R + r;
         const float xv = s_dx[tl * CH + c].y;
         const float yv = fmaf(Dv, xv, tot) * s_gz[tl * CH + c];
-        if (full_tile || (ch_ok && tl < nval32)) yb[(uint32_t)tl * dim32 + (uint32_t)c] = (TX)yv;
+        if (full_tile || (ch_ok && tl < nval32)) yb[urow(tl) * dim32 + (uint32_t)c] = (TX)yv;
       }
       if (tb + U < T) {
         cur = nxt;
@@ -546,10 +562,12 @@ void scan_kernel(ScanArgs a, int64_t groups_per_batch) {
     ia[s] = 1.f / an;
     tiny = tiny || !(fabsf(an) >= 1e-2f);
   }
-  if (!XB || __builtin_amdgcn_ballot_w64(tiny) != 0)
-    scan_body<RR, XB, DB, S, MODE, true, VEC>(a, b, ch0, chunk, a2, ia, av, s_dx, s_gz, s_bc);
+  if (a.euler)
+    scan_body<RR, XB, DB, S, MODE, kGainEuler, VEC>(a, b, ch0, chunk, a2, ia, av, s_dx, s_gz, s_bc);
+  else if (!XB || __builtin_amdgcn_ballot_w64(tiny) != 0)
+    scan_body<RR, XB, DB, S, MODE, kGainAccurate, VEC>(a, b, ch0, chunk, a2, ia, av, s_dx, s_gz, s_bc);
   else
-    scan_body<RR, XB, DB, S, MODE, false, VEC>(a, b, ch0, chunk, a2, ia, av, s_dx, s_gz, s_bc);
+    scan_body<RR, XB, DB, S, MODE, kGainShort, VEC>(a, b, ch0, chunk, a2, ia, av, s_dx, s_gz, s_bc);
 }
 
 // The vectorised tile path needs whole chunks of the x and B/C tiles per lane.

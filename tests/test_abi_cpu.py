@@ -69,6 +69,31 @@ def test_scan_argument_errors(kw, code):
     assert lib.ssm_last_error() != b""
 
 
+def scan_ex(lib, flags, **kw):
+    a = dict(x=P, delta=P, A=P, B=P, C=P, D=None, z=None, bias=None, sp=0, h0=None, y=P, hf=None,
+             batch=1, seqlen=4, dim=4, dstate=4, act=1, ddt=1, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return lib.ssm_scan_fwd_ex(a["x"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"], a["sp"],
+                               a["h0"], a["y"], a["hf"], a["batch"], a["seqlen"], a["dim"], a["dstate"], a["act"],
+                               a["ddt"], flags, a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("flags", [8, 16, 1 << 30, -1])
+def test_scan_ex_rejects_unknown_flags(flags):
+    lib = _lib()
+    assert scan_ex(lib, flags) == 4
+    assert b"flag" in lib.ssm_last_error()
+
+
+@pytest.mark.parametrize("kw,code", [(dict(x=None), 1), (dict(delta=None), 1), (dict(batch=-1), 2),
+                                     (dict(dstate=129), 4), (dict(ddt=5), 3), (dict(x=P + 1), 7)])
+def test_scan_ex_argument_errors(kw, code):
+    # every flag combination goes through the same validation as ssm_scan_fwd
+    lib = _lib()
+    for flags in range(8):
+        assert scan_ex(lib, flags, **kw) == code, (flags, kw)
+
+
 def test_empty_batch_is_noop():
     lib = _lib()
     assert scan(lib, batch=0) == 0
