@@ -184,8 +184,8 @@ struct TileShape {
 // GAIN: kGainShort (e^q - 1)/a, kGainAccurate (series near q = 0), kGainEuler dt.
 enum GainMode : int { kGainShort = 0, kGainAccurate = 1, kGainEuler = 2 };
 
-template <int RR, bool XB, bool DB, int S, int MODE, int GAIN, bool VEC>
-__device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t ch0, int64_t chunk,
+template <int RR, bool XB, bool DB, int S, int MODE, int GAIN, bool VEC, int W>
+__device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t ch0, int64_t chunk, int w,
                                           const float (&a2)[S], const float (&ia)[S], const float (&av)[S],
                                           float2* __restrict__ s_dx, float* __restrict__ s_gz,
                                           float* __restrict__ s_bc) {
@@ -195,8 +195,12 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
   constexpr int R = TS::R, CH = TS::CH, NP = TS::NP, T = TS::T, KX = TS::KX, KB = TS::KB;
   constexpr bool FULL = (MODE == kModeFull);
   constexpr bool ACC = GAIN != kGainShort;   // accurate softplus as well
-  const int lane = threadIdx.x;
+  static_assert(VEC || W == 1, "the scalar tile path runs one wave per workgroup");
+  constexpr int WCH = W * CH;                 // channels per workgroup (LDS row width)
+  const int tid = threadIdx.x;                // thread in the workgroup
+  const int lane = tid % 64;
   const int r = lane / CH, c = lane % CH;
+  const int wc = w * CH + c;                  // this lane's channel within the workgroup
   const int64_t L = a.seqlen, dim = a.dim, N = a.dstate;
   const int64_t ch = ch0 + c;
   const bool ch_ok = ch < dim;
@@ -286,8 +290,8 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
       const float v = Raw<DB>::f32(pd[k]) + bias;
       float dt = a.softplus ? (ACC ? softplus_f(v) : softplus_short(v)) : v;
       dt = (t < nvalid) ? dt : 0.f;
-      s_dx[t * CH + c] = make_float2(dt, Raw<XB>::f32(px[k]));
-      if (FULL) s_gz[t * CH + c] = has_z ? silu_f(Raw<XB>::f32(pz[k])) : 1.f;
+      s_dx[t * WCH + wc] = make_float2(dt, Raw<XB>::f32(px[k]));
+      if (FULL) s_gz[t * WCH + wc] = has_z ? silu_f(Raw<XB>::f32(pz[k])) : 1.f;
     }
 #pragma unroll
     for (int j = 0; j < KB; ++j) {
@@ -302,26 +306,39 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
 
 
   // ---- vectorised tile I/O (every channel group full, pointers 16-byte
-  // aligned, N == NP, delta stored like x): each lane moves whole 16-byte
-  // chunks.  Chunk k of a tile covers token k / XROW, channels
-  // (k % XROW) * EX .. + EX of x, delta and z, and elements k*EX .. + EX of
-  // the (token, state)-contiguous B and C tiles.
-  constexpr int VB = CH * (int)sizeof(RX) < 16 ? CH * (int)sizeof(RX) : 16;  // bytes per chunk
-  constexpr int NW = VB / 4;                                // dwords per chunk
-  using VT = typename VecOf<NW>::T;
-  constexpr int EX = VB / (int)sizeof(RX);                  // elements per chunk
-  constexpr int XROW = CH / EX;                             // chunks per token row
-  constexpr int CXN = (T * CH) / (64 * EX);                 // x chunks per lane
-  constexpr int CBN = (T * NP) / (64 * EX) > 0 ? (T * NP) / (64 * EX) : 1;  // B chunks per lane
-  constexpr int GW = S < EX ? S : EX;                       // floats per LDS write of B/C
-  VT vx[CXN], vd[CXN], vz[CXN], vb[CBN], vc[CBN];
-  const int vc0 = (lane % XROW) * EX;                       // this lane's first channel in a row
+  // aligned, N == NP, delta stored like x).  The W waves of the workgroup
+  // cover W*CH consecutive channels and load the tiles together: thread tid
+  // moves whole chunks of VX bytes.  Chunk k of the x (delta, z) tile covers
+  // token k / XROW, workgroup channels (k % XROW) * EX .. + EX, so each token
+  // row of the workgroup is read as one contiguous run; B and C, shared by
+  // every channel, are loaded once per workgroup in chunks of VBC bytes of the
+  // (token, state)-contiguous tile.
+  constexpr int NT = 64 * W;                                // threads per workgroup
+  constexpr int XT = T * WCH * (int)sizeof(RX);             // bytes of one x tile
+  constexpr int VX = XT / NT < 16 ? XT / NT : 16;           // bytes per x chunk
+  using VTX = typename VecOf<VX / 4>::T;
+  constexpr int EX = VX / (int)sizeof(RX);                  // channels per x chunk
+  constexpr int XROW = WCH / EX;                            // chunks per token row
+  constexpr int CXN = XT / (NT * VX);                       // x chunks per thread
+  constexpr int BT = T * NP * (int)sizeof(RX);              // bytes of one B tile
+  // bytes per B chunk: 8 when that gives every thread one, else 16 (with only
+  // the first BT / 16 threads loading when the tile is smaller than that)
+  constexpr int VBC = BT / NT == 8 ? 8 : 16;
+  using VTB = typename VecOf<VBC / 4>::T;
+  constexpr int EB = VBC / (int)sizeof(RX);                 // elements per B chunk
+  constexpr int CBN = BT >= NT * VBC ? BT / (NT * VBC) : 1;  // B chunks per thread
+  constexpr bool BPART = BT < NT * VBC;                     // some threads hold no B chunk
+  constexpr int GW = S < EB ? S : EB;                       // floats per LDS write of B/C
+  VTX vx[CXN], vd[CXN], vz[CXN];
+  VTB vb[CBN], vc[CBN];
+  const int vc0 = (tid % XROW) * EX;                        // this thread's first workgroup channel
+  const int64_t chw0 = ch0 - (int64_t)w * CH;               // first channel of the workgroup
   float vbias[EX];
 #pragma unroll
-  for (int e = 0; e < EX; ++e) vbias[e] = (VEC && a.delta_bias != nullptr) ? a.delta_bias[ch0 + vc0 + e] : 0.f;
+  for (int e = 0; e < EX; ++e) vbias[e] = (VEC && a.delta_bias != nullptr) ? a.delta_bias[chw0 + vc0 + e] : 0.f;
   // (the element is copied to a scalar first: bit-casting a vector-element
   // lvalue directly reads element 0 with this compiler)
-  auto raw_elem = [](const VT& v, int e) -> float {
+  auto raw_elem = [](const auto& v, int e) -> float {
     if constexpr (sizeof(RX) == 2) {
       const unsigned u = (v[e >> 1] >> (16 * (e & 1))) << 16;
       return __builtin_bit_cast(float, u);
@@ -333,38 +350,39 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
   auto fetch_vec = [&](int64_t t0) {
     const bool tail = t0 + T > t_stop;
     const int64_t last = t_stop - 1 - t0;
-    const int64_t row0 = (b * L + grow0(t0)) * dim + ch0;   // uniform
+    const int64_t row0 = (b * L + grow0(t0)) * dim + chw0;  // uniform
     const char* xb = (const char*)(gx + row0);
     const char* db = (const char*)(gd + row0);
     const char* zb = (const char*)(gz + row0);
     const uint32_t rowb = dim32 * (uint32_t)sizeof(RX);
 #pragma unroll
     for (int q = 0; q < CXN; ++q) {
-      const int k = lane + 64 * q;
+      const int k = tid + NT * q;
       int tl = k / XROW;
       if (tail) tl = tl < last ? tl : (int)last;
-      const uint32_t off = urow(tl) * rowb + (uint32_t)(k % XROW) * (uint32_t)VB;
-      vx[q] = *reinterpret_cast<const VT*>(xb + off);
-      vd[q] = *reinterpret_cast<const VT*>(db + off);
-      if (has_z) vz[q] = *reinterpret_cast<const VT*>(zb + off);
+      const uint32_t off = urow(tl) * rowb + (uint32_t)(k % XROW) * (uint32_t)VX;
+      vx[q] = *reinterpret_cast<const VTX*>(xb + off);
+      vd[q] = *reinterpret_cast<const VTX*>(db + off);
+      if (has_z) vz[q] = *reinterpret_cast<const VTX*>(zb + off);
     }
     const RX* bb = gB + (b * L + grow0(t0)) * N;            // uniform
     const RX* cb = gC + (b * L + grow0(t0)) * N;
 #pragma unroll
     for (int q = 0; q < CBN; ++q) {
-      const int e0 = (lane + 64 * q) * EX;
+      const int e0 = (tid + NT * q) * EB;
+      if (BPART && e0 >= T * NP) break;
       int t = e0 / NP;
       if (tail) t = t < last ? t : (int)last;
       const uint32_t off = urow(t) * (uint32_t)NP + (uint32_t)(e0 % NP);
-      vb[q] = *reinterpret_cast<const VT*>(bb + off);
-      if (FULL) vc[q] = *reinterpret_cast<const VT*>(cb + off);
+      vb[q] = *reinterpret_cast<const VTB*>(bb + off);
+      if (FULL) vc[q] = *reinterpret_cast<const VTB*>(cb + off);
     }
   };
   auto stage_vec = [&](int64_t t0) {
     const int64_t nvalid = t_stop - t0;
 #pragma unroll
     for (int q = 0; q < CXN; ++q) {
-      const int k = lane + 64 * q;
+      const int k = tid + NT * q;
       const int tl = k / XROW;
       const bool ok = tl < nvalid;
       float dxv[2 * EX];
@@ -375,24 +393,25 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
         dxv[2 * e] = ok ? dt : 0.f;
         dxv[2 * e + 1] = raw_elem(vx[q], e);
       }
-      float4* dst = reinterpret_cast<float4*>(s_dx + tl * CH + vc0);
+      float4* dst = reinterpret_cast<float4*>(s_dx + tl * WCH + vc0);
 #pragma unroll
       for (int e = 0; e < EX / 2; ++e) dst[e] = make_float4(dxv[4 * e], dxv[4 * e + 1], dxv[4 * e + 2], dxv[4 * e + 3]);
       if (FULL) {
         float gzv[EX];
 #pragma unroll
         for (int e = 0; e < EX; ++e) gzv[e] = has_z ? silu_f(raw_elem(vz[q], e)) : 1.f;
-        float4* gd4 = reinterpret_cast<float4*>(s_gz + tl * CH + vc0);
+        float4* gd4 = reinterpret_cast<float4*>(s_gz + tl * WCH + vc0);
 #pragma unroll
         for (int e = 0; e < EX / 4; ++e) gd4[e] = make_float4(gzv[4 * e], gzv[4 * e + 1], gzv[4 * e + 2], gzv[4 * e + 3]);
       }
     }
 #pragma unroll
     for (int q = 0; q < CBN; ++q) {
-      const int e0 = (lane + 64 * q) * EX;
+      const int e0 = (tid + NT * q) * EB;
+      if (BPART && e0 >= T * NP) break;
       const int t = e0 / NP, n0 = e0 % NP;
 #pragma unroll
-      for (int g = 0; g < EX / GW; ++g) {
+      for (int g = 0; g < EB / GW; ++g) {
         const int n = n0 + g * GW;
         const int base = ((t * R + n / S) * 2) * S + (n % S);
 #pragma unroll
@@ -435,7 +454,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
 #pragma unroll
       for (int j = 0; j < U; ++j) {
         const int tt = tb + j;
-        g.dx[j] = s_dx[tt * CH + c];
+        g.dx[j] = s_dx[tt * WCH + wc];
         const float* bc = s_bc + ((tt * R + r) * 2) * S;
         if constexpr (S >= 4) {
 #pragma unroll
@@ -496,8 +515,8 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
       if (FULL && (R == U || (tb + U) % R == 0)) {
         const float tot = reduce_scatter_rows<R>(pr);
         const int tl = tb + U - R + r;
-        const float xv = s_dx[tl * CH + c].y;
-        const float yv = fmaf(Dv, xv, tot) * s_gz[tl * CH + c];
+        const float xv = s_dx[tl * WCH + wc].y;
+        const float yv = fmaf(Dv, xv, tot) * s_gz[tl * WCH + wc];
         if (full_tile || (ch_ok && tl < nval32)) yb[urow(tl) * dim32 + (uint32_t)c] = (TX)yv;
       }
       if (tb + U < T) {
@@ -531,12 +550,15 @@ constexpr int scan_waves_per_simd() {
   return RR == 4 ? 1 : RR == 8 ? 2 : 3;
 }
 
-template <int RR, bool XB, bool DB, int S, int MODE, bool VEC>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(scan_waves_per_simd<RR>())))
+// W waves per workgroup (1, or 4 on the vector path): the waves of a
+// workgroup scan W consecutive channel groups of one batch row and share the
+// staged tiles.
+template <int RR, bool XB, bool DB, int S, int MODE, bool VEC, int W>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(scan_waves_per_simd<RR>())))
 void scan_kernel(ScanArgs a, int64_t groups_per_batch) {
   using TS = TileShape<RR, S>;
-  __shared__ __attribute__((aligned(16))) float2 s_dx[TS::T * TS::CH];
-  __shared__ __attribute__((aligned(16))) float s_gz[TS::T * TS::CH];
+  __shared__ __attribute__((aligned(16))) float2 s_dx[TS::T * TS::CH * W];
+  __shared__ __attribute__((aligned(16))) float s_gz[TS::T * TS::CH * W];
   __shared__ __attribute__((aligned(16))) float s_bc[TS::T * TS::R * 2 * S];
 
   // XCD-aware order: dispatch id i runs on XCD i % 8; give each XCD a contiguous
@@ -544,11 +566,13 @@ void scan_kernel(ScanArgs a, int64_t groups_per_batch) {
   const int64_t nb = gridDim.x;
   int64_t lin = blockIdx.x;
   if ((nb & 7) == 0) lin = (lin & 7) * (nb >> 3) + (lin >> 3);
-  const int64_t b = lin / groups_per_batch;
-  const int64_t ch0 = (lin % groups_per_batch) * TS::CH;
+  const int64_t wgs_per_batch = groups_per_batch / W;     // the host launches whole workgroups
+  const int w = (int)(threadIdx.x / 64);
+  const int64_t b = lin / wgs_per_batch;
+  const int64_t ch0 = ((lin % wgs_per_batch) * W + w) * TS::CH;
   const int64_t chunk = blockIdx.y;
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x % 64;
   const int r = lane / TS::CH, c = lane % TS::CH;
   const int64_t ch = ch0 + c;
   float a2[S], ia[S], av[S];
@@ -562,42 +586,56 @@ void scan_kernel(ScanArgs a, int64_t groups_per_batch) {
     ia[s] = 1.f / an;
     tiny = tiny || !(fabsf(an) >= 1e-2f);
   }
+  // the gain form is chosen once for the whole workgroup (its waves pass the
+  // same barriers)
+  const bool any_tiny = W == 1 ? __builtin_amdgcn_ballot_w64(tiny) != 0 : __syncthreads_or(tiny) != 0;
   if (a.euler)
-    scan_body<RR, XB, DB, S, MODE, kGainEuler, VEC>(a, b, ch0, chunk, a2, ia, av, s_dx, s_gz, s_bc);
-  else if (!XB || __builtin_amdgcn_ballot_w64(tiny) != 0)
-    scan_body<RR, XB, DB, S, MODE, kGainAccurate, VEC>(a, b, ch0, chunk, a2, ia, av, s_dx, s_gz, s_bc);
+    scan_body<RR, XB, DB, S, MODE, kGainEuler, VEC, W>(a, b, ch0, chunk, w, a2, ia, av, s_dx, s_gz, s_bc);
+  else if (!XB || any_tiny)
+    scan_body<RR, XB, DB, S, MODE, kGainAccurate, VEC, W>(a, b, ch0, chunk, w, a2, ia, av, s_dx, s_gz, s_bc);
   else
-    scan_body<RR, XB, DB, S, MODE, kGainShort, VEC>(a, b, ch0, chunk, a2, ia, av, s_dx, s_gz, s_bc);
+    scan_body<RR, XB, DB, S, MODE, kGainShort, VEC, W>(a, b, ch0, chunk, w, a2, ia, av, s_dx, s_gz, s_bc);
 }
 
-// The vectorised tile path needs whole chunks of the x and B/C tiles per lane.
-template <int RR, bool XB, int S>
+// The vectorised tile path needs whole chunks of the x and B/C tiles per thread.
+template <int RR, bool XB, int S, int W>
 constexpr bool vec_shape_ok() {
   using TS = TileShape<RR, S>;
   constexpr int sz = XB ? 2 : 4;
-  constexpr int VB = TS::CH * sz < 16 ? TS::CH * sz : 16;
-  constexpr int EX = VB / sz;
-  return (TS::T * TS::NP) % (64 * EX) == 0 && (TS::T * TS::CH) % (64 * EX) == 0 && TS::CH % EX == 0;
+  constexpr int NT = 64 * W;
+  constexpr int XT = TS::T * TS::CH * W * sz;
+  constexpr int VX = XT / NT < 16 ? XT / NT : 16;
+  constexpr int BT = TS::T * TS::NP * sz;
+  return (VX == 8 || VX == 16) && XT % (NT * VX) == 0 && BT % 16 == 0 && (TS::CH * W) % (VX / sz) == 0;
 }
-template <int RR, bool XB, int S>
+template <int RR, bool XB, int S, int W>
 bool vec_ok(const ScanArgs& a) {
-  return vec_shape_ok<RR, XB, S>() && a.dstate == TileShape<RR, S>::NP && a.dim % TileShape<RR, S>::CH == 0;
+  return vec_shape_ok<RR, XB, S, W>() && a.dstate == TileShape<RR, S>::NP && a.dim % (TileShape<RR, S>::CH * W) == 0;
 }
 
-// Launch the scan kernel for one (rows, act dtype, delta dtype, states-per-lane) combination.
+// Launch the scan kernel for one (rows, act dtype, delta dtype, states-per-lane)
+// combination.  `grid.x` counts channel groups; the vector path runs four of
+// them per workgroup when the channels split into whole workgroups.
 template <int RR, bool XB, bool DB, int SV>
 hipError_t launch_scan_variant(int mode, const ScanArgs& a, dim3 grid, int64_t gpb, hipStream_t st) {
-  bool vec = false;
-  if constexpr (vec_shape_ok<RR, XB, SV>()) vec = a.vec_io && vec_ok<RR, XB, SV>(a);
-  if constexpr (vec_shape_ok<RR, XB, SV>()) {
-    if (vec) {
-      if (mode == kModeFull) scan_kernel<RR, XB, DB, SV, kModeFull, true><<<grid, 64, 0, st>>>(a, gpb);
-      else scan_kernel<RR, XB, DB, SV, kModeState, true><<<grid, 64, 0, st>>>(a, gpb);
+  constexpr int WV = 4;
+  if constexpr (vec_shape_ok<RR, XB, SV, WV>()) {
+    if (a.vec_io && vec_ok<RR, XB, SV, WV>(a) && gpb % WV == 0) {
+      const dim3 g4(grid.x / WV, grid.y);
+      if (mode == kModeFull) scan_kernel<RR, XB, DB, SV, kModeFull, true, WV><<<g4, 64 * WV, 0, st>>>(a, gpb);
+      else scan_kernel<RR, XB, DB, SV, kModeState, true, WV><<<g4, 64 * WV, 0, st>>>(a, gpb);
       return hipGetLastError();
     }
   }
-  if (mode == kModeFull) scan_kernel<RR, XB, DB, SV, kModeFull, false><<<grid, 64, 0, st>>>(a, gpb);
-  else scan_kernel<RR, XB, DB, SV, kModeState, false><<<grid, 64, 0, st>>>(a, gpb);
+  if constexpr (vec_shape_ok<RR, XB, SV, 1>()) {
+    if (a.vec_io && vec_ok<RR, XB, SV, 1>(a)) {
+      if (mode == kModeFull) scan_kernel<RR, XB, DB, SV, kModeFull, true, 1><<<grid, 64, 0, st>>>(a, gpb);
+      else scan_kernel<RR, XB, DB, SV, kModeState, true, 1><<<grid, 64, 0, st>>>(a, gpb);
+      return hipGetLastError();
+    }
+  }
+  if (mode == kModeFull) scan_kernel<RR, XB, DB, SV, kModeFull, false, 1><<<grid, 64, 0, st>>>(a, gpb);
+  else scan_kernel<RR, XB, DB, SV, kModeState, false, 1><<<grid, 64, 0, st>>>(a, gpb);
   return hipGetLastError();
 }
 

@@ -83,6 +83,20 @@ def test_long_sequence_time_split(ssm, dtype, L, D):
     check(ssm, inp, label="long %s L=%d D=%d" % (dtype, L, D))
 
 
+# Lane layouts and workgroup shapes, compared in full: 8 rows with four waves per workgroup
+# (8x2048 channels), 4 rows with four waves (16x2048; dstate 64 and 128 at 128 / 64 channels),
+# 16 rows with four waves and a ragged tile, and 16 rows with one wave per workgroup (channel
+# groups not a multiple of four), each in bf16 and fp32.
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", [(8, 100, 2048, 16), (16, 80, 2048, 16), (2, 300, 128, 64), (2, 150, 64, 128),
+                                   (2, 257, 48, 16), (3, 100, 20, 16)])
+def test_workgroup_layouts(ssm, dtype, shape):
+    b, L, D, N = shape
+    inp = workloads.scan_inputs(b, L, D, N, dtype=dtype, seed=sum(shape) + 5, dt="softplus_bias", gate=True,
+                                softplus=True, skip=True, h0=True)
+    check(ssm, inp, label="layout %s %s" % (dtype, shape))
+
+
 @pytest.mark.parametrize("L", [300, 5000])
 def test_final_state_entry(ssm, L):
     inp = workloads.scan_inputs(2, L, 24, 16, dtype="bf16", seed=L + 1, dt="softplus_bias", softplus=True, h0=True)
