@@ -131,8 +131,14 @@ __device__ __forceinline__ u16 half_of(const u32x4& v, int q) {
   return (u16)(w >> (16 * (q & 1)));
 }
 
-template <int N, bool DTB>
-__global__ __launch_bounds__(512) void ssd_fused_kernel(SsdArgs a) {
+// FULL: outputs for one time chunk, starting from the state carried into it.
+// !FULL: the chunk's own state contribution (from a zero state) and its total
+// decay exponent a * sum(dt), for the carry pass; no outputs.  The state pass
+// needs few registers and is held to 128 VGPRs (two workgroups per CU); the
+// full pass keeps its 2 waves per SIMD (capping it at 128 VGPRs spills and
+// measured 2.5x slower).
+template <int N, bool DTB, bool FULL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(FULL ? 2 : 4))) void ssd_fused_kernel(SsdArgs a) {
   constexpr int SN = N + 8;        // row stride of [*][N] LDS arrays (bf16 elements)
   constexpr int SQ = QB + 8;       // row stride of [*][64] LDS arrays
   constexpr int SP = PS + 8;       // row stride of the x tile
@@ -169,6 +175,10 @@ __global__ __launch_bounds__(512) void ssd_fused_kernel(SsdArgs a) {
   const float bias = a.dt_bias != nullptr ? a.dt_bias[h] : 0.f;
   const float Dv = a.Dskip != nullptr ? a.Dskip[h] : 0.f;
   const int64_t p0 = (int64_t)ph * PS;
+  const int64_t chunk = blockIdx.y;
+  const int64_t t_begin = chunk * a.tchunk;
+  const int64_t t_end = t_begin + a.tchunk < L ? t_begin + a.tchunk : L;
+  const int64_t slice = a.batch * H * P * N;     // one state per (batch, head)
 
   const u16* gX = (const u16*)a.x;
   const u16* gB = (const u16*)a.B;
@@ -182,7 +192,9 @@ __global__ __launch_bounds__(512) void ssd_fused_kernel(SsdArgs a) {
     Ml[i] = 0;
   }
 
-  // ---- state: wave w owns p-tile pw and n-tiles [NTW*tw, NTW*tw + NTW)
+  // ---- state: wave w owns p-tile pw and n-tiles [NTW*tw, NTW*tw + NTW).
+  // FULL: h0, or the carry into this chunk; !FULL: zero.
+  const float* hin = !FULL ? nullptr : (a.nchunks > 1 ? a.ws_state + chunk * slice : a.h0);
   f32x4 Hacc[NTW];
 #pragma unroll
   for (int j = 0; j < NTW; ++j) {
@@ -190,7 +202,7 @@ __global__ __launch_bounds__(512) void ssd_fused_kernel(SsdArgs a) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int p = pw * 16 + 4 * g4 + v;
-      Hacc[j][v] = a.h0 != nullptr ? a.h0[((b * H + h) * P + p0 + p) * N + n] : 0.f;
+      Hacc[j][v] = hin != nullptr ? hin[((b * H + h) * P + p0 + p) * N + n] : 0.f;
     }
   }
   auto store_state_split = [&]() {
@@ -204,7 +216,7 @@ __global__ __launch_bounds__(512) void ssd_fused_kernel(SsdArgs a) {
         Hl[idx] = f2bf(Hacc[j][v] - bf2f(hb));
       }
   };
-  store_state_split();   // visible after the first barrier of the block loop
+  if (FULL) store_state_split();   // visible after the first barrier of the block loop
 
   // ---- register prefetch of one block
   u32x4 rc[BC_CHUNKS], rb[BC_CHUNKS], rx;
@@ -218,7 +230,7 @@ __global__ __launch_bounds__(512) void ssd_fused_kernel(SsdArgs a) {
       int64_t t = t0 + row;
       t = t < last ? t : last;
       const int64_t off = ((b * L + t) * a.ngroups + grp) * N + c8 * 8;
-      rc[j] = *reinterpret_cast<const u32x4*>(gC + off);
+      if (FULL) rc[j] = *reinterpret_cast<const u32x4*>(gC + off);
       rb[j] = *reinterpret_cast<const u32x4*>(gB + off);
     }
     if (tid < QB * PS / 8) {
@@ -235,16 +247,17 @@ __global__ __launch_bounds__(512) void ssd_fused_kernel(SsdArgs a) {
     }
   };
 
-  const int nblk = (int)((L + QB - 1) / QB);
-  fetch(0);
+  const int nblk = (int)((t_end - t_begin + QB - 1) / QB);
+  float dsum = 0.f;                  // a * sum of dt over the chunk (wave 0)
+  fetch(t_begin);
   for (int blk = 0; blk < nblk; ++blk) {
-    const int64_t t0 = (int64_t)blk * QB;
+    const int64_t t0 = t_begin + (int64_t)blk * QB;
     // ---------------- stage the block (natural layouts) and the decay terms
 #pragma unroll
     for (int j = 0; j < BC_CHUNKS; ++j) {
       const int e = tid + NWAVE * 64 * j;
       const int row = e / CPR, c8 = e % CPR;
-      *reinterpret_cast<u32x4*>(Cs + row * SN + c8 * 8) = rc[j];
+      if (FULL) *reinterpret_cast<u32x4*>(Cs + row * SN + c8 * 8) = rc[j];
       *reinterpret_cast<u32x4*>(Bs + row * SN + c8 * 8) = rb[j];
     }
     if (tid < QB * PS / 8) {
@@ -264,12 +277,13 @@ __global__ __launch_bounds__(512) void ssd_fused_kernel(SsdArgs a) {
       eS[l] = exp_f(cum);
       wS[l] = exp_f(cend - cum) * gv;
       if (l == 0) decayS = exp_f(cend);
+      dsum += cend;
     }
     __syncthreads();
     if (blk + 1 < nblk) fetch(t0 + QB);
 
     // ---------------- C B^T tiles -> mask -> M (bf16 high/low) in LDS
-    {
+    if constexpr (FULL) {
       auto cb_tile = [&](int ti, int tj) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -302,7 +316,7 @@ __global__ __launch_bounds__(512) void ssd_fused_kernel(SsdArgs a) {
     // ---------------- Y_off = C H^T for (token tile tw, channel tile pw); H = state entering the block
     f32x4 yoff = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < KN; ++kk) {
+    for (int kk = 0; kk < (FULL ? KN : 0); ++kk) {
       const bf16x8 ca = frag_rows(Cs, tw * 16 + l16, kk * 32 + g4 * 8, SN);
       yoff = mfma(ca, frag_rows(Hs, pw * 16 + l16, kk * 32 + g4 * 8, SN), yoff);
       yoff = mfma(ca, frag_rows(Hl, pw * 16 + l16, kk * 32 + g4 * 8, SN), yoff);
@@ -342,7 +356,7 @@ __global__ __launch_bounds__(512) void ssd_fused_kernel(SsdArgs a) {
 
     // ---------------- Y_diag = M X for (token tile tw, channel tile pw), epilogue
     f32x4 ydiag = {0.f, 0.f, 0.f, 0.f};
-    {
+    if constexpr (FULL) {
       const int ksteps = (tw < 2) ? 1 : 2;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
@@ -353,7 +367,7 @@ __global__ __launch_bounds__(512) void ssd_fused_kernel(SsdArgs a) {
         }
       }
     }
-    {
+    if constexpr (FULL) {
       const int p = pw * 16 + l16;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
@@ -368,21 +382,39 @@ __global__ __launch_bounds__(512) void ssd_fused_kernel(SsdArgs a) {
         }
       }
     }
-    store_state_split();   // the state entering the next block
+    if (FULL) store_state_split();   // the state entering the next block
     __syncthreads();
   }
 
-  if (a.h_final != nullptr) {
+  float* hout = FULL ? (chunk == a.nchunks - 1 ? a.h_final : nullptr) : a.ws_state + chunk * slice;
+  if (hout != nullptr) {
 #pragma unroll
     for (int j = 0; j < NTW; ++j) {
       const int n = (NTW * tw + j) * 16 + l16;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int p = pw * 16 + 4 * g4 + v;
-        a.h_final[((b * H + h) * P + p0 + p) * N + n] = Hacc[j][v];
+        hout[((b * H + h) * P + p0 + p) * N + n] = Hacc[j][v];
       }
     }
   }
+  if (!FULL && w == 0 && l == 0 && ph == 0) a.ws_dsum[chunk * a.batch * H + b * H + h] = dsum;
+}
+
+// Combine the chunk states in order: slot c of ws_state receives the state
+// entering chunk c, h_in(c+1) = exp(dsum_c) h_in(c) + s(c), h_in(0) = h0.
+__global__ __launch_bounds__(256) void ssd_carry_kernel(SsdArgs a) {
+  const int64_t slice = a.batch * a.nheads * a.headdim * a.dstate;
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= slice) return;
+  const int64_t bh = i / (a.headdim * a.dstate);
+  float hv = a.h0 != nullptr ? a.h0[i] : 0.f;
+  for (int64_t c = 0; c + 1 < a.nchunks; ++c) {
+    const float loc = a.ws_state[c * slice + i];
+    a.ws_state[c * slice + i] = hv;
+    hv = fmaf(exp_f(a.ws_dsum[c * a.batch * a.nheads + bh]), hv, loc);
+  }
+  a.ws_state[(a.nchunks - 1) * slice + i] = hv;
 }
 
 // seqlen == 0: the state passes through unchanged.
@@ -393,9 +425,55 @@ __global__ __launch_bounds__(256) void ssd_copy_state(const float* h0, float* ou
 
 }  // namespace
 
-size_t ssd_ws_bytes(int64_t, int64_t, int64_t, int64_t, int64_t, int64_t, int64_t) { return 0; }
+SsdPlan plan_ssd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate, int num_cus) {
+  // The full pass runs one workgroup per CU (its registers allow no second),
+  // so time is split only when the (batch, head, half) workgroups cannot fill
+  // the CUs: into enough chunks for one workgroup per CU, each of at least 8
+  // blocks.  A split costs a state-only pass over its chunks and a carry of
+  // one state per (batch, head); with the CUs already full it measured slower
+  // (0.48 against 0.39 ms on the b2 x 64-head workload).
+  SsdPlan p{1, 0, 0};
+  const int64_t cus = num_cus > 0 ? num_cus : 256;
+  const int64_t nwg = batch * nheads * (headdim / PS);
+  if (nwg > 0 && nwg < cus && seqlen > 0) {
+    int64_t nch = (cus + nwg - 1) / nwg;
+    const int64_t max_ch = seqlen / (8 * QB);
+    nch = nch < max_ch ? nch : max_ch;
+    nch = nch > 1 ? nch : 1;
+    const int64_t per = (seqlen + nch - 1) / nch;
+    p.tchunk = (per + QB - 1) / QB * QB;
+    p.nchunks = (seqlen + p.tchunk - 1) / p.tchunk;
+  }
+  p.tchunk = p.nchunks > 1 ? p.tchunk : (seqlen > 0 ? (seqlen + QB - 1) / QB * QB : QB);
+  if (p.nchunks > 1) {
+    const size_t st = (size_t)p.nchunks * (size_t)(batch * nheads * headdim * dstate) * sizeof(float);
+    p.ws_bytes = (st + 255) / 256 * 256 + (size_t)p.nchunks * (size_t)(batch * nheads) * sizeof(float);
+  }
+  return p;
+}
 
-int launch_ssd(const SsdArgs& a, void* stream) {
+size_t ssd_ws_bytes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t, int64_t dstate,
+                    int64_t) {
+  return plan_ssd(batch, seqlen, nheads, headdim, dstate, device_cu_count()).ws_bytes;
+}
+
+template <int N, bool DTB>
+hipError_t launch_ssd_n(const SsdArgs& a, dim3 grid, hipStream_t st) {
+  if (a.nchunks > 1) {
+    ssd_fused_kernel<N, DTB, false><<<dim3(grid.x, (unsigned)(a.nchunks - 1)), NWAVE * 64, 0, st>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t slice = a.batch * a.nheads * a.headdim * a.dstate;
+    ssd_carry_kernel<<<dim3((unsigned)((slice + 255) / 256)), 256, 0, st>>>(a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  ssd_fused_kernel<N, DTB, true><<<dim3(grid.x, (unsigned)a.nchunks), NWAVE * 64, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+int launch_ssd(const SsdArgs& a0, void* stream) {
+  SsdArgs a = a0;
   hipStream_t st = (hipStream_t)stream;
   if (a.seqlen == 0) {
     if (a.h_final != nullptr) {
@@ -408,15 +486,20 @@ int launch_ssd(const SsdArgs& a, void* stream) {
   }
   const int64_t nwg = a.batch * a.nheads * (a.headdim / PS);
   if (nwg > 0x7fffffffLL) return fail(4, "grid too large");
-  dim3 grid((unsigned)nwg);
-  if (a.dstate == 128) {
-    if (a.dt_bf16) ssd_fused_kernel<128, true><<<grid, NWAVE * 64, 0, st>>>(a);
-    else ssd_fused_kernel<128, false><<<grid, NWAVE * 64, 0, st>>>(a);
-  } else {
-    if (a.dt_bf16) ssd_fused_kernel<64, true><<<grid, NWAVE * 64, 0, st>>>(a);
-    else ssd_fused_kernel<64, false><<<grid, NWAVE * 64, 0, st>>>(a);
+  const SsdPlan p = plan_ssd(a.batch, a.seqlen, a.nheads, a.headdim, a.dstate, device_cu_count());
+  if (p.nchunks > 65535) return fail(4, "grid too large");
+  a.nchunks = p.nchunks;
+  a.tchunk = p.tchunk;
+  if (p.nchunks > 1) {
+    if (a.ws == nullptr) return fail(5, "SSD time split needs its workspace");
+    const size_t st_bytes = (size_t)p.nchunks * (size_t)(a.batch * a.nheads * a.headdim * a.dstate) * sizeof(float);
+    a.ws_state = (float*)a.ws;
+    a.ws_dsum = (float*)((char*)a.ws + (st_bytes + 255) / 256 * 256);
   }
-  hipError_t e = hipGetLastError();
+  dim3 grid((unsigned)nwg);
+  hipError_t e;
+  if (a.dstate == 128) e = a.dt_bf16 ? launch_ssd_n<128, true>(a, grid, st) : launch_ssd_n<128, false>(a, grid, st);
+  else e = a.dt_bf16 ? launch_ssd_n<64, true>(a, grid, st) : launch_ssd_n<64, false>(a, grid, st);
   if (e != hipSuccess) return fail(6, std::string("SSD kernel launch: ") + hipGetErrorString(e));
   return 0;
 }

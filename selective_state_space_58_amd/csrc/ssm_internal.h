@@ -109,8 +109,19 @@ struct SsdArgs {
   int softplus;
   int dt_bf16;
   void* ws;
+  // time chunks run in parallel (set by launch_ssd from the plan)
+  int64_t tchunk, nchunks;
+  float* ws_state;     // nchunks x (batch, nheads, headdim, dstate): chunk states, then carries
+  float* ws_dsum;      // nchunks x (batch, nheads): a * sum of dt over the chunk
 };
 
+// Time split of the SSD pass: nchunks chunks of tchunk tokens (a multiple of
+// 64) whose states are computed in parallel and combined by a carry pass.
+struct SsdPlan {
+  int64_t nchunks, tchunk;
+  size_t ws_bytes;
+};
+SsdPlan plan_ssd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate, int num_cus);
 size_t ssd_ws_bytes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t ngroups,
                     int64_t dstate, int64_t chunk);
 int launch_ssd(const SsdArgs& a, void* stream);

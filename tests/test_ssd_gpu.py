@@ -67,6 +67,31 @@ def test_chunk_size_invariance(ssm):
     assert rel_err(outs[0][0], outs[2][0]) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("N,G,L", [(128, 2, 3000), (64, 1, 2077)])
+def test_time_split(ssm, N, G, L):
+    # few (batch, head) pairs and a long sequence: the pass is split into time chunks whose states are
+    # computed in parallel and carried (workspace > 0), here with a ragged last chunk and block
+    inp = workloads.ssd_inputs(1, L, 4, 64, N, ngroups=G, seed=L + N + G, gate=True, skip=True, h0=True,
+                               dt_softplus=True)
+    assert ssm.ssd_workspace_bytes(1, L, 4, 64, G, N, 256) > 0
+    check(ssm, inp, "time split L=%d N=%d G=%d" % (L, N, G))
+
+
+def test_time_split_workspace_checks(ssm):
+    inp = workloads.ssd_inputs(1, 3000, 4, 64, 128, seed=5)
+    t = workloads.to_device(inp, DEV)
+    nb = ssm.ssd_workspace_bytes(1, 3000, 4, 64, 1, 128, 256)
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    y, hf = ssm.ssd_chunk_scan_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], chunk_size=256, workspace=ws,
+                                   return_final_state=True)
+    torch.cuda.synchronize()
+    y_ref, h_ref = oracle_ssd(inp)
+    assert rel_err(y.float().cpu().numpy(), y_ref) <= TOL["bf16"] and rel_err(hf.cpu().numpy(), h_ref) <= TOL["bf16"]
+    small = torch.empty(nb - 256, dtype=torch.uint8, device=DEV)
+    with pytest.raises(ssm.SSMError):
+        ssm.ssd_chunk_scan_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], chunk_size=256, workspace=small)
+
+
 def test_empty_and_single_token(ssm):
     inp = workloads.ssd_inputs(1, 0, 2, 64, 64, seed=3, h0=True)
     y, hf = run(ssm, inp)
