@@ -4,8 +4,9 @@ One step = one full selective-scan forward (discretize + recurrence + readout
 + skip + gate) over the Mamba-130M-like layer workload: batch 8, 1536
 channels, 2048 tokens, 16 states, bf16 inputs/outputs, fp32 state, softplus dt
 with per-channel bias, silu(z) gate.  Inputs are resident in HBM before the
-timed region; each step reads one of four rotating input copies (> the 256 MB
-last-level cache) so no step reads another step's inputs from cache.
+timed region; each step reads one of six rotating input copies (1.2 GB, far
+beyond the 256 MB last-level cache) so no step reads another step's inputs
+from cache.
 
 Prints one JSON line with the headline throughput (token*channels/s), the
 roofline of the scan kernel measured with HIP events on the launch stream, the
@@ -43,7 +44,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-others", action="store_true")
-    p.add_argument("--only", choices=["scan-2.8b", "scan-long", "ssd", "step", "ssd-step", "conv", "bwd", "copy"],
+    p.add_argument("--only", choices=["scan-2.8b", "scan-long", "ssd", "step", "ssd-step", "conv", "bwd", "copy",
+                                      "ubench"],
                    default=None,
                    help="time only this other workload (for profiling); skips the headline JSON line")
     return p.parse_args()
@@ -148,6 +150,37 @@ def time_calls(fn, steps, warmup, torch):
     torch.cuda.synchronize()
     per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
     return start.elapsed_time(end), per
+
+
+def run_microbench(workloads):
+    """Measured unit rates (libssm_microbench.so) and the scan ceilings they imply."""
+    import ctypes
+    from selective_state_space_58_amd import build as _build
+    lib = ctypes.CDLL(_build.MB_LIB)
+    for name in ("ssm_mb_fma_rate", "ssm_mb_exp_rate", "ssm_mb_scan_element_rate", "ssm_mb_mfma_bf16_flops"):
+        getattr(lib, name).restype = ctypes.c_double
+        getattr(lib, name).argtypes = []
+    lib.ssm_mb_copy_bytes_per_s.restype = ctypes.c_double
+    lib.ssm_mb_copy_bytes_per_s.argtypes = [ctypes.c_size_t]
+    fma, ex, el = lib.ssm_mb_fma_rate(), lib.ssm_mb_exp_rate(), lib.ssm_mb_scan_element_rate()
+    mfma, copy = lib.ssm_mb_mfma_bf16_flops(), lib.ssm_mb_copy_bytes_per_s(1 << 30)
+    if min(fma, ex, el, mfma, copy) <= 0:
+        raise RuntimeError("a microbenchmark failed")
+    out = {"fma_T_lane_ops_s": round(fma / 1e12, 3), "exp_T_lane_ops_s": round(ex / 1e12, 3),
+           "scan_element_T_s": round(el / 1e12, 4), "mfma_bf16_TFLOPs": round(mfma / 1e12, 1),
+           "copy_GBs_read_plus_write": round(copy / 1e9, 1),
+           "published": {"valu_T_lane_slots_s": round(VALU_PEAK_TSLOTS, 3), "mfma_bf16_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
+                         "hbm_GBs": HBM_PEAK_GBS}}
+    # floor of each scan workload at the measured per-element rate (one exp + six VALU ops per element)
+    ceil = {}
+    for cfg in workloads.CONFIGS:
+        if cfg["kind"] != "scan":
+            continue
+        elems = cfg["batch"] * cfg["seqlen"] * cfg["dim"] * cfg["dstate"]
+        ceil[cfg["name"]] = {"elements": elems, "valu_floor_ms": round(elems / el * 1e3, 4),
+                             "hbm_floor_ms_measured_copy": round(scan_bytes(cfg) / copy * 1e3, 4)}
+    out["scan_ceilings"] = ceil
+    return out
 
 
 def run_other(oi, steps, warmup, ssm, workloads, torch, dev):
@@ -278,6 +311,9 @@ def main():
                           "ms": round(tot / steps, 4), "GBs_read_plus_write": round(2 * nbytes / (tot / steps * 1e-3) / 1e9, 1)}),
               flush=True)
         return
+    if args.only == "ubench":
+        print(json.dumps({"only": "ubench", **run_microbench(workloads)}), flush=True)
+        return
     if args.only == "bwd":
         print(json.dumps({"only": "bwd", **run_bwd(steps, warmup, ssm, workloads, torch, dev, np)}), flush=True)
         return
@@ -296,13 +332,14 @@ def main():
     # ---------------------------------------------------------------- headline workload
     idx = 1
     inp, cfg = workloads.config_inputs(idx)
-    copies = [workloads.to_device(inp, dev) for _ in range(4)]
+    ncopy = 6
+    copies = [workloads.to_device(inp, dev) for _ in range(ncopy)]
     ys = [torch.empty_like(c["x"]) for c in copies]
 
     def step(i):
-        t = copies[i % 4]
+        t = copies[i % ncopy]
         ssm.ssm_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], delta_bias=t["delta_bias"],
-                         delta_softplus=True, y=ys[i % 4])
+                         delta_softplus=True, y=ys[i % ncopy])
 
     total_ms, per = time_calls(step, steps, warmup, torch)
     ms = total_ms / steps
@@ -331,6 +368,9 @@ def main():
                    "gate": True, "skip": True},
         "hbm": {"algorithmic_bytes": nbytes, "achieved_GBs": round(hbm_gbs, 1), "peak_GBs": HBM_PEAK_GBS,
                 "frac": round(hbm_gbs / HBM_PEAK_GBS, 4)},
+        "timing": {"kernel_ms_p10": round(float(np.percentile(per, 10)), 5),
+                   "kernel_ms_p50": round(float(np.percentile(per, 50)), 5),
+                   "kernel_ms_p90": round(float(np.percentile(per, 90)), 5), "input_copies": ncopy},
         "roofline": {"bound": "alu", "achieved": round(slots, 3), "peak": round(VALU_PEAK_TSLOTS, 3),
                      "unit": "T VALU lane-slots/s (algorithmic: 8 per state element)",
                      "frac": round(slots / VALU_PEAK_TSLOTS, 4), "traffic": measured_traffic(),

@@ -14,6 +14,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libssm_mi355x.so")
+# measurement-only microbenchmarks (include/ssm_microbench.h), a library of their own
+MB_LIB = os.path.join(HERE, "libssm_microbench.so")
+MB_SOURCE = ("microbench.hip", [])
 SOURCES = [("api.cpp", []), ("scan_host.hip", []), ("ssd_kernels.hip", []), ("step_kernels.hip", []), ("conv_kernels.hip", []), ("scan_bwd.hip", [])] + [
     ("scan_inst.hip", ["-DSSM_R=%d" % rr, "-DSSM_XB=%d" % xb, "-DSSM_DB=%d" % db, "-DSSM_S=%d" % sv])
     for rr, sv in ((4, 32), (4, 16), (4, 8), (4, 4), (4, 2), (4, 1), (8, 2), (16, 1))
@@ -38,17 +41,19 @@ def _compile(item) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(min(len(SOURCES), os.cpu_count() or 8, 16)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp] + objs
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("link failed")
-    os.replace(tmp, LIB)
-    if verbose:
-        print("built", LIB)
+    with ThreadPoolExecutor(min(len(SOURCES) + 1, os.cpu_count() or 8, 16)) as ex:
+        objs = list(ex.map(_compile, SOURCES + [MB_SOURCE]))
+    mb_obj = objs.pop()
+    for lib, parts in ((LIB, objs), (MB_LIB, [mb_obj])):
+        tmp = lib + ".tmp%d" % os.getpid()
+        cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp] + parts
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            sys.stderr.write(r.stdout + r.stderr)
+            raise RuntimeError("link failed")
+        os.replace(tmp, lib)
+        if verbose:
+            print("built", lib)
     return LIB
 
 
