@@ -408,10 +408,25 @@ def main():
         oracle.selective_scan(f["x"], f["delta"], f["A"], f["B"], f["C"], Dskip=f["D"], z=f["z"],
                               delta_bias=f["delta_bias"], delta_softplus=True, threads=threads)
         sec = time.perf_counter() - t0
+        # one thread on batch row 0 (2048 x 1536 token-channels)
+        sl = lambda a: None if a is None else a[:1]
+        t1 = time.perf_counter()
+        oracle.selective_scan(sl(f["x"]), sl(f["delta"]), f["A"], sl(f["B"]), sl(f["C"]), Dskip=f["D"], z=sl(f["z"]),
+                              delta_bias=f["delta_bias"], delta_softplus=True, threads=1)
+        sec1 = time.perf_counter() - t1
+        model = ""
+        try:
+            with open("/proc/cpuinfo") as fh:
+                model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
+        except OSError:
+            pass
         out["cpu_baseline"] = {"value": round(tc / sec / 1e9, 5), "unit": "Gtoken*channel/s", "cores": threads,
                                "kind": "oracle",
                                "sample": "the whole workload (8 x 2048 x 1536 token-channels, 16 states), fp64, "
-                                         "%.1f s wall" % sec}
+                                         "%.1f s wall" % sec,
+                               "value_1_thread": round(tc / 8 / sec1 / 1e9, 5),
+                               "sample_1_thread": "batch row 0 (2048 x 1536 token-channels), %.2f s wall" % sec1,
+                               "host": {"cpu_model": model, "cpu_count": os.cpu_count()}}
     print(json.dumps(out), flush=True)
 
 
