@@ -83,6 +83,18 @@ def test_long_sequence_time_split(ssm, dtype, L, D):
     check(ssm, inp, label="long %s L=%d D=%d" % (dtype, L, D))
 
 
+# Sequence lengths of one token, a few, exactly one tile and just past a power of two, each
+# with and without skip and gate, softplus on and off.
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("L", [1, 7, 64, 4097])
+@pytest.mark.parametrize("skip,gate,softplus", [(False, False, False), (True, True, True)])
+def test_lengths_and_optional_terms(ssm, dtype, L, skip, gate, softplus):
+    inp = workloads.scan_inputs(2, L, 24, 16, dtype=dtype, seed=L * 7 + skip * 3 + gate,
+                                dt="softplus_bias" if softplus else "loguniform", gate=gate, softplus=softplus,
+                                skip=skip, h0=True)
+    check(ssm, inp, label="L=%d %s skip=%s gate=%s softplus=%s" % (L, dtype, skip, gate, softplus))
+
+
 # Lane layouts and workgroup shapes, compared in full: 8 rows with four waves per workgroup
 # (8x2048 channels), 4 rows with four waves (16x2048; dstate 64 and 128 at 128 / 64 channels),
 # 16 rows with four waves and a ragged tile, and 16 rows with one wave per workgroup (channel
