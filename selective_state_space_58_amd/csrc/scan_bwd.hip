@@ -9,16 +9,20 @@
 //   dA_n   = sum_t lam_n (h_{t-1,n} E dt + B_n x dg/da),  dB, dC = sums over channels
 // with E = exp(dt a), g = (E - 1)/a, dy = dout * silu(z).
 //
-// Mapping: the forward's lane layout (one wave per 16 channels of one batch
-// row, 4 rows of 16 lanes, S states per lane).  A forward pass stores the
-// state at the start of every 16-token tile in the workspace; the reverse pass
-// then walks the tiles from the last, recomputes the tile's states into LDS
-// (with the readout, which the gate's gradient needs), and runs the adjoint
-// backwards with lam in registers.  Per-(token, channel) sums over the states
-// use the forward's row reduce-scatter; per-(token, state) sums over channels
-// (dB, dC) are reduced over the 16 lanes of a row with DPP and added to the
-// output with one atomic per wave; dA, Dskip and bias gradients are summed in
-// registers and added once per wave.
+// Mapping: the forward's 16-row lane layout (lane = state n x 4 channels, one
+// state per lane, dstate <= 16) with four waves per workgroup covering 16
+// consecutive channels of one batch row, which share the staged tiles.  A
+// forward pass stores the state at the start of every 16-token tile in the
+// workspace; the reverse pass then walks the tiles from the last, recomputes
+// the tile's states and decays into LDS (with the readout, which the gate's
+// gradient needs), and runs the adjoint backwards with lam in registers.
+// Per-(token, channel) sums over the states (dx, ddt) use the forward's row
+// reduce-scatter.  Per-(token, state) sums over channels (dB, dC) are summed
+// over the 4 channels of a wave with DPP and over the 4 waves in LDS, then
+// written as one partial per (workgroup, token, state) to the workspace; a
+// second kernel adds the partials of the workgroups of a batch row (no
+// atomics on the per-token gradients).  dA, Dskip and bias gradients are
+// summed in registers and added once per wave.
 #include <hip/hip_runtime.h>
 
 #include "scan_impl.h"
@@ -31,45 +35,57 @@ using scan_dev::hw_exp2;
 using scan_dev::hw_rcp;
 using scan_dev::kLog2e;
 using scan_dev::Raw;
-using scan_dev::reduce_scatter_rows;
 using scan_dev::silu_f;
 using scan_dev::softplus_f;
 using scan_dev::zoh_gain_accurate;
 
-constexpr int BT = 16;   // tokens per tile (states and decays of a tile are kept in LDS)
-constexpr int BR = 4;    // lane rows
-constexpr int BCH = 16;  // channels per wave
+constexpr int BT = 16;    // tokens per tile (states and decays of a tile are kept in LDS)
+constexpr int BR = 16;    // lane rows: one state per lane
+constexpr int BCH = 4;    // channels per wave
+constexpr int BW = 4;     // waves per workgroup
+constexpr int BWC = BW * BCH;   // channels per workgroup
+constexpr int BG = 4;     // tokens per row reduction (token j of a group ends in rows 4j .. 4j+3)
 
 __device__ __forceinline__ float sigmoid_f(float v) { return hw_rcp(1.f + hw_exp2(-v * kLog2e)); }
 
 // d/da of the ZOH gain (e^{dt a} - 1)/a: (dt E - g)/a, or dt^2 psi(q) with
-// psi(q) = sum_{k>=2} (k-1) q^{k-2}/k! for |q| < 1/8 (truncation < 1e-9).
+// psi(q) = sum_{k>=2} (k-1) q^{k-2}/k! for |q| < 1/8 (truncation < 1e-9).  The
+// short form alone (bf16 inputs) loses ~2e-7/|q| relative accuracy, far below
+// bf16 resolution.
+template <bool ACC>
 __device__ __forceinline__ float gain_da(float dt, float a, float ia, float E, float g) {
+  const float dl = (dt * E - g) * ia;
+  if (!ACC) return dl;
   const float q = dt * a;
   const float psi = fmaf(q, fmaf(q, fmaf(q, fmaf(q, fmaf(q, 1.f / 840.f, 1.f / 144.f), 1.f / 30.f), 1.f / 8.f),
                                  1.f / 3.f), 0.5f);
-  return fabsf(q) < 0.125f ? dt * dt * psi : (dt * E - g) * ia;
+  return fabsf(q) < 0.125f ? dt * dt * psi : dl;
 }
 
 // ZOH gain from E = e^{dt a}: the accurate form (fp32 activations, or any
-// |a| < 1e-2 in the wave) or the short form (E - 1)/a, as in the forward.
+// |a| < 1e-2 in the workgroup) or the short form (E - 1)/a, as in the forward.
 template <bool ACC>
 __device__ __forceinline__ float bwd_gain(float E, float dt, float a, float ia) {
   return ACC ? zoh_gain_accurate(E, dt, a, ia) : fmaf(E, ia, -ia);
 }
 
-// Sum over the 16 lanes of a row (row_shr inclusive scan): lane 15 of the row
-// holds the total.  Lanes shifted in from outside the row read 0 (bound_ctrl),
-// which lets each step fold into one v_add_f32 with a DPP source.
-template <int CTRL>
-__device__ __forceinline__ float dpp_shr(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, true));
+// p[j] holds, in every lane, a partial for token j of a group of 4.  Returns
+// in lane (row r, column c) the sum of p[r / 4] over the 16 rows of column c:
+// a reduce-scatter over lane bits 5 and 4 (row bits 3 and 2) leaves token r/4
+// summed over four rows, and a butterfly over lane bits 3 and 2 adds the rest.
+__device__ __forceinline__ float reduce4_rows(const float (&p)[4]) {
+  const float u0 = scan_dev::pair_sum<32>(p[0], p[2]);
+  const float u1 = scan_dev::pair_sum<32>(p[1], p[3]);
+  float v = scan_dev::pair_sum<16>(u0, u1);
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xf, 0xf, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x101f));
+  return v;
 }
-__device__ __forceinline__ float row_sum_to_lane15(float v) {
-  v += dpp_shr<0x111>(v);
-  v += dpp_shr<0x112>(v);
-  v += dpp_shr<0x114>(v);
-  v += dpp_shr<0x118>(v);
+
+// Sum over the 4 lanes of a quad (the 4 channels of a row); every lane gets it.
+__device__ __forceinline__ float quad_sum(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xf, 0xf, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xf, 0xf, false));
   return v;
 }
 
@@ -78,45 +94,49 @@ __global__ __launch_bounds__(256) void bwd_zero_kernel(float* p, int64_t n) {
   if (i < n) p[i] = 0.f;
 }
 
-template <int S>
+// dB, dC = sums of the per-workgroup partials of each batch row.
+__global__ __launch_bounds__(256) void bwd_sum_partials_kernel(const float* part_b, const float* part_c, float* dB,
+                                                               float* dC, int64_t per_group, int64_t groups) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= per_group) return;
+  float sb = 0.f, sc = 0.f;
+  for (int64_t g = 0; g < groups; ++g) {
+    sb += part_b[g * per_group + i];
+    sc += part_c[g * per_group + i];
+  }
+  dB[i] = sb;
+  dC[i] = sc;
+}
+
 struct BwdLds {
-  float2 dx[BT * BCH];           // (dt, x)
-  float v[BT * BCH];             // delta + bias (before softplus)
-  float dout[BT * BCH];          // dout
-  float z[BT * BCH];             // z
-  float dy[BT * BCH];            // dout * silu(z)
-  float bc[BT * BR * 2 * S];     // B, C per (token, row)
-  float h[BT * S * 64];          // h_t per (token, state slot, lane)
-  float E[BT * S * 64];          // e^{dt_t a} per (token, state slot, lane)
+  float2 dx[BT * BWC];          // (dt, x) per (token, workgroup channel)
+  float v[BT * BWC];            // delta + bias (before softplus)
+  float dout[BT * BWC];
+  float z[BT * BWC];
+  float dy[BT * BWC];           // dout * silu(z)
+  float bc[BT * BR * 2];        // (B, C) per (token, state)
+  float h[BW * BT * 64];        // h_t per (wave, token, lane)
+  float E[BW * BT * 64];        // e^{dt_t a} per (wave, token, lane)
+  float red[BW * BT * BR * 2];  // per-wave (dB, dC) partial per (token, state)
 };
 
-template <bool XB, bool DB, int S, bool ACC>
-__device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t gpb, const float (&av)[S],
-                                              const float (&a2)[S], const float (&ia)[S], const bool (&nok)[S],
-                                              BwdLds<S>* lds) {
-  BwdLds<S>& sm = *lds;
-  float2* s_dx = sm.dx;
-  float* s_v = sm.v;
-  float* s_do = sm.dout;
-  float* s_z = sm.z;
-  float* s_dy = sm.dy;
-  float* s_bc = sm.bc;
-  float* s_h = sm.h;
-  float* s_E = sm.E;
-
+template <bool XB, bool DB, bool ACC>
+__device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64_t chw0, int64_t grp, float av,
+                                              float a2, float ia, bool nok, BwdLds& sm) {
   using RX = typename Raw<XB>::T;
   using RD = typename Raw<DB>::T;
-  const int64_t nb = gridDim.x;
-  int64_t lin = blockIdx.x;
-  if ((nb & 7) == 0) lin = (lin & 7) * (nb >> 3) + (lin >> 3);
-  const int64_t b = lin / gpb;
-  const int64_t ch0 = (lin % gpb) * BCH;
-  const int lane = threadIdx.x;
-  const int r = lane >> 4, c = lane & 15;
+  using TX = typename scan_dev::Act<XB>::T;
+  using TD = typename scan_dev::Act<DB>::T;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
+  const int r = lane >> 2, c = lane & 3;
+  const int wc = w * BCH + c;                // channel within the workgroup
   const int64_t L = a.seqlen, dim = a.dim, N = a.dstate;
-  const int64_t ch = ch0 + c;
+  const int64_t ch = chw0 + wc;
   const bool ch_ok = ch < dim;
   const int ntile = (int)((L + BT - 1) / BT);
+  const int64_t slice = a.batch * dim * N;
+  const int64_t hidx = (b * dim + ch) * N + r;   // this lane's state (valid when nok)
 
   const float Dv = (a.Dskip != nullptr && ch_ok) ? a.Dskip[ch] : 0.f;
   const RX* gx = (const RX*)a.x;
@@ -125,259 +145,250 @@ __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t gpb, con
   const RX* gdo = (const RX*)a.dout;
   const RX* gB = (const RX*)a.B;
   const RX* gC = (const RX*)a.C;
-  const int64_t slice = a.batch * dim * N;
 
-  // Stage tile k: (dt, x), v, dout, z per (token, channel); B and C per (token, row).
-  auto stage = [&](int k, bool need_c) {
+  // Stage tile k: per (token, channel) one item per thread, per (token, state) one item per thread.
+  auto stage = [&](int k, bool full) {
     const int64_t t0 = (int64_t)k * BT;
-    for (int e = lane; e < BT * BCH; e += 64) {
-      const int tl = e / BCH, cc = e % BCH;
+    {
+      const int tl = tid / BWC, cc = tid % BWC;
       const int64_t t = t0 + tl;
-      const int64_t chl = ch0 + cc < dim ? ch0 + cc : dim - 1;
-      const bool ok = t < L && ch0 + cc < dim;
+      const int64_t chl = chw0 + cc < dim ? chw0 + cc : dim - 1;
+      const bool ok = t < L && chw0 + cc < dim;
       const int64_t i = (b * L + (t < L ? t : L - 1)) * dim + chl;
       const float v = Raw<DB>::f32(gd[i]) + ((a.delta_bias != nullptr) ? a.delta_bias[chl] : 0.f);
       const float dt = ok ? (a.softplus ? softplus_f(v) : v) : 0.f;
-      s_dx[e] = make_float2(dt, Raw<XB>::f32(gx[i]));
-      s_v[e] = v;
-      if (need_c) {
-        s_do[e] = ok ? Raw<XB>::f32(gdo[i]) : 0.f;
-        s_z[e] = (a.z != nullptr) ? Raw<XB>::f32(gz[i]) : 0.f;
+      sm.dx[tid] = make_float2(dt, Raw<XB>::f32(gx[i]));
+      if (full) {
+        sm.v[tid] = v;
+        sm.dout[tid] = ok ? Raw<XB>::f32(gdo[i]) : 0.f;
+        sm.z[tid] = (a.z != nullptr) ? Raw<XB>::f32(gz[i]) : 0.f;
       }
     }
-    for (int e = lane; e < BT * BR * S; e += 64) {
-      const int tl = e / (BR * S), n = e % (BR * S);
+    {
+      const int tl = tid / BR, n = tid % BR;
       const int64_t t = t0 + tl;
       const bool ok = t < L && n < N;
       const int64_t i = (b * L + (t < L ? t : L - 1)) * N + (n < N ? n : 0);
-      const int base = ((tl * BR + n / S) * 2) * S + (n % S);
-      s_bc[base] = ok ? Raw<XB>::f32(gB[i]) : 0.f;
-      if (need_c) s_bc[base + S] = ok ? Raw<XB>::f32(gC[i]) : 0.f;
+      sm.bc[(tl * BR + n) * 2] = ok ? Raw<XB>::f32(gB[i]) : 0.f;
+      if (full) sm.bc[(tl * BR + n) * 2 + 1] = ok ? Raw<XB>::f32(gC[i]) : 0.f;
     }
   };
 
-  // ---- forward: state at the start of every tile into the workspace
-  float h[S];
-#pragma unroll
-  for (int s = 0; s < S; ++s) h[s] = (a.h0 != nullptr && nok[s]) ? a.h0[(b * dim + ch) * N + r * S + s] : 0.f;
+  // ---- forward: the state at the start of every tile into the workspace
+  float h = (a.h0 != nullptr && nok) ? a.h0[hidx] : 0.f;
   for (int k = 0; k < ntile; ++k) {
-#pragma unroll
-    for (int s = 0; s < S; ++s)
-      if (nok[s]) a.ws_ckpt[(int64_t)k * slice + (b * dim + ch) * N + r * S + s] = h[s];
+    if (nok) a.ws_ckpt[(int64_t)k * slice + hidx] = h;
     __syncthreads();
     stage(k, false);
     __syncthreads();
+#pragma unroll 4
     for (int tl = 0; tl < BT; ++tl) {
-      const float2 dx = s_dx[tl * BCH + c];
-      const float* bc = s_bc + ((tl * BR + r) * 2) * S;
-#pragma unroll
-      for (int s = 0; s < S; ++s) {
-        const float E = hw_exp2(dx.x * a2[s]);
-        h[s] = fmaf(E, h[s], bwd_gain<ACC>(E, dx.x, av[s], ia[s]) * (bc[s] * dx.y));
-      }
+      const float2 dx = sm.dx[tl * BWC + wc];
+      const float Bn = sm.bc[(tl * BR + r) * 2];
+      const float E = hw_exp2(dx.x * a2);
+      h = fmaf(E, h, bwd_gain<ACC>(E, dx.x, av, ia) * (Bn * dx.y));
     }
   }
 
   // ---- reverse
-  float lam[S], dA[S];
-#pragma unroll
-  for (int s = 0; s < S; ++s) {
-    lam[s] = (a.dh_final != nullptr && nok[s]) ? a.dh_final[(b * dim + ch) * N + r * S + s] : 0.f;
-    dA[s] = 0.f;
-  }
-  float dDacc = 0.f, dbacc = 0.f;
+  float lam = (a.dh_final != nullptr && nok) ? a.dh_final[hidx] : 0.f;
+  float dA = 0.f, dDacc = 0.f, dbacc = 0.f;
+  float* hw = sm.h + w * BT * 64;
+  float* ew = sm.E + w * BT * 64;
+  float* rw = sm.red + w * BT * BR * 2;
+  const int64_t per_group = a.batch * L * N;
   for (int k = ntile - 1; k >= 0; --k) {
     const int64_t t0 = (int64_t)k * BT;
     __syncthreads();
     stage(k, true);
     __syncthreads();
-    // recompute the tile's states (into LDS) and its readout; y gives dz and dy
-    float hs[S];
+    // recompute the tile's states and decays (into LDS) and its readout; y gives dz and dy
+    const float hstart = nok ? a.ws_ckpt[(int64_t)k * slice + hidx] : 0.f;
+    float hs = hstart;
+#pragma unroll 1
+    for (int tb = 0; tb < BT; tb += BG) {
+      float pr[BG];
 #pragma unroll
-    for (int s = 0; s < S; ++s) hs[s] = nok[s] ? a.ws_ckpt[(int64_t)k * slice + (b * dim + ch) * N + r * S + s] : 0.f;
-    float hstart[S];
-#pragma unroll
-    for (int s = 0; s < S; ++s) hstart[s] = hs[s];
-    for (int tb = 0; tb < BT; tb += BR) {
-      float pr[BR];
-#pragma unroll
-      for (int j = 0; j < BR; ++j) {
+      for (int j = 0; j < BG; ++j) {
         const int tl = tb + j;
-        const float2 dx = s_dx[tl * BCH + c];
-        const float* bc = s_bc + ((tl * BR + r) * 2) * S;
-        float acc = 0.f;
-#pragma unroll
-        for (int s = 0; s < S; ++s) {
-          const float E = hw_exp2(dx.x * a2[s]);
-          hs[s] = fmaf(E, hs[s], bwd_gain<ACC>(E, dx.x, av[s], ia[s]) * (bc[s] * dx.y));
-          s_h[(tl * S + s) * 64 + lane] = hs[s];
-          s_E[(tl * S + s) * 64 + lane] = E;
-          acc = fmaf(bc[S + s], hs[s], acc);
+        const float2 dx = sm.dx[tl * BWC + wc];
+        const float Bn = sm.bc[(tl * BR + r) * 2], Cn = sm.bc[(tl * BR + r) * 2 + 1];
+        const float E = hw_exp2(dx.x * a2);
+        hs = fmaf(E, hs, bwd_gain<ACC>(E, dx.x, av, ia) * (Bn * dx.y));
+        hw[tl * 64 + lane] = hs;
+        ew[tl * 64 + lane] = E;
+        pr[j] = Cn * hs;
+      }
+      const float tot = reduce4_rows(pr);   // rows 4j .. 4j+3: readout of token tb + j
+      if ((r & 3) == 0) {
+        const int tl = tb + (r >> 2);
+        const int e = tl * BWC + wc;
+        const float y = fmaf(Dv, sm.dx[e].y, tot);
+        const float dout = sm.dout[e];
+        float dy = dout;
+        if (a.z != nullptr) {
+          const float zz = sm.z[e];
+          const float sg = sigmoid_f(zz);
+          dy = dout * zz * sg;
+          if (ch_ok && t0 + tl < L)
+            ((TX*)a.dz)[(b * L + t0 + tl) * dim + ch] = (TX)(dout * y * (sg + zz * sg * (1.f - sg)));
         }
-        pr[j] = acc;
+        sm.dy[e] = dy;
       }
-      const float tot = reduce_scatter_rows<BR>(pr);
-      const int tl = tb + r;
-      const int e = tl * BCH + c;
-      const float xv = s_dx[e].y;
-      const float y = fmaf(Dv, xv, tot);
-      const float dout = s_do[e];
-      float dy = dout;
-      if (a.z != nullptr) {
-        const float zz = s_z[e];
-        const float sg = sigmoid_f(zz);
-        dy = dout * zz * sg;
-        if (ch_ok && t0 + tl < L)
-          ((typename scan_dev::Act<XB>::T*)a.dz)[(b * L + t0 + tl) * dim + ch] =
-              (typename scan_dev::Act<XB>::T)(dout * y * (sg + zz * sg * (1.f - sg)));
-      }
-      s_dy[e] = dy;
     }
     __syncthreads();
-    // adjoint, tokens in reverse, groups of 4 for the row reduce-scatter
-    for (int tb = BT - BR; tb >= 0; tb -= BR) {
-      float pdx[BR], pdt[BR];
+    // adjoint, tokens in reverse, in groups of 4 for the row reductions
+#pragma unroll 1
+    for (int tb = BT - BG; tb >= 0; tb -= BG) {
+    float pdx[BG], pdt[BG];
 #pragma unroll
-      for (int j = BR - 1; j >= 0; --j) {
-        const int tl = tb + j;
-        const float2 dx = s_dx[tl * BCH + c];
-        const float dy = s_dy[tl * BCH + c];
-        const float* bc = s_bc + ((tl * BR + r) * 2) * S;
-        const int64_t bt = (b * L + t0 + tl) * N;
-        const bool tok = t0 + tl < L;
-        float sx = 0.f, st = 0.f;
-        float cdc[S], cdb[S];
-#pragma unroll
-        for (int s = 0; s < S; ++s) {
-          const float Bn = bc[s], Cn = bc[S + s];
-          const float E = s_E[(tl * S + s) * 64 + lane];
-          const float g = bwd_gain<ACC>(E, dx.x, av[s], ia[s]);
-          lam[s] = fmaf(Cn, dy, lam[s]);
-          const float ht = s_h[(tl * S + s) * 64 + lane];
-          const float hp = tl > 0 ? s_h[((tl - 1) * S + s) * 64 + lane] : hstart[s];
-          // dC = sum over channels of h_t dy; dB = sum over channels of lam g x
-          cdc[s] = row_sum_to_lane15(ht * dy);
-          cdb[s] = row_sum_to_lane15(lam[s] * g * dx.y);
-          const float dE = lam[s] * hp;
-          const float dg = lam[s] * Bn * dx.y;
-          sx = fmaf(lam[s] * g, Bn, sx);
-          st = fmaf(dE * E, av[s], fmaf(dg, E, st));
-          dA[s] = fmaf(dE * E, dx.x, fmaf(dg, gain_da(dx.x, av[s], ia[s], E, g), dA[s]));
-          lam[s] *= E;
-        }
-        if (c == 15 && tok) {
-#pragma unroll
-          for (int s = 0; s < S; ++s) {
-            if (r * S + s < N) {
-              atomicAdd(a.dC + bt + r * S + s, cdc[s]);
-              atomicAdd(a.dB + bt + r * S + s, cdb[s]);
-            }
-          }
-        }
-        pdx[j] = sx;
-        pdt[j] = st;
+    for (int j = BG - 1; j >= 0; --j) {
+      const int tl = tb + j;
+      const float2 dx = sm.dx[tl * BWC + wc];
+      const float dy = sm.dy[tl * BWC + wc];
+      const float Bn = sm.bc[(tl * BR + r) * 2], Cn = sm.bc[(tl * BR + r) * 2 + 1];
+      const float E = ew[tl * 64 + lane];
+      const float ht = hw[tl * 64 + lane];
+      const float hp = tl > 0 ? hw[(tl - 1) * 64 + lane] : hstart;
+      const float g = bwd_gain<ACC>(E, dx.x, av, ia);
+      lam = fmaf(Cn, dy, lam);
+      // dC = sum over channels of h_t dy; dB = sum over channels of lam g x
+      const float sc = quad_sum(ht * dy);
+      const float sb = quad_sum(lam * g * dx.y);
+      if (c == 0) {
+        rw[(tl * BR + r) * 2] = sb;
+        rw[(tl * BR + r) * 2 + 1] = sc;
       }
-      const float tdx = reduce_scatter_rows<BR>(pdx);
-      const float tdt = reduce_scatter_rows<BR>(pdt);
-      const int tl = tb + r;
-      const int e = tl * BCH + c;
-      if (ch_ok && t0 + tl < L) {
-        const float dy = s_dy[e];
-        const float xv = s_dx[e].y;
-        const float dv = a.softplus ? tdt * sigmoid_f(s_v[e]) : tdt;
-        const int64_t i = (b * L + t0 + tl) * dim + ch;
-        ((typename scan_dev::Act<XB>::T*)a.dx)[i] = (typename scan_dev::Act<XB>::T)fmaf(Dv, dy, tdx);
-        ((typename scan_dev::Act<DB>::T*)a.ddelta)[i] = (typename scan_dev::Act<DB>::T)dv;
-        dDacc = fmaf(dy, xv, dDacc);
-        dbacc += dv;
+      const float dE = lam * hp;
+      const float dg = lam * Bn * dx.y;
+      pdx[j] = lam * g * Bn;
+      pdt[j] = fmaf(dE * E, av, dg * E);
+      dA = fmaf(dE * E, dx.x, fmaf(dg, gain_da<ACC>(dx.x, av, ia, E, g), dA));
+      lam *= E;
+    }
+    const float tdx = reduce4_rows(pdx);
+    const float tdt = reduce4_rows(pdt);
+    const int tl = tb + (r >> 2);
+    if ((r & 3) == 0 && ch_ok && t0 + tl < L) {
+      const int e = tl * BWC + wc;
+      const float dy = sm.dy[e];
+      const float dv = a.softplus ? tdt * sigmoid_f(sm.v[e]) : tdt;
+      const int64_t i = (b * L + t0 + tl) * dim + ch;
+      ((TX*)a.dx)[i] = (TX)fmaf(Dv, dy, tdx);
+      ((TD*)a.ddelta)[i] = (TD)dv;
+      dDacc = fmaf(dy, sm.dx[e].y, dDacc);
+      dbacc += dv;
+    }
+    }
+    __syncthreads();
+    // dB, dC partial of this workgroup: sum of the 4 waves
+    {
+      const int tl = tid / BR, n = tid % BR;
+      if (t0 + tl < L && n < N) {
+        float sb = 0.f, sc = 0.f;
+#pragma unroll
+        for (int q = 0; q < BW; ++q) {
+          sb += sm.red[((q * BT + tl) * BR + n) * 2];
+          sc += sm.red[((q * BT + tl) * BR + n) * 2 + 1];
+        }
+        const int64_t o = grp * per_group + (b * L + t0 + tl) * N + n;
+        a.ws_part[o] = sb;
+        a.ws_part[(int64_t)a.ws_groups * per_group + o] = sc;
       }
     }
   }
 
-  // ---- per-wave sums
-#pragma unroll
-  for (int s = 0; s < S; ++s) {
-    if (!nok[s]) continue;
-    const int64_t n = r * S + s;
-    if (a.dh0 != nullptr) a.dh0[(b * dim + ch) * N + n] = lam[s];
-    atomicAdd(a.dA + ch * N + n, dA[s]);
+  // ---- per-wave sums: dh0, dA per lane; Dskip and bias gradients summed over the 16 rows
+  if (nok) {
+    if (a.dh0 != nullptr) a.dh0[hidx] = lam;
+    atomicAdd(a.dA + ch * N + r, dA);
   }
-  if (ch_ok) {
+#pragma unroll
+  for (int o = 4; o < 64; o <<= 1) {
+    dDacc += __shfl_xor(dDacc, o);
+    dbacc += __shfl_xor(dbacc, o);
+  }
+  if (ch_ok && r == 0) {
     if (a.dDskip != nullptr) atomicAdd(a.dDskip + ch, dDacc);
     if (a.ddelta_bias != nullptr) atomicAdd(a.ddelta_bias + ch, dbacc);
   }
 }
 
-template <bool XB, bool DB, int S>
-__global__ __launch_bounds__(64) void scan_bwd_kernel(BwdArgs a, int64_t gpb) {
-  const int lane = threadIdx.x;
-  const int r = lane >> 4, c = lane & 15;
+// One workgroup of four waves per 16 channels of a batch row.
+template <bool XB, bool DB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void scan_bwd_kernel(BwdArgs a,
+                                                                                              int64_t wgs_per_batch) {
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
+  const int r = lane >> 2, c = lane & 3;
   const int64_t nb = gridDim.x;
   int64_t lin = blockIdx.x;
   if ((nb & 7) == 0) lin = (lin & 7) * (nb >> 3) + (lin >> 3);
-  const int64_t ch = (lin % gpb) * BCH + c;
-  const int64_t N = a.dstate;
-  float av[S], a2[S], ia[S];
-  bool nok[S];
-  bool tiny = false;
-#pragma unroll
-  for (int s = 0; s < S; ++s) {
-    const int64_t n = r * S + s;
-    nok[s] = ch < a.dim && n < N;
-    av[s] = nok[s] ? a.A[ch * N + n] : -1.f;
-    a2[s] = av[s] * kLog2e;
-    ia[s] = 1.f / av[s];
-    tiny = tiny || !(fabsf(av[s]) >= 1e-2f);
-  }
-  __shared__ __attribute__((aligned(16))) BwdLds<S> lds;
-  if (!XB || __builtin_amdgcn_ballot_w64(tiny) != 0) scan_bwd_body<XB, DB, S, true>(a, gpb, av, a2, ia, nok, &lds);
-  else scan_bwd_body<XB, DB, S, false>(a, gpb, av, a2, ia, nok, &lds);
+  const int64_t b = lin / wgs_per_batch;
+  const int64_t grp = lin % wgs_per_batch;
+  const int64_t chw0 = grp * BWC;
+  const int64_t ch = chw0 + w * BCH + c;
+  const bool nok = ch < a.dim && r < a.dstate;
+  const float av = nok ? a.A[ch * a.dstate + r] : -1.f;
+  const float a2 = av * kLog2e, ia = 1.f / av;
+  const bool tiny = !(fabsf(av) >= 1e-2f);
+  __shared__ __attribute__((aligned(16))) BwdLds lds;
+  if (!XB || __syncthreads_or(tiny)) scan_bwd_body<XB, DB, true>(a, b, chw0, grp, av, a2, ia, nok, lds);
+  else scan_bwd_body<XB, DB, false>(a, b, chw0, grp, av, a2, ia, nok, lds);
 }
 
 template <bool XB, bool DB>
-hipError_t launch_bwd_xd(int S, const BwdArgs& a, dim3 grid, int64_t gpb, hipStream_t st) {
-  switch (S) {
-    case 1: scan_bwd_kernel<XB, DB, 1><<<grid, 64, 0, st>>>(a, gpb); break;
-    case 2: scan_bwd_kernel<XB, DB, 2><<<grid, 64, 0, st>>>(a, gpb); break;
-    case 4: scan_bwd_kernel<XB, DB, 4><<<grid, 64, 0, st>>>(a, gpb); break;
-    default: return hipErrorInvalidValue;
-  }
+hipError_t launch_bwd_xd(const BwdArgs& a, dim3 grid, int64_t wgs, hipStream_t st) {
+  scan_bwd_kernel<XB, DB><<<grid, 256, 0, st>>>(a, wgs);
   return hipGetLastError();
+}
+
+size_t ckpt_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
+  const int64_t ntile = (seqlen + BT - 1) / BT;
+  return ((size_t)(ntile * batch * dim * dstate) * sizeof(float) + 255) / 256 * 256;
 }
 
 }  // namespace
 
 size_t scan_bwd_ws_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
-  const int64_t ntile = (seqlen + BT - 1) / BT;
-  return (size_t)(ntile * batch * dim * dstate) * sizeof(float);
+  const int64_t groups = (dim + BWC - 1) / BWC;
+  return ckpt_bytes(batch, seqlen, dim, dstate) + (size_t)(2 * groups * batch * seqlen * dstate) * sizeof(float);
 }
 
-int launch_scan_bwd(const BwdArgs& a, void* stream) {
+int launch_scan_bwd(const BwdArgs& a0, void* stream) {
   hipStream_t st = (hipStream_t)stream;
-  // the channel-shared and batch-shared gradients are accumulated: clear them first
+  BwdArgs a = a0;
+  // the gradients summed over batch and time are accumulated: clear them first
   auto zero = [&](float* p, int64_t n) -> hipError_t {
     if (p == nullptr || n == 0) return hipSuccess;
     bwd_zero_kernel<<<dim3((unsigned)((n + 255) / 256)), 256, 0, st>>>(p, n);
     return hipGetLastError();
   };
   hipError_t e = zero(a.dA, a.dim * a.dstate);
-  if (e == hipSuccess) e = zero(a.dB, a.batch * a.seqlen * a.dstate);
-  if (e == hipSuccess) e = zero(a.dC, a.batch * a.seqlen * a.dstate);
   if (e == hipSuccess) e = zero(a.dDskip, a.dim);
   if (e == hipSuccess) e = zero(a.ddelta_bias, a.dim);
   if (e != hipSuccess) return fail(6, std::string("backward clear: ") + hipGetErrorString(e));
-  int S = 1;
-  while (S * BR < a.dstate) S *= 2;
-  if (S > 4) return fail(4, "the backward pass supports dstate <= 16");
-  const int64_t gpb = (a.dim + BCH - 1) / BCH;
-  const int64_t nb = a.batch * gpb;
+  if (a.dstate > BR) return fail(4, "the backward pass supports dstate <= 16");
+  const int64_t wgs = (a.dim + BWC - 1) / BWC;
+  const int64_t nb = a.batch * wgs;
   if (nb > 0x7fffffffLL) return fail(4, "grid too large");
+  a.ws_groups = wgs;
+  a.ws_part = a.ws_ckpt != nullptr
+                  ? (float*)((char*)a.ws_ckpt + ckpt_bytes(a.batch, a.seqlen, a.dim, a.dstate))
+                  : nullptr;
   const dim3 grid((unsigned)nb);
-  if (a.act_bf16 && a.delta_bf16) e = launch_bwd_xd<true, true>(S, a, grid, gpb, st);
-  else if (a.act_bf16) e = launch_bwd_xd<true, false>(S, a, grid, gpb, st);
-  else if (a.delta_bf16) e = launch_bwd_xd<false, true>(S, a, grid, gpb, st);
-  else e = launch_bwd_xd<false, false>(S, a, grid, gpb, st);
+  if (a.act_bf16 && a.delta_bf16) e = launch_bwd_xd<true, true>(a, grid, wgs, st);
+  else if (a.act_bf16) e = launch_bwd_xd<true, false>(a, grid, wgs, st);
+  else if (a.delta_bf16) e = launch_bwd_xd<false, true>(a, grid, wgs, st);
+  else e = launch_bwd_xd<false, false>(a, grid, wgs, st);
   if (e != hipSuccess) return fail(6, std::string("backward launch: ") + hipGetErrorString(e));
+  const int64_t per_group = a.batch * a.seqlen * a.dstate;
+  if (per_group > 0) {
+    bwd_sum_partials_kernel<<<dim3((unsigned)((per_group + 255) / 256)), 256, 0, st>>>(
+        a.ws_part, a.ws_part + wgs * per_group, a.dB, a.dC, per_group, wgs);
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail(6, std::string("backward partial sums: ") + hipGetErrorString(e));
+  }
   return 0;
 }
 

@@ -84,6 +84,8 @@ struct BwdArgs {
   float* ddelta_bias;      // (dim) or null
   float* dh0;              // (batch, dim, dstate) or null
   float* ws_ckpt;          // (ntiles, batch, dim, dstate) states at tile starts
+  float* ws_part;          // 2 x (groups, batch, seqlen, dstate) dB, dC partials of the channel groups
+  int64_t ws_groups;       // channel groups (workgroups per batch row)
   int64_t batch, seqlen, dim, dstate;
   int softplus;
   int act_bf16, delta_bf16;

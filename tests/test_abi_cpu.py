@@ -250,6 +250,9 @@ def test_scan_bwd_argument_errors(kw, code):
 
 def test_scan_bwd_workspace_query():
     lib = _lib()
-    assert lib.ssm_scan_bwd_workspace_bytes(2, 100, 40, 16) == 7 * 2 * 40 * 16 * 4
+    # states at the start of each of the 7 16-token tiles (rounded up to 256 bytes), then the dB and dC
+    # partials of the 3 groups of 16 channels per token and state
+    ckpt = (7 * 2 * 40 * 16 * 4 + 255) // 256 * 256
+    assert lib.ssm_scan_bwd_workspace_bytes(2, 100, 40, 16) == ckpt + 2 * 3 * 2 * 100 * 16 * 4
     assert lib.ssm_scan_bwd_workspace_bytes(2, 100, 40, 17) == 0
     assert bwd(lib, batch=0) == 0
