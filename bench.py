@@ -89,7 +89,8 @@ def scan_bytes(cfg):
     e = 2 if cfg["dtype"] == "bf16" else 4
     ed = 2 if cfg["delta_dtype"] == "bf16" else 4
     per_tc = e * 2 + ed + (e if cfg["gate"] else 0)            # x, y, delta, z
-    total = b * L * D * per_tc + 2 * b * L * N * e + D * N * 4 + 3 * D * 4
+    per_channel = (1 if cfg["skip"] else 0) + (1 if cfg["dt"] == "softplus_bias" else 0)   # Dskip, delta bias
+    total = b * L * D * per_tc + 2 * b * L * N * e + D * N * 4 + per_channel * D * 4
     if cfg.get("final_state"):
         total += b * D * N * 4
     return total
