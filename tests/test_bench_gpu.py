@@ -2,33 +2,32 @@
 around resident inputs that do not fit the last-level cache (achieved bandwidth stays below a plain
 copy's), and the measured unit rates it reports are physically plausible."""
 import json
-import os
-import subprocess
 import sys
 
 import pytest
 
+import bench
+
 pytestmark = pytest.mark.gpu
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+def run_bench(capsys, monkeypatch, *args):
+    """bench.main() in this process (no second process on the GPU), returning its last JSON line."""
+    monkeypatch.setattr(sys, "argv", ["bench.py", *args])
+    capsys.readouterr()
+    bench.main()
+    return json.loads(capsys.readouterr().out.strip().splitlines()[-1])
 
 
-def run_bench(*args):
-    r = subprocess.run([sys.executable, "-u", os.path.join(ROOT, "bench.py"), *args], capture_output=True, text=True,
-                       timeout=600, cwd=ROOT)
-    assert r.returncode == 0, r.stderr[-2000:]
-    return json.loads(r.stdout.strip().splitlines()[-1])
-
-
-def test_bench_line_contract_and_cache_flush():
-    d = run_bench("--no-others", "--no-cpu-baseline", "--steps", "10", "--warmup", "3")
+def test_bench_line_contract_and_cache_flush(capsys, monkeypatch):
+    d = run_bench(capsys, monkeypatch, "--no-others", "--no-cpu-baseline", "--steps", "10", "--warmup", "3")
     for k in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better", "scaling",
               "vs_baseline", "dtype", "data", "config", "roofline"):
         assert k in d, k
     assert d["n_gpus"] == 1 and d["steps"] == 10 and d["warmup"] == 3 and d["config"]["workload"]
     rl = d["roofline"]
     assert rl["bound"] == "alu" and 0 < rl["frac"] <= 1 and abs(rl["achieved"] / rl["peak"] - rl["frac"]) < 1e-3
-    mb = run_bench("--only", "ubench")
+    mb = run_bench(capsys, monkeypatch, "--only", "ubench")
     # six rotating input copies: the achieved algorithmic bandwidth cannot exceed a plain HBM copy's
     assert d["hbm"]["achieved_GBs"] < mb["copy_GBs_read_plus_write"]
     # measured rates below the published unit peaks, exp at about half the FMA rate
