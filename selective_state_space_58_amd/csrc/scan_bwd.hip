@@ -83,9 +83,13 @@ __device__ __forceinline__ float reduce4_rows(const float (&p)[4]) {
 }
 
 // Sum over the 4 lanes of a quad (the 4 channels of a row); every lane gets it.
+// The empty asm hides where v came from, so the compiler cannot fuse the
+// product that feeds v into the first add (an FMA cannot take a DPP source):
+// each level stays one v_add_f32 with a DPP source.
 __device__ __forceinline__ float quad_sum(float v) {
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xf, 0xf, false));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xf, 0xf, false));
+  asm("" : "+v"(v));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xf, 0xf, true));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xf, 0xf, true));
   return v;
 }
 
@@ -205,7 +209,7 @@ __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64
     // recompute the tile's states and decays (into LDS) and its readout; y gives dz and dy
     const float hstart = nok ? a.ws_ckpt[(int64_t)k * slice + hidx] : 0.f;
     float hs = hstart;
-#pragma unroll 1
+#pragma unroll
     for (int tb = 0; tb < BT; tb += BG) {
       float pr[BG];
 #pragma unroll
@@ -238,7 +242,7 @@ __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64
     }
     __syncthreads();
     // adjoint, tokens in reverse, in groups of 4 for the row reductions
-#pragma unroll 1
+#pragma unroll 2
     for (int tb = BT - BG; tb >= 0; tb -= BG) {
     float pdx[BG], pdt[BG];
 #pragma unroll
