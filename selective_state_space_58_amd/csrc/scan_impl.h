@@ -440,6 +440,17 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
     if (t0 + T < t_stop) fetch(t0 + T);
     const int64_t nvalid = t_stop - t0;
     TX* yb = gy + (b * L + grow0(t0)) * dim + ch0;   // uniform
+    const bool full_tile = ch_ok && nvalid >= T;       // uniform on the vector path
+    const int nval32 = nvalid < T ? (int)nvalid : T;
+    // Readout of the group of R tokens starting at tg: row r gets token tg + r.
+    auto emit = [&](int tg, const float (&pr)[R]) {
+      const float tot = reduce_scatter_rows<R>(pr);
+      const int tl = tg + r;
+      const float xv = s_dx[tl * WCH + wc].y;
+      const float yv = fmaf(Dv, xv, tot) * s_gz[tl * WCH + wc];
+      if (full_tile || (ch_ok && tl < nval32)) yb[urow(tl) * dim32 + (uint32_t)c] = (TX)yv;
+    };
+    if constexpr (S < 16) {
     // Operands of one step of U = 4 tokens: (dt, x) and this row's B/C
     // slices.  The next step's operands are read from LDS while the current
     // step is computed, so LDS latency overlaps the VALU work; a group of R
@@ -484,12 +495,8 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
         for (int s = 0; s < S; ++s) E[j][s] = hw_exp2(g.dx[j].x * a2[s]);
     };
     step_exp(cur, Ecur);
-    const bool full_tile = ch_ok && nvalid >= T;       // uniform on the vector path
-    const int nval32 = nvalid < T ? (int)nvalid : T;
     float pr[R];
-    // full unroll for small S; wide S (N > 32) keeps the loop to bound code size
-    constexpr int kStepUnroll = (S <= 8) ? T / U : 2;
-    static_assert(R == U || kStepUnroll == T / U, "rows beyond one step need the fully unrolled loop");
+    constexpr int kStepUnroll = T / U;   // full unroll: static register indices
 #pragma unroll kStepUnroll
     for (int tb = 0; tb < T; tb += U) {
       if (tb + U < T) {
@@ -512,19 +519,51 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
         pr[R == U ? j : (tb + j) % R] = acc;   // static index: R == U, or the loop is fully unrolled
         if (!FULL) dsum += dx.x;
       }
-      if (FULL && (R == U || (tb + U) % R == 0)) {
-        const float tot = reduce_scatter_rows<R>(pr);
-        const int tl = tb + U - R + r;
-        const float xv = s_dx[tl * WCH + wc].y;
-        const float yv = fmaf(Dv, xv, tot) * s_gz[tl * WCH + wc];
-        if (full_tile || (ch_ok && tl < nval32)) yb[urow(tl) * dim32 + (uint32_t)c] = (TX)yv;
-      }
+      if (FULL && (R == U || (tb + U) % R == 0)) emit(tb + U - R, pr);
       if (tb + U < T) {
         cur = nxt;
 #pragma unroll
         for (int j = 0; j < U; ++j)
 #pragma unroll
           for (int s = 0; s < S; ++s) Ecur[j][s] = Enxt[j][s];
+      }
+    }
+    } else {
+      // Wide lanes (16 or 32 states, 4 rows): one token at a time, operands
+      // read and exponentials taken as they are used.  The S independent
+      // state chains of a token cover the exp and LDS latencies; staging a
+      // step ahead would hold 8S registers per lane and spill.
+      static_assert(R == 4, "wide lanes use the 4-row layout");
+#pragma unroll 1
+      for (int tb = 0; tb < T; tb += R) {
+        float pr[R];
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+          const int tt = tb + j;
+          const float2 dx = s_dx[tt * WCH + wc];
+          const float4* bc4 = reinterpret_cast<const float4*>(s_bc + ((tt * R + r) * 2) * S);
+          float acc = 0.f;
+#pragma unroll
+          for (int q = 0; q < S / 4; ++q) {
+            const float4 vb = bc4[q];
+            const float4 vc = FULL ? bc4[S / 4 + q] : make_float4(0.f, 0.f, 0.f, 0.f);
+            const float bq[4] = {vb.x, vb.y, vb.z, vb.w};
+            const float cq[4] = {vc.x, vc.y, vc.z, vc.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int st = 4 * q + e;
+              const float E = hw_exp2(dx.x * a2[st]);
+              const float g = GAIN == kGainEuler      ? dx.x
+                              : GAIN == kGainAccurate ? zoh_gain_accurate(E, dx.x, av[st], ia[st])
+                                                      : fmaf(E, ia[st], -ia[st]);
+              h[st] = fmaf(E, h[st], g * (bq[e] * dx.y));
+              if (FULL) acc = fmaf(cq[e], h[st], acc);
+            }
+          }
+          pr[j] = acc;
+          if (!FULL) dsum += dx.x;
+        }
+        if (FULL) emit(tb, pr);
       }
     }
   }
