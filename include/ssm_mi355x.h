@@ -291,13 +291,15 @@ int ssm_causal_conv1d_fwd(const void* x, const float* weight, const float* bias,
  *   dz          : (batch, seqlen, dim) act dtype, required when z is given
  *   ddelta_bias : (dim) fp32, required when delta_bias is given
  *   dh0         : (batch, dim, dstate) fp32 or NULL
- * dstate 1..16.  dB and dC are summed over channels in a fixed order (per
+ * dstate 1..128 (one pass over the sequence per 16 states).  dB and dC are
+ * summed over channels in a fixed order (per
  * 16-channel group, then over the groups), so they are deterministic; the
  * sums over channels and batch of dA, and over batch of dDskip and
  * ddelta_bias, use fp32 atomics, so their last bits vary from run to run.
- * Workspace: ssm_scan_bwd_workspace_bytes() (the states at every 16-token
- * tile start, and the dB/dC partials of every 16-channel group), or NULL for
- * stream-ordered scratch.
+ * Workspace: ssm_scan_bwd_workspace_bytes() (the states of a block of 16 at
+ * every 16-token tile start, the dB/dC partials of every 16-channel group,
+ * and for dstate > 16 three fp32 accumulators of batch x seqlen x dim), or
+ * NULL for stream-ordered scratch.
  */
 int ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
                  const float* Dskip, const void* z, const float* delta_bias, int delta_softplus,

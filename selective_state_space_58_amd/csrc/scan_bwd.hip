@@ -10,7 +10,7 @@
 // with E = exp(dt a), g = (E - 1)/a, dy = dout * silu(z).
 //
 // Mapping: the forward's 16-row lane layout (lane = state n x 4 channels, one
-// state per lane, dstate <= 16) with four waves per workgroup covering 16
+// state per lane, 16 states per pass) with four waves per workgroup covering 16
 // consecutive channels of one batch row, which share the staged tiles.  A
 // forward pass stores the state at the start of every 16-token tile in the
 // workspace; the reverse pass then walks the tiles from the last, recomputes
@@ -23,7 +23,15 @@
 // second kernel adds the partials of the workgroups of a batch row (no
 // atomics on the per-token gradients).  dA, Dskip and bias gradients are
 // summed in registers and added once per wave.
+//
+// More than 16 states: given dy, the adjoint of each state is independent of
+// the others, and the per-(token, channel) gradients (dx, ddt, dz) are sums
+// over the states.  The pass therefore runs once per block of 16 states (in
+// stream order), each adding its contribution to fp32 accumulators, and the
+// last block writes the outputs; the skip terms enter with the first block.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "scan_impl.h"
 #include "ssm_internal.h"
@@ -98,18 +106,24 @@ __global__ __launch_bounds__(256) void bwd_zero_kernel(float* p, int64_t n) {
   if (i < n) p[i] = 0.f;
 }
 
-// dB, dC = sums of the per-workgroup partials of each batch row.
+// dB, dC of states n0 .. n0+width-1 = sums of the per-workgroup partials of
+// each batch row (partials laid out (group, batch * token, 16)).
 __global__ __launch_bounds__(256) void bwd_sum_partials_kernel(const float* part_b, const float* part_c, float* dB,
-                                                               float* dC, int64_t per_group, int64_t groups) {
+                                                               float* dC, int64_t rows, int64_t groups, int64_t N,
+                                                               int64_t n0, int width) {
   const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (i >= per_group) return;
+  if (i >= rows * width) return;
+  const int64_t bt = i / width;
+  const int nl = (int)(i - bt * width);
+  const int64_t per_group = rows * BR;
+  const int64_t o = bt * BR + nl;
   float sb = 0.f, sc = 0.f;
   for (int64_t g = 0; g < groups; ++g) {
-    sb += part_b[g * per_group + i];
-    sc += part_c[g * per_group + i];
+    sb += part_b[g * per_group + o];
+    sc += part_c[g * per_group + o];
   }
-  dB[i] = sb;
-  dC[i] = sc;
+  dB[bt * N + n0 + nl] = sb;
+  dC[bt * N + n0 + nl] = sc;
 }
 
 struct BwdLds {
@@ -124,7 +138,8 @@ struct BwdLds {
   float red[BW * BT * BR * 2];  // per-wave (dB, dC) partial per (token, state)
 };
 
-template <bool XB, bool DB, bool ACC>
+// MULTI: more than one block of 16 states (per-token gradients accumulated).
+template <bool XB, bool DB, bool ACC, bool MULTI>
 __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64_t chw0, int64_t grp, float av,
                                               float a2, float ia, bool nok, BwdLds& sm) {
   using RX = typename Raw<XB>::T;
@@ -139,10 +154,14 @@ __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64
   const int64_t ch = chw0 + wc;
   const bool ch_ok = ch < dim;
   const int ntile = (int)((L + BT - 1) / BT);
-  const int64_t slice = a.batch * dim * N;
-  const int64_t hidx = (b * dim + ch) * N + r;   // this lane's state (valid when nok)
+  const int64_t n0 = a.n0;                       // first state of this block of 16
+  const int64_t hidx = (b * dim + ch) * N + n0 + r;   // this lane's state (valid when nok)
+  const int64_t slice = a.batch * dim * BR;      // one checkpoint of the block's states
+  const int64_t cidx = (b * dim + ch) * BR + r;
+  const int64_t tcd = a.batch * L * dim;         // token-channel elements of one accumulator
 
-  const float Dv = (a.Dskip != nullptr && ch_ok) ? a.Dskip[ch] : 0.f;
+  // the skip term and the Dskip gradient belong to the first block of states only
+  const float Dv = (a.Dskip != nullptr && ch_ok && a.first) ? a.Dskip[ch] : 0.f;
   const RX* gx = (const RX*)a.x;
   const RD* gd = (const RD*)a.delta;
   const RX* gz = (const RX*)a.z;
@@ -171,17 +190,32 @@ __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64
     {
       const int tl = tid / BR, n = tid % BR;
       const int64_t t = t0 + tl;
-      const bool ok = t < L && n < N;
-      const int64_t i = (b * L + (t < L ? t : L - 1)) * N + (n < N ? n : 0);
+      const bool ok = t < L && n0 + n < N;
+      const int64_t i = (b * L + (t < L ? t : L - 1)) * N + (n0 + n < N ? n0 + n : 0);
       sm.bc[(tl * BR + n) * 2] = ok ? Raw<XB>::f32(gB[i]) : 0.f;
       if (full) sm.bc[(tl * BR + n) * 2 + 1] = ok ? Raw<XB>::f32(gC[i]) : 0.f;
     }
+  };
+  // Per (token, channel) gradient k (0 dx, 1 ddelta, 2 dz) at element i: written
+  // directly with one block of states; with several, summed in an fp32
+  // accumulator (each element by the same lane in every block, blocks in
+  // stream order) and converted after the last block.
+  auto put = [&](int k, int64_t i, float v, auto* out) {
+    using T = typename std::remove_pointer<decltype(out)>::type;
+    if constexpr (!MULTI) {
+      out[i] = (T)v;
+      return;
+    }
+    float* p = a.acc + k * tcd + i;
+    const float sum = a.first ? v : *p + v;
+    if (a.last) out[i] = (T)sum;
+    else *p = sum;
   };
 
   // ---- forward: the state at the start of every tile into the workspace
   float h = (a.h0 != nullptr && nok) ? a.h0[hidx] : 0.f;
   for (int k = 0; k < ntile; ++k) {
-    if (nok) a.ws_ckpt[(int64_t)k * slice + hidx] = h;
+    if (nok) a.ws_ckpt[(int64_t)k * slice + cidx] = h;
     __syncthreads();
     stage(k, false);
     __syncthreads();
@@ -200,14 +234,14 @@ __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64
   float* hw = sm.h + w * BT * 64;
   float* ew = sm.E + w * BT * 64;
   float* rw = sm.red + w * BT * BR * 2;
-  const int64_t per_group = a.batch * L * N;
+  const int64_t per_group = a.batch * L * BR;
   for (int k = ntile - 1; k >= 0; --k) {
     const int64_t t0 = (int64_t)k * BT;
     __syncthreads();
     stage(k, true);
     __syncthreads();
     // recompute the tile's states and decays (into LDS) and its readout; y gives dz and dy
-    const float hstart = nok ? a.ws_ckpt[(int64_t)k * slice + hidx] : 0.f;
+    const float hstart = nok ? a.ws_ckpt[(int64_t)k * slice + cidx] : 0.f;
     float hs = hstart;
 #pragma unroll
     for (int tb = 0; tb < BT; tb += BG) {
@@ -235,7 +269,7 @@ __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64
           const float sg = sigmoid_f(zz);
           dy = dout * zz * sg;
           if (ch_ok && t0 + tl < L)
-            ((TX*)a.dz)[(b * L + t0 + tl) * dim + ch] = (TX)(dout * y * (sg + zz * sg * (1.f - sg)));
+            put(2, (b * L + t0 + tl) * dim + ch, dout * y * (sg + zz * sg * (1.f - sg)), (TX*)a.dz);
         }
         sm.dy[e] = dy;
       }
@@ -278,9 +312,9 @@ __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64
       const float dy = sm.dy[e];
       const float dv = a.softplus ? tdt * sigmoid_f(sm.v[e]) : tdt;
       const int64_t i = (b * L + t0 + tl) * dim + ch;
-      ((TX*)a.dx)[i] = (TX)fmaf(Dv, dy, tdx);
-      ((TD*)a.ddelta)[i] = (TD)dv;
-      dDacc = fmaf(dy, sm.dx[e].y, dDacc);
+      put(0, i, fmaf(Dv, dy, tdx), (TX*)a.dx);
+      put(1, i, dv, (TD*)a.ddelta);
+      if (a.first) dDacc = fmaf(dy, sm.dx[e].y, dDacc);
       dbacc += dv;
     }
     }
@@ -288,14 +322,14 @@ __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64
     // dB, dC partial of this workgroup: sum of the 4 waves
     {
       const int tl = tid / BR, n = tid % BR;
-      if (t0 + tl < L && n < N) {
+      if (t0 + tl < L && n0 + n < N) {
         float sb = 0.f, sc = 0.f;
 #pragma unroll
         for (int q = 0; q < BW; ++q) {
           sb += sm.red[((q * BT + tl) * BR + n) * 2];
           sc += sm.red[((q * BT + tl) * BR + n) * 2 + 1];
         }
-        const int64_t o = grp * per_group + (b * L + t0 + tl) * N + n;
+        const int64_t o = grp * per_group + (b * L + t0 + tl) * BR + n;
         a.ws_part[o] = sb;
         a.ws_part[(int64_t)a.ws_groups * per_group + o] = sc;
       }
@@ -305,7 +339,7 @@ __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64
   // ---- per-wave sums: dh0, dA per lane; Dskip and bias gradients summed over the 16 rows
   if (nok) {
     if (a.dh0 != nullptr) a.dh0[hidx] = lam;
-    atomicAdd(a.dA + ch * N + r, dA);
+    atomicAdd(a.dA + ch * N + n0 + r, dA);
   }
 #pragma unroll
   for (int o = 4; o < 64; o <<= 1) {
@@ -319,7 +353,7 @@ __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64
 }
 
 // One workgroup of four waves per 16 channels of a batch row.
-template <bool XB, bool DB>
+template <bool XB, bool DB, bool MULTI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void scan_bwd_kernel(BwdArgs a,
                                                                                               int64_t wgs_per_batch) {
   const int tid = threadIdx.x;
@@ -332,31 +366,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
   const int64_t grp = lin % wgs_per_batch;
   const int64_t chw0 = grp * BWC;
   const int64_t ch = chw0 + w * BCH + c;
-  const bool nok = ch < a.dim && r < a.dstate;
-  const float av = nok ? a.A[ch * a.dstate + r] : -1.f;
+  const bool nok = ch < a.dim && a.n0 + r < a.dstate;
+  const float av = nok ? a.A[ch * a.dstate + a.n0 + r] : -1.f;
   const float a2 = av * kLog2e, ia = 1.f / av;
   const bool tiny = !(fabsf(av) >= 1e-2f);
   __shared__ __attribute__((aligned(16))) BwdLds lds;
-  if (!XB || __syncthreads_or(tiny)) scan_bwd_body<XB, DB, true>(a, b, chw0, grp, av, a2, ia, nok, lds);
-  else scan_bwd_body<XB, DB, false>(a, b, chw0, grp, av, a2, ia, nok, lds);
+  if (!XB || __syncthreads_or(tiny)) scan_bwd_body<XB, DB, true, MULTI>(a, b, chw0, grp, av, a2, ia, nok, lds);
+  else scan_bwd_body<XB, DB, false, MULTI>(a, b, chw0, grp, av, a2, ia, nok, lds);
 }
 
 template <bool XB, bool DB>
 hipError_t launch_bwd_xd(const BwdArgs& a, dim3 grid, int64_t wgs, hipStream_t st) {
-  scan_bwd_kernel<XB, DB><<<grid, 256, 0, st>>>(a, wgs);
+  if (a.acc != nullptr) scan_bwd_kernel<XB, DB, true><<<grid, 256, 0, st>>>(a, wgs);
+  else scan_bwd_kernel<XB, DB, false><<<grid, 256, 0, st>>>(a, wgs);
   return hipGetLastError();
 }
 
-size_t ckpt_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
+// Workspace: the states of one block of 16 at every tile start, the dB/dC
+// partials of one block, and (dstate > 16) the three fp32 accumulators.
+size_t ckpt_bytes(int64_t batch, int64_t seqlen, int64_t dim) {
   const int64_t ntile = (seqlen + BT - 1) / BT;
-  return ((size_t)(ntile * batch * dim * dstate) * sizeof(float) + 255) / 256 * 256;
+  return ((size_t)(ntile * batch * dim * BR) * sizeof(float) + 255) / 256 * 256;
+}
+size_t part_bytes(int64_t batch, int64_t seqlen, int64_t dim) {
+  const int64_t groups = (dim + BWC - 1) / BWC;
+  return ((size_t)(2 * groups * batch * seqlen * BR) * sizeof(float) + 255) / 256 * 256;
 }
 
 }  // namespace
 
 size_t scan_bwd_ws_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
-  const int64_t groups = (dim + BWC - 1) / BWC;
-  return ckpt_bytes(batch, seqlen, dim, dstate) + (size_t)(2 * groups * batch * seqlen * dstate) * sizeof(float);
+  const size_t acc = dstate > BR ? (size_t)(3 * batch * seqlen * dim) * sizeof(float) : 0;
+  return ckpt_bytes(batch, seqlen, dim) + part_bytes(batch, seqlen, dim) + acc;
 }
 
 int launch_scan_bwd(const BwdArgs& a0, void* stream) {
@@ -372,26 +413,38 @@ int launch_scan_bwd(const BwdArgs& a0, void* stream) {
   if (e == hipSuccess) e = zero(a.dDskip, a.dim);
   if (e == hipSuccess) e = zero(a.ddelta_bias, a.dim);
   if (e != hipSuccess) return fail(6, std::string("backward clear: ") + hipGetErrorString(e));
-  if (a.dstate > BR) return fail(4, "the backward pass supports dstate <= 16");
   const int64_t wgs = (a.dim + BWC - 1) / BWC;
   const int64_t nb = a.batch * wgs;
   if (nb > 0x7fffffffLL) return fail(4, "grid too large");
   a.ws_groups = wgs;
-  a.ws_part = a.ws_ckpt != nullptr
-                  ? (float*)((char*)a.ws_ckpt + ckpt_bytes(a.batch, a.seqlen, a.dim, a.dstate))
-                  : nullptr;
+  a.ws_part = nullptr;
+  a.acc = nullptr;
+  if (a.ws_ckpt != nullptr) {
+    char* base = (char*)a.ws_ckpt;
+    a.ws_part = (float*)(base + ckpt_bytes(a.batch, a.seqlen, a.dim));
+    if (a.dstate > BR)
+      a.acc = (float*)(base + ckpt_bytes(a.batch, a.seqlen, a.dim) + part_bytes(a.batch, a.seqlen, a.dim));
+  }
   const dim3 grid((unsigned)nb);
-  if (a.act_bf16 && a.delta_bf16) e = launch_bwd_xd<true, true>(a, grid, wgs, st);
-  else if (a.act_bf16) e = launch_bwd_xd<true, false>(a, grid, wgs, st);
-  else if (a.delta_bf16) e = launch_bwd_xd<false, true>(a, grid, wgs, st);
-  else e = launch_bwd_xd<false, false>(a, grid, wgs, st);
-  if (e != hipSuccess) return fail(6, std::string("backward launch: ") + hipGetErrorString(e));
-  const int64_t per_group = a.batch * a.seqlen * a.dstate;
-  if (per_group > 0) {
-    bwd_sum_partials_kernel<<<dim3((unsigned)((per_group + 255) / 256)), 256, 0, st>>>(
-        a.ws_part, a.ws_part + wgs * per_group, a.dB, a.dC, per_group, wgs);
-    e = hipGetLastError();
-    if (e != hipSuccess) return fail(6, std::string("backward partial sums: ") + hipGetErrorString(e));
+  const int64_t rows = a.batch * a.seqlen;
+  // the states are independent given dy: one pass per block of 16, in stream order
+  for (int64_t n0 = 0; n0 < a.dstate; n0 += BR) {
+    a.n0 = n0;
+    a.first = n0 == 0;
+    a.last = n0 + BR >= a.dstate;
+    if (a.act_bf16 && a.delta_bf16) e = launch_bwd_xd<true, true>(a, grid, wgs, st);
+    else if (a.act_bf16) e = launch_bwd_xd<true, false>(a, grid, wgs, st);
+    else if (a.delta_bf16) e = launch_bwd_xd<false, true>(a, grid, wgs, st);
+    else e = launch_bwd_xd<false, false>(a, grid, wgs, st);
+    if (e != hipSuccess) return fail(6, std::string("backward launch: ") + hipGetErrorString(e));
+    if (rows > 0) {
+      const int width = (int)(a.dstate - n0 < BR ? a.dstate - n0 : BR);
+      const int64_t items = rows * width;
+      bwd_sum_partials_kernel<<<dim3((unsigned)((items + 255) / 256)), 256, 0, st>>>(
+          a.ws_part, a.ws_part + wgs * rows * BR, a.dB, a.dC, rows, wgs, a.dstate, n0, width);
+      e = hipGetLastError();
+      if (e != hipSuccess) return fail(6, std::string("backward partial sums: ") + hipGetErrorString(e));
+    }
   }
   return 0;
 }

@@ -84,8 +84,11 @@ struct BwdArgs {
   float* ddelta_bias;      // (dim) or null
   float* dh0;              // (batch, dim, dstate) or null
   float* ws_ckpt;          // (ntiles, batch, dim, dstate) states at tile starts
-  float* ws_part;          // 2 x (groups, batch, seqlen, dstate) dB, dC partials of the channel groups
+  float* ws_part;          // 2 x (groups, batch, seqlen, 16) dB, dC partials of the channel groups
   int64_t ws_groups;       // channel groups (workgroups per batch row)
+  float* acc;              // 3 x (batch, seqlen, dim) fp32: dx, ddelta, dz summed over state blocks (dstate > 16)
+  int64_t n0;              // first state of the block of 16 this pass handles
+  int first, last;         // first / last block of states
   int64_t batch, seqlen, dim, dstate;
   int softplus;
   int act_bf16, delta_bf16;

@@ -240,7 +240,7 @@ def bwd(lib, **kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(dout=None), 1), (dict(dx=None), 1), (dict(ddelta=None), 1), (dict(dA=None), 1), (dict(dB=None), 1),
     (dict(z=P), 1), (dict(D=P), 1), (dict(bias=P), 1), (dict(seqlen=-1), 2), (dict(act=3), 3),
-    (dict(dstate=17), 4), (dict(dx=P + 0x100001), 7), (dict(dA=P + 0x100002), 7),
+    (dict(dstate=129), 4), (dict(dx=P + 0x100001), 7), (dict(dA=P + 0x100002), 7),
 ])
 def test_scan_bwd_argument_errors(kw, code):
     lib = _lib()
@@ -253,6 +253,10 @@ def test_scan_bwd_workspace_query():
     # states at the start of each of the 7 16-token tiles (rounded up to 256 bytes), then the dB and dC
     # partials of the 3 groups of 16 channels per token and state
     ckpt = (7 * 2 * 40 * 16 * 4 + 255) // 256 * 256
-    assert lib.ssm_scan_bwd_workspace_bytes(2, 100, 40, 16) == ckpt + 2 * 3 * 2 * 100 * 16 * 4
-    assert lib.ssm_scan_bwd_workspace_bytes(2, 100, 40, 17) == 0
+    part = (2 * 3 * 2 * 100 * 16 * 4 + 255) // 256 * 256
+    assert lib.ssm_scan_bwd_workspace_bytes(2, 100, 40, 16) == ckpt + part
+    # more than 16 states: the same per-block buffers plus three fp32 accumulators of dx, ddelta, dz
+    assert lib.ssm_scan_bwd_workspace_bytes(2, 100, 40, 17) == ckpt + part + 3 * 2 * 100 * 40 * 4
+    assert lib.ssm_scan_bwd_workspace_bytes(2, 100, 40, 128) == ckpt + part + 3 * 2 * 100 * 40 * 4
+    assert lib.ssm_scan_bwd_workspace_bytes(2, 100, 40, 129) == 0
     assert bwd(lib, batch=0) == 0

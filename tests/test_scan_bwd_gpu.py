@@ -71,6 +71,17 @@ def test_scan_bwd_shapes(ssm, dtype, shape):
     check(ssm, inp, "bwd %s %s" % (dtype, shape))
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(2, 70, 40, 17), (1, 100, 32, 32), (2, 53, 24, 64), (1, 40, 20, 100),
+                                   (1, 33, 16, 128)])
+def test_scan_bwd_more_states(ssm, dtype, shape):
+    # one pass per block of 16 states, the per-token gradients summed over the blocks
+    b, L, D, N = shape
+    inp = workloads.scan_inputs(b, L, D, N, dtype=dtype, seed=sum(shape) + 17, dt="softplus_bias", gate=True,
+                                softplus=True, skip=True, h0=True)
+    check(ssm, inp, "bwd %s %s" % (dtype, shape))
+
+
 @pytest.mark.parametrize("flags", [dict(gate=False, softplus=False, skip=False, h0=False),
                                    dict(gate=True, softplus=False, skip=False, h0=False),
                                    dict(gate=False, softplus=True, skip=True, h0=True)])
