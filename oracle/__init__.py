@@ -62,6 +62,8 @@ def _load():
             lib.oracle_lti_conv.restype = None
             lib.oracle_selective_scan_bwd.argtypes = [P] * 8 + [I] + [P] * 12 + [I64] * 6
             lib.oracle_selective_scan_bwd.restype = None
+            lib.oracle_selective_scan_bwd_euler.argtypes = [P] * 8 + [I] + [P] * 12 + [I64] * 6
+            lib.oracle_selective_scan_bwd_euler.restype = None
             lib.oracle_causal_conv1d.argtypes = [P] * 4 + [I, P, P] + [I64] * 6
             lib.oracle_causal_conv1d.restype = None
             _lib = lib
@@ -131,10 +133,21 @@ def selective_scan(x, delta, A, B, C, Dskip=None, z=None, delta_bias=None,
 
 
 def selective_scan_bwd(x, delta, A, B, C, dout, Dskip=None, z=None, delta_bias=None, delta_softplus=False,
-                       h0=None, dh_final=None, threads=None):
+                       h0=None, dh_final=None, threads=None, euler=False, reverse=False):
     """O5: gradients of sum(dout * y) + sum(dh_final * h_final) for O1, float64.  Returns a dict with
     dx, ddelta, dA, dB, dC and, for the optional inputs given, dDskip, dz, ddelta_bias, dh0.
-    Threads accumulate the shared gradients (dA, dB, dC, dDskip, ddelta_bias) in private buffers."""
+    Threads accumulate the shared gradients (dA, dB, dC, dDskip, ddelta_bias) in private buffers.
+    euler: the gradient of O1e (O5e).  reverse: the gradient of the reversed scan flip(scan(flip)), by
+    definition the flipped gradients of the scan of the flipped inputs."""
+    if reverse:
+        flip = lambda a: None if a is None else np.ascontiguousarray(np.flip(np.asarray(a, dtype=np.float64), 1))
+        g = selective_scan_bwd(flip(x), flip(delta), A, flip(B), flip(C), flip(dout), Dskip=Dskip, z=flip(z),
+                               delta_bias=delta_bias, delta_softplus=delta_softplus, h0=h0, dh_final=dh_final,
+                               threads=threads, euler=euler)
+        for k in ("dx", "ddelta", "dB", "dC", "dz"):
+            if k in g:
+                g[k] = flip(g[k])
+        return g
     x = _f64(x)
     batch, seqlen, dim = x.shape
     A = _f64(A)
@@ -161,7 +174,8 @@ def selective_scan_bwd(x, delta, A, B, C, dout, Dskip=None, z=None, delta_bias=N
 
     def run(i):
         a = acc[i]
-        lib.oracle_selective_scan_bwd(
+        fn = lib.oracle_selective_scan_bwd_euler if euler else lib.oracle_selective_scan_bwd
+        fn(
             _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(z), _ptr(delta_bias),
             int(bool(delta_softplus)), _ptr(h0), _ptr(dout), _ptr(dh_final), _ptr(dx), _ptr(ddelta), _ptr(a["dA"]),
             _ptr(a["dB"]), _ptr(a["dC"]), _ptr(a["dD"]) if Dskip is not None else None, _ptr(dz),

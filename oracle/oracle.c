@@ -369,14 +369,14 @@ static double zoh_gain_da(double dt, double a) {
  *   dA_n += dE E dt + dg dg/da;
  *   lam_n *= E
  */
-void oracle_selective_scan_bwd(const double* x, const double* delta, const double* A,
-                               const double* B, const double* C, const double* Dskip,
-                               const double* z, const double* delta_bias, int delta_softplus,
-                               const double* h0, const double* dout, const double* dh_final,
-                               double* dx, double* ddelta, double* dA, double* dB, double* dC,
-                               double* dDskip, double* dz, double* ddelta_bias, double* dh0,
-                               int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
-                               int64_t s_begin, int64_t s_end) {
+static void selective_scan_bwd_impl(const double* x, const double* delta, const double* A,
+                                    const double* B, const double* C, const double* Dskip,
+                                    const double* z, const double* delta_bias, int delta_softplus,
+                                    const double* h0, const double* dout, const double* dh_final,
+                                    double* dx, double* ddelta, double* dA, double* dB, double* dC,
+                                    double* dDskip, double* dz, double* ddelta_bias, double* dh0,
+                                    int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                                    int64_t s_begin, int64_t s_end, int euler) {
   (void)batch;
   size_t nh = (size_t)((seqlen + 1) * dstate > 0 ? (seqlen + 1) * dstate : 1);
   double* hs = (double*)malloc(sizeof(double) * nh);       /* h_t for t = -1 .. L-1 */
@@ -395,7 +395,8 @@ void oracle_selective_scan_bwd(const double* x, const double* delta, const doubl
       double acc = 0.0;
       for (int64_t n = 0; n < dstate; ++n) {
         double a = A[d * dstate + n];
-        double h = exp(dt * a) * hs[t * dstate + n] + zoh_gain(dt, a) * B[r + n] * x[i];
+        double g = euler ? dt : zoh_gain(dt, a);
+        double h = exp(dt * a) * hs[t * dstate + n] + g * B[r + n] * x[i];
         hs[(t + 1) * dstate + n] = h;
         acc += C[r + n] * h;
       }
@@ -416,15 +417,16 @@ void oracle_selective_scan_bwd(const double* x, const double* delta, const doubl
       double dt = dts[t], ddt = 0.0;
       for (int64_t n = 0; n < dstate; ++n) {
         double a = A[d * dstate + n];
-        double E = exp(dt * a), g = zoh_gain(dt, a);
+        double E = exp(dt * a), g = euler ? dt : zoh_gain(dt, a);
         lam[n] += C[r + n] * dy;
         dC[r + n] += hs[(t + 1) * dstate + n] * dy;
         double dE = lam[n] * hs[t * dstate + n];
         double dg = lam[n] * B[r + n] * x[i];
         dB[r + n] += lam[n] * g * x[i];
         dxi += lam[n] * g * B[r + n];
-        ddt += dE * E * a + dg * E;
-        dA[d * dstate + n] += dE * E * dt + dg * zoh_gain_da(dt, a);
+        /* dg/ddt: E for ZOH, 1 for Euler; dg/da: zoh_gain_da for ZOH, 0 for Euler */
+        ddt += dE * E * a + dg * (euler ? 1.0 : E);
+        dA[d * dstate + n] += dE * E * dt + (euler ? 0.0 : dg * zoh_gain_da(dt, a));
         lam[n] *= E;
       }
       dx[i] = dxi;
@@ -440,4 +442,32 @@ void oracle_selective_scan_bwd(const double* x, const double* delta, const doubl
   free(dts);
   free(ys);
   free(lam);
+}
+
+void oracle_selective_scan_bwd(const double* x, const double* delta, const double* A,
+                               const double* B, const double* C, const double* Dskip,
+                               const double* z, const double* delta_bias, int delta_softplus,
+                               const double* h0, const double* dout, const double* dh_final,
+                               double* dx, double* ddelta, double* dA, double* dB, double* dC,
+                               double* dDskip, double* dz, double* ddelta_bias, double* dh0,
+                               int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                               int64_t s_begin, int64_t s_end) {
+  selective_scan_bwd_impl(x, delta, A, B, C, Dskip, z, delta_bias, delta_softplus, h0, dout, dh_final, dx,
+                          ddelta, dA, dB, dC, dDskip, dz, ddelta_bias, dh0, batch, seqlen, dim, dstate, s_begin,
+                          s_end, 0);
+}
+
+/* O5e. The gradient of O1e (Euler input discretization, gain dt): the same
+ * adjoint with dg/ddt = 1 and dg/da = 0. */
+void oracle_selective_scan_bwd_euler(const double* x, const double* delta, const double* A,
+                                     const double* B, const double* C, const double* Dskip,
+                                     const double* z, const double* delta_bias, int delta_softplus,
+                                     const double* h0, const double* dout, const double* dh_final,
+                                     double* dx, double* ddelta, double* dA, double* dB, double* dC,
+                                     double* dDskip, double* dz, double* ddelta_bias, double* dh0,
+                                     int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                                     int64_t s_begin, int64_t s_end) {
+  selective_scan_bwd_impl(x, delta, A, B, C, Dskip, z, delta_bias, delta_softplus, h0, dout, dh_final, dx,
+                          ddelta, dA, dB, dC, dDskip, dz, ddelta_bias, dh0, batch, seqlen, dim, dstate, s_begin,
+                          s_end, 1);
 }

@@ -287,16 +287,20 @@ def test_causal_conv1d_impulse_and_state_handoff(oracle_mod):
     assert np.array_equal(st_full, np.transpose(x[:, L - (W - 1):, :], (0, 2, 1)))
 
 
-def _scan_loss(oracle_mod, p, dout, dh_final, softplus):
+def _scan_loss(oracle_mod, p, dout, dh_final, softplus, euler=False, reverse=False):
     y, hf = oracle_mod.selective_scan(p["x"], p["delta"], p["A"], p["B"], p["C"], Dskip=p.get("Dskip"), z=p.get("z"),
-                                      delta_bias=p.get("delta_bias"), delta_softplus=softplus, h0=p.get("h0"))
+                                      delta_bias=p.get("delta_bias"), delta_softplus=softplus, h0=p.get("h0"),
+                                      euler=euler, reverse=reverse)
     return float(np.sum(dout * y) + np.sum(dh_final * hf))
 
 
-@pytest.mark.parametrize("softplus,full", [(True, True), (False, True), (False, False)])
-def test_scan_backward_against_finite_differences(oracle_mod, softplus, full):
-    # every gradient of O5 against central differences of the forward O1 (which is pinned above)
-    rng = np.random.default_rng(80 + 2 * softplus + full)
+@pytest.mark.parametrize("softplus,full,euler,reverse", [(True, True, False, False), (False, True, False, False),
+                                                         (False, False, False, False), (True, True, True, False),
+                                                         (False, True, False, True), (True, True, True, True)])
+def test_scan_backward_against_finite_differences(oracle_mod, softplus, full, euler, reverse):
+    # every gradient of O5 (O5e for Euler, the flipped form for reverse) against central differences of the
+    # matching forward (O1 / O1e, pinned above)
+    rng = np.random.default_rng(80 + 2 * softplus + full + 4 * euler + 8 * reverse)
     b, L, D, N = 2, 6, 3, 4
     p = dict(x=rng.standard_normal((b, L, D)),
              delta=(rng.standard_normal((b, L, D)) if softplus else rng.uniform(0.05, 0.8, (b, L, D))),
@@ -310,7 +314,7 @@ def test_scan_backward_against_finite_differences(oracle_mod, softplus, full):
     dh_final = rng.standard_normal((b, D, N))
     g = oracle_mod.selective_scan_bwd(p["x"], p["delta"], p["A"], p["B"], p["C"], dout, Dskip=p.get("Dskip"),
                                       z=p.get("z"), delta_bias=p.get("delta_bias"), delta_softplus=softplus,
-                                      h0=p.get("h0"), dh_final=dh_final, threads=1)
+                                      h0=p.get("h0"), dh_final=dh_final, threads=1, euler=euler, reverse=reverse)
     names = dict(x="dx", delta="ddelta", A="dA", B="dB", C="dC", Dskip="dDskip", z="dz", delta_bias="ddelta_bias",
                  h0="dh0")
     for k, gk in names.items():
@@ -321,9 +325,9 @@ def test_scan_backward_against_finite_differences(oracle_mod, softplus, full):
             v0 = p[k][idx]
             eps = 1e-6 * max(1.0, abs(v0))
             p[k][idx] = v0 + eps
-            lp = _scan_loss(oracle_mod, p, dout, dh_final, softplus)
+            lp = _scan_loss(oracle_mod, p, dout, dh_final, softplus, euler, reverse)
             p[k][idx] = v0 - eps
-            lm = _scan_loss(oracle_mod, p, dout, dh_final, softplus)
+            lm = _scan_loss(oracle_mod, p, dout, dh_final, softplus, euler, reverse)
             p[k][idx] = v0
             num[idx] = (lp - lm) / (2 * eps)
         err = np.max(np.abs(g[gk] - num)) / max(np.max(np.abs(num)), 1e-12)
