@@ -310,6 +310,24 @@ int ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B
                  int act_dtype, int delta_dtype,
                  void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Backward pass of ssm_scan_fwd_ex: the same arguments, layouts, ownership,
+ * errors and workspace as ssm_scan_bwd, for the forward variant selected by
+ * `flags` (SSM_SCAN_REVERSE, SSM_SCAN_EULER or both; 0 is ssm_scan_bwd).
+ * With SSM_SCAN_REVERSE the gradients are those of the reversed scan (h0 enters
+ * at the last token, dh_final applies to the state after token 0); with
+ * SSM_SCAN_EULER those of the gain dt (dgain/ddt = 1, no dependence on A).
+ * SSM_SCAN_DELTA_PER_TOKEN and unknown bits return SSM_ERR_UNSUPPORTED.
+ */
+int ssm_scan_bwd_ex(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                    const float* Dskip, const void* z, const float* delta_bias, int delta_softplus,
+                    const float* h0, const void* dout, const float* dh_final,
+                    void* dx, void* ddelta, float* dA, float* dB, float* dC, float* dDskip, void* dz,
+                    float* ddelta_bias, float* dh0,
+                    int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                    int act_dtype, int delta_dtype, int flags,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
 size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
 
 /* Static text for a status code (never NULL). */

@@ -63,6 +63,8 @@ def load_library():
         lib.ssm_causal_conv1d_fwd.restype = _I
         lib.ssm_scan_bwd.argtypes = [_P] * 8 + [_I] + [_P] * 12 + [_I64] * 4 + [_I, _I, _P, _SZ, _P]
         lib.ssm_scan_bwd.restype = _I
+        lib.ssm_scan_bwd_ex.argtypes = [_P] * 8 + [_I] + [_P] * 12 + [_I64] * 4 + [_I, _I, _I, _P, _SZ, _P]
+        lib.ssm_scan_bwd_ex.restype = _I
         lib.ssm_scan_bwd_workspace_bytes.argtypes = [_I64] * 4
         lib.ssm_scan_bwd_workspace_bytes.restype = _SZ
         lib.ssm_status_string.argtypes = [_I]
@@ -343,13 +345,19 @@ def ssm_causal_conv1d_fwd(x, weight, bias=None, state_in=None, silu=True, out=No
     return (out, state_out) if (return_state or state_out is not None) else out
 
 
+def ssm_scan_bwd_ex(x, delta, A, B, C, dout, reverse=False, euler=False, **kw):
+    """Backward of ssm_scan_fwd_ex's variants (reverse and/or euler); the arguments of ssm_scan_bwd."""
+    return ssm_scan_bwd(x, delta, A, B, C, dout, reverse=reverse, euler=euler, **kw)
+
+
 def ssm_scan_bwd_workspace_bytes(batch, seqlen, dim, dstate) -> int:
     return int(load_library().ssm_scan_bwd_workspace_bytes(batch, seqlen, dim, dstate))
 
 
 def ssm_scan_bwd(x, delta, A, B, C, dout, D=None, z=None, delta_bias=None, delta_softplus=False, h0=None,
-                 dh_final=None, want_dh0=False, workspace=None):
-    """Gradients of sum(dout * y) + sum(dh_final * h_final) for ssm_scan_fwd with the same inputs.
+                 dh_final=None, want_dh0=False, workspace=None, reverse=False, euler=False):
+    """Gradients of sum(dout * y) + sum(dh_final * h_final) for ssm_scan_fwd with the same inputs
+    (for ssm_scan_fwd_ex's reverse / euler variants when those are set: ssm_scan_bwd_ex).
     Returns a dict: dx, ddelta (input dtypes), dA, dB, dC (fp32) and, for the optional inputs given,
     dD, dz, ddelta_bias, and dh0 (with h0 or want_dh0)."""
     lib = load_library()
@@ -383,10 +391,15 @@ def ssm_scan_bwd(x, delta, A, B, C, dout, D=None, z=None, delta_bias=None, delta
     if h0 is not None or want_dh0:
         g["dh0"] = torch.empty((batch, dim, dstate), **f32)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    rc = lib.ssm_scan_bwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
-                          int(bool(delta_softplus)), _ptr(h0), _ptr(dout), _ptr(dh_final), _ptr(g["dx"]),
-                          _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g.get("dD")),
-                          _ptr(g.get("dz")), _ptr(g.get("ddelta_bias")), _ptr(g.get("dh0")),
-                          batch, seqlen, dim, dstate, act, dcode, _ptr(workspace), wsb, _stream(dev))
-    _check(lib, "ssm_scan_bwd", rc)
+    args = (_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+            int(bool(delta_softplus)), _ptr(h0), _ptr(dout), _ptr(dh_final), _ptr(g["dx"]), _ptr(g["ddelta"]),
+            _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g.get("dD")), _ptr(g.get("dz")),
+            _ptr(g.get("ddelta_bias")), _ptr(g.get("dh0")), batch, seqlen, dim, dstate, act, dcode)
+    flags = (SSM_SCAN_REVERSE if reverse else 0) | (SSM_SCAN_EULER if euler else 0)
+    if flags == 0:
+        rc = lib.ssm_scan_bwd(*args, _ptr(workspace), wsb, _stream(dev))
+        _check(lib, "ssm_scan_bwd", rc)
+    else:
+        rc = lib.ssm_scan_bwd_ex(*args, flags, _ptr(workspace), wsb, _stream(dev))
+        _check(lib, "ssm_scan_bwd_ex", rc)
     return g

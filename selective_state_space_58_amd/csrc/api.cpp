@@ -373,13 +373,17 @@ size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, 
   return scan_bwd_ws_bytes(batch, seqlen, dim, dstate);
 }
 
-int ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* Dskip,
-                 const void* z, const float* delta_bias, int delta_softplus, const float* h0, const void* dout,
-                 const float* dh_final, void* dx, void* ddelta, float* dA, float* dB, float* dC, float* dDskip,
-                 void* dz, float* ddelta_bias, float* dh0, int64_t batch, int64_t seqlen, int64_t dim,
-                 int64_t dstate, int act_dtype, int delta_dtype, void* workspace, size_t workspace_bytes,
-                 void* stream) {
+static int bwd_common(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                      const float* Dskip, const void* z, const float* delta_bias, int delta_softplus, const float* h0,
+                      const void* dout, const float* dh_final, void* dx, void* ddelta, float* dA, float* dB,
+                      float* dC, float* dDskip, void* dz, float* ddelta_bias, float* dh0, int64_t batch,
+                      int64_t seqlen, int64_t dim, int64_t dstate, int act_dtype, int delta_dtype, int flags,
+                      void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error.clear();
+  if ((flags & ~(SSM_SCAN_REVERSE | SSM_SCAN_EULER | SSM_SCAN_DELTA_PER_TOKEN)) != 0)
+    return fail(SSM_ERR_UNSUPPORTED, "unknown scan flag bits");
+  if ((flags & SSM_SCAN_DELTA_PER_TOKEN) != 0)
+    return fail(SSM_ERR_UNSUPPORTED, "the backward pass does not support the per-token delta flag");
   int rc = validate_scan(x, delta, A, B, C, dx, false, Dskip, z, delta_bias, h0, dh0, batch, seqlen, dim, dstate,
                          act_dtype, delta_dtype, delta_softplus);
   if (rc != SSM_OK) return rc;
@@ -411,7 +415,31 @@ int ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B
   a.dh0 = dh0; a.ws_ckpt = (float*)ws;
   a.batch = batch; a.seqlen = seqlen; a.dim = dim; a.dstate = dstate;
   a.softplus = delta_softplus; a.act_bf16 = act_dtype == SSM_BF16; a.delta_bf16 = delta_dtype == SSM_BF16;
+  a.reverse = (flags & SSM_SCAN_REVERSE) != 0;
+  a.euler = (flags & SSM_SCAN_EULER) != 0;
   return launch_scan_bwd(a, stream);
+}
+
+int ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* Dskip,
+                 const void* z, const float* delta_bias, int delta_softplus, const float* h0, const void* dout,
+                 const float* dh_final, void* dx, void* ddelta, float* dA, float* dB, float* dC, float* dDskip,
+                 void* dz, float* ddelta_bias, float* dh0, int64_t batch, int64_t seqlen, int64_t dim,
+                 int64_t dstate, int act_dtype, int delta_dtype, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  return bwd_common(x, delta, A, B, C, Dskip, z, delta_bias, delta_softplus, h0, dout, dh_final, dx, ddelta, dA, dB,
+                    dC, dDskip, dz, ddelta_bias, dh0, batch, seqlen, dim, dstate, act_dtype, delta_dtype, 0,
+                    workspace, workspace_bytes, stream);
+}
+
+int ssm_scan_bwd_ex(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                    const float* Dskip, const void* z, const float* delta_bias, int delta_softplus, const float* h0,
+                    const void* dout, const float* dh_final, void* dx, void* ddelta, float* dA, float* dB, float* dC,
+                    float* dDskip, void* dz, float* ddelta_bias, float* dh0, int64_t batch, int64_t seqlen,
+                    int64_t dim, int64_t dstate, int act_dtype, int delta_dtype, int flags, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return bwd_common(x, delta, A, B, C, Dskip, z, delta_bias, delta_softplus, h0, dout, dh_final, dx, ddelta, dA, dB,
+                    dC, dDskip, dz, ddelta_bias, dh0, batch, seqlen, dim, dstate, act_dtype, delta_dtype, flags,
+                    workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

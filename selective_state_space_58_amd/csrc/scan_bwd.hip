@@ -110,10 +110,10 @@ __global__ __launch_bounds__(256) void bwd_zero_kernel(float* p, int64_t n) {
 // each batch row (partials laid out (group, batch * token, 16)).
 __global__ __launch_bounds__(256) void bwd_sum_partials_kernel(const float* part_b, const float* part_c, float* dB,
                                                                float* dC, int64_t rows, int64_t groups, int64_t N,
-                                                               int64_t n0, int width) {
+                                                               int64_t n0, int width, int64_t L, int reverse) {
   const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (i >= rows * width) return;
-  const int64_t bt = i / width;
+  const int64_t bt = i / width;                  // (batch, token) in processing order
   const int nl = (int)(i - bt * width);
   const int64_t per_group = rows * BR;
   const int64_t o = bt * BR + nl;
@@ -122,8 +122,10 @@ __global__ __launch_bounds__(256) void bwd_sum_partials_kernel(const float* part
     sb += part_b[g * per_group + o];
     sc += part_c[g * per_group + o];
   }
-  dB[bt * N + n0 + nl] = sb;
-  dC[bt * N + n0 + nl] = sc;
+  const int64_t t = bt % L;
+  const int64_t row = reverse ? bt - t + (L - 1 - t) : bt;
+  dB[row * N + n0 + nl] = sb;
+  dC[row * N + n0 + nl] = sc;
 }
 
 struct BwdLds {
@@ -139,13 +141,18 @@ struct BwdLds {
 };
 
 // MULTI: more than one block of 16 states (per-token gradients accumulated).
-template <bool XB, bool DB, bool ACC, bool MULTI>
+// GAIN: 0 short ZOH, 1 accurate ZOH, 2 Euler (gain dt).  REV: reversed scan.
+template <bool XB, bool DB, int GAIN, bool MULTI, bool REV>
 __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64_t chw0, int64_t grp, float av,
                                               float a2, float ia, bool nok, BwdLds& sm) {
   using RX = typename Raw<XB>::T;
   using RD = typename Raw<DB>::T;
   using TX = typename scan_dev::Act<XB>::T;
   using TD = typename scan_dev::Act<DB>::T;
+  constexpr bool ACC = GAIN == 1;
+  constexpr bool EULER = GAIN == 2;
+  // ZOH gain (E - 1)/a, or dt for the Euler discretization
+  auto gain = [&](float E, float dt) -> float { return EULER ? dt : bwd_gain<ACC>(E, dt, av, ia); };
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
   const int r = lane >> 2, c = lane & 3;
@@ -159,6 +166,8 @@ __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64
   const int64_t slice = a.batch * dim * BR;      // one checkpoint of the block's states
   const int64_t cidx = (b * dim + ch) * BR + r;
   const int64_t tcd = a.batch * L * dim;         // token-channel elements of one accumulator
+  // processing-order token t sits at row L - 1 - t of the inputs when the scan runs in reverse
+  auto grow = [&](int64_t t) -> int64_t { return REV ? L - 1 - t : t; };
 
   // the skip term and the Dskip gradient belong to the first block of states only
   const float Dv = (a.Dskip != nullptr && ch_ok && a.first) ? a.Dskip[ch] : 0.f;
@@ -177,7 +186,7 @@ __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64
       const int64_t t = t0 + tl;
       const int64_t chl = chw0 + cc < dim ? chw0 + cc : dim - 1;
       const bool ok = t < L && chw0 + cc < dim;
-      const int64_t i = (b * L + (t < L ? t : L - 1)) * dim + chl;
+      const int64_t i = (b * L + grow(t < L ? t : L - 1)) * dim + chl;
       const float v = Raw<DB>::f32(gd[i]) + ((a.delta_bias != nullptr) ? a.delta_bias[chl] : 0.f);
       const float dt = ok ? (a.softplus ? softplus_f(v) : v) : 0.f;
       sm.dx[tid] = make_float2(dt, Raw<XB>::f32(gx[i]));
@@ -191,7 +200,7 @@ __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64
       const int tl = tid / BR, n = tid % BR;
       const int64_t t = t0 + tl;
       const bool ok = t < L && n0 + n < N;
-      const int64_t i = (b * L + (t < L ? t : L - 1)) * N + (n0 + n < N ? n0 + n : 0);
+      const int64_t i = (b * L + grow(t < L ? t : L - 1)) * N + (n0 + n < N ? n0 + n : 0);
       sm.bc[(tl * BR + n) * 2] = ok ? Raw<XB>::f32(gB[i]) : 0.f;
       if (full) sm.bc[(tl * BR + n) * 2 + 1] = ok ? Raw<XB>::f32(gC[i]) : 0.f;
     }
@@ -224,7 +233,7 @@ __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64
       const float2 dx = sm.dx[tl * BWC + wc];
       const float Bn = sm.bc[(tl * BR + r) * 2];
       const float E = hw_exp2(dx.x * a2);
-      h = fmaf(E, h, bwd_gain<ACC>(E, dx.x, av, ia) * (Bn * dx.y));
+      h = fmaf(E, h, gain(E, dx.x) * (Bn * dx.y));
     }
   }
 
@@ -252,7 +261,7 @@ __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64
         const float2 dx = sm.dx[tl * BWC + wc];
         const float Bn = sm.bc[(tl * BR + r) * 2], Cn = sm.bc[(tl * BR + r) * 2 + 1];
         const float E = hw_exp2(dx.x * a2);
-        hs = fmaf(E, hs, bwd_gain<ACC>(E, dx.x, av, ia) * (Bn * dx.y));
+        hs = fmaf(E, hs, gain(E, dx.x) * (Bn * dx.y));
         hw[tl * 64 + lane] = hs;
         ew[tl * 64 + lane] = E;
         pr[j] = Cn * hs;
@@ -269,7 +278,7 @@ __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64
           const float sg = sigmoid_f(zz);
           dy = dout * zz * sg;
           if (ch_ok && t0 + tl < L)
-            put(2, (b * L + t0 + tl) * dim + ch, dout * y * (sg + zz * sg * (1.f - sg)), (TX*)a.dz);
+            put(2, (b * L + grow(t0 + tl)) * dim + ch, dout * y * (sg + zz * sg * (1.f - sg)), (TX*)a.dz);
         }
         sm.dy[e] = dy;
       }
@@ -288,7 +297,7 @@ __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64
       const float E = ew[tl * 64 + lane];
       const float ht = hw[tl * 64 + lane];
       const float hp = tl > 0 ? hw[(tl - 1) * 64 + lane] : hstart;
-      const float g = bwd_gain<ACC>(E, dx.x, av, ia);
+      const float g = gain(E, dx.x);
       lam = fmaf(Cn, dy, lam);
       // dC = sum over channels of h_t dy; dB = sum over channels of lam g x
       const float sc = quad_sum(ht * dy);
@@ -300,8 +309,9 @@ __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64
       const float dE = lam * hp;
       const float dg = lam * Bn * dx.y;
       pdx[j] = lam * g * Bn;
-      pdt[j] = fmaf(dE * E, av, dg * E);
-      dA = fmaf(dE * E, dx.x, fmaf(dg, gain_da<ACC>(dx.x, av, ia, E, g), dA));
+      // dg/ddt is E for ZOH and 1 for Euler; dg/da is zero for Euler
+      pdt[j] = fmaf(dE * E, av, EULER ? dg : dg * E);
+      dA = EULER ? fmaf(dE * E, dx.x, dA) : fmaf(dE * E, dx.x, fmaf(dg, gain_da<ACC>(dx.x, av, ia, E, g), dA));
       lam *= E;
     }
     const float tdx = reduce4_rows(pdx);
@@ -311,7 +321,7 @@ __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64
       const int e = tl * BWC + wc;
       const float dy = sm.dy[e];
       const float dv = a.softplus ? tdt * sigmoid_f(sm.v[e]) : tdt;
-      const int64_t i = (b * L + t0 + tl) * dim + ch;
+      const int64_t i = (b * L + grow(t0 + tl)) * dim + ch;
       put(0, i, fmaf(Dv, dy, tdx), (TX*)a.dx);
       put(1, i, dv, (TD*)a.ddelta);
       if (a.first) dDacc = fmaf(dy, sm.dx[e].y, dDacc);
@@ -353,7 +363,7 @@ __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64
 }
 
 // One workgroup of four waves per 16 channels of a batch row.
-template <bool XB, bool DB, bool MULTI>
+template <bool XB, bool DB, bool MULTI, bool REV>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void scan_bwd_kernel(BwdArgs a,
                                                                                               int64_t wgs_per_batch) {
   const int tid = threadIdx.x;
@@ -371,14 +381,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
   const float a2 = av * kLog2e, ia = 1.f / av;
   const bool tiny = !(fabsf(av) >= 1e-2f);
   __shared__ __attribute__((aligned(16))) BwdLds lds;
-  if (!XB || __syncthreads_or(tiny)) scan_bwd_body<XB, DB, true, MULTI>(a, b, chw0, grp, av, a2, ia, nok, lds);
-  else scan_bwd_body<XB, DB, false, MULTI>(a, b, chw0, grp, av, a2, ia, nok, lds);
+  if (a.euler) scan_bwd_body<XB, DB, 2, MULTI, REV>(a, b, chw0, grp, av, a2, ia, nok, lds);
+  else if (!XB || __syncthreads_or(tiny)) scan_bwd_body<XB, DB, 1, MULTI, REV>(a, b, chw0, grp, av, a2, ia, nok, lds);
+  else scan_bwd_body<XB, DB, 0, MULTI, REV>(a, b, chw0, grp, av, a2, ia, nok, lds);
 }
 
 template <bool XB, bool DB>
 hipError_t launch_bwd_xd(const BwdArgs& a, dim3 grid, int64_t wgs, hipStream_t st) {
-  if (a.acc != nullptr) scan_bwd_kernel<XB, DB, true><<<grid, 256, 0, st>>>(a, wgs);
-  else scan_bwd_kernel<XB, DB, false><<<grid, 256, 0, st>>>(a, wgs);
+  if (a.reverse) {
+    if (a.acc != nullptr) scan_bwd_kernel<XB, DB, true, true><<<grid, 256, 0, st>>>(a, wgs);
+    else scan_bwd_kernel<XB, DB, false, true><<<grid, 256, 0, st>>>(a, wgs);
+  } else {
+    if (a.acc != nullptr) scan_bwd_kernel<XB, DB, true, false><<<grid, 256, 0, st>>>(a, wgs);
+    else scan_bwd_kernel<XB, DB, false, false><<<grid, 256, 0, st>>>(a, wgs);
+  }
   return hipGetLastError();
 }
 
@@ -441,7 +457,7 @@ int launch_scan_bwd(const BwdArgs& a0, void* stream) {
       const int width = (int)(a.dstate - n0 < BR ? a.dstate - n0 : BR);
       const int64_t items = rows * width;
       bwd_sum_partials_kernel<<<dim3((unsigned)((items + 255) / 256)), 256, 0, st>>>(
-          a.ws_part, a.ws_part + wgs * rows * BR, a.dB, a.dC, rows, wgs, a.dstate, n0, width);
+          a.ws_part, a.ws_part + wgs * rows * BR, a.dB, a.dC, rows, wgs, a.dstate, n0, width, a.seqlen, a.reverse);
       e = hipGetLastError();
       if (e != hipSuccess) return fail(6, std::string("backward partial sums: ") + hipGetErrorString(e));
     }

@@ -89,6 +89,8 @@ struct BwdArgs {
   float* acc;              // 3 x (batch, seqlen, dim) fp32: dx, ddelta, dz summed over state blocks (dstate > 16)
   int64_t n0;              // first state of the block of 16 this pass handles
   int first, last;         // first / last block of states
+  int reverse;             // gradients of the reversed scan (tokens from the last to the first)
+  int euler;               // gradients of the Euler discretization (gain dt)
   int64_t batch, seqlen, dim, dstate;
   int softplus;
   int act_bf16, delta_bf16;

@@ -248,6 +248,21 @@ def test_scan_bwd_argument_errors(kw, code):
     assert lib.ssm_last_error() != b""
 
 
+def test_scan_bwd_ex_flag_checks():
+    lib = _lib()
+    # x .. delta_bias, softplus, h0, dout, dh_final, dx, ddelta, dA, dB, dC, dDskip, dz, ddelta_bias, dh0,
+    # batch, seqlen, dim, dstate, act, delta dtype
+    base = [P] * 8 + [0] + [None, P, None, P, P, P, P, P, None, None, None, None] + [1, 4, 4, 4, 1, 1]
+    for flags, code in ((4, 4), (8, 4), (5, 4)):    # per-token delta has no backward; unknown bits
+        assert lib.ssm_scan_bwd_ex(*base, flags, None, 0, None) == code
+        assert lib.ssm_last_error() != b""
+    # REVERSE / EULER go through the same validation as ssm_scan_bwd
+    bad = list(base)
+    bad[0] = None
+    for flags in (1, 2, 3):
+        assert lib.ssm_scan_bwd_ex(*bad, flags, None, 0, None) == 1
+
+
 def test_scan_bwd_workspace_query():
     lib = _lib()
     # states at the start of each of the 7 16-token tiles (rounded up to 256 bytes), then the dB and dC

@@ -33,7 +33,7 @@ def upstream(inp, seed):
     return dout, rng.standard_normal((b, D, N), dtype=np.float32)
 
 
-def check(ssm, inp, label, dh_final=True, tol=None):
+def check(ssm, inp, label, dh_final=True, tol=None, reverse=False, euler=False):
     print("case", label, flush=True)
     tol = tol or TOL[inp["meta"]["dtype"]]
     dout, dhf = upstream(inp, 7)
@@ -43,14 +43,16 @@ def check(ssm, inp, label, dh_final=True, tol=None):
     act = t["x"].dtype
     g = ssm.ssm_scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], torch.from_numpy(dout).to(DEV, act), D=t["D"],
                          z=t["z"], delta_bias=t["delta_bias"], delta_softplus=inp["meta"]["softplus"], h0=t["h0"],
-                         dh_final=None if dhf is None else torch.from_numpy(dhf).to(DEV), want_dh0=True)
+                         dh_final=None if dhf is None else torch.from_numpy(dhf).to(DEV), want_dh0=True,
+                         reverse=reverse, euler=euler)
     torch.cuda.synchronize()
     f = workloads.to_f64(inp)
     ref = oracle.selective_scan_bwd(f["x"], f["delta"], f["A"], f["B"], f["C"], dout.astype(np.float64),
                                     Dskip=f["D"], z=f["z"], delta_bias=f["delta_bias"],
                                     delta_softplus=inp["meta"]["softplus"],
                                     h0=f["h0"] if f["h0"] is not None else np.zeros(g["dh0"].shape),
-                                    dh_final=None if dhf is None else dhf.astype(np.float64))
+                                    dh_final=None if dhf is None else dhf.astype(np.float64),
+                                    reverse=reverse, euler=euler)
     errs = {}
     for k, rk in GRADS.items():
         if k in g:
@@ -80,6 +82,17 @@ def test_scan_bwd_more_states(ssm, dtype, shape):
     inp = workloads.scan_inputs(b, L, D, N, dtype=dtype, seed=sum(shape) + 17, dt="softplus_bias", gate=True,
                                 softplus=True, skip=True, h0=True)
     check(ssm, inp, "bwd %s %s" % (dtype, shape))
+
+
+@pytest.mark.parametrize("reverse,euler", [(True, False), (False, True), (True, True)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(2, 100, 40, 16), (1, 77, 24, 40)])
+def test_scan_bwd_variants(ssm, reverse, euler, dtype, shape):
+    # gradients of ssm_scan_fwd_ex's reverse and Euler variants (ssm_scan_bwd_ex) against O5e / the flipped O5
+    b, L, D, N = shape
+    inp = workloads.scan_inputs(b, L, D, N, dtype=dtype, seed=sum(shape) + 29, dt="softplus_bias", gate=True,
+                                softplus=True, skip=True, h0=True)
+    check(ssm, inp, "bwd %s %s reverse=%s euler=%s" % (dtype, shape, reverse, euler), reverse=reverse, euler=euler)
 
 
 @pytest.mark.parametrize("flags", [dict(gate=False, softplus=False, skip=False, h0=False),
