@@ -192,29 +192,32 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(FULL ? 2 : 
     Ml[i] = 0;
   }
 
-  // ---- state: wave w owns p-tile pw and n-tiles [NTW*tw, NTW*tw + NTW).
+  // ---- state: wave w owns p-tile pw and n-tiles [NTW*tw, NTW*tw + NTW).  The products are
+  // computed transposed (state^T = B^T (X o w), so each accumulator lane holds four consecutive
+  // states of one channel: H[p = 16 pw + l16][n = 16 nt + 4 g4 + v], v = 0..3.
   // FULL: h0, or the carry into this chunk; !FULL: zero.
   const float* hin = !FULL ? nullptr : (a.nchunks > 1 ? a.ws_state + chunk * slice : a.h0);
+  const int64_t hrow = ((b * H + h) * P + p0 + pw * 16 + l16) * N;   // this lane's channel row of a state
   f32x4 Hacc[NTW];
 #pragma unroll
   for (int j = 0; j < NTW; ++j) {
-    const int n = (NTW * tw + j) * 16 + l16;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int p = pw * 16 + 4 * g4 + v;
-      Hacc[j][v] = hin != nullptr ? hin[((b * H + h) * P + p0 + p) * N + n] : 0.f;
-    }
+    const int n = (NTW * tw + j) * 16 + 4 * g4;
+    Hacc[j] = hin != nullptr ? *reinterpret_cast<const f32x4*>(hin + hrow + n) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
   auto store_state_split = [&]() {
 #pragma unroll
-    for (int j = 0; j < NTW; ++j)
+    for (int j = 0; j < NTW; ++j) {
+      const int idx = (pw * 16 + l16) * SN + (NTW * tw + j) * 16 + 4 * g4;
+      u32x2 hi, lo;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int idx = (pw * 16 + 4 * g4 + v) * SN + (NTW * tw + j) * 16 + l16;
-        const u16 hb = f2bf(Hacc[j][v]);
-        Hs[idx] = hb;
-        Hl[idx] = f2bf(Hacc[j][v] - bf2f(hb));
+      for (int v = 0; v < 4; v += 2) {
+        const u16 h0b = f2bf(Hacc[j][v]), h1b = f2bf(Hacc[j][v + 1]);
+        hi[v >> 1] = (unsigned)h0b | ((unsigned)h1b << 16);
+        lo[v >> 1] = (unsigned)f2bf(Hacc[j][v] - bf2f(h0b)) | ((unsigned)f2bf(Hacc[j][v + 1] - bf2f(h1b)) << 16);
       }
+      *reinterpret_cast<u32x2*>(Hs + idx) = hi;
+      *reinterpret_cast<u32x2*>(Hl + idx) = lo;
+    }
   };
   if (FULL) store_state_split();   // visible after the first barrier of the block loop
 
@@ -284,22 +287,28 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(FULL ? 2 : 
 
     // ---------------- C B^T tiles -> mask -> M (bf16 high/low) in LDS
     if constexpr (FULL) {
+      // (B C^T)[s][t]: lane (l16, g4) gets M's row t = 16 ti + l16 at s = 16 tj + 4 g4 .. +3
       auto cb_tile = [&](int ti, int tj) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < KN; ++kk)
-          acc = mfma(frag_rows(Cs, ti * 16 + l16, kk * 32 + g4 * 8, SN), frag_rows(Bs, tj * 16 + l16, kk * 32 + g4 * 8, SN),
+          acc = mfma(frag_rows(Bs, tj * 16 + l16, kk * 32 + g4 * 8, SN), frag_rows(Cs, ti * 16 + l16, kk * 32 + g4 * 8, SN),
                      acc);
-        const int s = tj * 16 + l16;
-        const float cs = cumS[s], gs = gS[s];
+        const int t = ti * 16 + l16;
+        const int s0 = tj * 16 + 4 * g4;
+        const float ct = cumS[t];
+        u32x2 hi, lo;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int t = ti * 16 + 4 * g4 + v;
-          const float m = (t >= s) ? acc[v] * exp_f(cumS[t] - cs) * gs : 0.f;
-          const u16 mh = f2bf(m);
-          Ms[t * SQ + s] = mh;
-          Ml[t * SQ + s] = f2bf(m - bf2f(mh));
+        for (int v = 0; v < 4; v += 2) {
+          const int s = s0 + v;
+          const float m0 = (t >= s) ? acc[v] * exp_f(ct - cumS[s]) * gS[s] : 0.f;
+          const float m1 = (t >= s + 1) ? acc[v + 1] * exp_f(ct - cumS[s + 1]) * gS[s + 1] : 0.f;
+          const u16 h0b = f2bf(m0), h1b = f2bf(m1);
+          hi[v >> 1] = (unsigned)h0b | ((unsigned)h1b << 16);
+          lo[v >> 1] = (unsigned)f2bf(m0 - bf2f(h0b)) | ((unsigned)f2bf(m1 - bf2f(h1b)) << 16);
         }
+        *reinterpret_cast<u32x2*>(Ms + t * SQ + s0) = hi;
+        *reinterpret_cast<u32x2*>(Ml + t * SQ + s0) = lo;
       };
       // 10 causal tiles: two each for four of the waves whose diagonal product is short
       switch (w) {
@@ -313,16 +322,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(FULL ? 2 : 
       }
     }
 
-    // ---------------- Y_off = C H^T for (token tile tw, channel tile pw); H = state entering the block
+    // ---------------- Y_off^T = H C^T for (channel tile pw, token tile tw); H = state entering the block
     f32x4 yoff = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < (FULL ? KN : 0); ++kk) {
-      const bf16x8 ca = frag_rows(Cs, tw * 16 + l16, kk * 32 + g4 * 8, SN);
-      yoff = mfma(ca, frag_rows(Hs, pw * 16 + l16, kk * 32 + g4 * 8, SN), yoff);
-      yoff = mfma(ca, frag_rows(Hl, pw * 16 + l16, kk * 32 + g4 * 8, SN), yoff);
+      const bf16x8 cb = frag_rows(Cs, tw * 16 + l16, kk * 32 + g4 * 8, SN);
+      yoff = mfma(frag_rows(Hs, pw * 16 + l16, kk * 32 + g4 * 8, SN), cb, yoff);
+      yoff = mfma(frag_rows(Hl, pw * 16 + l16, kk * 32 + g4 * 8, SN), cb, yoff);
     }
 
-    // ---------------- S = (X o w)^T B for (channel tile pw, state tiles of this wave); H <- decay H + S
+    // ---------------- S^T = B^T (X o w) for (state tiles of this wave, channel tile pw); H <- decay H + S
     {
       bf16x8 xh[2], xl[2];
 #pragma unroll
@@ -345,8 +354,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(FULL ? 2 : 
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
           const bf16x8 bt = __builtin_bit_cast(bf16x8, frag_cols_raw(Bs, kk * 32 + g4 * 8, nt * 16, SN, l16));
-          s = mfma(xh[kk], bt, s);
-          s = mfma(xl[kk], bt, s);
+          s = mfma(bt, xh[kk], s);
+          s = mfma(bt, xl[kk], s);
         }
 #pragma unroll
         for (int v = 0; v < 4; ++v) Hacc[j][v] = fmaf(dec, Hacc[j][v], s[v]);
@@ -354,7 +363,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(FULL ? 2 : 
     }
     __syncthreads();   // M complete; every wave has finished reading Hs/Hl
 
-    // ---------------- Y_diag = M X for (token tile tw, channel tile pw), epilogue
+    // ---------------- Y_diag^T = X^T M^T for (channel tile pw, token tile tw), epilogue
     f32x4 ydiag = {0.f, 0.f, 0.f, 0.f};
     if constexpr (FULL) {
       const int ksteps = (tw < 2) ? 1 : 2;
@@ -362,24 +371,36 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(FULL ? 2 : 
       for (int kk = 0; kk < 2; ++kk) {
         if (kk < ksteps) {
           const bf16x8 xb = __builtin_bit_cast(bf16x8, frag_cols_raw(Xs, kk * 32 + g4 * 8, pw * 16, SP, l16));
-          ydiag = mfma(frag_rows(Ms, tw * 16 + l16, kk * 32 + g4 * 8, SQ), xb, ydiag);
-          ydiag = mfma(frag_rows(Ml, tw * 16 + l16, kk * 32 + g4 * 8, SQ), xb, ydiag);
+          ydiag = mfma(xb, frag_rows(Ms, tw * 16 + l16, kk * 32 + g4 * 8, SQ), ydiag);
+          ydiag = mfma(xb, frag_rows(Ml, tw * 16 + l16, kk * 32 + g4 * 8, SQ), ydiag);
         }
       }
     }
     if constexpr (FULL) {
-      const int p = pw * 16 + l16;
+      // lane (l16, g4): token t0 + 16 tw + l16, channels 16 pw + 4 g4 .. +3 (one 8-byte store)
+      const int tl = tw * 16 + l16;
+      const int p = pw * 16 + 4 * g4;
+      const int64_t t = t0 + tl;
+      if (t < L) {
+        const float et = eS[tl];
+        float yv[4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int tl = tw * 16 + 4 * g4 + v;
-        const int64_t t = t0 + tl;
-        float yv = fmaf(eS[tl], yoff[v], ydiag[v]);
-        if (t < L) {
-          const int64_t gi = ((b * L + t) * H + h) * P + p0 + p;
-          if (a.Dskip != nullptr) yv = fmaf(Dv, bf2f(Xs[tl * SP + p]), yv);
-          if (a.z != nullptr) yv *= silu_f(bf2f(gZ[gi]));
-          gY[gi] = f2bf(yv);
+        for (int v = 0; v < 4; ++v) yv[v] = fmaf(et, yoff[v], ydiag[v]);
+        const int64_t gi = ((b * L + t) * H + h) * P + p0 + p;
+        if (a.Dskip != nullptr) {
+          const u32x2 xr = *reinterpret_cast<const u32x2*>(Xs + tl * SP + p);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) yv[v] = fmaf(Dv, bf2f((u16)(xr[v >> 1] >> (16 * (v & 1)))), yv[v]);
         }
+        if (a.z != nullptr) {
+          const u32x2 zr = *reinterpret_cast<const u32x2*>(gZ + gi);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) yv[v] *= silu_f(bf2f((u16)(zr[v >> 1] >> (16 * (v & 1)))));
+        }
+        u32x2 out;
+        out[0] = (unsigned)f2bf(yv[0]) | ((unsigned)f2bf(yv[1]) << 16);
+        out[1] = (unsigned)f2bf(yv[2]) | ((unsigned)f2bf(yv[3]) << 16);
+        *reinterpret_cast<u32x2*>(gY + gi) = out;
       }
     }
     if (FULL) store_state_split();   // the state entering the next block
@@ -389,14 +410,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(FULL ? 2 : 
   float* hout = FULL ? (chunk == a.nchunks - 1 ? a.h_final : nullptr) : a.ws_state + chunk * slice;
   if (hout != nullptr) {
 #pragma unroll
-    for (int j = 0; j < NTW; ++j) {
-      const int n = (NTW * tw + j) * 16 + l16;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int p = pw * 16 + 4 * g4 + v;
-        hout[((b * H + h) * P + p0 + p) * N + n] = Hacc[j][v];
-      }
-    }
+    for (int j = 0; j < NTW; ++j) *reinterpret_cast<f32x4*>(hout + hrow + (NTW * tw + j) * 16 + 4 * g4) = Hacc[j];
   }
   if (!FULL && w == 0 && l == 0 && ph == 0) a.ws_dsum[chunk * a.batch * H + b * H + h] = dsum;
 }
