@@ -151,6 +151,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(FULL ? 2 : 
   __shared__ __attribute__((aligned(16))) u16 Cs[QB * SN];   // C block [t][n]
   __shared__ __attribute__((aligned(16))) u16 Bs[QB * SN];   // B block [s][n]
   __shared__ __attribute__((aligned(16))) u16 Xs[QB * SP];   // x block [s][p]
+  __shared__ __attribute__((aligned(16))) u16 XWh[QB * SP];  // x_s[p] * w_s [s][p], high part
+  __shared__ __attribute__((aligned(16))) u16 XWl[QB * SP];  // low part
   __shared__ __attribute__((aligned(16))) u16 Ms[QB * SQ];   // masked decayed C B^T [t][s], high part
   __shared__ __attribute__((aligned(16))) u16 Ml[QB * SQ];   // low part
   __shared__ __attribute__((aligned(16))) u16 Hs[PS * SN];   // state [p][n], high part
@@ -283,6 +285,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(FULL ? 2 : 
       dsum += cend;
     }
     __syncthreads();
+    if (tid < QB * PS / 8) {
+      // x * w for the state product, once per workgroup, from the staged registers
+      const int row = tid >> 2, c8 = tid & 3;
+      const float ws = wS[row];
+      u32x4 hi, lo;
+#pragma unroll
+      for (int q = 0; q < 8; q += 2) {
+        const float f0 = bf2f(half_of(rx, q)) * ws, f1 = bf2f(half_of(rx, q + 1)) * ws;
+        const u16 h0b = f2bf(f0), h1b = f2bf(f1);
+        hi[q >> 1] = (unsigned)h0b | ((unsigned)h1b << 16);
+        lo[q >> 1] = (unsigned)f2bf(f0 - bf2f(h0b)) | ((unsigned)f2bf(f1 - bf2f(h1b)) << 16);
+      }
+      *reinterpret_cast<u32x4*>(XWh + row * SP + c8 * 8) = hi;
+      *reinterpret_cast<u32x4*>(XWl + row * SP + c8 * 8) = lo;
+    }
     if (blk + 1 < nblk) fetch(t0 + QB);
 
     // ---------------- C B^T tiles -> mask -> M (bf16 high/low) in LDS
@@ -310,15 +327,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(FULL ? 2 : 
         *reinterpret_cast<u32x2*>(Ms + t * SQ + s0) = hi;
         *reinterpret_cast<u32x2*>(Ml + t * SQ + s0) = lo;
       };
-      // 10 causal tiles: two each for four of the waves whose diagonal product is short
+      // 10 causal tiles: one per wave, a second for two of the waves that have no x * w to form
       switch (w) {
-        case 0: cb_tile(0, 0); cb_tile(1, 0); break;
-        case 1: cb_tile(1, 1); cb_tile(2, 0); break;
+        case 0: cb_tile(0, 0); break;
+        case 1: cb_tile(1, 0); break;
+        case 2: cb_tile(1, 1); break;
+        case 3: cb_tile(2, 0); break;
         case 4: cb_tile(2, 1); cb_tile(2, 2); break;
         case 5: cb_tile(3, 0); cb_tile(3, 1); break;
-        case 2: cb_tile(3, 2); break;
-        case 3: cb_tile(3, 3); break;
-        default: break;
+        case 6: cb_tile(3, 2); break;
+        default: cb_tile(3, 3); break;
       }
     }
 
@@ -331,20 +349,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(FULL ? 2 : 
       yoff = mfma(frag_rows(Hl, pw * 16 + l16, kk * 32 + g4 * 8, SN), cb, yoff);
     }
 
+    __syncthreads();   // M and x*w complete; every wave has finished reading Hs/Hl
+
     // ---------------- S^T = B^T (X o w) for (state tiles of this wave, channel tile pw); H <- decay H + S
     {
       bf16x8 xh[2], xl[2];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        // rows s = 32kk + 8g4 .. +7 of column p = 16pw + l16 of X, scaled by w_s
-        const u32x4 raw = frag_cols_raw(Xs, kk * 32 + g4 * 8, pw * 16, SP, l16);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const float f = bf2f(half_of(raw, q)) * wS[kk * 32 + g4 * 8 + q];
-          const __bf16 fh = (__bf16)f;
-          xh[kk][q] = fh;
-          xl[kk][q] = (__bf16)(f - (float)fh);
-        }
+        // rows s = 32kk + 8g4 .. +7 of column p = 16pw + l16 of x*w
+        xh[kk] = __builtin_bit_cast(bf16x8, frag_cols_raw(XWh, kk * 32 + g4 * 8, pw * 16, SP, l16));
+        xl[kk] = __builtin_bit_cast(bf16x8, frag_cols_raw(XWl, kk * 32 + g4 * 8, pw * 16, SP, l16));
       }
       const float dec = decayS;
 #pragma unroll
@@ -361,7 +375,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(FULL ? 2 : 
         for (int v = 0; v < 4; ++v) Hacc[j][v] = fmaf(dec, Hacc[j][v], s[v]);
       }
     }
-    __syncthreads();   // M complete; every wave has finished reading Hs/Hl
+
 
     // ---------------- Y_diag^T = X^T M^T for (channel tile pw, token tile tw), epilogue
     f32x4 ydiag = {0.f, 0.f, 0.f, 0.f};
