@@ -186,10 +186,12 @@ int ssd_chunk_scan_fwd(const void* x, const void* dt, const float* A, const void
                        int act_dtype, int dt_dtype,
                        void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace needed by ssd_chunk_scan_fwd for these shapes: nonzero when the
- * (batch, head) pairs are too few to fill the device and the sequence is
- * split into time chunks whose states are carried on the device.  Depends on
- * the current device. */
+/* Workspace needed by ssd_chunk_scan_fwd for these shapes: the C_t . B_s
+ * products of every 64-token block and group (10 causal 16x16 fp32 tiles,
+ * formed once and shared by the group's heads), plus, when the (batch, head)
+ * pairs are too few to fill the device and the sequence is split into time
+ * chunks, the chunk states carried on the device.  Zero only for seqlen 0.
+ * Depends on the current device. */
 size_t ssd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                            int64_t ngroups, int64_t dstate, int64_t chunk_size);
 

@@ -105,6 +105,13 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// 32x32x16 bf16 MFMA: lane l supplies A[l % 32][8 (l / 32) .. +7] and B[8 (l / 32) .. +7][l % 32]; result
+// item v of lane l is D[8 (v / 4) + 4 (l / 32) + v % 4][l % 32].
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
 // Fragment with 8 consecutive bf16 of row `row` from column `col` (row-major LDS matrix).
 __device__ __forceinline__ bf16x8 frag_rows(const u16* base, int row, int col, int stride) {
   return *reinterpret_cast<const bf16x8*>(base + row * stride + col);
@@ -131,22 +138,60 @@ __device__ __forceinline__ u16 half_of(const u32x4& v, int q) {
   return (u16)(w >> (16 * (q & 1)));
 }
 
+// Causal 16x16 tiles (ti, tj), ti >= tj, of a 64-token block, in the order
+// the pre-pass stores them: tile c has ti = floor((sqrt(8c+1)-1)/2).
+__device__ __forceinline__ int cb_tile_row(int c) { return c < 1 ? 0 : (c < 3 ? 1 : (c < 6 ? 2 : 3)); }
+constexpr int NCB = 10;   // causal tiles per block
+
+// Pre-pass: (B C^T)[s][t] = C_t . B_s for the 10 causal 16x16 tiles of every
+// 64-token block and group, in the lane layout the mask reads them in (lane
+// (l16, g4) of tile (ti, tj) holds t = 16 ti + l16, s = 16 tj + 4 g4 .. +3).
+// One wave per tile; fragments come straight from global memory (rows past
+// the end of the sequence repeat the last token and are never used).
+template <int N>
+__global__ __launch_bounds__(64 * NCB) void ssd_cb_kernel(SsdArgs a, int64_t nblk_total) {
+  constexpr int KN = N / 32;
+  const int l = threadIdx.x & 63, l16 = l & 15, g4 = l >> 4;
+  const int c = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ti = cb_tile_row(c), tj = c - ti * (ti + 1) / 2;
+  const int64_t blk = blockIdx.x, grp = blockIdx.y, b = blockIdx.z;
+  const int64_t L = a.seqlen, G = a.ngroups;
+  int64_t tt = blk * QB + ti * 16 + l16, ts = blk * QB + tj * 16 + l16;
+  tt = tt < L ? tt : L - 1;
+  ts = ts < L ? ts : L - 1;
+  const u16* crow = (const u16*)a.C + ((b * L + tt) * G + grp) * N;
+  const u16* brow = (const u16*)a.B + ((b * L + ts) * G + grp) * N;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < KN; ++kk)
+    acc = mfma(*reinterpret_cast<const bf16x8*>(brow + kk * 32 + g4 * 8),
+               *reinterpret_cast<const bf16x8*>(crow + kk * 32 + g4 * 8), acc);
+  reinterpret_cast<f32x4*>(a.ws_cb)[(((b * nblk_total + blk) * G + grp) * NCB + c) * 64 + l] = acc;
+}
+
 // FULL: outputs for one time chunk, starting from the state carried into it.
 // !FULL: the chunk's own state contribution (from a zero state) and its total
-// decay exponent a * sum(dt), for the carry pass; no outputs.  The state pass
-// needs few registers and is held to 128 VGPRs (two workgroups per CU); the
-// full pass keeps its 2 waves per SIMD (capping it at 128 VGPRs spills and
-// measured 2.5x slower).
+// decay exponent a * sum(dt), for the carry pass; no outputs.
+//
+// Block products use the 32x32x16 MFMA, which reads half the operand bytes
+// per FLOP of the 16x16x32 form.  Waves 0 and 1 each own the 32-channel x
+// 32-token output of half the block (Y_off in phase A, Y_diag added in phase
+// B, both transposed so a lane holds 4 x 4 consecutive channels of one
+// token); waves 2 .. 2 + N/32 - 1 each own a 32-state slice of the state
+// (S^T = B^T (X o w) and the update in phase B); every wave masks one or two
+// of the block's C B^T tiles (from the pre-pass) in phase A, and waves 4-7
+// form x*w.
 template <int N, bool DTB, bool FULL>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(FULL ? 2 : 4))) void ssd_fused_kernel(SsdArgs a) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void ssd_fused_kernel(SsdArgs a) {
   constexpr int SN = N + 8;        // row stride of [*][N] LDS arrays (bf16 elements)
   constexpr int SQ = QB + 8;       // row stride of [*][64] LDS arrays
-  constexpr int SP = PS + 8;       // row stride of the x tile
-  constexpr int KN = N / 32;       // k-steps over the state dimension
-  constexpr int NTW = N / 64;      // 16-wide state tiles owned by each wave (4 waves per p-tile)
+  constexpr int SP = PS + 8;       // row stride of the x tiles
+  constexpr int NQ = N / 32;       // 32-state slices of the state
+  constexpr int KS = N / 16;       // 16-deep k-steps over the states
   constexpr int CPR = N / 8;       // 16-byte chunks per B/C row
   constexpr int BC_CHUNKS = QB * CPR / (NWAVE * 64);  // B (and C) chunks per thread per block
-  static_assert(BC_CHUNKS >= 1 && (QB * CPR) % (NWAVE * 64) == 0, "tile shape");
+  constexpr int X0 = 256;          // threads [X0, X0 + 256) load x and form x*w: waves 4-7
+  static_assert(BC_CHUNKS >= 1 && (QB * CPR) % (NWAVE * 64) == 0 && QB * PS / 8 == 256, "tile shape");
 
   __shared__ __attribute__((aligned(16))) u16 Cs[QB * SN];   // C block [t][n]
   __shared__ __attribute__((aligned(16))) u16 Bs[QB * SN];   // B block [s][n]
@@ -162,9 +207,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(FULL ? 2 : 
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
-  const int l = tid & 63, l16 = l & 15, g4 = l >> 4;
-  const int tw = w & 3;        // this wave's 16-token tile of the block (outputs)
-  const int pw = w >> 2;       // this wave's 16-channel tile of the 32 head channels
+  const int l = tid & 63, l16 = l & 15, c32 = l & 31, hk = l >> 5;
+  const int c16 = 16 * ((l >> 4) & 1);   // column offset of this lane's 16-lane group within a 32-wide tile
   const int64_t H = a.nheads, P = a.headdim, L = a.seqlen;
   const int64_t nb = gridDim.x;
   int64_t lin = blockIdx.x;
@@ -194,28 +238,34 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(FULL ? 2 : 
     Ml[i] = 0;
   }
 
-  // ---- state: wave w owns p-tile pw and n-tiles [NTW*tw, NTW*tw + NTW).  The products are
-  // computed transposed (state^T = B^T (X o w), so each accumulator lane holds four consecutive
-  // states of one channel: H[p = 16 pw + l16][n = 16 nt + 4 g4 + v], v = 0..3.
+  // ---- state: wave 2 + q (q < N/32) owns states [32 q, 32 q + 32) of the 32 channels.  Lane l holds
+  // H[p = l % 32][n = 32 q + 8 g + 4 (l / 32) + j] in Hacc[4 g + j], g, j = 0..3.
   // FULL: h0, or the carry into this chunk; !FULL: zero.
+  const bool has_st = w >= 2 && w < 2 + NQ;
+  const int nq = w - 2;
   const float* hin = !FULL ? nullptr : (a.nchunks > 1 ? a.ws_state + chunk * slice : a.h0);
-  const int64_t hrow = ((b * H + h) * P + p0 + pw * 16 + l16) * N;   // this lane's channel row of a state
-  f32x4 Hacc[NTW];
+  const int64_t hrow = ((b * H + h) * P + p0 + c32) * N;   // this lane's channel row of a state
+  f32x16 Hacc = {};
+  if (has_st && hin != nullptr) {
 #pragma unroll
-  for (int j = 0; j < NTW; ++j) {
-    const int n = (NTW * tw + j) * 16 + 4 * g4;
-    Hacc[j] = hin != nullptr ? *reinterpret_cast<const f32x4*>(hin + hrow + n) : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(hin + hrow + 32 * nq + 8 * g + 4 * hk);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) Hacc[4 * g + j] = v[j];
+    }
   }
   auto store_state_split = [&]() {
+    if (!has_st) return;
 #pragma unroll
-    for (int j = 0; j < NTW; ++j) {
-      const int idx = (pw * 16 + l16) * SN + (NTW * tw + j) * 16 + 4 * g4;
+    for (int g = 0; g < 4; ++g) {
+      const int idx = c32 * SN + 32 * nq + 8 * g + 4 * hk;
       u32x2 hi, lo;
 #pragma unroll
-      for (int v = 0; v < 4; v += 2) {
-        const u16 h0b = f2bf(Hacc[j][v]), h1b = f2bf(Hacc[j][v + 1]);
-        hi[v >> 1] = (unsigned)h0b | ((unsigned)h1b << 16);
-        lo[v >> 1] = (unsigned)f2bf(Hacc[j][v] - bf2f(h0b)) | ((unsigned)f2bf(Hacc[j][v + 1] - bf2f(h1b)) << 16);
+      for (int j = 0; j < 4; j += 2) {
+        const float v0 = Hacc[4 * g + j], v1 = Hacc[4 * g + j + 1];
+        const u16 h0b = f2bf(v0), h1b = f2bf(v1);
+        hi[j >> 1] = (unsigned)h0b | ((unsigned)h1b << 16);
+        lo[j >> 1] = (unsigned)f2bf(v0 - bf2f(h0b)) | ((unsigned)f2bf(v1 - bf2f(h1b)) << 16);
       }
       *reinterpret_cast<u32x2*>(Hs + idx) = hi;
       *reinterpret_cast<u32x2*>(Hl + idx) = lo;
@@ -223,11 +273,25 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(FULL ? 2 : 
   };
   if (FULL) store_state_split();   // visible after the first barrier of the block loop
 
+  // ---- this wave's causal C B^T tiles of each block (index c = ti (ti + 1) / 2 + tj): waves 0, 1 and
+  // 4-7 one each, waves 2 and 3 two each
+  const int cb0 = w < 2 ? w : (w < 4 ? 2 + 2 * (w - 2) : w + 2);
+  const int cb1 = (w == 2 || w == 3) ? cb0 + 1 : -1;
+  const int64_t nblk_total = (L + QB - 1) / QB;
+  const f32x4* gcb = reinterpret_cast<const f32x4*>(a.ws_cb) + ((b * nblk_total) * a.ngroups + grp) * NCB * 64;
+
   // ---- register prefetch of one block
-  u32x4 rc[BC_CHUNKS], rb[BC_CHUNKS], rx;
+  u32x4 rc[BC_CHUNKS], rb[BC_CHUNKS], rx = {0u, 0u, 0u, 0u};
+  f32x4 rcb0 = {0.f, 0.f, 0.f, 0.f}, rcb1 = {0.f, 0.f, 0.f, 0.f};
   float rdt = 0.f;
   const int64_t last = L - 1;
+  const bool x_thread = tid >= X0;
   auto fetch = [&](int64_t t0) {
+    if (FULL) {
+      const f32x4* cbp = gcb + (t0 / QB) * a.ngroups * NCB * 64;
+      rcb0 = cbp[cb0 * 64 + l];
+      if (cb1 >= 0) rcb1 = cbp[cb1 * 64 + l];
+    }
 #pragma unroll
     for (int j = 0; j < BC_CHUNKS; ++j) {
       const int e = tid + NWAVE * 64 * j;
@@ -238,8 +302,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(FULL ? 2 : 
       if (FULL) rc[j] = *reinterpret_cast<const u32x4*>(gC + off);
       rb[j] = *reinterpret_cast<const u32x4*>(gB + off);
     }
-    if (tid < QB * PS / 8) {
-      const int row = tid >> 2, c8 = tid & 3;
+    if (x_thread) {
+      const int e = tid - X0, row = e >> 2, c8 = e & 3;
       int64_t t = t0 + row;
       t = t < last ? t : last;
       rx = *reinterpret_cast<const u32x4*>(gX + ((b * L + t) * H + h) * P + p0 + c8 * 8);
@@ -254,6 +318,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(FULL ? 2 : 
 
   const int nblk = (int)((t_end - t_begin + QB - 1) / QB);
   float dsum = 0.f;                  // a * sum of dt over the chunk (wave 0)
+  f32x16 yacc = {};                  // waves 0, 1: e^{cum_t} Y_off, then + Y_diag
   fetch(t_begin);
   for (int blk = 0; blk < nblk; ++blk) {
     const int64_t t0 = t_begin + (int64_t)blk * QB;
@@ -265,8 +330,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(FULL ? 2 : 
       if (FULL) *reinterpret_cast<u32x4*>(Cs + row * SN + c8 * 8) = rc[j];
       *reinterpret_cast<u32x4*>(Bs + row * SN + c8 * 8) = rb[j];
     }
-    if (tid < QB * PS / 8) {
-      const int row = tid >> 2, c8 = tid & 3;
+    if (x_thread) {
+      const int e = tid - X0, row = e >> 2, c8 = e & 3;
       *reinterpret_cast<u32x4*>(Xs + row * SP + c8 * 8) = rx;
     }
     if (w == 0) {
@@ -285,9 +350,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(FULL ? 2 : 
       dsum += cend;
     }
     __syncthreads();
-    if (tid < QB * PS / 8) {
+
+    // ---------------- phase A: x*w, Y_off, mask
+    const f32x4 cb_cur0 = rcb0, cb_cur1 = rcb1;
+    if (x_thread) {
       // x * w for the state product, once per workgroup, from the staged registers
-      const int row = tid >> 2, c8 = tid & 3;
+      const int e = tid - X0, row = e >> 2, c8 = e & 3;
       const float ws = wS[row];
       u32x4 hi, lo;
 #pragma unroll
@@ -302,17 +370,30 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(FULL ? 2 : 
     }
     if (blk + 1 < nblk) fetch(t0 + QB);
 
-    // ---------------- C B^T tiles -> mask -> M (bf16 high/low) in LDS
     if constexpr (FULL) {
-      // (B C^T)[s][t]: lane (l16, g4) gets M's row t = 16 ti + l16 at s = 16 tj + 4 g4 .. +3
-      auto cb_tile = [&](int ti, int tj) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      if (w < 2) {
+        // Y_off^T = H C^T for tokens [32 w, 32 w + 32) of the block; H = state entering the block.  Two
+        // accumulation chains (even and odd k-steps).
+        f32x16 ya = {}, yb = {};
 #pragma unroll
-        for (int kk = 0; kk < KN; ++kk)
-          acc = mfma(frag_rows(Bs, tj * 16 + l16, kk * 32 + g4 * 8, SN), frag_rows(Cs, ti * 16 + l16, kk * 32 + g4 * 8, SN),
-                     acc);
+        for (int ks = 0; ks < KS; ++ks) {
+          const int k0 = 16 * ks + 8 * hk;
+          const bf16x8 cfr = frag_rows(Cs, 32 * w + c32, k0, SN);
+          if (ks & 1) {
+            yb = mfma32(frag_rows(Hs, c32, k0, SN), cfr, yb);
+            yb = mfma32(frag_rows(Hl, c32, k0, SN), cfr, yb);
+          } else {
+            ya = mfma32(frag_rows(Hs, c32, k0, SN), cfr, ya);
+            ya = mfma32(frag_rows(Hl, c32, k0, SN), cfr, ya);
+          }
+        }
+        yacc = (ya + yb) * eS[32 * w + c32];
+      }
+      // mask this wave's C B^T tiles: lane (l16, g4) holds M's row t = 16 ti + l16 at s = 16 tj + 4 g4 .. +3
+      auto mask_tile = [&](int c, const f32x4& acc) {
+        const int ti = cb_tile_row(c), tj = c - ti * (ti + 1) / 2;
         const int t = ti * 16 + l16;
-        const int s0 = tj * 16 + 4 * g4;
+        const int s0 = tj * 16 + 4 * (l >> 4);
         const float ct = cumS[t];
         u32x2 hi, lo;
 #pragma unroll
@@ -327,94 +408,65 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(FULL ? 2 : 
         *reinterpret_cast<u32x2*>(Ms + t * SQ + s0) = hi;
         *reinterpret_cast<u32x2*>(Ml + t * SQ + s0) = lo;
       };
-      // 10 causal tiles: one per wave, a second for two of the waves that have no x * w to form
-      switch (w) {
-        case 0: cb_tile(0, 0); break;
-        case 1: cb_tile(1, 0); break;
-        case 2: cb_tile(1, 1); break;
-        case 3: cb_tile(2, 0); break;
-        case 4: cb_tile(2, 1); cb_tile(2, 2); break;
-        case 5: cb_tile(3, 0); cb_tile(3, 1); break;
-        case 6: cb_tile(3, 2); break;
-        default: cb_tile(3, 3); break;
-      }
+      mask_tile(cb0, cb_cur0);
+      if (cb1 >= 0) mask_tile(cb1, cb_cur1);
     }
-
-    // ---------------- Y_off^T = H C^T for (channel tile pw, token tile tw); H = state entering the block
-    f32x4 yoff = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < (FULL ? KN : 0); ++kk) {
-      const bf16x8 cb = frag_rows(Cs, tw * 16 + l16, kk * 32 + g4 * 8, SN);
-      yoff = mfma(frag_rows(Hs, pw * 16 + l16, kk * 32 + g4 * 8, SN), cb, yoff);
-      yoff = mfma(frag_rows(Hl, pw * 16 + l16, kk * 32 + g4 * 8, SN), cb, yoff);
-    }
-
     __syncthreads();   // M and x*w complete; every wave has finished reading Hs/Hl
 
-    // ---------------- S^T = B^T (X o w) for (state tiles of this wave, channel tile pw); H <- decay H + S
-    {
-      bf16x8 xh[2], xl[2];
+    // ---------------- phase B: state slices; Y_diag and the outputs
+    if (has_st) {
+      // S^T = B^T (X o w) for states [32 nq, 32 nq + 32); H <- decay H + S
+      f32x16 s = {};
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        // rows s = 32kk + 8g4 .. +7 of column p = 16pw + l16 of x*w
-        xh[kk] = __builtin_bit_cast(bf16x8, frag_cols_raw(XWh, kk * 32 + g4 * 8, pw * 16, SP, l16));
-        xl[kk] = __builtin_bit_cast(bf16x8, frag_cols_raw(XWl, kk * 32 + g4 * 8, pw * 16, SP, l16));
+      for (int ks = 0; ks < QB / 16; ++ks) {
+        const int k0 = 16 * ks + 8 * hk;
+        const bf16x8 bt = __builtin_bit_cast(bf16x8, frag_cols_raw(Bs, k0, 32 * nq + c16, SN, l16));
+        s = mfma32(bt, __builtin_bit_cast(bf16x8, frag_cols_raw(XWh, k0, c16, SP, l16)), s);
+        s = mfma32(bt, __builtin_bit_cast(bf16x8, frag_cols_raw(XWl, k0, c16, SP, l16)), s);
       }
       const float dec = decayS;
 #pragma unroll
-      for (int j = 0; j < NTW; ++j) {
-        const int nt = NTW * tw + j;
-        f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const bf16x8 bt = __builtin_bit_cast(bf16x8, frag_cols_raw(Bs, kk * 32 + g4 * 8, nt * 16, SN, l16));
-          s = mfma(bt, xh[kk], s);
-          s = mfma(bt, xl[kk], s);
-        }
-#pragma unroll
-        for (int v = 0; v < 4; ++v) Hacc[j][v] = fmaf(dec, Hacc[j][v], s[v]);
-      }
-    }
-
-
-    // ---------------- Y_diag^T = X^T M^T for (channel tile pw, token tile tw), epilogue
-    f32x4 ydiag = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (FULL) {
-      const int ksteps = (tw < 2) ? 1 : 2;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        if (kk < ksteps) {
-          const bf16x8 xb = __builtin_bit_cast(bf16x8, frag_cols_raw(Xs, kk * 32 + g4 * 8, pw * 16, SP, l16));
-          ydiag = mfma(xb, frag_rows(Ms, tw * 16 + l16, kk * 32 + g4 * 8, SQ), ydiag);
-          ydiag = mfma(xb, frag_rows(Ml, tw * 16 + l16, kk * 32 + g4 * 8, SQ), ydiag);
-        }
-      }
+      for (int v = 0; v < 16; ++v) Hacc[v] = fmaf(dec, Hacc[v], s[v]);
     }
     if constexpr (FULL) {
-      // lane (l16, g4): token t0 + 16 tw + l16, channels 16 pw + 4 g4 .. +3 (one 8-byte store)
-      const int tl = tw * 16 + l16;
-      const int p = pw * 16 + 4 * g4;
-      const int64_t t = t0 + tl;
-      if (t < L) {
-        const float et = eS[tl];
-        float yv[4];
+      if (w < 2) {
+        // Y_diag^T = X^T M^T for tokens [32 w, 32 w + 32): causal, so s < 32 (w + 1)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) yv[v] = fmaf(et, yoff[v], ydiag[v]);
-        const int64_t gi = ((b * L + t) * H + h) * P + p0 + p;
-        if (a.Dskip != nullptr) {
-          const u32x2 xr = *reinterpret_cast<const u32x2*>(Xs + tl * SP + p);
-#pragma unroll
-          for (int v = 0; v < 4; ++v) yv[v] = fmaf(Dv, bf2f((u16)(xr[v >> 1] >> (16 * (v & 1)))), yv[v]);
+        for (int ks = 0; ks < 4; ++ks) {
+          if (ks < 2 * (w + 1)) {
+            const int k0 = 16 * ks + 8 * hk;
+            const bf16x8 xb = __builtin_bit_cast(bf16x8, frag_cols_raw(Xs, k0, c16, SP, l16));
+            yacc = mfma32(xb, frag_rows(Ms, 32 * w + c32, k0, SQ), yacc);
+            yacc = mfma32(xb, frag_rows(Ml, 32 * w + c32, k0, SQ), yacc);
+          }
         }
-        if (a.z != nullptr) {
-          const u32x2 zr = *reinterpret_cast<const u32x2*>(gZ + gi);
+        // lane l: token t0 + 32 w + l % 32, channels 8 g + 4 (l / 32) .. +3 for g = 0..3 (8-byte stores)
+        const int tl = 32 * w + c32;
+        const int64_t t = t0 + tl;
+        if (t < L) {
 #pragma unroll
-          for (int v = 0; v < 4; ++v) yv[v] *= silu_f(bf2f((u16)(zr[v >> 1] >> (16 * (v & 1)))));
+          for (int g = 0; g < 4; ++g) {
+            const int p = 8 * g + 4 * hk;
+            float yv[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) yv[j] = yacc[4 * g + j];
+            const int64_t gi = ((b * L + t) * H + h) * P + p0 + p;
+            if (a.Dskip != nullptr) {
+              const u32x2 xr = *reinterpret_cast<const u32x2*>(Xs + tl * SP + p);
+#pragma unroll
+              for (int j = 0; j < 4; ++j) yv[j] = fmaf(Dv, bf2f((u16)(xr[j >> 1] >> (16 * (j & 1)))), yv[j]);
+            }
+            if (a.z != nullptr) {
+              const u32x2 zr = *reinterpret_cast<const u32x2*>(gZ + gi);
+#pragma unroll
+              for (int j = 0; j < 4; ++j) yv[j] *= silu_f(bf2f((u16)(zr[j >> 1] >> (16 * (j & 1)))));
+            }
+            u32x2 out;
+            out[0] = (unsigned)f2bf(yv[0]) | ((unsigned)f2bf(yv[1]) << 16);
+            out[1] = (unsigned)f2bf(yv[2]) | ((unsigned)f2bf(yv[3]) << 16);
+            *reinterpret_cast<u32x2*>(gY + gi) = out;
+          }
         }
-        u32x2 out;
-        out[0] = (unsigned)f2bf(yv[0]) | ((unsigned)f2bf(yv[1]) << 16);
-        out[1] = (unsigned)f2bf(yv[2]) | ((unsigned)f2bf(yv[3]) << 16);
-        *reinterpret_cast<u32x2*>(gY + gi) = out;
       }
     }
     if (FULL) store_state_split();   // the state entering the next block
@@ -422,9 +474,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(FULL ? 2 : 
   }
 
   float* hout = FULL ? (chunk == a.nchunks - 1 ? a.h_final : nullptr) : a.ws_state + chunk * slice;
-  if (hout != nullptr) {
+  if (hout != nullptr && has_st) {
 #pragma unroll
-    for (int j = 0; j < NTW; ++j) *reinterpret_cast<f32x4*>(hout + hrow + (NTW * tw + j) * 16 + 4 * g4) = Hacc[j];
+    for (int g = 0; g < 4; ++g) {
+      f32x4 v;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = Hacc[4 * g + j];
+      *reinterpret_cast<f32x4*>(hout + hrow + 32 * nq + 8 * g + 4 * hk) = v;
+    }
   }
   if (!FULL && w == 0 && l == 0 && ph == 0) a.ws_dsum[chunk * a.batch * H + b * H + h] = dsum;
 }
@@ -453,14 +510,15 @@ __global__ __launch_bounds__(256) void ssd_copy_state(const float* h0, float* ou
 
 }  // namespace
 
-SsdPlan plan_ssd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate, int num_cus) {
+SsdPlan plan_ssd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t ngroups, int64_t dstate,
+                 int num_cus) {
   // The full pass runs one workgroup per CU (its registers allow no second),
   // so time is split only when the (batch, head, half) workgroups cannot fill
   // the CUs: into enough chunks for one workgroup per CU, each of at least 8
   // blocks.  A split costs a state-only pass over its chunks and a carry of
   // one state per (batch, head); with the CUs already full it measured slower
   // (0.48 against 0.39 ms on the b2 x 64-head workload).
-  SsdPlan p{1, 0, 0};
+  SsdPlan p{1, 0, 0, 0, 0};
   const int64_t cus = num_cus > 0 ? num_cus : 256;
   const int64_t nwg = batch * nheads * (headdim / PS);
   if (nwg > 0 && nwg < cus && seqlen > 0) {
@@ -473,20 +531,29 @@ SsdPlan plan_ssd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
     p.nchunks = (seqlen + p.tchunk - 1) / p.tchunk;
   }
   p.tchunk = p.nchunks > 1 ? p.tchunk : (seqlen > 0 ? (seqlen + QB - 1) / QB * QB : QB);
+  auto round256 = [](size_t v) { return (v + 255) / 256 * 256; };
   if (p.nchunks > 1) {
     const size_t st = (size_t)p.nchunks * (size_t)(batch * nheads * headdim * dstate) * sizeof(float);
-    p.ws_bytes = (st + 255) / 256 * 256 + (size_t)p.nchunks * (size_t)(batch * nheads) * sizeof(float);
+    p.dsum_off = round256(st);
+    p.cb_off = p.dsum_off + round256((size_t)p.nchunks * (size_t)(batch * nheads) * sizeof(float));
   }
+  // C B^T tiles: 10 causal 16x16 fp32 tiles per (batch, 64-token block, group)
+  const size_t nblk = (size_t)((seqlen + QB - 1) / QB);
+  p.ws_bytes = seqlen > 0 ? p.cb_off + (size_t)batch * nblk * (size_t)ngroups * NCB * 256 * sizeof(float) : 0;
   return p;
 }
 
-size_t ssd_ws_bytes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t, int64_t dstate,
+size_t ssd_ws_bytes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t ngroups, int64_t dstate,
                     int64_t) {
-  return plan_ssd(batch, seqlen, nheads, headdim, dstate, device_cu_count()).ws_bytes;
+  return plan_ssd(batch, seqlen, nheads, headdim, ngroups, dstate, device_cu_count()).ws_bytes;
 }
 
 template <int N, bool DTB>
 hipError_t launch_ssd_n(const SsdArgs& a, dim3 grid, hipStream_t st) {
+  const int64_t nblk_total = (a.seqlen + QB - 1) / QB;
+  ssd_cb_kernel<N><<<dim3((unsigned)nblk_total, (unsigned)a.ngroups, (unsigned)a.batch), 64 * NCB, 0, st>>>(a, nblk_total);
+  hipError_t e0 = hipGetLastError();
+  if (e0 != hipSuccess) return e0;
   if (a.nchunks > 1) {
     ssd_fused_kernel<N, DTB, false><<<dim3(grid.x, (unsigned)(a.nchunks - 1)), NWAVE * 64, 0, st>>>(a);
     hipError_t e = hipGetLastError();
@@ -514,16 +581,15 @@ int launch_ssd(const SsdArgs& a0, void* stream) {
   }
   const int64_t nwg = a.batch * a.nheads * (a.headdim / PS);
   if (nwg > 0x7fffffffLL) return fail(4, "grid too large");
-  const SsdPlan p = plan_ssd(a.batch, a.seqlen, a.nheads, a.headdim, a.dstate, device_cu_count());
-  if (p.nchunks > 65535) return fail(4, "grid too large");
+  const SsdPlan p = plan_ssd(a.batch, a.seqlen, a.nheads, a.headdim, a.ngroups, a.dstate, device_cu_count());
+  if (p.nchunks > 65535 || a.batch > 65535 || a.ngroups > 65535 || (a.seqlen + QB - 1) / QB > 0x7fffffffLL)
+    return fail(4, "grid too large");
+  if (a.ws == nullptr) return fail(5, "SSD needs its workspace");
   a.nchunks = p.nchunks;
   a.tchunk = p.tchunk;
-  if (p.nchunks > 1) {
-    if (a.ws == nullptr) return fail(5, "SSD time split needs its workspace");
-    const size_t st_bytes = (size_t)p.nchunks * (size_t)(a.batch * a.nheads * a.headdim * a.dstate) * sizeof(float);
-    a.ws_state = (float*)a.ws;
-    a.ws_dsum = (float*)((char*)a.ws + (st_bytes + 255) / 256 * 256);
-  }
+  a.ws_state = (float*)a.ws;
+  a.ws_dsum = (float*)((char*)a.ws + p.dsum_off);
+  a.ws_cb = (float*)((char*)a.ws + p.cb_off);
   dim3 grid((unsigned)nwg);
   hipError_t e;
   if (a.dstate == 128) e = a.dt_bf16 ? launch_ssd_n<128, true>(a, grid, st) : launch_ssd_n<128, false>(a, grid, st);

@@ -120,15 +120,21 @@ struct SsdArgs {
   int64_t tchunk, nchunks;
   float* ws_state;     // nchunks x (batch, nheads, headdim, dstate): chunk states, then carries
   float* ws_dsum;      // nchunks x (batch, nheads): a * sum of dt over the chunk
+  float* ws_cb;        // (batch, 64-token block, group, causal 16x16 tile, lane) x 4: C_t . B_s per block
 };
 
-// Time split of the SSD pass: nchunks chunks of tchunk tokens (a multiple of
-// 64) whose states are computed in parallel and combined by a carry pass.
+// Workspace plan of the SSD pass.  The C B^T products of every 64-token block
+// (shared by all heads of a group) are formed once by a pre-pass.  When the
+// (batch, head) pairs cannot fill the device, the sequence is also split into
+// nchunks chunks of tchunk tokens (a multiple of 64) whose states are computed
+// in parallel and combined by a carry pass.
 struct SsdPlan {
   int64_t nchunks, tchunk;
   size_t ws_bytes;
+  size_t dsum_off, cb_off;   // byte offsets of ws_dsum and ws_cb (ws_state at 0)
 };
-SsdPlan plan_ssd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate, int num_cus);
+SsdPlan plan_ssd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t ngroups, int64_t dstate,
+                 int num_cus);
 size_t ssd_ws_bytes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t ngroups,
                     int64_t dstate, int64_t chunk);
 int launch_ssd(const SsdArgs& a, void* stream);

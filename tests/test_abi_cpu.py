@@ -148,11 +148,15 @@ def test_workspace_queries():
     # few slices, long sequence: the time-split path needs workspace
     assert lib.ssm_scan_workspace_bytes(1, 131072, 2048, 16, 0) > 0
     assert lib.ssm_scan_workspace_bytes(8, 2048, 1536, 16, 0) == 0
-    # SSD: the b2 x 64-head layer fills the CUs (no split); 1 x 4 heads x 3000 tokens splits into 5 chunks of
-    # 640 tokens: 5 fp32 states of 4 x 64 x 128 plus 5 x 4 decay sums
-    assert lib.ssd_workspace_bytes(2, 8192, 64, 64, 1, 128, 256) == 0
-    assert lib.ssd_workspace_bytes(1, 3000, 4, 64, 1, 128, 256) == 5 * 4 * 64 * 128 * 4 + 5 * 4 * 4
-    assert lib.ssd_workspace_bytes(1, 500, 4, 64, 1, 128, 256) == 0   # chunks would be shorter than 8 blocks
+    # SSD: every call keeps the C B^T products of each (batch, 64-token block, group): 10 causal 16 x 16 fp32
+    # tiles.  The b2 x 64-head layer fills the CUs (no split); 1 x 4 heads x 3000 tokens splits into 5 chunks
+    # of 640 tokens: 5 fp32 states of 4 x 64 x 128, then 5 x 4 decay sums, each part 256-byte aligned
+    cb = 10 * 256 * 4
+    assert lib.ssd_workspace_bytes(2, 8192, 64, 64, 1, 128, 256) == 2 * 128 * cb
+    assert lib.ssd_workspace_bytes(2, 8192, 64, 64, 4, 128, 256) == 2 * 128 * 4 * cb
+    assert lib.ssd_workspace_bytes(1, 3000, 4, 64, 1, 128, 256) == 5 * 4 * 64 * 128 * 4 + 256 + 47 * cb
+    assert lib.ssd_workspace_bytes(1, 500, 4, 64, 1, 128, 256) == 8 * cb   # chunks would be shorter than 8 blocks
+    assert lib.ssd_workspace_bytes(1, 0, 4, 64, 1, 128, 256) == 0
 
 
 def step(lib, **kw):
