@@ -13,20 +13,23 @@
 //   S_blk    = (X o w)^T B,     w_s = exp(cum_end - cum_s) g_s
 //   H       <- exp(cum_end) H + S_blk
 //
-// Mapping.  One workgroup of 8 waves per (batch, head, half of the 64 head
-// channels): 256 workgroups for the 2-batch, 64-head workload, one per CU and
-// two waves per SIMD.  The workgroup walks the sequence in 64-token blocks;
-// the fp32 state H (32 x dstate) stays in MFMA accumulator registers for the
-// whole sequence and is never written to HBM.  All products are
-// v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  B, C and x are staged in
-// LDS in their natural token-major layout; the products that contract over
-// tokens (X for M X, X and B for (X o w)^T B) read their operands with the
-// gfx950 LDS transpose load (ds_read_b64_tr_b16), so no transposed copies are
-// made.  The fp32 operands (M, x*w and the state) enter as a bf16 high part
-// plus a bf16 low part, keeping ~16 bits instead of 8: a single bf16 copy of
-// the state loses accuracy where C.H cancels over the states.  The block's
-// decay prefix sum is a DPP scan in one wave during staging; the next block's
-// B, C, x and dt are loaded into registers while the current one computes.
+// Mapping.  C B^T does not depend on the head, so a pre-pass forms it once
+// per (batch, 64-token block, group).  The main kernel runs one workgroup of
+// 8 waves per (batch, head, half of the 64 head channels): 256 workgroups for
+// the 2-batch, 64-head workload, one per CU.  The workgroup walks the
+// sequence in 64-token blocks; the fp32 state H (32 x dstate) stays in
+// registers for the whole sequence and is never written to HBM.  The block
+// products run on the 32x32x16 bf16 MFMA with fp32 accumulation, computed
+// transposed (Y^T, S^T) so that result lanes hold runs of consecutive
+// channels or states.  B, C and x are staged in LDS in their natural
+// token-major layout; the products that contract over tokens read their
+// operands with the gfx950 LDS transpose load (ds_read_b64_tr_b16), so no
+// transposed copies are made.  The fp32 operands (M, x*w and the state)
+// enter as a bf16 high part plus a bf16 low part, keeping ~16 bits instead
+// of 8: a single bf16 copy of the state loses accuracy where C.H cancels over
+// the states.  The block's decay prefix sum is a DPP scan in one wave during
+// staging; the next block's B, C, x, dt and C B^T tiles are loaded into
+// registers while the current one computes.
 //
 // Block size.  Any chunk length that is a multiple of 64 gives the same map
 // (the state entering a 64-token block is the decayed sum of everything
