@@ -174,7 +174,7 @@ size_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int6
  *   B, C    : (batch, seqlen, ngroups, dstate)  act dtype
  *   Dskip, dt_bias : (nheads) fp32 or NULL
  *   h0, h_final    : (batch, nheads, headdim, dstate) fp32 or NULL
- * Supported: act_dtype SSM_BF16, headdim == 64, dstate in {64, 128},
+ * Supported: act_dtype SSM_BF16, headdim in {64, 128}, dstate in {64, 128},
  * chunk_size in {64, 128, 256}, nheads % ngroups == 0.  Other valid shapes
  * return SSM_ERR_UNSUPPORTED.
  */

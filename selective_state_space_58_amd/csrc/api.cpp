@@ -239,7 +239,7 @@ int ssd_chunk_scan_fwd(const void* x, const void* dt, const float* A, const void
       !elems_ok({batch, nheads, headdim, dstate}))
     return fail(SSM_ERR_SHAPE, "sizes overflow 64-bit indexing");
   if (act_dtype != SSM_BF16) return fail(SSM_ERR_UNSUPPORTED, "SSD supports bf16 activations only");
-  if (headdim != 64) return fail(SSM_ERR_UNSUPPORTED, "SSD supports headdim 64");
+  if (headdim != 64 && headdim != 128) return fail(SSM_ERR_UNSUPPORTED, "SSD supports headdim 64 or 128");
   if (dstate != 64 && dstate != 128) return fail(SSM_ERR_UNSUPPORTED, "SSD supports dstate 64 or 128");
   if (chunk_size != 64 && chunk_size != 128 && chunk_size != 256)
     return fail(SSM_ERR_UNSUPPORTED, "SSD supports chunk_size 64, 128 or 256");

@@ -15,8 +15,8 @@
 //
 // Mapping.  C B^T does not depend on the head, so a pre-pass forms it once
 // per (batch, 64-token block, group).  The main kernel runs one workgroup of
-// 8 waves per (batch, head, half of the 64 head channels): 256 workgroups for
-// the 2-batch, 64-head workload, one per CU.  The workgroup walks the
+// 8 waves per (batch, head, 32-channel slice of the head): 256 workgroups for
+// the 2-batch, 64-head, 64-channel workload, one per CU.  The workgroup walks the
 // sequence in 64-token blocks; the fp32 state H (32 x dstate) stays in
 // registers for the whole sequence and is never written to HBM.  The block
 // products run on the 32x32x16 bf16 MFMA with fp32 accumulation, computed
@@ -216,9 +216,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   const int64_t nb = gridDim.x;
   int64_t lin = blockIdx.x;
   if ((nb & 7) == 0) lin = (lin & 7) * (nb >> 3) + (lin >> 3);  // a contiguous range of heads per XCD
-  const int ph = (int)(lin & 1);
-  const int64_t h = (lin >> 1) % H;
-  const int64_t b = (lin >> 1) / H;
+  const int64_t nsl = P / PS;                    // 32-channel slices per head
+  const int ph = (int)(lin % nsl);
+  const int64_t h = (lin / nsl) % H;
+  const int64_t b = (lin / nsl) / H;
   const int64_t grp = h / (H / a.ngroups);
   const float av = a.A[h];
   const float bias = a.dt_bias != nullptr ? a.dt_bias[h] : 0.f;

@@ -134,7 +134,8 @@ def ssd(lib, **kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(x=None), 1), (dict(y=None), 1), (dict(nheads=3, ngroups=2), 2), (dict(headdim=-1), 2),
-    (dict(act=7), 3), (dict(act=0), 4), (dict(headdim=32), 4), (dict(dstate=96), 4), (dict(chunk=100), 4),
+    (dict(act=7), 3), (dict(act=0), 4), (dict(headdim=32), 4), (dict(headdim=96), 4), (dict(headdim=256), 4),
+    (dict(dstate=96), 4), (dict(chunk=100), 4),
     (dict(x=P + 2), 7),
 ])
 def test_ssd_argument_errors(kw, code):

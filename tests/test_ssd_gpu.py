@@ -77,6 +77,14 @@ def test_time_split(ssm, N, G, L):
     check(ssm, inp, "time split L=%d N=%d G=%d" % (L, N, G))
 
 
+@pytest.mark.parametrize("N,G,L", [(128, 1, 333), (64, 2, 700), (128, 2, 3000)])
+def test_headdim_128(ssm, N, G, L):
+    # four 32-channel slices per head; L=3000 on 4 heads also takes the time split
+    inp = workloads.ssd_inputs(1, L, 4, 128, N, ngroups=G, seed=L + 7 * N + G, gate=True, skip=True, h0=True,
+                               dt_softplus=True)
+    check(ssm, inp, "headdim 128 L=%d N=%d G=%d" % (L, N, G))
+
+
 def test_time_split_workspace_checks(ssm):
     inp = workloads.ssd_inputs(1, 3000, 4, 64, 128, seed=5)
     t = workloads.to_device(inp, DEV)
