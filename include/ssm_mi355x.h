@@ -58,7 +58,7 @@ enum ssm_status {
   SSM_ERR_NULL = 1,         /* a required pointer is NULL */
   SSM_ERR_SHAPE = 2,        /* a size is negative, inconsistent or overflows 64-bit indexing */
   SSM_ERR_DTYPE = 3,        /* unknown dtype code */
-  SSM_ERR_UNSUPPORTED = 4,  /* valid but not implemented here (e.g. dstate > 128) */
+  SSM_ERR_UNSUPPORTED = 4,  /* valid but not implemented here (e.g. scan dstate > 256) */
   SSM_ERR_WORKSPACE = 5,    /* workspace given but smaller than required */
   SSM_ERR_HIP = 6,          /* a HIP runtime call failed (see ssm_last_error) */
   SSM_ERR_ALIGNMENT = 7     /* a pointer is not aligned to its element size */
@@ -89,7 +89,7 @@ enum ssm_status {
  *   h0             : (batch, dim, dstate) fp32 or NULL (zeros)
  *   y              : required output
  *   h_final        : (batch, dim, dstate) fp32 output or NULL
- *   dstate         : 1..128
+ *   dstate         : 1..256 (129..256 run 8 rows of 32 states per wave)
  * Long sequences with few (batch, channel) slices are split into time chunks
  * whose carries are combined on the device (needs workspace).
  */

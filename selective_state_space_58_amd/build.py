@@ -19,7 +19,7 @@ MB_LIB = os.path.join(HERE, "libssm_microbench.so")
 MB_SOURCE = ("microbench.hip", [])
 SOURCES = [("api.cpp", []), ("scan_host.hip", []), ("ssd_kernels.hip", []), ("step_kernels.hip", []), ("conv_kernels.hip", []), ("scan_bwd.hip", [])] + [
     ("scan_inst.hip", ["-DSSM_R=%d" % rr, "-DSSM_XB=%d" % xb, "-DSSM_DB=%d" % db, "-DSSM_S=%d" % sv])
-    for rr, sv in ((4, 32), (4, 16), (4, 8), (4, 4), (4, 2), (4, 1), (8, 2), (16, 1))
+    for rr, sv in ((4, 32), (8, 32), (4, 16), (4, 8), (4, 4), (4, 2), (4, 1), (8, 2), (16, 1))
     for xb in (1, 0) for db in (1, 0)]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-Wall", "-Wno-unused-command-line-argument",

@@ -83,7 +83,7 @@ int validate_scan(const void* x, const void* delta, const float* A, const void* 
   if (!elems_ok({batch, seqlen, dim}) || !elems_ok({batch, seqlen, dstate}) || !elems_ok({batch, dim, dstate}) ||
       !elems_ok({dim, dstate}))
     return fail(SSM_ERR_SHAPE, "sizes overflow 64-bit indexing");
-  if (dstate > 128) return fail(SSM_ERR_UNSUPPORTED, "dstate > 128 is not supported");
+  if (dstate > 256) return fail(SSM_ERR_UNSUPPORTED, "dstate > 256 is not supported");
   const size_t as = dsize(act_dtype), ds = dsize(delta_dtype);
   if (!aligned(x, as) || !aligned(B, as) || !aligned(C, as) || !aligned(z, as) || !aligned(y_or_hf, final_only ? 4 : as) ||
       !aligned(delta, ds) || !aligned(A, 4) || !aligned(Dskip, 4) || !aligned(bias, 4) || !aligned(h0, 4) ||
@@ -137,7 +137,7 @@ const char* ssm_status_string(int status) {
 const char* ssm_last_error(void) { return g_last_error.c_str(); }
 
 size_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int final_state_only) {
-  if (batch <= 0 || seqlen <= 0 || dim <= 0 || dstate <= 0 || dstate > 128) return 0;
+  if (batch <= 0 || seqlen <= 0 || dim <= 0 || dstate <= 0 || dstate > 256) return 0;
   return plan_scan(batch, seqlen, dim, dstate, final_state_only != 0, device_cu_count()).ws_bytes;
 }
 

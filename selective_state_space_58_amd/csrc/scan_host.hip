@@ -13,7 +13,8 @@ namespace ssm {
                                                      hipStream_t st);
 #define SSM_DECL_ALL(XB, DB)                                                                             \
   SSM_DECL(4, XB, DB, 1) SSM_DECL(4, XB, DB, 2) SSM_DECL(4, XB, DB, 4) SSM_DECL(4, XB, DB, 8)            \
-  SSM_DECL(4, XB, DB, 16) SSM_DECL(4, XB, DB, 32) SSM_DECL(8, XB, DB, 2) SSM_DECL(16, XB, DB, 1)
+  SSM_DECL(4, XB, DB, 16) SSM_DECL(4, XB, DB, 32) SSM_DECL(8, XB, DB, 2) SSM_DECL(8, XB, DB, 32)          \
+  SSM_DECL(16, XB, DB, 1)
 SSM_DECL_ALL(0, 0)
 SSM_DECL_ALL(0, 1)
 SSM_DECL_ALL(1, 0)
@@ -54,6 +55,7 @@ hipError_t launch_s(int R, int S, int mode, const ScanArgs& a, dim3 grid, int64_
   hipError_t launch_s<XB, DB>(int R, int S, int mode, const ScanArgs& a, dim3 grid, int64_t gpb,          \
                               hipStream_t st) {                                                           \
     if (R == 8 && S == 2) return launch_scan_r8_x##XB##_d##DB##_s2(mode, a, grid, gpb, st);               \
+    if (R == 8 && S == 32) return launch_scan_r8_x##XB##_d##DB##_s32(mode, a, grid, gpb, st);             \
     if (R == 16 && S == 1) return launch_scan_r16_x##XB##_d##DB##_s1(mode, a, grid, gpb, st);             \
     if (R != 4) return hipErrorInvalidValue;                                                              \
     switch (S) {                                                                                          \
@@ -103,8 +105,13 @@ ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, b
     else if (waves4 < 2 * simds) p.R = 8;
   }
   if (p.R != 4) S = 16 / p.R;
+  if (dstate > 128) {
+    // 129..256 states: 8 rows of 32 states (one wave per SIMD, 16-token tiles)
+    p.R = 8;
+    S = 32;
+  }
   p.S = S;
-  p.T = p.R == 4 ? 32 : 64;
+  p.T = p.R == 4 ? 32 : (S >= 16 ? 16 : 64);   // the kernel's LDS tile
   const int64_t waves = batch * ceil_div(dim, 64 / p.R);
   int64_t nch = 1;
   // Split time only when fewer than half of the SIMDs would get a wave: the

@@ -170,13 +170,19 @@ template <>
 struct VecOf<2> {
   using T = u32x2;
 };
+// (one word: declared by the 8-row wide-lane tiles, whose vector path is never taken)
+typedef unsigned u32x1 __attribute__((ext_vector_type(1)));
+template <>
+struct VecOf<1> {
+  using T = u32x1;
+};
 
 template <int R_, int S>
 struct TileShape {
   static constexpr int R = R_;
   static constexpr int CH = 64 / R;                // channels per wave
   static constexpr int NP = R * S;                 // padded state count of the wave
-  static constexpr int T = R == 4 ? 32 : 64;       // tokens per LDS tile
+  static constexpr int T = R == 4 ? 32 : (S >= 16 ? 16 : 64);   // tokens per LDS tile
   static constexpr int KX = T / R;                 // (token, channel) items per lane per tile
   static constexpr int KB = T * NP / 64;           // B (and C) items per lane per tile
 };
@@ -533,7 +539,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
       // read and exponentials taken as they are used.  The S independent
       // state chains of a token cover the exp and LDS latencies; staging a
       // step ahead would hold 8S registers per lane and spill.
-      static_assert(R == 4, "wide lanes use the 4-row layout");
+      static_assert(R == 4 || R == 8, "wide lanes use the 4- or 8-row layout");
 #pragma unroll 1
       for (int tb = 0; tb < T; tb += R) {
         float pr[R];
@@ -582,18 +588,19 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
   if (!FULL && a.nchunks > 1 && r == 0 && ch_ok) a.ws_dsum[chunk * a.batch * dim + b * dim + ch] = dsum;
 }
 
-// Waves per SIMD the register budget is sized for: the 4-row layout runs one
-// wave per SIMD on its target shapes, the 8- and 16-row layouts two and three.
-template <int RR>
+// Waves per SIMD the register budget is sized for: the 4-row layout and wide
+// lanes run one wave per SIMD on their target shapes, the 8- and 16-row
+// layouts two and three.
+template <int RR, int S>
 constexpr int scan_waves_per_simd() {
-  return RR == 4 ? 1 : RR == 8 ? 2 : 3;
+  return (RR == 4 || S >= 16) ? 1 : RR == 8 ? 2 : 3;
 }
 
 // W waves per workgroup (1, or 4 on the vector path): the waves of a
 // workgroup scan W consecutive channel groups of one batch row and share the
 // staged tiles.
 template <int RR, bool XB, bool DB, int S, int MODE, bool VEC, int W>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(scan_waves_per_simd<RR>())))
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(scan_waves_per_simd<RR, S>())))
 void scan_kernel(ScanArgs a, int64_t groups_per_batch) {
   using TS = TileShape<RR, S>;
   __shared__ __attribute__((aligned(16))) float2 s_dx[TS::T * TS::CH * W];

@@ -75,7 +75,7 @@ def scan(lib, **kw):
     (dict(batch=-1), 2), (dict(seqlen=-1), 2), (dict(dim=-2), 2), (dict(dstate=0), 2), (dict(sp=2), 2),
     (dict(batch=1 << 40, seqlen=1 << 20, dim=1 << 10), 2),
     (dict(act=5), 3), (dict(ddt=-1), 3),
-    (dict(dstate=129), 4),
+    (dict(dstate=257), 4),
     (dict(x=P + 1), 7), (dict(A=P + 2), 7), (dict(h0=P + 2), 7),
 ])
 def test_scan_argument_errors(kw, code):
@@ -101,7 +101,7 @@ def test_scan_ex_rejects_unknown_flags(flags):
 
 
 @pytest.mark.parametrize("kw,code", [(dict(x=None), 1), (dict(delta=None), 1), (dict(batch=-1), 2),
-                                     (dict(dstate=129), 4), (dict(ddt=5), 3), (dict(x=P + 1), 7)])
+                                     (dict(dstate=257), 4), (dict(ddt=5), 3), (dict(x=P + 1), 7)])
 def test_scan_ex_argument_errors(kw, code):
     # every flag combination goes through the same validation as ssm_scan_fwd
     lib = _lib()
@@ -149,6 +149,9 @@ def test_workspace_queries():
     # few slices, long sequence: the time-split path needs workspace
     assert lib.ssm_scan_workspace_bytes(1, 131072, 2048, 16, 0) > 0
     assert lib.ssm_scan_workspace_bytes(8, 2048, 1536, 16, 0) == 0
+    # 129..256 states run 8 rows of 32 states per wave; 257 is unsupported
+    assert lib.ssm_scan_workspace_bytes(1, 65536, 64, 256, 0) > 0
+    assert lib.ssm_scan_workspace_bytes(1, 65536, 64, 257, 0) == 0
     # SSD: every call keeps the C B^T products of each (batch, 64-token block, group): 10 causal 16 x 16 fp32
     # tiles.  The b2 x 64-head layer fills the CUs (no split); 1 x 4 heads x 3000 tokens splits into 5 chunks
     # of 640 tokens: 5 fp32 states of 4 x 64 x 128, then 5 x 4 decay sums, each part 256-byte aligned

@@ -60,7 +60,7 @@ def test_ragged_shapes_gate_softplus_h0(ssm, dtype, shape):
     check(ssm, inp, label="%s %s" % (dtype, shape))
 
 
-@pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 8, 12, 16, 17, 32, 64, 100, 128])
+@pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 8, 12, 16, 17, 32, 64, 100, 128, 129, 200, 256])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_state_sizes(ssm, N, dtype):
     inp = workloads.scan_inputs(2, 150, 20, N, dtype=dtype, seed=1000 + N, dt="loguniform", gate=False,
@@ -81,6 +81,16 @@ def test_long_sequence_time_split(ssm, dtype, L, D):
                                 skip=True, gate=(dtype == "bf16"), h0=True)
     assert ssm.ssm_scan_workspace_bytes(1, L, D, 16) > 0       # exercises the chunk + carry path
     check(ssm, inp, label="long %s L=%d D=%d" % (dtype, L, D))
+
+
+@pytest.mark.parametrize("dtype,N", [("bf16", 256), ("f32", 200)])
+def test_wide_state_time_split(ssm, dtype, N):
+    # 129..256 states (8 rows of 32 states per wave) on few channels and a long sequence: chunk states
+    # computed in parallel and carried
+    inp = workloads.scan_inputs(1, 6000, 16, N, dtype=dtype, seed=6000 + N, dt="loguniform", dt_lo=1e-4, dt_hi=1e-1,
+                                skip=True, gate=True, h0=True)
+    assert ssm.ssm_scan_workspace_bytes(1, 6000, 16, N) > 0
+    check(ssm, inp, label="wide time split %s N=%d" % (dtype, N))
 
 
 # Sequence lengths of one token, a few, exactly one tile and just past a power of two, each
@@ -109,9 +119,9 @@ def test_workgroup_layouts(ssm, dtype, shape):
     check(ssm, inp, label="layout %s %s" % (dtype, shape))
 
 
-@pytest.mark.parametrize("L", [300, 5000])
-def test_final_state_entry(ssm, L):
-    inp = workloads.scan_inputs(2, L, 24, 16, dtype="bf16", seed=L + 1, dt="softplus_bias", softplus=True, h0=True)
+@pytest.mark.parametrize("L,N", [(300, 16), (5000, 16), (700, 256)])
+def test_final_state_entry(ssm, L, N):
+    inp = workloads.scan_inputs(2, L, 24, N, dtype="bf16", seed=L + N + 1, dt="softplus_bias", softplus=True, h0=True)
     t = workloads.to_device(inp, DEV)
     hf = ssm.ssm_scan_final_state(t["x"], t["delta"], t["A"], t["B"], delta_bias=t["delta_bias"],
                                   delta_softplus=True, h0=t["h0"])

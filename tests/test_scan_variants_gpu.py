@@ -61,9 +61,10 @@ VARIANTS = [(True, False), (False, True), (True, True)]
 
 # shapes covering each lane layout: 16 rows (few slices, short), 4 rows with several states per
 # lane (dstate 64), 4 rows split in time (long, few slices), ragged tiles and channel groups,
-# the vector tile path (dim a multiple of the group width) and the scalar path
+# the vector tile path (dim a multiple of the group width) and the scalar path, and 8 rows of 32
+# states (dstate 200)
 SHAPES = [(2, 300, 48, 16), (3, 97, 33, 16), (2, 301, 40, 64), (1, 3000, 40, 16), (1, 1, 17, 16),
-          (2, 130, 24, 5)]
+          (2, 130, 24, 5), (2, 90, 20, 200)]
 
 
 @pytest.mark.parametrize("reverse,euler", VARIANTS)
