@@ -293,7 +293,7 @@ int ssm_causal_conv1d_fwd(const void* x, const float* weight, const float* bias,
  *   dz          : (batch, seqlen, dim) act dtype, required when z is given
  *   ddelta_bias : (dim) fp32, required when delta_bias is given
  *   dh0         : (batch, dim, dstate) fp32 or NULL
- * dstate 1..128 (one pass over the sequence per 16 states).  dB and dC are
+ * dstate 1..256 (one pass over the sequence per 16 states).  dB and dC are
  * summed over channels in a fixed order (per
  * 16-channel group, then over the groups), so they are deterministic; the
  * sums over channels and batch of dA, and over batch of dDskip and

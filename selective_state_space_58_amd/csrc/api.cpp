@@ -368,7 +368,7 @@ int ssm_causal_conv1d_fwd(const void* x, const float* weight, const float* bias,
 }
 
 size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
-  if (batch <= 0 || seqlen <= 0 || dim <= 0 || dstate <= 0 || dstate > 128) return 0;
+  if (batch <= 0 || seqlen <= 0 || dim <= 0 || dstate <= 0 || dstate > 256) return 0;
   if (!elems_ok({batch, seqlen, dim, dstate})) return 0;
   return scan_bwd_ws_bytes(batch, seqlen, dim, dstate);
 }
@@ -392,7 +392,7 @@ static int bwd_common(const void* x, const void* delta, const float* A, const vo
       (dim > 0 && dA == nullptr) || (has_tok && z != nullptr && dz == nullptr) ||
       (dim > 0 && Dskip != nullptr && dDskip == nullptr) || (dim > 0 && delta_bias != nullptr && ddelta_bias == nullptr))
     return fail(SSM_ERR_NULL, "dout, dx, ddelta, dA, dB, dC and the gradients of the optional inputs given are required");
-  if (dstate > 128) return fail(SSM_ERR_UNSUPPORTED, "the backward pass supports dstate <= 128");
+  if (dstate > 256) return fail(SSM_ERR_UNSUPPORTED, "the backward pass supports dstate <= 256");
   const size_t as = dsize(act_dtype), ds = dsize(delta_dtype);
   if (!aligned(dout, as) || !aligned(dx, as) || !aligned(dz, as) || !aligned(ddelta, ds) || !aligned(dA, 4) ||
       !aligned(dB, 4) || !aligned(dC, 4) || !aligned(dDskip, 4) || !aligned(ddelta_bias, 4) ||

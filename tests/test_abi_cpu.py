@@ -248,7 +248,7 @@ def bwd(lib, **kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(dout=None), 1), (dict(dx=None), 1), (dict(ddelta=None), 1), (dict(dA=None), 1), (dict(dB=None), 1),
     (dict(z=P), 1), (dict(D=P), 1), (dict(bias=P), 1), (dict(seqlen=-1), 2), (dict(act=3), 3),
-    (dict(dstate=129), 4), (dict(dx=P + 0x100001), 7), (dict(dA=P + 0x100002), 7),
+    (dict(dstate=257), 4), (dict(dx=P + 0x100001), 7), (dict(dA=P + 0x100002), 7),
 ])
 def test_scan_bwd_argument_errors(kw, code):
     lib = _lib()
@@ -281,5 +281,6 @@ def test_scan_bwd_workspace_query():
     # more than 16 states: the same per-block buffers plus three fp32 accumulators of dx, ddelta, dz
     assert lib.ssm_scan_bwd_workspace_bytes(2, 100, 40, 17) == ckpt + part + 3 * 2 * 100 * 40 * 4
     assert lib.ssm_scan_bwd_workspace_bytes(2, 100, 40, 128) == ckpt + part + 3 * 2 * 100 * 40 * 4
-    assert lib.ssm_scan_bwd_workspace_bytes(2, 100, 40, 129) == 0
+    assert lib.ssm_scan_bwd_workspace_bytes(2, 100, 40, 256) == ckpt + part + 3 * 2 * 100 * 40 * 4
+    assert lib.ssm_scan_bwd_workspace_bytes(2, 100, 40, 257) == 0
     assert bwd(lib, batch=0) == 0

@@ -75,7 +75,7 @@ def test_scan_bwd_shapes(ssm, dtype, shape):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("shape", [(2, 70, 40, 17), (1, 100, 32, 32), (2, 53, 24, 64), (1, 40, 20, 100),
-                                   (1, 33, 16, 128)])
+                                   (1, 33, 16, 128), (1, 30, 12, 200), (1, 21, 8, 256)])
 def test_scan_bwd_more_states(ssm, dtype, shape):
     # one pass per block of 16 states, the per-token gradients summed over the blocks
     b, L, D, N = shape
