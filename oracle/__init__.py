@@ -103,7 +103,10 @@ def selective_scan(x, delta, A, B, C, Dskip=None, z=None, delta_bias=None,
     """O1: y (batch, seqlen, dim) and h_final (batch, dim, dstate), both float64.
     euler: the Euler input discretization Bbar = dt * B (O1e).  reverse: the scan run over the
     time-reversed sequence, by definition flip(scan(flip(inputs))): h0 is the state before the last
-    token, h_final the state after token 0, and y_t depends on tokens t .. L-1."""
+    token, h_final the state after token 0, and y_t depends on tokens t .. L-1.
+    delta of shape (batch, seqlen): one step size per token, read by every channel ("SSM & Mamba",
+    the numpy selective SSM implementation projects one step size per token), i.e. O1 with delta
+    broadcast over the channel axis."""
     if reverse:
         flip = lambda a: None if a is None else np.ascontiguousarray(np.flip(np.asarray(a, dtype=np.float64), 1))
         y, hf = selective_scan(flip(x), flip(delta), A, flip(B), flip(C), Dskip=Dskip, z=flip(z),
@@ -114,6 +117,8 @@ def selective_scan(x, delta, A, B, C, Dskip=None, z=None, delta_bias=None,
     batch, seqlen, dim = x.shape
     A = _f64(A)
     dstate = A.shape[1]
+    if np.ndim(delta) == 2:
+        delta = np.repeat(_f64(delta, (batch, seqlen))[:, :, None], dim, axis=2)
     delta = _f64(delta, x.shape)
     B = _f64(B, (batch, seqlen, dstate))
     C = _f64(C, (batch, seqlen, dstate))
@@ -138,7 +143,9 @@ def selective_scan_bwd(x, delta, A, B, C, dout, Dskip=None, z=None, delta_bias=N
     dx, ddelta, dA, dB, dC and, for the optional inputs given, dDskip, dz, ddelta_bias, dh0.
     Threads accumulate the shared gradients (dA, dB, dC, dDskip, ddelta_bias) in private buffers.
     euler: the gradient of O1e (O5e).  reverse: the gradient of the reversed scan flip(scan(flip)), by
-    definition the flipped gradients of the scan of the flipped inputs."""
+    definition the flipped gradients of the scan of the flipped inputs.  delta of shape (batch, seqlen)
+    (one step size per token, shared by the channels): O1 with delta broadcast over the channels, so
+    ddelta is the broadcast form's ddelta summed over the channel axis (the chain rule of a broadcast)."""
     if reverse:
         flip = lambda a: None if a is None else np.ascontiguousarray(np.flip(np.asarray(a, dtype=np.float64), 1))
         g = selective_scan_bwd(flip(x), flip(delta), A, flip(B), flip(C), flip(dout), Dskip=Dskip, z=flip(z),
@@ -147,6 +154,13 @@ def selective_scan_bwd(x, delta, A, B, C, dout, Dskip=None, z=None, delta_bias=N
         for k in ("dx", "ddelta", "dB", "dC", "dz"):
             if k in g:
                 g[k] = flip(g[k])
+        return g
+    if np.ndim(delta) == 2:
+        nd = np.shape(x)[2]
+        full = np.repeat(_f64(delta)[:, :, None], nd, axis=2)
+        g = selective_scan_bwd(x, full, A, B, C, dout, Dskip=Dskip, z=z, delta_bias=delta_bias,
+                               delta_softplus=delta_softplus, h0=h0, dh_final=dh_final, threads=threads, euler=euler)
+        g["ddelta"] = g["ddelta"].sum(axis=2)
         return g
     x = _f64(x)
     batch, seqlen, dim = x.shape

@@ -294,16 +294,19 @@ def _scan_loss(oracle_mod, p, dout, dh_final, softplus, euler=False, reverse=Fal
     return float(np.sum(dout * y) + np.sum(dh_final * hf))
 
 
-@pytest.mark.parametrize("softplus,full,euler,reverse", [(True, True, False, False), (False, True, False, False),
-                                                         (False, False, False, False), (True, True, True, False),
-                                                         (False, True, False, True), (True, True, True, True)])
-def test_scan_backward_against_finite_differences(oracle_mod, softplus, full, euler, reverse):
-    # every gradient of O5 (O5e for Euler, the flipped form for reverse) against central differences of the
-    # matching forward (O1 / O1e, pinned above)
-    rng = np.random.default_rng(80 + 2 * softplus + full + 4 * euler + 8 * reverse)
+@pytest.mark.parametrize("softplus,full,euler,reverse,per_token",
+                         [(True, True, False, False, False), (False, True, False, False, False),
+                          (False, False, False, False, False), (True, True, True, False, False),
+                          (False, True, False, True, False), (True, True, True, True, False),
+                          (True, True, False, False, True), (False, False, True, True, True)])
+def test_scan_backward_against_finite_differences(oracle_mod, softplus, full, euler, reverse, per_token):
+    # every gradient of O5 (O5e for Euler, the flipped form for reverse, the channel-summed ddelta for one
+    # step size per token) against central differences of the matching forward (O1 / O1e, pinned above)
+    rng = np.random.default_rng(80 + 2 * softplus + full + 4 * euler + 8 * reverse + 16 * per_token)
     b, L, D, N = 2, 6, 3, 4
+    dshape = (b, L) if per_token else (b, L, D)
     p = dict(x=rng.standard_normal((b, L, D)),
-             delta=(rng.standard_normal((b, L, D)) if softplus else rng.uniform(0.05, 0.8, (b, L, D))),
+             delta=(rng.standard_normal(dshape) if softplus else rng.uniform(0.05, 0.8, dshape)),
              A=-rng.uniform(0.2, 3.0, (D, N)), B=rng.standard_normal((b, L, N)), C=rng.standard_normal((b, L, N)))
     p["A"][0, 0] = 0.0                       # the a = 0 limit of the gain and its derivative
     p["A"][1, 1] = -1e-7                     # |dt a| far below the series threshold
