@@ -313,13 +313,18 @@ int ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Backward pass of ssm_scan_fwd_ex: the same arguments, layouts, ownership,
- * errors and workspace as ssm_scan_bwd, for the forward variant selected by
- * `flags` (SSM_SCAN_REVERSE, SSM_SCAN_EULER or both; 0 is ssm_scan_bwd).
- * With SSM_SCAN_REVERSE the gradients are those of the reversed scan (h0 enters
- * at the last token, dh_final applies to the state after token 0); with
- * SSM_SCAN_EULER those of the gain dt (dgain/ddt = 1, no dependence on A).
- * SSM_SCAN_DELTA_PER_TOKEN and unknown bits return SSM_ERR_UNSUPPORTED.
+ * Backward pass of ssm_scan_fwd_ex: the same arguments, layouts, ownership and
+ * errors as ssm_scan_bwd, for the forward variant selected by `flags` (any
+ * combination of SSM_SCAN_REVERSE, SSM_SCAN_EULER, SSM_SCAN_DELTA_PER_TOKEN;
+ * 0 is ssm_scan_bwd).  With SSM_SCAN_REVERSE the gradients are those of the
+ * reversed scan (h0 enters at the last token, dh_final applies to the state
+ * after token 0); with SSM_SCAN_EULER those of the gain dt (dgain/ddt = 1, no
+ * dependence on A).  With SSM_SCAN_DELTA_PER_TOKEN, delta and ddelta are
+ * (batch, seqlen) in the delta dtype: one step size per token shared by every
+ * channel, so ddelta is the per-channel gradient summed over the channels (in
+ * a fixed order: deterministic); ddelta_bias stays per channel.  Workspace:
+ * ssm_scan_bwd_ex_workspace_bytes() for these flags, or NULL.  Unknown bits
+ * return SSM_ERR_UNSUPPORTED.
  */
 int ssm_scan_bwd_ex(const void* x, const void* delta, const float* A, const void* B, const void* C,
                     const float* Dskip, const void* z, const float* delta_bias, int delta_softplus,
@@ -331,6 +336,11 @@ int ssm_scan_bwd_ex(const void* x, const void* delta, const float* A, const void
                     void* workspace, size_t workspace_bytes, void* stream);
 
 size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
+
+/* Workspace of ssm_scan_bwd_ex with these flags: ssm_scan_bwd's, plus, with
+ * SSM_SCAN_DELTA_PER_TOKEN, an fp32 batch x seqlen x dim buffer of the
+ * per-channel ddelta.  0 for unsupported sizes or flags. */
+size_t ssm_scan_bwd_ex_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int flags);
 
 /* Static text for a status code (never NULL). */
 const char* ssm_status_string(int status);

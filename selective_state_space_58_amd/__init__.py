@@ -16,6 +16,7 @@ from ._binding import (  # noqa: F401
     ssm_causal_conv1d_fwd,
     ssm_scan_bwd,
     ssm_scan_bwd_ex,
+    ssm_scan_bwd_ex_workspace_bytes,
     ssm_scan_bwd_workspace_bytes,
     ssd_chunk_scan_fwd,
     ssd_state_update,

@@ -67,6 +67,8 @@ def load_library():
         lib.ssm_scan_bwd_ex.restype = _I
         lib.ssm_scan_bwd_workspace_bytes.argtypes = [_I64] * 4
         lib.ssm_scan_bwd_workspace_bytes.restype = _SZ
+        lib.ssm_scan_bwd_ex_workspace_bytes.argtypes = [_I64] * 4 + [_I]
+        lib.ssm_scan_bwd_ex_workspace_bytes.restype = _SZ
         lib.ssm_status_string.argtypes = [_I]
         lib.ssm_status_string.restype = ctypes.c_char_p
         lib.ssm_last_error.argtypes = []
@@ -346,12 +348,19 @@ def ssm_causal_conv1d_fwd(x, weight, bias=None, state_in=None, silu=True, out=No
 
 
 def ssm_scan_bwd_ex(x, delta, A, B, C, dout, reverse=False, euler=False, **kw):
-    """Backward of ssm_scan_fwd_ex's variants (reverse and/or euler); the arguments of ssm_scan_bwd."""
+    """Backward of ssm_scan_fwd_ex's variants (reverse and/or euler, and delta of shape (batch, seqlen):
+    one step size per token, whose ddelta is summed over the channels); the arguments of ssm_scan_bwd."""
     return ssm_scan_bwd(x, delta, A, B, C, dout, reverse=reverse, euler=euler, **kw)
 
 
 def ssm_scan_bwd_workspace_bytes(batch, seqlen, dim, dstate) -> int:
     return int(load_library().ssm_scan_bwd_workspace_bytes(batch, seqlen, dim, dstate))
+
+
+def ssm_scan_bwd_ex_workspace_bytes(batch, seqlen, dim, dstate, reverse=False, euler=False, delta_per_token=False) -> int:
+    flags = ((SSM_SCAN_REVERSE if reverse else 0) | (SSM_SCAN_EULER if euler else 0) |
+             (SSM_SCAN_DELTA_PER_TOKEN if delta_per_token else 0))
+    return int(load_library().ssm_scan_bwd_ex_workspace_bytes(batch, seqlen, dim, dstate, flags))
 
 
 def ssm_scan_bwd(x, delta, A, B, C, dout, D=None, z=None, delta_bias=None, delta_softplus=False, h0=None,
@@ -365,7 +374,8 @@ def ssm_scan_bwd(x, delta, A, B, C, dout, D=None, z=None, delta_bias=None, delta
     _need(x, "x", device=dev)
     batch, seqlen, dim = x.shape
     act = _act_code(x, "x")
-    _need(delta, "delta", shape=x.shape, device=dev)
+    per_token = isinstance(delta, torch.Tensor) and delta.dim() == 2
+    _need(delta, "delta", shape=(batch, seqlen) if per_token else x.shape, device=dev)
     dcode = _act_code(delta, "delta")
     _need(A, "A", torch.float32, device=dev)
     if A.dim() != 2 or A.shape[0] != dim:
@@ -395,7 +405,8 @@ def ssm_scan_bwd(x, delta, A, B, C, dout, D=None, z=None, delta_bias=None, delta
             int(bool(delta_softplus)), _ptr(h0), _ptr(dout), _ptr(dh_final), _ptr(g["dx"]), _ptr(g["ddelta"]),
             _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g.get("dD")), _ptr(g.get("dz")),
             _ptr(g.get("ddelta_bias")), _ptr(g.get("dh0")), batch, seqlen, dim, dstate, act, dcode)
-    flags = (SSM_SCAN_REVERSE if reverse else 0) | (SSM_SCAN_EULER if euler else 0)
+    flags = ((SSM_SCAN_REVERSE if reverse else 0) | (SSM_SCAN_EULER if euler else 0) |
+             (SSM_SCAN_DELTA_PER_TOKEN if per_token else 0))
     if flags == 0:
         rc = lib.ssm_scan_bwd(*args, _ptr(workspace), wsb, _stream(dev))
         _check(lib, "ssm_scan_bwd", rc)

@@ -370,7 +370,14 @@ int ssm_causal_conv1d_fwd(const void* x, const float* weight, const float* bias,
 size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
   if (batch <= 0 || seqlen <= 0 || dim <= 0 || dstate <= 0 || dstate > 256) return 0;
   if (!elems_ok({batch, seqlen, dim, dstate})) return 0;
-  return scan_bwd_ws_bytes(batch, seqlen, dim, dstate);
+  return scan_bwd_ws_bytes(batch, seqlen, dim, dstate, false);
+}
+
+size_t ssm_scan_bwd_ex_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int flags) {
+  if ((flags & ~(SSM_SCAN_REVERSE | SSM_SCAN_EULER | SSM_SCAN_DELTA_PER_TOKEN)) != 0) return 0;
+  if (batch <= 0 || seqlen <= 0 || dim <= 0 || dstate <= 0 || dstate > 256) return 0;
+  if (!elems_ok({batch, seqlen, dim, dstate})) return 0;
+  return scan_bwd_ws_bytes(batch, seqlen, dim, dstate, (flags & SSM_SCAN_DELTA_PER_TOKEN) != 0);
 }
 
 static int bwd_common(const void* x, const void* delta, const float* A, const void* B, const void* C,
@@ -382,8 +389,6 @@ static int bwd_common(const void* x, const void* delta, const float* A, const vo
   g_last_error.clear();
   if ((flags & ~(SSM_SCAN_REVERSE | SSM_SCAN_EULER | SSM_SCAN_DELTA_PER_TOKEN)) != 0)
     return fail(SSM_ERR_UNSUPPORTED, "unknown scan flag bits");
-  if ((flags & SSM_SCAN_DELTA_PER_TOKEN) != 0)
-    return fail(SSM_ERR_UNSUPPORTED, "the backward pass does not support the per-token delta flag");
   int rc = validate_scan(x, delta, A, B, C, dx, false, Dskip, z, delta_bias, h0, dh0, batch, seqlen, dim, dstate,
                          act_dtype, delta_dtype, delta_softplus);
   if (rc != SSM_OK) return rc;
@@ -402,7 +407,8 @@ static int bwd_common(const void* x, const void* delta, const float* A, const vo
   hipStream_t st = (hipStream_t)stream;
   Scratch own;
   void* ws = nullptr;
-  rc = get_workspace(workspace, workspace_bytes, seqlen > 0 ? scan_bwd_ws_bytes(batch, seqlen, dim, dstate) : 0, st,
+  const bool tok = (flags & SSM_SCAN_DELTA_PER_TOKEN) != 0;
+  rc = get_workspace(workspace, workspace_bytes, seqlen > 0 ? scan_bwd_ws_bytes(batch, seqlen, dim, dstate, tok) : 0, st,
                      &own, &ws);
   if (rc != SSM_OK) return rc;
   BwdArgs a{};
@@ -417,6 +423,7 @@ static int bwd_common(const void* x, const void* delta, const float* A, const vo
   a.softplus = delta_softplus; a.act_bf16 = act_dtype == SSM_BF16; a.delta_bf16 = delta_dtype == SSM_BF16;
   a.reverse = (flags & SSM_SCAN_REVERSE) != 0;
   a.euler = (flags & SSM_SCAN_EULER) != 0;
+  a.tok_delta = tok;
   return launch_scan_bwd(a, stream);
 }
 

@@ -186,8 +186,9 @@ __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64
       const int64_t t = t0 + tl;
       const int64_t chl = chw0 + cc < dim ? chw0 + cc : dim - 1;
       const bool ok = t < L && chw0 + cc < dim;
-      const int64_t i = (b * L + grow(t < L ? t : L - 1)) * dim + chl;
-      const float v = Raw<DB>::f32(gd[i]) + ((a.delta_bias != nullptr) ? a.delta_bias[chl] : 0.f);
+      const int64_t row = b * L + grow(t < L ? t : L - 1);
+      const int64_t i = row * dim + chl;
+      const float v = Raw<DB>::f32(gd[a.tok_delta ? row : i]) + ((a.delta_bias != nullptr) ? a.delta_bias[chl] : 0.f);
       const float dt = ok ? (a.softplus ? softplus_f(v) : v) : 0.f;
       sm.dx[tid] = make_float2(dt, Raw<XB>::f32(gx[i]));
       if (full) {
@@ -209,15 +210,21 @@ __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64
   // directly with one block of states; with several, summed in an fp32
   // accumulator (each element by the same lane in every block, blocks in
   // stream order) and converted after the last block.
+  // With one delta per token, ddelta goes per channel to an fp32 buffer that a
+  // second kernel sums over the channels.
   auto put = [&](int k, int64_t i, float v, auto* out) {
     using T = typename std::remove_pointer<decltype(out)>::type;
+    auto store = [&](float s) {
+      if (k == 1 && a.tok_delta) a.ddelta_tc[i] = s;
+      else out[i] = (T)s;
+    };
     if constexpr (!MULTI) {
-      out[i] = (T)v;
+      store(v);
       return;
     }
     float* p = a.acc + k * tcd + i;
     const float sum = a.first ? v : *p + v;
-    if (a.last) out[i] = (T)sum;
+    if (a.last) store(sum);
     else *p = sum;
   };
 
@@ -398,6 +405,26 @@ hipError_t launch_bwd_xd(const BwdArgs& a, dim3 grid, int64_t wgs, hipStream_t s
   return hipGetLastError();
 }
 
+// One delta per token: ddelta[row] = sum over the channels of the per-channel
+// ddelta, in a fixed order (lane-strided partial sums, then a wave tree), so
+// it is deterministic.  One wave per (batch, token) row.
+template <bool DB>
+__global__ __launch_bounds__(256) void bwd_sum_channels_kernel(const float* __restrict__ tc, void* out, int64_t rows,
+                                                               int64_t dim) {
+  const int64_t row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int l = threadIdx.x & 63;
+  if (row >= rows) return;
+  const float* p = tc + row * dim;
+  float s = 0.f;
+  for (int64_t c = l; c < dim; c += 64) s += p[c];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+  if (l == 0) {
+    if (DB) ((__bf16*)out)[row] = (__bf16)s;
+    else ((float*)out)[row] = s;
+  }
+}
+
 // Workspace: the states of one block of 16 at every tile start, the dB/dC
 // partials of one block, and (dstate > 16) the three fp32 accumulators.
 size_t ckpt_bytes(int64_t batch, int64_t seqlen, int64_t dim) {
@@ -411,9 +438,13 @@ size_t part_bytes(int64_t batch, int64_t seqlen, int64_t dim) {
 
 }  // namespace
 
-size_t scan_bwd_ws_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
-  const size_t acc = dstate > BR ? (size_t)(3 * batch * seqlen * dim) * sizeof(float) : 0;
-  return ckpt_bytes(batch, seqlen, dim) + part_bytes(batch, seqlen, dim) + acc;
+size_t acc_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
+  return dstate > BR ? ((size_t)(3 * batch * seqlen * dim) * sizeof(float) + 255) / 256 * 256 : 0;
+}
+
+size_t scan_bwd_ws_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, bool tok_delta) {
+  const size_t tc = tok_delta ? (size_t)(batch * seqlen * dim) * sizeof(float) : 0;
+  return ckpt_bytes(batch, seqlen, dim) + part_bytes(batch, seqlen, dim) + acc_bytes(batch, seqlen, dim, dstate) + tc;
 }
 
 int launch_scan_bwd(const BwdArgs& a0, void* stream) {
@@ -435,11 +466,13 @@ int launch_scan_bwd(const BwdArgs& a0, void* stream) {
   a.ws_groups = wgs;
   a.ws_part = nullptr;
   a.acc = nullptr;
+  a.ddelta_tc = nullptr;
   if (a.ws_ckpt != nullptr) {
     char* base = (char*)a.ws_ckpt;
-    a.ws_part = (float*)(base + ckpt_bytes(a.batch, a.seqlen, a.dim));
-    if (a.dstate > BR)
-      a.acc = (float*)(base + ckpt_bytes(a.batch, a.seqlen, a.dim) + part_bytes(a.batch, a.seqlen, a.dim));
+    const size_t ck = ckpt_bytes(a.batch, a.seqlen, a.dim), pb = part_bytes(a.batch, a.seqlen, a.dim);
+    a.ws_part = (float*)(base + ck);
+    if (a.dstate > BR) a.acc = (float*)(base + ck + pb);
+    if (a.tok_delta) a.ddelta_tc = (float*)(base + ck + pb + acc_bytes(a.batch, a.seqlen, a.dim, a.dstate));
   }
   const dim3 grid((unsigned)nb);
   const int64_t rows = a.batch * a.seqlen;
@@ -461,6 +494,13 @@ int launch_scan_bwd(const BwdArgs& a0, void* stream) {
       e = hipGetLastError();
       if (e != hipSuccess) return fail(6, std::string("backward partial sums: ") + hipGetErrorString(e));
     }
+  }
+  if (a.tok_delta && rows > 0) {
+    const dim3 g((unsigned)((rows + 3) / 4));
+    if (a.delta_bf16) bwd_sum_channels_kernel<true><<<g, 256, 0, st>>>(a.ddelta_tc, a.ddelta, rows, a.dim);
+    else bwd_sum_channels_kernel<false><<<g, 256, 0, st>>>(a.ddelta_tc, a.ddelta, rows, a.dim);
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail(6, std::string("backward channel sum: ") + hipGetErrorString(e));
   }
   return 0;
 }

@@ -91,12 +91,14 @@ struct BwdArgs {
   int first, last;         // first / last block of states
   int reverse;             // gradients of the reversed scan (tokens from the last to the first)
   int euler;               // gradients of the Euler discretization (gain dt)
+  int tok_delta;           // delta (and ddelta) of shape (batch, seqlen), shared by every channel
+  float* ddelta_tc;        // tok_delta: fp32 (batch, seqlen, dim) per-channel ddelta, summed after the passes
   int64_t batch, seqlen, dim, dstate;
   int softplus;
   int act_bf16, delta_bf16;
 };
 
-size_t scan_bwd_ws_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
+size_t scan_bwd_ws_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, bool tok_delta);
 int launch_scan_bwd(const BwdArgs& a, void* stream);
 
 // ---------------------------------------------------------------- SSD

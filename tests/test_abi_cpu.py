@@ -261,13 +261,13 @@ def test_scan_bwd_ex_flag_checks():
     # x .. delta_bias, softplus, h0, dout, dh_final, dx, ddelta, dA, dB, dC, dDskip, dz, ddelta_bias, dh0,
     # batch, seqlen, dim, dstate, act, delta dtype
     base = [P] * 8 + [0] + [None, P, None, P, P, P, P, P, None, None, None, None] + [1, 4, 4, 4, 1, 1]
-    for flags, code in ((4, 4), (8, 4), (5, 4)):    # per-token delta has no backward; unknown bits
+    for flags, code in ((8, 4), (12, 4), (1 << 20, 4)):    # unknown bits
         assert lib.ssm_scan_bwd_ex(*base, flags, None, 0, None) == code
         assert lib.ssm_last_error() != b""
-    # REVERSE / EULER go through the same validation as ssm_scan_bwd
+    # every known flag combination goes through the same validation as ssm_scan_bwd
     bad = list(base)
     bad[0] = None
-    for flags in (1, 2, 3):
+    for flags in range(8):
         assert lib.ssm_scan_bwd_ex(*bad, flags, None, 0, None) == 1
 
 
@@ -283,4 +283,11 @@ def test_scan_bwd_workspace_query():
     assert lib.ssm_scan_bwd_workspace_bytes(2, 100, 40, 128) == ckpt + part + 3 * 2 * 100 * 40 * 4
     assert lib.ssm_scan_bwd_workspace_bytes(2, 100, 40, 256) == ckpt + part + 3 * 2 * 100 * 40 * 4
     assert lib.ssm_scan_bwd_workspace_bytes(2, 100, 40, 257) == 0
+    # the _ex query: the same for the reverse / Euler flags (bits 1 and 2); one delta per token (bit 4) adds
+    # the fp32 per-channel ddelta buffer; unknown bits give 0
+    for flags in (0, 1, 2, 3):
+        assert lib.ssm_scan_bwd_ex_workspace_bytes(2, 100, 40, 16, flags) == ckpt + part
+    assert lib.ssm_scan_bwd_ex_workspace_bytes(2, 100, 40, 16, 4) == ckpt + part + 2 * 100 * 40 * 4
+    assert lib.ssm_scan_bwd_ex_workspace_bytes(2, 100, 40, 17, 5) == ckpt + part + 4 * 2 * 100 * 40 * 4
+    assert lib.ssm_scan_bwd_ex_workspace_bytes(2, 100, 40, 16, 8) == 0
     assert bwd(lib, batch=0) == 0

@@ -95,6 +95,21 @@ def test_scan_bwd_variants(ssm, reverse, euler, dtype, shape):
     check(ssm, inp, "bwd %s %s reverse=%s euler=%s" % (dtype, shape, reverse, euler), reverse=reverse, euler=euler)
 
 
+@pytest.mark.parametrize("reverse,euler", [(False, False), (True, False), (False, True)])
+@pytest.mark.parametrize("dtype,delta_dtype", [("f32", "f32"), ("bf16", "bf16"), ("bf16", "f32")])
+@pytest.mark.parametrize("shape", [(2, 100, 40, 16), (1, 77, 24, 40)])
+def test_scan_bwd_delta_per_token(ssm, reverse, euler, dtype, delta_dtype, shape):
+    # one step size per (batch, token) shared by every channel: ddelta (batch, seqlen) is the per-channel
+    # gradient summed over the channels, against O5 with delta broadcast (and 16 / 40 states: one and three
+    # passes over the states)
+    b, L, D, N = shape
+    inp = workloads.scan_inputs(b, L, D, N, dtype=dtype, delta_dtype=delta_dtype, seed=sum(shape) + 41,
+                                dt="softplus_bias", gate=True, softplus=True, skip=True, h0=True)
+    inp["delta"] = np.ascontiguousarray(inp["delta"][:, :, 0])
+    check(ssm, inp, "bwd per-token delta %s/%s %s reverse=%s euler=%s" % (dtype, delta_dtype, shape, reverse, euler),
+          tol=TOL["bf16"] if "bf16" in (dtype, delta_dtype) else None, reverse=reverse, euler=euler)
+
+
 @pytest.mark.parametrize("flags", [dict(gate=False, softplus=False, skip=False, h0=False),
                                    dict(gate=True, softplus=False, skip=False, h0=False),
                                    dict(gate=False, softplus=True, skip=True, h0=True)])
