@@ -14,6 +14,8 @@
 // token) and a run of 16 tokens, keeps the W-tap window in registers and
 // slides it one token at a time; neighbouring threads own neighbouring
 // channel groups, so each token row is read as contiguous 1 KB wave accesses.
+// out is stored with the nontemporal (streaming) hint (27.5 -> 26.9 us on the
+// b8 x 2048 x 1536 pass); x is not, since its halo rows are read again.
 #include <hip/hip_runtime.h>
 
 #include "ssm_internal.h"
@@ -47,7 +49,7 @@ struct Vec8<true> {  // 8 bf16 in 16 bytes
       const unsigned hi = __builtin_bit_cast(unsigned short, (__bf16)v[2 * q + 1]);
       r[q] = lo | (hi << 16);
     }
-    *reinterpret_cast<u32x4*>((unsigned short*)p + i) = r;
+    __builtin_nontemporal_store(r, reinterpret_cast<u32x4*>((unsigned short*)p + i));
   }
 };
 template <>
@@ -58,8 +60,9 @@ struct Vec8<false> {  // 8 fp32 in 32 bytes
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
   }
   static __device__ __forceinline__ void store(void* p, int64_t i, const float (&v)[8]) {
-    *reinterpret_cast<float4*>((float*)p + i) = make_float4(v[0], v[1], v[2], v[3]);
-    *reinterpret_cast<float4*>((float*)p + i + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4*>((float*)p + i));
+    __builtin_nontemporal_store(f32x4{v[4], v[5], v[6], v[7]}, reinterpret_cast<f32x4*>((float*)p + i + 4));
   }
 };
 

@@ -18,7 +18,10 @@
 // and store when the layout allows, so a wave streams 1 KB of contiguous state
 // per access; each lane group handles 2 or 4 channels a block apart and issues all
 // their state loads first, to keep enough bytes in flight to cover HBM
-// latency.  The readout sum is reduced over the G lanes of the group with
+// latency.  The state is touched once per call, so its loads and stores carry
+// the nontemporal (streaming) hint: measured 165.7 -> 147.6 us on the b128 x
+// 80-head Mamba-2 decode (4.57 TB/s) and 27.9 -> 26.7 us on the b128 x
+// 5120-channel Mamba decode.  The readout sum is reduced over the G lanes of the group with
 // cross-lane shuffles; lane 0 of the group applies skip and gate and stores y.
 #include <hip/hip_runtime.h>
 
@@ -34,6 +37,7 @@ using scan_dev::silu_f;
 using scan_dev::softplus_f;
 
 constexpr int kStepThreads = 256;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float load_act(const void* p, int64_t i, bool bf16) {
   if (bf16) return __builtin_bit_cast(float, (unsigned)(((const unsigned short*)p)[i]) << 16);
@@ -105,8 +109,8 @@ __global__ __launch_bounds__(kStepThreads) void state_update_kernel(StepArgs a, 
     if (d >= dim || valid == 0) continue;
     const float* st = a.state + (row + d) * N + n0;
     if (VEC) {
-      const float4 hv = *reinterpret_cast<const float4*>(st);
-      h[u][0] = hv.x; h[u][1] = hv.y; h[u][2] = hv.z; h[u][3] = hv.w;
+      const f32x4 hv = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(st));
+      h[u][0] = hv[0]; h[u][1] = hv[1]; h[u][2] = hv[2]; h[u][3] = hv[3];
     } else {
 #pragma unroll
       for (int k = 0; k < 4; ++k) h[u][k] = k < valid ? st[k] : 0.f;
@@ -158,7 +162,7 @@ __global__ __launch_bounds__(kStepThreads) void state_update_kernel(StepArgs a, 
       }
       float* st = a.state + (row + d) * N + n0;
       if (VEC) {
-        *reinterpret_cast<float4*>(st) = make_float4(h[u][0], h[u][1], h[u][2], h[u][3]);
+        __builtin_nontemporal_store(f32x4{h[u][0], h[u][1], h[u][2], h[u][3]}, reinterpret_cast<f32x4*>(st));
       } else {
 #pragma unroll
         for (int k = 0; k < 4; ++k)
