@@ -286,8 +286,8 @@ def run_bwd(steps, warmup, ssm, workloads, torch, dev, np):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path (see DESIGN.md for how the scan "
-              "would shard); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (the scan's (batch, channel) slices "
+              "would shard with no communication); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
