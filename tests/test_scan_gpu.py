@@ -130,16 +130,18 @@ def test_final_state_entry(ssm, L, N):
     assert rel_err(hf.cpu().numpy(), h_ref) <= TOL["bf16"]
 
 
-def test_empty_sequence_passes_state(ssm):
-    inp = workloads.scan_inputs(2, 0, 8, 16, dtype="f32", seed=3, h0=True)
+@pytest.mark.parametrize("N", [16, 256])
+def test_empty_sequence_passes_state(ssm, N):
+    inp = workloads.scan_inputs(2, 0, 8, N, dtype="f32", seed=3, h0=True)
     y, hf = run(ssm, inp)
     assert y.shape == (2, 0, 8)
     assert np.array_equal(hf, inp["h0"])
 
 
-def test_single_token_decode_in_place(ssm):
+@pytest.mark.parametrize("N", [16, 200])
+def test_single_token_decode_in_place(ssm, N):
     # one token, state updated in place (h_final aliases h0): the recurrent inference step
-    inp = workloads.scan_inputs(3, 1, 50, 16, dtype="f32", seed=9, dt="softplus_bias", gate=True, softplus=True,
+    inp = workloads.scan_inputs(3, 1, 50, N, dtype="f32", seed=9 + N, dt="softplus_bias", gate=True, softplus=True,
                                 h0=True)
     t = workloads.to_device(inp, DEV)
     state = t["h0"].clone()

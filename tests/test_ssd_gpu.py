@@ -100,12 +100,13 @@ def test_time_split_workspace_checks(ssm):
         ssm.ssd_chunk_scan_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], chunk_size=256, workspace=small)
 
 
-def test_empty_and_single_token(ssm):
-    inp = workloads.ssd_inputs(1, 0, 2, 64, 64, seed=3, h0=True)
+@pytest.mark.parametrize("P", [64, 128])
+def test_empty_and_single_token(ssm, P):
+    inp = workloads.ssd_inputs(1, 0, 2, P, 64, seed=3, h0=True)
     y, hf = run(ssm, inp)
-    assert y.shape == (1, 0, 2, 64) and np.array_equal(hf, inp["h0"])
-    inp1 = workloads.ssd_inputs(2, 1, 2, 64, 128, seed=4, h0=True, skip=True, gate=True)
-    check(ssm, inp1, "single token")
+    assert y.shape == (1, 0, 2, P) and np.array_equal(hf, inp["h0"])
+    inp1 = workloads.ssd_inputs(2, 1, 2, P, 128, seed=4, h0=True, skip=True, gate=True)
+    check(ssm, inp1, "single token P=%d" % P)
 
 
 def test_full_size_workload_sampled_heads(ssm):
