@@ -118,9 +118,12 @@ __global__ __launch_bounds__(256) void bwd_sum_partials_kernel(const float* part
   const int64_t per_group = rows * BR;
   const int64_t o = bt * BR + nl;
   float sb = 0.f, sc = 0.f;
+  // unrolled so that several groups' loads are in flight (52.8 -> 32.4 us on the 96-group headline layer);
+  // each partial is read once (streaming hint)
+#pragma unroll 8
   for (int64_t g = 0; g < groups; ++g) {
-    sb += part_b[g * per_group + o];
-    sc += part_c[g * per_group + o];
+    sb += __builtin_nontemporal_load(part_b + g * per_group + o);
+    sc += __builtin_nontemporal_load(part_c + g * per_group + o);
   }
   const int64_t t = bt % L;
   const int64_t row = reverse ? bt - t + (L - 1 - t) : bt;
