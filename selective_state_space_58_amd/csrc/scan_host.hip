@@ -32,10 +32,24 @@ __global__ __launch_bounds__(256) void carry_kernel(ScanArgs a, int64_t nlocal, 
   const int64_t n = i % a.dstate, bd = i / a.dstate, d = bd % a.dim;
   const float an = a.A[d * a.dstate + n];
   float h = a.h0 != nullptr ? a.h0[i] : 0.f;
-  for (int64_t c = 0; c < nlocal; ++c) {
-    const float loc = a.ws_state[c * total + i];
-    a.ws_state[c * total + i] = h;
-    h = expf(an * a.ws_dsum[c * a.batch * a.dim + bd]) * h + loc;
+  // the chunk values are loaded 8 at a time before they are combined, so the
+  // loads overlap instead of each waiting behind the previous step
+  constexpr int K = 8;
+  for (int64_t c0 = 0; c0 < nlocal; c0 += K) {
+    float loc[K], ds[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const int64_t c = c0 + j < nlocal ? c0 + j : nlocal - 1;
+      loc[j] = a.ws_state[c * total + i];
+      ds[j] = a.ws_dsum[c * a.batch * a.dim + bd];
+    }
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      if (c0 + j < nlocal) {
+        a.ws_state[(c0 + j) * total + i] = h;
+        h = expf(an * ds[j]) * h + loc[j];
+      }
+    }
   }
   if (nlocal < a.nchunks) a.ws_state[nlocal * total + i] = h;
   if (write_final && a.h_final != nullptr) a.h_final[i] = h;

@@ -498,10 +498,24 @@ __global__ __launch_bounds__(256) void ssd_carry_kernel(SsdArgs a) {
   if (i >= slice) return;
   const int64_t bh = i / (a.headdim * a.dstate);
   float hv = a.h0 != nullptr ? a.h0[i] : 0.f;
-  for (int64_t c = 0; c + 1 < a.nchunks; ++c) {
-    const float loc = a.ws_state[c * slice + i];
-    a.ws_state[c * slice + i] = hv;
-    hv = fmaf(exp_f(a.ws_dsum[c * a.batch * a.nheads + bh]), hv, loc);
+  // chunk values loaded 8 at a time ahead of the dependent combine
+  constexpr int K = 8;
+  const int64_t nl = a.nchunks - 1;
+  for (int64_t c0 = 0; c0 < nl; c0 += K) {
+    float loc[K], ds[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const int64_t c = c0 + j < nl ? c0 + j : nl - 1;
+      loc[j] = a.ws_state[c * slice + i];
+      ds[j] = a.ws_dsum[c * a.batch * a.nheads + bh];
+    }
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      if (c0 + j < nl) {
+        a.ws_state[(c0 + j) * slice + i] = hv;
+        hv = fmaf(exp_f(ds[j]), hv, loc[j]);
+      }
+    }
   }
   a.ws_state[(a.nchunks - 1) * slice + i] = hv;
 }
