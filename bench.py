@@ -44,7 +44,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-others", action="store_true")
-    p.add_argument("--only", choices=["scan-2.8b", "scan-long", "ssd", "step", "ssd-step", "conv", "bwd", "copy",
+    p.add_argument("--only", choices=["scan-2.8b", "scan-long", "ssd", "step", "ssd-step", "conv", "bwd", "train", "copy",
                                       "ubench"],
                    default=None,
                    help="time only this other workload (for profiling); skips the headline JSON line")
@@ -283,6 +283,40 @@ def run_bwd(steps, warmup, ssm, workloads, torch, dev, np):
             "Gtc_s": round(tc / (ms * 1e-3) / 1e9, 2)}
 
 
+def run_train(steps, warmup, ssm, workloads, torch, dev, np):
+    """Time one training step of the headline layer's scan two ways: ssm_scan_fwd + ssm_scan_bwd (the
+    backward reruns the recurrence to store its tile states), and the training pair ssm_scan_fwd_train +
+    ssm_scan_bwd_train (the forward stores them on the way)."""
+    inp, cfg = workloads.config_inputs(1)
+    t = workloads.to_device(inp, dev)
+    rng = np.random.default_rng(7)
+    dout = torch.from_numpy(workloads.round_to(rng.standard_normal(inp["x"].shape, dtype=np.float32), "bf16")).to(
+        dev, torch.bfloat16)
+    b, L, D, N = cfg["batch"], cfg["seqlen"], cfg["dim"], cfg["dstate"]
+    ws = torch.empty(max(ssm.ssm_scan_bwd_workspace_bytes(b, L, D, N), 1), dtype=torch.uint8, device=dev)
+    states = torch.empty(((L + 15) // 16, b, D, N), dtype=torch.float32, device=dev)
+    y = torch.empty_like(t["x"])
+    kw = dict(D=t["D"], z=t["z"], delta_bias=t["delta_bias"], delta_softplus=True)
+
+    def plain(i):
+        ssm.ssm_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], y=y, **kw)
+        ssm.ssm_scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], dout, workspace=ws, **kw)
+
+    def fwd_train(i):
+        ssm.ssm_scan_fwd_train(t["x"], t["delta"], t["A"], t["B"], t["C"], y=y, states=states, **kw)
+
+    def bwd_train(i):
+        ssm.ssm_scan_bwd_train(t["x"], t["delta"], t["A"], t["B"], t["C"], dout, states, workspace=ws, **kw)
+
+    res = {"name": "scan_train_step_" + cfg["name"][len("scan_"):]}
+    for key, fn in (("fwd_plus_bwd_ms", plain), ("fwd_train_ms", fwd_train), ("bwd_train_ms", bwd_train)):
+        tot, _ = time_calls(fn, steps, warmup, torch)
+        res[key] = round(tot / steps, 4)
+    res["train_pair_ms"] = round(res["fwd_train_ms"] + res["bwd_train_ms"], 4)
+    res["states_bytes"] = states.numel() * 4
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -317,6 +351,9 @@ def main():
         return
     if args.only == "bwd":
         print(json.dumps({"only": "bwd", **run_bwd(steps, warmup, ssm, workloads, torch, dev, np)}), flush=True)
+        return
+    if args.only == "train":
+        print(json.dumps({"only": "train", **run_train(steps, warmup, ssm, workloads, torch, dev, np)}), flush=True)
         return
     if args.only == "conv":
         print(json.dumps({"only": "conv", **run_conv(0, steps, warmup, ssm, workloads, torch, dev)}), flush=True)
@@ -396,6 +433,9 @@ def main():
             others[res.pop("name")] = res
             torch.cuda.empty_cache()
         res = run_bwd(5, 2, ssm, workloads, torch, dev, np)
+        others[res.pop("name")] = res
+        torch.cuda.empty_cache()
+        res = run_train(5, 2, ssm, workloads, torch, dev, np)
         others[res.pop("name")] = res
         torch.cuda.empty_cache()
         out["other_workloads"] = others

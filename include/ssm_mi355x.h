@@ -137,6 +137,32 @@ int ssm_scan_fwd_ex(const void* x, const void* delta, const float* A, const void
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Training forward: ssm_scan_fwd_ex (same arguments, layouts, ownership,
+ * flags and errors) that also writes the recurrent state entering every 16th
+ * token, for ssm_scan_bwd_train.  [expl] "hardware-aware scan": the states
+ * are not kept per token; the backward pass recomputes them inside each
+ * 16-token tile from the state stored at the tile's start, so only one
+ * state in 16 leaves the chip.
+ *   states : fp32, (ceil(seqlen / 16), batch, dim, dstate), required when
+ *            batch, seqlen and dim are all > 0.  states[k, b, d, n] is the
+ *            state h[b, d, n] before the token at position 16k in processing
+ *            order (token 16k forward, token seqlen-1-16k with
+ *            SSM_SCAN_REVERSE); states[0] is h0 (zeros without h0).  Size:
+ *            ssm_scan_train_states_bytes().  Every element is written.
+ * Workspace: ssm_scan_workspace_bytes() for the same shapes, or NULL.
+ */
+int ssm_scan_fwd_train(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                       const float* Dskip, const void* z, const float* delta_bias, int delta_softplus,
+                       const float* h0, void* y, float* h_final,
+                       int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                       int act_dtype, int delta_dtype, int flags, float* states,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of ssm_scan_fwd_train's states: ceil(seqlen/16) * batch * dim *
+ * dstate * 4.  0 for empty or unsupported sizes (dstate > 256). */
+size_t ssm_scan_train_states_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
+
+/*
  * Final state only: the same recurrence as ssm_scan_fwd, writing h_final
  * (required) and no y; C, Dskip and z are not needed.  ([guide] sec. 2/4:
  * recurrent inference keeps only the fixed-size state.)
@@ -341,6 +367,28 @@ size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, 
  * SSM_SCAN_DELTA_PER_TOKEN, an fp32 batch x seqlen x dim buffer of the
  * per-channel ddelta.  0 for unsupported sizes or flags. */
 size_t ssm_scan_bwd_ex_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int flags);
+
+/*
+ * Training backward: ssm_scan_bwd_ex (same arguments, layouts, ownership,
+ * flags and errors) taking the states that ssm_scan_fwd_train wrote for the
+ * same inputs, h0 and flags, in place of its own forward pass over the
+ * sequence (the pass that stores a state every 16 tokens).  The results
+ * equal ssm_scan_bwd_ex's.  `states` is read only and required when batch,
+ * seqlen and dim are all > 0; states from other inputs give meaningless
+ * gradients (no check is possible).  Workspace:
+ * ssm_scan_bwd_train_workspace_bytes() for these flags (ssm_scan_bwd_ex's
+ * less the stored states), or NULL.
+ */
+int ssm_scan_bwd_train(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                       const float* Dskip, const void* z, const float* delta_bias, int delta_softplus,
+                       const float* h0, const void* dout, const float* dh_final,
+                       void* dx, void* ddelta, float* dA, float* dB, float* dC, float* dDskip, void* dz,
+                       float* ddelta_bias, float* dh0,
+                       int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                       int act_dtype, int delta_dtype, int flags, const float* states,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+size_t ssm_scan_bwd_train_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int flags);
 
 /* Static text for a status code (never NULL). */
 const char* ssm_status_string(int status);

@@ -17,6 +17,8 @@ from ._binding import (  # noqa: F401
     ssm_scan_bwd,
     ssm_scan_bwd_ex,
     ssm_scan_bwd_ex_workspace_bytes,
+    ssm_scan_bwd_train,
+    ssm_scan_bwd_train_workspace_bytes,
     ssm_scan_bwd_workspace_bytes,
     ssd_chunk_scan_fwd,
     ssd_state_update,
@@ -24,6 +26,8 @@ from ._binding import (  # noqa: F401
     ssm_scan_final_state,
     ssm_scan_fwd,
     ssm_scan_fwd_ex,
+    ssm_scan_fwd_train,
+    ssm_scan_train_states_bytes,
     ssm_state_update,
     ssm_scan_workspace_bytes,
 )

@@ -47,6 +47,10 @@ def load_library():
         lib.ssm_scan_fwd.restype = _I
         lib.ssm_scan_fwd_ex.argtypes = [_P] * 8 + [_I, _P, _P, _P] + [_I64] * 4 + [_I, _I, _I, _P, _SZ, _P]
         lib.ssm_scan_fwd_ex.restype = _I
+        lib.ssm_scan_fwd_train.argtypes = [_P] * 8 + [_I, _P, _P, _P] + [_I64] * 4 + [_I, _I, _I, _P, _P, _SZ, _P]
+        lib.ssm_scan_fwd_train.restype = _I
+        lib.ssm_scan_train_states_bytes.argtypes = [_I64] * 4
+        lib.ssm_scan_train_states_bytes.restype = _SZ
         lib.ssm_scan_final_state.argtypes = [_P] * 5 + [_I, _P, _P] + [_I64] * 4 + [_I, _I, _P, _SZ, _P]
         lib.ssm_scan_final_state.restype = _I
         lib.ssd_chunk_scan_fwd.argtypes = [_P] * 8 + [_I, _P, _P, _P] + [_I64] * 7 + [_I, _I, _P, _SZ, _P]
@@ -65,6 +69,10 @@ def load_library():
         lib.ssm_scan_bwd.restype = _I
         lib.ssm_scan_bwd_ex.argtypes = [_P] * 8 + [_I] + [_P] * 12 + [_I64] * 4 + [_I, _I, _I, _P, _SZ, _P]
         lib.ssm_scan_bwd_ex.restype = _I
+        lib.ssm_scan_bwd_train.argtypes = [_P] * 8 + [_I] + [_P] * 12 + [_I64] * 4 + [_I, _I, _I, _P, _P, _SZ, _P]
+        lib.ssm_scan_bwd_train.restype = _I
+        lib.ssm_scan_bwd_train_workspace_bytes.argtypes = [_I64] * 4 + [_I]
+        lib.ssm_scan_bwd_train_workspace_bytes.restype = _SZ
         lib.ssm_scan_bwd_workspace_bytes.argtypes = [_I64] * 4
         lib.ssm_scan_bwd_workspace_bytes.restype = _SZ
         lib.ssm_scan_bwd_ex_workspace_bytes.argtypes = [_I64] * 4 + [_I]
@@ -149,8 +157,32 @@ def ssm_scan_fwd_ex(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_so
                      workspace, flags)
 
 
+def ssm_scan_fwd_train(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False, h0=None,
+                       return_final_state=False, y=None, h_final=None, states=None, workspace=None, reverse=False,
+                       euler=False):
+    """ssm_scan_fwd_ex that also returns the states entering every 16th token (processing order),
+    fp32 (ceil(seqlen/16), batch, dim, dstate), for ssm_scan_bwd_train.  Returns (y, states) or
+    (y, h_final, states) with return_final_state."""
+    flags = (SSM_SCAN_REVERSE if reverse else 0) | (SSM_SCAN_EULER if euler else 0)
+    if isinstance(delta, torch.Tensor) and delta.dim() == 2:
+        flags |= SSM_SCAN_DELTA_PER_TOKEN
+    batch, seqlen, dim = x.shape
+    dstate = A.shape[1] if A.dim() == 2 else 0
+    shape = ((seqlen + 15) // 16, batch, dim, dstate)
+    if states is None:
+        states = torch.empty(shape, dtype=torch.float32, device=x.device)
+    _need(states, "states", torch.float32, shape, x.device)
+    out = _scan_fwd(x, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, return_final_state, y, h_final,
+                    workspace, flags, states)
+    return (*out, states) if isinstance(out, tuple) else (out, states)
+
+
+def ssm_scan_train_states_bytes(batch, seqlen, dim, dstate) -> int:
+    return int(load_library().ssm_scan_train_states_bytes(batch, seqlen, dim, dstate))
+
+
 def _scan_fwd(x, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, return_final_state, y, h_final, workspace,
-              flags):
+              flags, states=None):
     lib = load_library()
     dev = x.device
     _need(x, "x", device=dev)
@@ -178,7 +210,10 @@ def _scan_fwd(x, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, return_fi
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = (_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
             int(bool(delta_softplus)), _ptr(h0), _ptr(y), _ptr(h_final), batch, seqlen, dim, dstate, act, dcode)
-    if flags is None:
+    if states is not None:
+        rc = lib.ssm_scan_fwd_train(*args, int(flags), _ptr(states), _ptr(workspace), wsb, _stream(dev))
+        _check(lib, "ssm_scan_fwd_train", rc)
+    elif flags is None:
         rc = lib.ssm_scan_fwd(*args, _ptr(workspace), wsb, _stream(dev))
         _check(lib, "ssm_scan_fwd", rc)
     else:
@@ -353,6 +388,19 @@ def ssm_scan_bwd_ex(x, delta, A, B, C, dout, reverse=False, euler=False, **kw):
     return ssm_scan_bwd(x, delta, A, B, C, dout, reverse=reverse, euler=euler, **kw)
 
 
+def ssm_scan_bwd_train(x, delta, A, B, C, dout, states, **kw):
+    """ssm_scan_bwd(_ex) that reads the states ssm_scan_fwd_train wrote for the same inputs, h0 and flags
+    instead of running its own forward pass; the same arguments and results."""
+    return ssm_scan_bwd(x, delta, A, B, C, dout, states=states, **kw)
+
+
+def ssm_scan_bwd_train_workspace_bytes(batch, seqlen, dim, dstate, reverse=False, euler=False,
+                                       delta_per_token=False) -> int:
+    flags = ((SSM_SCAN_REVERSE if reverse else 0) | (SSM_SCAN_EULER if euler else 0) |
+             (SSM_SCAN_DELTA_PER_TOKEN if delta_per_token else 0))
+    return int(load_library().ssm_scan_bwd_train_workspace_bytes(batch, seqlen, dim, dstate, flags))
+
+
 def ssm_scan_bwd_workspace_bytes(batch, seqlen, dim, dstate) -> int:
     return int(load_library().ssm_scan_bwd_workspace_bytes(batch, seqlen, dim, dstate))
 
@@ -364,7 +412,7 @@ def ssm_scan_bwd_ex_workspace_bytes(batch, seqlen, dim, dstate, reverse=False, e
 
 
 def ssm_scan_bwd(x, delta, A, B, C, dout, D=None, z=None, delta_bias=None, delta_softplus=False, h0=None,
-                 dh_final=None, want_dh0=False, workspace=None, reverse=False, euler=False):
+                 dh_final=None, want_dh0=False, workspace=None, reverse=False, euler=False, states=None):
     """Gradients of sum(dout * y) + sum(dh_final * h_final) for ssm_scan_fwd with the same inputs
     (for ssm_scan_fwd_ex's reverse / euler variants when those are set: ssm_scan_bwd_ex).
     Returns a dict: dx, ddelta (input dtypes), dA, dB, dC (fp32) and, for the optional inputs given,
@@ -389,6 +437,7 @@ def ssm_scan_bwd(x, delta, A, B, C, dout, D=None, z=None, delta_bias=None, delta
     _need(delta_bias, "delta_bias", torch.float32, (dim,), dev)
     _need(h0, "h0", torch.float32, (batch, dim, dstate), dev)
     _need(dh_final, "dh_final", torch.float32, (batch, dim, dstate), dev)
+    _need(states, "states", torch.float32, ((seqlen + 15) // 16, batch, dim, dstate), dev)
     f32 = dict(dtype=torch.float32, device=dev)
     g = dict(dx=torch.empty_like(x), ddelta=torch.empty_like(delta), dA=torch.empty((dim, dstate), **f32),
              dB=torch.empty((batch, seqlen, dstate), **f32), dC=torch.empty((batch, seqlen, dstate), **f32))
@@ -407,7 +456,10 @@ def ssm_scan_bwd(x, delta, A, B, C, dout, D=None, z=None, delta_bias=None, delta
             _ptr(g.get("ddelta_bias")), _ptr(g.get("dh0")), batch, seqlen, dim, dstate, act, dcode)
     flags = ((SSM_SCAN_REVERSE if reverse else 0) | (SSM_SCAN_EULER if euler else 0) |
              (SSM_SCAN_DELTA_PER_TOKEN if per_token else 0))
-    if flags == 0:
+    if states is not None:
+        rc = lib.ssm_scan_bwd_train(*args, flags, _ptr(states), _ptr(workspace), wsb, _stream(dev))
+        _check(lib, "ssm_scan_bwd_train", rc)
+    elif flags == 0:
         rc = lib.ssm_scan_bwd(*args, _ptr(workspace), wsb, _stream(dev))
         _check(lib, "ssm_scan_bwd", rc)
     else:

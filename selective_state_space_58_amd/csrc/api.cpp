@@ -145,13 +145,17 @@ static int scan_common(const void* x, const void* delta, const float* A, const v
                        const float* Dskip, const void* z, const float* delta_bias, int delta_softplus,
                        const float* h0, void* y, float* h_final, int64_t batch, int64_t seqlen, int64_t dim,
                        int64_t dstate, int act_dtype, int delta_dtype, void* workspace, size_t workspace_bytes,
-                       void* stream, bool final_only, int flags = 0) {
+                       void* stream, bool final_only, int flags = 0, float* save_states = nullptr,
+                       bool want_save = false) {
   g_last_error.clear();
   if ((flags & ~(SSM_SCAN_REVERSE | SSM_SCAN_EULER | SSM_SCAN_DELTA_PER_TOKEN)) != 0)
     return fail(SSM_ERR_UNSUPPORTED, "unknown scan flag bits");
   int rc = validate_scan(x, delta, A, B, C, final_only ? (const void*)h_final : y, final_only, Dskip, z, delta_bias,
                          h0, h_final, batch, seqlen, dim, dstate, act_dtype, delta_dtype, delta_softplus);
   if (rc != SSM_OK) return rc;
+  if (want_save && batch > 0 && seqlen > 0 && dim > 0 && save_states == nullptr)
+    return fail(SSM_ERR_NULL, "states is required");
+  if (!aligned(save_states, 4)) return fail(SSM_ERR_ALIGNMENT, "states must be 4-byte aligned");
   if (batch == 0 || dim == 0) return SSM_OK;
   ScanPlan p = plan_scan(batch, seqlen, dim, dstate, final_only, device_cu_count());
   hipStream_t st = (hipStream_t)stream;
@@ -173,6 +177,7 @@ static int scan_common(const void* x, const void* delta, const float* A, const v
   a.reverse = (flags & SSM_SCAN_REVERSE) != 0;
   a.euler = (flags & SSM_SCAN_EULER) != 0;
   a.delta_per_token = (flags & SSM_SCAN_DELTA_PER_TOKEN) != 0;
+  a.save_states = want_save ? save_states : nullptr;
   a.vec_io = act_dtype == delta_dtype && !a.delta_per_token && aligned16(x) && aligned16(delta) &&
              aligned16(B) && (final_only || aligned16(C)) && (final_only || aligned16(z));
   if (ws != nullptr) {
@@ -199,6 +204,21 @@ int ssm_scan_fwd_ex(const void* x, const void* delta, const float* A, const void
                     size_t workspace_bytes, void* stream) {
   return scan_common(x, delta, A, B, C, Dskip, z, delta_bias, delta_softplus, h0, y, h_final, batch, seqlen, dim,
                      dstate, act_dtype, delta_dtype, workspace, workspace_bytes, stream, false, flags);
+}
+
+int ssm_scan_fwd_train(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                       const float* Dskip, const void* z, const float* delta_bias, int delta_softplus,
+                       const float* h0, void* y, float* h_final, int64_t batch, int64_t seqlen, int64_t dim,
+                       int64_t dstate, int act_dtype, int delta_dtype, int flags, float* states, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  return scan_common(x, delta, A, B, C, Dskip, z, delta_bias, delta_softplus, h0, y, h_final, batch, seqlen, dim,
+                     dstate, act_dtype, delta_dtype, workspace, workspace_bytes, stream, false, flags, states, true);
+}
+
+size_t ssm_scan_train_states_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
+  if (batch <= 0 || seqlen <= 0 || dim <= 0 || dstate <= 0 || dstate > 256) return 0;
+  if (!elems_ok({batch, seqlen, dim, dstate})) return 0;
+  return (size_t)((seqlen + kSaveTile - 1) / kSaveTile) * (size_t)(batch * dim * dstate) * sizeof(float);
 }
 
 int ssm_scan_final_state(const void* x, const void* delta, const float* A, const void* B, const float* delta_bias,
@@ -370,14 +390,21 @@ int ssm_causal_conv1d_fwd(const void* x, const float* weight, const float* bias,
 size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
   if (batch <= 0 || seqlen <= 0 || dim <= 0 || dstate <= 0 || dstate > 256) return 0;
   if (!elems_ok({batch, seqlen, dim, dstate})) return 0;
-  return scan_bwd_ws_bytes(batch, seqlen, dim, dstate, false);
+  return scan_bwd_ws_bytes(batch, seqlen, dim, dstate, false, false);
 }
 
 size_t ssm_scan_bwd_ex_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int flags) {
   if ((flags & ~(SSM_SCAN_REVERSE | SSM_SCAN_EULER | SSM_SCAN_DELTA_PER_TOKEN)) != 0) return 0;
   if (batch <= 0 || seqlen <= 0 || dim <= 0 || dstate <= 0 || dstate > 256) return 0;
   if (!elems_ok({batch, seqlen, dim, dstate})) return 0;
-  return scan_bwd_ws_bytes(batch, seqlen, dim, dstate, (flags & SSM_SCAN_DELTA_PER_TOKEN) != 0);
+  return scan_bwd_ws_bytes(batch, seqlen, dim, dstate, (flags & SSM_SCAN_DELTA_PER_TOKEN) != 0, false);
+}
+
+size_t ssm_scan_bwd_train_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int flags) {
+  if ((flags & ~(SSM_SCAN_REVERSE | SSM_SCAN_EULER | SSM_SCAN_DELTA_PER_TOKEN)) != 0) return 0;
+  if (batch <= 0 || seqlen <= 0 || dim <= 0 || dstate <= 0 || dstate > 256) return 0;
+  if (!elems_ok({batch, seqlen, dim, dstate})) return 0;
+  return scan_bwd_ws_bytes(batch, seqlen, dim, dstate, (flags & SSM_SCAN_DELTA_PER_TOKEN) != 0, true);
 }
 
 static int bwd_common(const void* x, const void* delta, const float* A, const void* B, const void* C,
@@ -385,7 +412,8 @@ static int bwd_common(const void* x, const void* delta, const float* A, const vo
                       const void* dout, const float* dh_final, void* dx, void* ddelta, float* dA, float* dB,
                       float* dC, float* dDskip, void* dz, float* ddelta_bias, float* dh0, int64_t batch,
                       int64_t seqlen, int64_t dim, int64_t dstate, int act_dtype, int delta_dtype, int flags,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+                      void* workspace, size_t workspace_bytes, void* stream, const float* saved = nullptr,
+                      bool want_saved = false) {
   g_last_error.clear();
   if ((flags & ~(SSM_SCAN_REVERSE | SSM_SCAN_EULER | SSM_SCAN_DELTA_PER_TOKEN)) != 0)
     return fail(SSM_ERR_UNSUPPORTED, "unknown scan flag bits");
@@ -398,6 +426,8 @@ static int bwd_common(const void* x, const void* delta, const float* A, const vo
       (dim > 0 && Dskip != nullptr && dDskip == nullptr) || (dim > 0 && delta_bias != nullptr && ddelta_bias == nullptr))
     return fail(SSM_ERR_NULL, "dout, dx, ddelta, dA, dB, dC and the gradients of the optional inputs given are required");
   if (dstate > 256) return fail(SSM_ERR_UNSUPPORTED, "the backward pass supports dstate <= 256");
+  if (want_saved && has_tok && saved == nullptr) return fail(SSM_ERR_NULL, "states is required");
+  if (!aligned(saved, 4)) return fail(SSM_ERR_ALIGNMENT, "states must be 4-byte aligned");
   const size_t as = dsize(act_dtype), ds = dsize(delta_dtype);
   if (!aligned(dout, as) || !aligned(dx, as) || !aligned(dz, as) || !aligned(ddelta, ds) || !aligned(dA, 4) ||
       !aligned(dB, 4) || !aligned(dC, 4) || !aligned(dDskip, 4) || !aligned(ddelta_bias, 4) ||
@@ -408,7 +438,8 @@ static int bwd_common(const void* x, const void* delta, const float* A, const vo
   Scratch own;
   void* ws = nullptr;
   const bool tok = (flags & SSM_SCAN_DELTA_PER_TOKEN) != 0;
-  rc = get_workspace(workspace, workspace_bytes, seqlen > 0 ? scan_bwd_ws_bytes(batch, seqlen, dim, dstate, tok) : 0, st,
+  rc = get_workspace(workspace, workspace_bytes,
+                     seqlen > 0 ? scan_bwd_ws_bytes(batch, seqlen, dim, dstate, tok, want_saved) : 0, st,
                      &own, &ws);
   if (rc != SSM_OK) return rc;
   BwdArgs a{};
@@ -424,6 +455,7 @@ static int bwd_common(const void* x, const void* delta, const float* A, const vo
   a.reverse = (flags & SSM_SCAN_REVERSE) != 0;
   a.euler = (flags & SSM_SCAN_EULER) != 0;
   a.tok_delta = tok;
+  a.saved = want_saved ? saved : nullptr;
   return launch_scan_bwd(a, stream);
 }
 
@@ -447,6 +479,17 @@ int ssm_scan_bwd_ex(const void* x, const void* delta, const float* A, const void
   return bwd_common(x, delta, A, B, C, Dskip, z, delta_bias, delta_softplus, h0, dout, dh_final, dx, ddelta, dA, dB,
                     dC, dDskip, dz, ddelta_bias, dh0, batch, seqlen, dim, dstate, act_dtype, delta_dtype, flags,
                     workspace, workspace_bytes, stream);
+}
+
+int ssm_scan_bwd_train(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                       const float* Dskip, const void* z, const float* delta_bias, int delta_softplus, const float* h0,
+                       const void* dout, const float* dh_final, void* dx, void* ddelta, float* dA, float* dB, float* dC,
+                       float* dDskip, void* dz, float* ddelta_bias, float* dh0, int64_t batch, int64_t seqlen,
+                       int64_t dim, int64_t dstate, int act_dtype, int delta_dtype, int flags, const float* states,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_common(x, delta, A, B, C, Dskip, z, delta_bias, delta_softplus, h0, dout, dh_final, dx, ddelta, dA, dB,
+                    dC, dDskip, dz, ddelta_bias, dh0, batch, seqlen, dim, dstate, act_dtype, delta_dtype, flags,
+                    workspace, workspace_bytes, stream, states, true);
 }
 
 }  // extern "C"

@@ -48,6 +48,7 @@ using scan_dev::softplus_f;
 using scan_dev::zoh_gain_accurate;
 
 constexpr int BT = 16;    // tokens per tile (states and decays of a tile are kept in LDS)
+static_assert(BT == kSaveTile, "saved forward states are one per backward tile");
 constexpr int BR = 16;    // lane rows: one state per lane
 constexpr int BCH = 4;    // channels per wave
 constexpr int BW = 4;     // waves per workgroup
@@ -231,9 +232,10 @@ __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64
     else *p = sum;
   };
 
-  // ---- forward: the state at the start of every tile into the workspace
+  // ---- forward: the state at the start of every tile into the workspace (unless the forward pass
+  // already stored the states at every tile start)
   float h = (a.h0 != nullptr && nok) ? a.h0[hidx] : 0.f;
-  for (int k = 0; k < ntile; ++k) {
+  for (int k = 0; k < (a.saved != nullptr ? 0 : ntile); ++k) {
     if (nok) a.ws_ckpt[(int64_t)k * slice + cidx] = h;
     __syncthreads();
     stage(k, false);
@@ -260,7 +262,9 @@ __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64
     stage(k, true);
     __syncthreads();
     // recompute the tile's states and decays (into LDS) and its readout; y gives dz and dy
-    const float hstart = nok ? a.ws_ckpt[(int64_t)k * slice + cidx] : 0.f;
+    const float hstart = !nok ? 0.f
+                               : (a.saved != nullptr ? a.saved[((int64_t)k * a.batch + b) * dim * N + ch * N + n0 + r]
+                                                     : a.ws_ckpt[(int64_t)k * slice + cidx]);
     float hs = hstart;
 #pragma unroll
     for (int tb = 0; tb < BT; tb += BG) {
@@ -445,9 +449,10 @@ size_t acc_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
   return dstate > BR ? ((size_t)(3 * batch * seqlen * dim) * sizeof(float) + 255) / 256 * 256 : 0;
 }
 
-size_t scan_bwd_ws_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, bool tok_delta) {
+size_t scan_bwd_ws_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, bool tok_delta, bool saved) {
   const size_t tc = tok_delta ? (size_t)(batch * seqlen * dim) * sizeof(float) : 0;
-  return ckpt_bytes(batch, seqlen, dim) + part_bytes(batch, seqlen, dim) + acc_bytes(batch, seqlen, dim, dstate) + tc;
+  return (saved ? 0 : ckpt_bytes(batch, seqlen, dim)) + part_bytes(batch, seqlen, dim) +
+         acc_bytes(batch, seqlen, dim, dstate) + tc;
 }
 
 int launch_scan_bwd(const BwdArgs& a0, void* stream) {
@@ -472,7 +477,8 @@ int launch_scan_bwd(const BwdArgs& a0, void* stream) {
   a.ddelta_tc = nullptr;
   if (a.ws_ckpt != nullptr) {
     char* base = (char*)a.ws_ckpt;
-    const size_t ck = ckpt_bytes(a.batch, a.seqlen, a.dim), pb = part_bytes(a.batch, a.seqlen, a.dim);
+    const size_t ck = a.saved != nullptr ? 0 : ckpt_bytes(a.batch, a.seqlen, a.dim);
+    const size_t pb = part_bytes(a.batch, a.seqlen, a.dim);
     a.ws_part = (float*)(base + ck);
     if (a.dstate > BR) a.acc = (float*)(base + ck + pb);
     if (a.tok_delta) a.ddelta_tc = (float*)(base + ck + pb + acc_bytes(a.batch, a.seqlen, a.dim, a.dstate));

@@ -172,7 +172,8 @@ int launch_scan(const ScanArgs& a0, const ScanPlan& p, bool final_only, void* st
   if (nb > 0x7fffffffLL || p.nchunks > 65535) return fail(4, "grid too large");
   hipError_t e = hipSuccess;
   if (p.nchunks == 1) {
-    e = launch_mode(p, final_only ? kModeState : kModeFull, a, dim3((unsigned)nb, 1), gpb, st);
+    const int full_mode = a.save_states != nullptr ? kModeSave : kModeFull;
+    e = launch_mode(p, final_only ? kModeState : full_mode, a, dim3((unsigned)nb, 1), gpb, st);
     if (e != hipSuccess) return fail(6, std::string("scan kernel launch: ") + hipGetErrorString(e));
     return 0;
   }
@@ -183,7 +184,8 @@ int launch_scan(const ScanArgs& a0, const ScanPlan& p, bool final_only, void* st
   e = hipGetLastError();
   if (e != hipSuccess) return fail(6, std::string("carry kernel launch: ") + hipGetErrorString(e));
   if (!final_only) {
-    e = launch_mode(p, kModeFull, a, dim3((unsigned)nb, (unsigned)p.nchunks), gpb, st);
+    e = launch_mode(p, a.save_states != nullptr ? kModeSave : kModeFull, a, dim3((unsigned)nb, (unsigned)p.nchunks),
+                    gpb, st);
     if (e != hipSuccess) return fail(6, std::string("scan kernel launch: ") + hipGetErrorString(e));
   }
   return 0;

@@ -199,7 +199,9 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
   using TX = typename Act<XB>::T;
   using TD = typename Act<DB>::T;
   constexpr int R = TS::R, CH = TS::CH, NP = TS::NP, T = TS::T, KX = TS::KX, KB = TS::KB;
-  constexpr bool FULL = (MODE == kModeFull);
+  constexpr bool FULL = (MODE != kModeState);
+  constexpr bool SAVE = (MODE == kModeSave);
+  static_assert(!SAVE || T % kSaveTile == 0, "tiles hold whole save intervals");
   constexpr bool ACC = GAIN != kGainShort;   // accurate softplus as well
   static_assert(VEC || W == 1, "the scalar tile path runs one wave per workgroup");
   constexpr int WCH = W * CH;                 // channels per workgroup (LDS row width)
@@ -324,6 +326,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
   constexpr int VX = XT / NT < 16 ? XT / NT : 16;           // bytes per x chunk
   using VTX = typename VecOf<VX / 4>::T;
   constexpr int EX = VX / (int)sizeof(RX);                  // channels per x chunk
+  static_assert(!VEC || EX % 2 == 0, "x chunks hold whole (dt, x) float4 pairs");
   constexpr int XROW = WCH / EX;                            // chunks per token row
   constexpr int CXN = XT / (NT * VX);                       // x chunks per thread
   constexpr int BT = T * NP * (int)sizeof(RX);              // bytes of one B tile
@@ -406,9 +409,17 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
         float gzv[EX];
 #pragma unroll
         for (int e = 0; e < EX; ++e) gzv[e] = has_z ? silu_f(raw_elem(vz[q], e)) : 1.f;
-        float4* gd4 = reinterpret_cast<float4*>(s_gz + tl * WCH + vc0);
+        if constexpr (EX % 4 == 0) {
+          float4* gd4 = reinterpret_cast<float4*>(s_gz + tl * WCH + vc0);
 #pragma unroll
-        for (int e = 0; e < EX / 4; ++e) gd4[e] = make_float4(gzv[4 * e], gzv[4 * e + 1], gzv[4 * e + 2], gzv[4 * e + 3]);
+          for (int e = 0; e < EX / 4; ++e)
+            gd4[e] = make_float4(gzv[4 * e], gzv[4 * e + 1], gzv[4 * e + 2], gzv[4 * e + 3]);
+        } else {
+          // two channels per chunk (fp32, 8 rows of 32 states): 8-byte writes
+          float2* gd2 = reinterpret_cast<float2*>(s_gz + tl * WCH + vc0);
+#pragma unroll
+          for (int e = 0; e < EX / 2; ++e) gd2[e] = make_float2(gzv[2 * e], gzv[2 * e + 1]);
+        }
       }
     }
 #pragma unroll
@@ -438,6 +449,14 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
   };
 
   float dsum = 0.f;
+  // kModeSave: the state entering token t (processing order, a multiple of 16) -> save_states[t / 16]
+  auto save_state = [&](int64_t t) {
+    if (!ch_ok || t >= L) return;
+    float* o = a.save_states + ((t / kSaveTile) * a.batch + b) * dim * N + ch * N + r * S;
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+      if (r * S + s < N) o[s] = h[s];
+  };
   fetch(t_begin);
   for (int64_t t0 = t_begin; t0 < t_stop; t0 += T) {
     __syncthreads();
@@ -511,6 +530,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
       }
 #pragma unroll
       for (int j = 0; j < U; ++j) {
+        if (SAVE && ((tb + j) % kSaveTile) == 0) save_state(t0 + tb + j);
         const float2 dx = cur.dx[j];
         float acc = 0.f;
 #pragma unroll
@@ -546,6 +566,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
 #pragma unroll
         for (int j = 0; j < R; ++j) {
           const int tt = tb + j;
+          if (SAVE && (tt % kSaveTile) == 0) save_state(t0 + tt);
           const float2 dx = s_dx[tt * WCH + wc];
           const float4* bc4 = reinterpret_cast<const float4*>(s_bc + ((tt * R + r) * 2) * S);
           float acc = 0.f;
@@ -669,6 +690,7 @@ hipError_t launch_scan_variant(int mode, const ScanArgs& a, dim3 grid, int64_t g
     if (a.vec_io && vec_ok<RR, XB, SV, WV>(a) && gpb % WV == 0) {
       const dim3 g4(grid.x / WV, grid.y);
       if (mode == kModeFull) scan_kernel<RR, XB, DB, SV, kModeFull, true, WV><<<g4, 64 * WV, 0, st>>>(a, gpb);
+      else if (mode == kModeSave) scan_kernel<RR, XB, DB, SV, kModeSave, true, WV><<<g4, 64 * WV, 0, st>>>(a, gpb);
       else scan_kernel<RR, XB, DB, SV, kModeState, true, WV><<<g4, 64 * WV, 0, st>>>(a, gpb);
       return hipGetLastError();
     }
@@ -676,11 +698,13 @@ hipError_t launch_scan_variant(int mode, const ScanArgs& a, dim3 grid, int64_t g
   if constexpr (vec_shape_ok<RR, XB, SV, 1>()) {
     if (a.vec_io && vec_ok<RR, XB, SV, 1>(a)) {
       if (mode == kModeFull) scan_kernel<RR, XB, DB, SV, kModeFull, true, 1><<<grid, 64, 0, st>>>(a, gpb);
+      else if (mode == kModeSave) scan_kernel<RR, XB, DB, SV, kModeSave, true, 1><<<grid, 64, 0, st>>>(a, gpb);
       else scan_kernel<RR, XB, DB, SV, kModeState, true, 1><<<grid, 64, 0, st>>>(a, gpb);
       return hipGetLastError();
     }
   }
   if (mode == kModeFull) scan_kernel<RR, XB, DB, SV, kModeFull, false, 1><<<grid, 64, 0, st>>>(a, gpb);
+  else if (mode == kModeSave) scan_kernel<RR, XB, DB, SV, kModeSave, false, 1><<<grid, 64, 0, st>>>(a, gpb);
   else scan_kernel<RR, XB, DB, SV, kModeState, false, 1><<<grid, 64, 0, st>>>(a, gpb);
   return hipGetLastError();
 }

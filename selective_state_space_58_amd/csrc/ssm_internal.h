@@ -19,7 +19,9 @@ int fail(int status, const std::string& msg);
 // R is 4 in general, 8 or 16 for layers with dstate <= 16 and too few
 // (batch, channel) slices to give every SIMD several waves at R = 4.
 
-enum ScanMode : int { kModeFull = 0, kModeState = 1 };
+// kModeSave: kModeFull that also stores the state at every 16-token tile start (for the backward)
+enum ScanMode : int { kModeFull = 0, kModeState = 1, kModeSave = 2 };
+constexpr int kSaveTile = 16;   // tokens between saved states
 
 struct ScanArgs {
   const void* x;
@@ -44,6 +46,7 @@ struct ScanArgs {
   int reverse;         // scan the sequence from the last token to the first
   int euler;           // input discretization Bbar = dt * B instead of ZOH
   int delta_per_token; // delta is (batch, seqlen), one dt per token shared by all channels
+  float* save_states;  // kModeSave: (ceil(seqlen/16), batch, dim, dstate) state entering every 16-token tile
 };
 
 struct ScanPlan {
@@ -93,12 +96,13 @@ struct BwdArgs {
   int euler;               // gradients of the Euler discretization (gain dt)
   int tok_delta;           // delta (and ddelta) of shape (batch, seqlen), shared by every channel
   float* ddelta_tc;        // tok_delta: fp32 (batch, seqlen, dim) per-channel ddelta, summed after the passes
+  const float* saved;      // states the forward stored at every 16-token tile start (no checkpoint pass), or null
   int64_t batch, seqlen, dim, dstate;
   int softplus;
   int act_bf16, delta_bf16;
 };
 
-size_t scan_bwd_ws_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, bool tok_delta);
+size_t scan_bwd_ws_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, bool tok_delta, bool saved);
 int launch_scan_bwd(const BwdArgs& a, void* stream);
 
 // ---------------------------------------------------------------- SSD

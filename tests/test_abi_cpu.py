@@ -291,3 +291,47 @@ def test_scan_bwd_workspace_query():
     assert lib.ssm_scan_bwd_ex_workspace_bytes(2, 100, 40, 17, 5) == ckpt + part + 4 * 2 * 100 * 40 * 4
     assert lib.ssm_scan_bwd_ex_workspace_bytes(2, 100, 40, 16, 8) == 0
     assert bwd(lib, batch=0) == 0
+
+
+def test_train_pair_argument_checks():
+    lib = _lib()
+    S = P + 0x200000
+    fwd = [P] * 8 + [0, None, P, None] + [1, 4, 4, 4, 1, 1]
+    # the states buffer is required for a non-empty scan and must be 4-byte aligned; flags as ssm_scan_fwd_ex
+    assert lib.ssm_scan_fwd_train(*fwd, 0, None, None, 0, None) == 1
+    assert b"states" in lib.ssm_last_error()
+    assert lib.ssm_scan_fwd_train(*fwd, 0, S + 2, None, 0, None) == 7
+    assert lib.ssm_scan_fwd_train(*fwd, 8, S, None, 0, None) == 4
+    empty = list(fwd)
+    empty[13] = 0    # seqlen 0: nothing to save, nothing launched
+    assert lib.ssm_scan_fwd_train(*empty, 0, None, None, 0, None) == 0
+    bad = list(fwd)
+    bad[15] = 257
+    assert lib.ssm_scan_fwd_train(*bad, 0, S, None, 0, None) == 4
+    # x, delta, A, B, C (no Dskip, z, delta_bias), softplus, h0, dout, dh_final, dx, ddelta, dA, dB, dC, ...
+    base = [P] * 5 + [None] * 3 + [0] + [None, P, None, P, P, P, P, P, None, None, None, None] + [1, 4, 4, 4, 1, 1]
+    assert lib.ssm_scan_bwd_train(*base, 0, None, None, 0, None) == 1
+    assert b"states" in lib.ssm_last_error()
+    assert lib.ssm_scan_bwd_train(*base, 0, S + 1, None, 0, None) == 7
+    assert lib.ssm_scan_bwd_train(*base, 16, S, None, 0, None) == 4
+    nox = list(base)
+    nox[0] = None
+    assert lib.ssm_scan_bwd_train(*nox, 0, S, None, 0, None) == 1
+
+
+def test_train_pair_queries():
+    lib = _lib()
+    # one fp32 state per (16-token tile, batch, channel, state): ceil(100/16) = 7 tiles
+    assert lib.ssm_scan_train_states_bytes(2, 100, 40, 16) == 7 * 2 * 40 * 16 * 4
+    assert lib.ssm_scan_train_states_bytes(2, 96, 40, 256) == 6 * 2 * 40 * 256 * 4
+    assert lib.ssm_scan_train_states_bytes(2, 100, 40, 257) == 0
+    assert lib.ssm_scan_train_states_bytes(2, 0, 40, 16) == 0
+    # the backward's workspace without its own stored states: the dB/dC partials (and the accumulators
+    # for dstate > 16, the per-channel ddelta with one delta per token)
+    part = (2 * 3 * 2 * 100 * 16 * 4 + 255) // 256 * 256
+    for flags in (0, 1, 2, 3):
+        assert lib.ssm_scan_bwd_train_workspace_bytes(2, 100, 40, 16, flags) == part
+    assert lib.ssm_scan_bwd_train_workspace_bytes(2, 100, 40, 17, 0) == part + 3 * 2 * 100 * 40 * 4
+    assert lib.ssm_scan_bwd_train_workspace_bytes(2, 100, 40, 16, 4) == part + 2 * 100 * 40 * 4
+    assert lib.ssm_scan_bwd_train_workspace_bytes(2, 100, 40, 16, 8) == 0
+    assert lib.ssm_scan_bwd_train_workspace_bytes(2, 100, 40, 257, 0) == 0

@@ -68,6 +68,19 @@ def test_state_sizes(ssm, N, dtype):
     check(ssm, inp, label="N=%d %s" % (N, dtype))
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(1, 21, 8, 256), (2, 150, 64, 256), (2, 70, 48, 128), (1, 90, 16, 32),
+                                   (2, 100, 64, 16), (2, 100, 32, 8)])
+def test_vector_tile_path_with_gate(ssm, dtype, shape):
+    # channel counts that fill whole channel groups (and whole 4-wave workgroups for 64 channels) with
+    # dstate equal to the lane layout's padded width: the vectorised tile loads, here with the z gate
+    # (fp32 with 256 states moves two channels per x chunk)
+    b, L, D, N = shape
+    inp = workloads.scan_inputs(b, L, D, N, dtype=dtype, seed=sum(shape) + 97, dt="softplus_bias", gate=True,
+                                softplus=True, skip=True, h0=True)
+    check(ssm, inp, label="vector tiles %s %s" % (dtype, shape))
+
+
 @pytest.mark.parametrize("xd,dd", [("f32", "bf16"), ("bf16", "f32")])
 def test_mixed_dtypes(ssm, xd, dd):
     inp = workloads.scan_inputs(2, 400, 36, 16, dtype=xd, delta_dtype=dd, seed=5, dt="softplus_bias", gate=True,
