@@ -42,6 +42,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--settle", type=float, default=SETTLE_S,
+                   help="seconds of untimed launches before the warmup steps (clocks settle)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-others", action="store_true")
     p.add_argument("--only", choices=["scan-2.8b", "scan-long", "ssd", "step", "ssd-step", "conv", "bwd", "train", "copy",
@@ -132,8 +134,22 @@ def step_bytes(cfg):
             + 12 * H)
 
 
-def time_calls(fn, steps, warmup, torch):
-    """Run fn(i) warmup times, then `steps` times bracketed by events; returns (total_ms, [per-call ms])."""
+SETTLE_S = 0.5
+
+
+def time_calls(fn, steps, warmup, torch, settle_s=None):
+    """Run fn(i) for settle_s seconds of wall time and then warmup times, untimed; then `steps` times
+    bracketed by events.  Returns (total_ms, [per-call ms]).  The settle phase is there because the GPU's
+    clocks rise over the first tenths of a second of sustained work: the headline scan measured 0.20 ms
+    per launch right after start and 0.168 ms after about 0.3 s of launches."""
+    settle_s = SETTLE_S if settle_s is None else settle_s
+    t_end = time.perf_counter() + settle_s
+    i = 0
+    while time.perf_counter() < t_end:
+        fn(i)
+        i += 1
+        if i % 16 == 0:
+            torch.cuda.synchronize()
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -336,6 +352,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     steps, warmup = args.steps, args.warmup
+    global SETTLE_S
+    SETTLE_S = args.settle
     if args.only == "copy":
         # plain device copy of a known size: calibrates the HBM byte counters
         nbytes = 1 << 30
