@@ -178,8 +178,9 @@ static int scan_common(const void* x, const void* delta, const float* A, const v
   a.euler = (flags & SSM_SCAN_EULER) != 0;
   a.delta_per_token = (flags & SSM_SCAN_DELTA_PER_TOKEN) != 0;
   a.save_states = want_save ? save_states : nullptr;
-  a.vec_io = act_dtype == delta_dtype && !a.delta_per_token && aligned16(x) && aligned16(delta) &&
-             aligned16(B) && (final_only || aligned16(C)) && (final_only || aligned16(z));
+  // vector tile I/O: 16-byte aligned tensors (delta, when it is per channel, in either dtype)
+  a.vec_io = aligned16(x) && (a.delta_per_token || aligned16(delta)) && aligned16(B) &&
+             (final_only || aligned16(C)) && (final_only || aligned16(z));
   if (ws != nullptr) {
     const size_t st_bytes = (size_t)p.nchunks * (size_t)(batch * dim * dstate) * sizeof(float);
     a.ws_state = (float*)ws;

@@ -170,7 +170,8 @@ template <>
 struct VecOf<2> {
   using T = u32x2;
 };
-// (one word: declared by the 8-row wide-lane tiles, whose vector path is never taken)
+// (one word: a chunk of two bf16 delta values beside fp32 x, and the bf16 8-row wide-lane tiles, whose
+// vector path is never taken)
 typedef unsigned u32x1 __attribute__((ext_vector_type(1)));
 template <>
 struct VecOf<1> {
@@ -250,7 +251,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
   const bool rev = a.reverse != 0;
   auto grow0 = [&](int64_t t0) -> int64_t { return rev ? L - t0 - T : t0; };
   auto urow = [&](int t) -> uint32_t { return (uint32_t)(rev ? T - 1 - t : t); };
-  const bool tok_delta = !VEC && a.delta_per_token != 0;
+  const bool tok_delta = a.delta_per_token != 0;
 
   // ---- register prefetch of one tile.  Row offsets are 32-bit, relative to a
   // wave-uniform 64-bit base, so loads use the scalar-base addressing form.
@@ -338,7 +339,15 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
   constexpr int CBN = BT >= NT * VBC ? BT / (NT * VBC) : 1;  // B chunks per thread
   constexpr bool BPART = BT < NT * VBC;                     // some threads hold no B chunk
   constexpr int GW = S < EB ? S : EB;                       // floats per LDS write of B/C
-  VTX vx[CXN], vd[CXN], vz[CXN];
+  // delta moves in chunks of the same EX channels in its own dtype: VD bytes, as DV loads of at most 16
+  // bytes (fp32 delta beside bf16 x can need two); one delta per token instead is loaded as a single
+  // value per chunk and kept, already converted to fp32, in the chunk's first word
+  constexpr int VD = EX * (int)sizeof(RD);
+  constexpr int DV = VD > 16 ? VD / 16 : 1;
+  using VTD = typename VecOf<VD / DV / 4>::T;
+  constexpr int EPD = EX / DV;                              // delta elements per load
+  VTX vx[CXN], vz[CXN];
+  VTD vd[CXN][DV];
   VTB vb[CBN], vc[CBN];
   const int vc0 = (tid % XROW) * EX;                        // this thread's first workgroup channel
   const int64_t chw0 = ch0 - (int64_t)w * CH;               // first channel of the workgroup
@@ -356,14 +365,27 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
       return __builtin_bit_cast(float, u);
     }
   };
+  auto raw_delta = [](const VTD (&v)[DV], int e) -> float {
+    const VTD w = v[e / EPD];
+    const int k = e % EPD;
+    if constexpr (sizeof(RD) == 2) {
+      const unsigned u = (w[k >> 1] >> (16 * (k & 1))) << 16;
+      return __builtin_bit_cast(float, u);
+    } else {
+      const unsigned u = w[k];
+      return __builtin_bit_cast(float, u);
+    }
+  };
   auto fetch_vec = [&](int64_t t0) {
     const bool tail = t0 + T > t_stop;
     const int64_t last = t_stop - 1 - t0;
     const int64_t row0 = (b * L + grow0(t0)) * dim + chw0;  // uniform
     const char* xb = (const char*)(gx + row0);
     const char* db = (const char*)(gd + row0);
+    const RD* dtok = gd + (b * L + grow0(t0));              // one delta per token
     const char* zb = (const char*)(gz + row0);
     const uint32_t rowb = dim32 * (uint32_t)sizeof(RX);
+    const uint32_t rowd = dim32 * (uint32_t)sizeof(RD);
 #pragma unroll
     for (int q = 0; q < CXN; ++q) {
       const int k = tid + NT * q;
@@ -371,7 +393,13 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
       if (tail) tl = tl < last ? tl : (int)last;
       const uint32_t off = urow(tl) * rowb + (uint32_t)(k % XROW) * (uint32_t)VX;
       vx[q] = *reinterpret_cast<const VTX*>(xb + off);
-      vd[q] = *reinterpret_cast<const VTX*>(db + off);
+      if (tok_delta) {
+        vd[q][0][0] = __builtin_bit_cast(unsigned, Raw<DB>::f32(dtok[urow(tl)]));
+      } else {
+        const uint32_t offd = urow(tl) * rowd + (uint32_t)(k % XROW) * (uint32_t)VD;
+#pragma unroll
+        for (int i = 0; i < DV; ++i) vd[q][i] = *reinterpret_cast<const VTD*>(db + offd + 16 * i);
+      }
       if (has_z) vz[q] = *reinterpret_cast<const VTX*>(zb + off);
     }
     const RX* bb = gB + (b * L + grow0(t0)) * N;            // uniform
@@ -395,9 +423,10 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
       const int tl = k / XROW;
       const bool ok = tl < nvalid;
       float dxv[2 * EX];
+      const unsigned dtok_bits = vd[q][0][0];
 #pragma unroll
       for (int e = 0; e < EX; ++e) {
-        const float v = raw_elem(vd[q], e) + vbias[e];
+        const float v = (tok_delta ? __builtin_bit_cast(float, dtok_bits) : raw_delta(vd[q], e)) + vbias[e];
         float dt = a.softplus ? (ACC ? softplus_f(v) : softplus_short(v)) : v;
         dxv[2 * e] = ok ? dt : 0.f;
         dxv[2 * e + 1] = raw_elem(vx[q], e);

@@ -42,7 +42,7 @@ struct ScanArgs {
   int64_t nchunks;    // number of time chunks (1 = unsplit)
   int softplus;
   int act_bf16, delta_bf16;
-  int vec_io;          // vector tile I/O allowed (16-byte aligned, delta stored like x)
+  int vec_io;          // vector tile I/O allowed (16-byte aligned inputs)
   int reverse;         // scan the sequence from the last token to the first
   int euler;           // input discretization Bbar = dt * B instead of ZOH
   int delta_per_token; // delta is (batch, seqlen), one dt per token shared by all channels

@@ -3,6 +3,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import workloads
 from tests.helpers import TOL, oracle_scan, oracle_scan_slices, rel_err
 
@@ -79,6 +80,33 @@ def test_vector_tile_path_with_gate(ssm, dtype, shape):
     inp = workloads.scan_inputs(b, L, D, N, dtype=dtype, seed=sum(shape) + 97, dt="softplus_bias", gate=True,
                                 softplus=True, skip=True, h0=True)
     check(ssm, inp, label="vector tiles %s %s" % (dtype, shape))
+
+
+@pytest.mark.parametrize("xd,dd,per_token", [("bf16", "f32", False), ("f32", "bf16", False), ("bf16", "bf16", True),
+                                              ("bf16", "f32", True), ("f32", "f32", True)])
+@pytest.mark.parametrize("shape", [(2, 100, 64, 16), (1, 77, 8, 16), (8, 40, 2048, 16), (2, 90, 32, 64),
+                                   (1, 21, 8, 256), (1, 2048, 64, 16)])
+def test_vector_tile_path_delta_forms(ssm, xd, dd, per_token, shape):
+    # the vectorised tile loads with delta in the other dtype (its own chunks of the same channels) or one
+    # delta per token (one value per chunk); the shapes pick the 16-, 8- and 4-row layouts, the wide
+    # 8-row layout and a time-split sequence
+    b, L, D, N = shape
+    inp = workloads.scan_inputs(b, L, D, N, dtype=xd, delta_dtype=dd, seed=sum(shape) + 131, dt="softplus_bias",
+                                gate=True, softplus=True, skip=True, h0=True)
+    if per_token:
+        inp["delta"] = np.ascontiguousarray(inp["delta"][:, :, 0])
+    print("case vector tiles x %s delta %s per_token=%s %s" % (xd, dd, per_token, shape), flush=True)
+    t = workloads.to_device(inp, DEV)
+    y, hf = ssm.ssm_scan_fwd_ex(t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                                delta_bias=t["delta_bias"], delta_softplus=True, h0=t["h0"], return_final_state=True)
+    torch.cuda.synchronize()
+    f = workloads.to_f64(inp)
+    y_ref, h_ref = oracle.selective_scan(f["x"], f["delta"], f["A"], f["B"], f["C"], Dskip=f["D"], z=f["z"],
+                                         delta_bias=f["delta_bias"], delta_softplus=True, h0=f["h0"])
+    tol = TOL["bf16"] if "bf16" in (xd, dd) else TOL["f32"]
+    ey, eh = rel_err(y.float().cpu().numpy(), y_ref), rel_err(hf.cpu().numpy(), h_ref)
+    print("  y rel err %.3g  h_final rel err %.3g  (tol %g)" % (ey, eh, tol))
+    assert ey <= tol and eh <= tol
 
 
 @pytest.mark.parametrize("xd,dd", [("f32", "bf16"), ("bf16", "f32")])
