@@ -103,20 +103,30 @@ ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, b
   (void)final_only;
   ScanPlan p{};
   const int64_t simds = 4LL * (num_cus > 0 ? num_cus : 256);
-  // Rows per wave.  Four rows of 16 channels run one wave per SIMD at best;
-  // when that leaves SIMDs idle or single-waved and the states fit, 16 rows of
-  // 4 channels (one state per lane) or 8 rows of 8 give 4x or 2x the waves,
-  // so every SIMD interleaves several.  Layers with so few (batch, channel)
-  // slices that even that cannot fill the chip are split in time instead
-  // (below), where 4 rows measured fastest.
+  // Rows per wave.  Four rows of 16 channels run one wave per SIMD at best
+  // and spend the fewest instructions per element; 16 rows of 4 channels
+  // (one state per lane) or 8 rows of 8 give 4x or 2x the waves, so every
+  // SIMD interleaves several, at more instructions per element.  With
+  // w4 = 4-row waves per SIMD, the 4- and 8-row layouts both run in w4
+  // rounds of workgroups, so a fractional w4 leaves their last round partly
+  // empty; 16 rows run in (4/3) w4 finer rounds.  Measured at settled clocks
+  // (16 states, bf16; ms for 16 / 8 / 4 rows): w4 0.75 (130M-like) 0.166 /
+  // 0.194 / -; 1.0 0.205 / 0.193 / 0.247; 1.25 (2.8B-like) 0.516 / 0.582 /
+  // 0.695; 1.5 0.303 / 0.296 / 0.352; 2.0 0.392 / 0.374 / 0.353; 2.5 0.471 /
+  // 0.467 / 0.539; 3.0 0.579 / 0.545 / 0.540; 5.0 0.901 / 0.889 / 0.850.
+  // Layers with so few (batch, channel) slices that even 16 rows cannot
+  // fill the chip are split in time instead (below), where 4 rows measured
+  // fastest.
   int S = 1;
   while (S * 4 < dstate) S *= 2;
   p.R = 4;
   const int64_t waves4 = batch * ceil_div(dim, 16);
   const bool time_split = waves4 > 0 && waves4 * 2 < simds && seqlen >= 16LL * 32;
   if (dstate <= 16 && !time_split) {
+    const int64_t rem = waves4 % simds;   // 4-row waves of the last, partly filled round
     if (waves4 < simds) p.R = 16;
-    else if (waves4 < 2 * simds) p.R = 8;
+    else if (waves4 < 2 * simds) p.R = (rem > 0 && 2 * rem < simds) ? 16 : 8;
+    else if (waves4 < 4 * simds) p.R = rem == 0 ? 4 : 8;
   }
   if (p.R != 4) S = 16 / p.R;
   if (dstate > 128) {

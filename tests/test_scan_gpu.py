@@ -84,12 +84,12 @@ def test_vector_tile_path_with_gate(ssm, dtype, shape):
 
 @pytest.mark.parametrize("xd,dd,per_token", [("bf16", "f32", False), ("f32", "bf16", False), ("bf16", "bf16", True),
                                               ("bf16", "f32", True), ("f32", "f32", True)])
-@pytest.mark.parametrize("shape", [(2, 100, 64, 16), (1, 77, 8, 16), (8, 40, 2048, 16), (2, 90, 32, 64),
-                                   (1, 21, 8, 256), (1, 2048, 64, 16)])
+@pytest.mark.parametrize("shape", [(2, 100, 64, 16), (1, 77, 8, 16), (8, 40, 2048, 16), (16, 24, 2048, 16),
+                                   (2, 90, 32, 64), (1, 21, 8, 256), (1, 2048, 64, 16)])
 def test_vector_tile_path_delta_forms(ssm, xd, dd, per_token, shape):
     # the vectorised tile loads with delta in the other dtype (its own chunks of the same channels) or one
-    # delta per token (one value per chunk); the shapes pick the 16-, 8- and 4-row layouts, the wide
-    # 8-row layout and a time-split sequence
+    # delta per token (one value per chunk); the shapes pick the 16-, 8- and 4-row layouts (one state
+    # per lane, two, four), the wide 4- and 8-row layouts and a time-split sequence
     b, L, D, N = shape
     inp = workloads.scan_inputs(b, L, D, N, dtype=xd, delta_dtype=dd, seed=sum(shape) + 131, dt="softplus_bias",
                                 gate=True, softplus=True, skip=True, h0=True)
@@ -146,13 +146,14 @@ def test_lengths_and_optional_terms(ssm, dtype, L, skip, gate, softplus):
     check(ssm, inp, label="L=%d %s skip=%s gate=%s softplus=%s" % (L, dtype, skip, gate, softplus))
 
 
-# Lane layouts and workgroup shapes, compared in full: 8 rows with four waves per workgroup
-# (8x2048 channels), 4 rows with four waves (16x2048; dstate 64 and 128 at 128 / 64 channels),
-# 16 rows with four waves and a ragged tile, and 16 rows with one wave per workgroup (channel
-# groups not a multiple of four), each in bf16 and fp32.
+# Lane layouts and workgroup shapes, compared in full: with 16 states and four waves per workgroup,
+# 8 rows (8x2048 channels: one 4-row wave per SIMD), 16 rows (10x2048: 1.25 per SIMD) and 4 rows
+# (16x2048: two per SIMD); 4 rows of wide lanes (dstate 64 and 128 at 128 / 64 channels); 16 rows
+# with four waves and a ragged tile, and 16 rows with one wave per workgroup (channel groups not a
+# multiple of four), each in bf16 and fp32.
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("shape", [(8, 100, 2048, 16), (16, 80, 2048, 16), (2, 300, 128, 64), (2, 150, 64, 128),
-                                   (2, 257, 48, 16), (3, 100, 20, 16)])
+@pytest.mark.parametrize("shape", [(8, 100, 2048, 16), (10, 60, 2048, 16), (16, 80, 2048, 16), (2, 300, 128, 64),
+                                   (2, 150, 64, 128), (2, 257, 48, 16), (3, 100, 20, 16)])
 def test_workgroup_layouts(ssm, dtype, shape):
     b, L, D, N = shape
     inp = workloads.scan_inputs(b, L, D, N, dtype=dtype, seed=sum(shape) + 5, dt="softplus_bias", gate=True,
