@@ -204,6 +204,10 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
   constexpr bool SAVE = (MODE == kModeSave);
   static_assert(!SAVE || T % kSaveTile == 0, "tiles hold whole save intervals");
   constexpr bool ACC = GAIN != kGainShort;   // accurate softplus as well
+  // The state-only pass with the short ZOH gain carries a*h instead of h:
+  // a*h' = E*(a*h) + (E - 1)*B*x, one instruction per element fewer than
+  // h' = E*h + ((E - 1)/a)*B*x; the scale is undone when the state is stored.
+  constexpr bool SCALED = !FULL && GAIN == kGainShort;
   static_assert(VEC || W == 1, "the scalar tile path runs one wave per workgroup");
   constexpr int WCH = W * CH;                 // channels per workgroup (LDS row width)
   const int tid = threadIdx.x;                // thread in the workgroup
@@ -238,6 +242,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
   for (int s = 0; s < S; ++s) {
     const int64_t n = r * S + s;
     h[s] = (hin != nullptr && ch_ok && n < N) ? hin[(b * dim + ch) * N + n] : 0.f;
+    if constexpr (SCALED) h[s] *= av[s];
   }
   const float Dv = (FULL && a.Dskip != nullptr && ch_ok) ? a.Dskip[ch] : 0.f;
   const float bias = (a.delta_bias != nullptr && ch_ok) ? a.delta_bias[ch] : 0.f;
@@ -565,10 +570,15 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
 #pragma unroll
         for (int s = 0; s < S; ++s) {
           const float E = Ecur[j][s];
-          const float g = GAIN == kGainEuler      ? dx.x
-                          : GAIN == kGainAccurate ? zoh_gain_accurate(E, dx.x, av[s], ia[s])
-                                                  : fmaf(E, ia[s], -ia[s]);
-          h[s] = fmaf(E, h[s], g * (cur.b[j][s] * dx.y));
+          if constexpr (SCALED) {
+            const float u = cur.b[j][s] * dx.y;
+            h[s] = fmaf(E, h[s], fmaf(E, u, -u));
+          } else {
+            const float g = GAIN == kGainEuler      ? dx.x
+                            : GAIN == kGainAccurate ? zoh_gain_accurate(E, dx.x, av[s], ia[s])
+                                                    : fmaf(E, ia[s], -ia[s]);
+            h[s] = fmaf(E, h[s], g * (cur.b[j][s] * dx.y));
+          }
           if (FULL) acc = fmaf(cur.c[j][s], h[s], acc);
         }
         pr[R == U ? j : (tb + j) % R] = acc;   // static index: R == U, or the loop is fully unrolled
@@ -609,10 +619,15 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
             for (int e = 0; e < 4; ++e) {
               const int st = 4 * q + e;
               const float E = hw_exp2(dx.x * a2[st]);
-              const float g = GAIN == kGainEuler      ? dx.x
-                              : GAIN == kGainAccurate ? zoh_gain_accurate(E, dx.x, av[st], ia[st])
-                                                      : fmaf(E, ia[st], -ia[st]);
-              h[st] = fmaf(E, h[st], g * (bq[e] * dx.y));
+              if constexpr (SCALED) {
+                const float u = bq[e] * dx.y;
+                h[st] = fmaf(E, h[st], fmaf(E, u, -u));
+              } else {
+                const float g = GAIN == kGainEuler      ? dx.x
+                                : GAIN == kGainAccurate ? zoh_gain_accurate(E, dx.x, av[st], ia[st])
+                                                        : fmaf(E, ia[st], -ia[st]);
+                h[st] = fmaf(E, h[st], g * (bq[e] * dx.y));
+              }
               if (FULL) acc = fmaf(cq[e], h[st], acc);
             }
           }
@@ -625,6 +640,10 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
   }
 
   // ---- end state
+  if constexpr (SCALED) {
+#pragma unroll
+    for (int s = 0; s < S; ++s) h[s] *= ia[s];
+  }
   float* hout = nullptr;
   if (FULL) hout = (chunk == a.nchunks - 1) ? a.h_final : nullptr;
   else hout = (a.nchunks == 1) ? a.h_final : a.ws_state + chunk * slice_elems;
