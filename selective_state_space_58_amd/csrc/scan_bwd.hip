@@ -298,7 +298,10 @@ __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64
       }
     }
     __syncthreads();
-    // adjoint, tokens in reverse, in groups of 4 for the row reductions
+    // adjoint, tokens in reverse, in groups of 4 for the row reductions; the
+    // state before token t is the state after token t-1, carried to the next
+    // (earlier) token instead of read again
+    float hcar = hw[(BT - 1) * 64 + lane];
 #pragma unroll 2
     for (int tb = BT - BG; tb >= 0; tb -= BG) {
     float pdx[BG], pdt[BG];
@@ -309,8 +312,9 @@ __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64
       const float dy = sm.dy[tl * BWC + wc];
       const float Bn = sm.bc[(tl * BR + r) * 2], Cn = sm.bc[(tl * BR + r) * 2 + 1];
       const float E = ew[tl * 64 + lane];
-      const float ht = hw[tl * 64 + lane];
+      const float ht = hcar;
       const float hp = tl > 0 ? hw[(tl - 1) * 64 + lane] : hstart;
+      hcar = hp;
       const float g = gain(E, dx.x);
       lam = fmaf(Cn, dy, lam);
       // dC = sum over channels of h_t dy; dB = sum over channels of lam g x
