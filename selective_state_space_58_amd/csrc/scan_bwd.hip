@@ -140,7 +140,6 @@ struct BwdLds {
   float dy[BT * BWC];           // dout * silu(z)
   float bc[BT * BR * 2];        // (B, C) per (token, state)
   float h[BW * BT * 64];        // h_t per (wave, token, lane)
-  float E[BW * BT * 64];        // e^{dt_t a} per (wave, token, lane)
   float red[BW * BT * BR * 2];  // per-wave (dB, dC) partial per (token, state)
 };
 
@@ -253,7 +252,6 @@ __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64
   float lam = (a.dh_final != nullptr && nok) ? a.dh_final[hidx] : 0.f;
   float dA = 0.f, dDacc = 0.f, dbacc = 0.f;
   float* hw = sm.h + w * BT * 64;
-  float* ew = sm.E + w * BT * 64;
   float* rw = sm.red + w * BT * BR * 2;
   const int64_t per_group = a.batch * L * BR;
   for (int k = ntile - 1; k >= 0; --k) {
@@ -277,7 +275,6 @@ __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64
         const float E = hw_exp2(dx.x * a2);
         hs = fmaf(E, hs, gain(E, dx.x) * (Bn * dx.y));
         hw[tl * 64 + lane] = hs;
-        ew[tl * 64 + lane] = E;
         pr[j] = Cn * hs;
       }
       const float tot = reduce4_rows(pr);   // rows 4j .. 4j+3: readout of token tb + j
@@ -311,7 +308,7 @@ __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64
       const float2 dx = sm.dx[tl * BWC + wc];
       const float dy = sm.dy[tl * BWC + wc];
       const float Bn = sm.bc[(tl * BR + r) * 2], Cn = sm.bc[(tl * BR + r) * 2 + 1];
-      const float E = ew[tl * 64 + lane];
+      const float E = hw_exp2(dx.x * a2);   // recomputed: cheaper than a store and a read of LDS
       const float ht = hcar;
       const float hp = tl > 0 ? hw[(tl - 1) * 64 + lane] : hstart;
       hcar = hp;
