@@ -343,10 +343,8 @@ def main():
     import torch
 
     import workloads
-    from selective_state_space_58_amd import _binding
-    if not os.path.exists(_binding.library_path()):
-        import __graft_entry__
-        __graft_entry__.build()
+    import __graft_entry__
+    __graft_entry__._ensure_built()   # builds only when the library is missing or stale
     import selective_state_space_58_amd as ssm
 
     dev = torch.device("cuda:0")

@@ -190,9 +190,13 @@ size_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int6
  *   S[p][n] = exp(dt*A[h]) S[p][n] + (exp(dt*A[h]) - 1)/A[h] * B[b,t,g,n] * x[b,t,h,p]
  *   y[b,t,h,p] = (sum_n C[b,t,g,n] S[p][n] + Dskip[h] x[b,t,h,p]) * silu(z[b,t,h,p])
  *
- * computed in chunks of `chunk_size` tokens: within a chunk as a causal,
- * decayed matrix product on the matrix cores, across chunks by passing the
- * state ([ssd] block decomposition).
+ * computed blockwise ([ssd] block decomposition): within a block of 64
+ * tokens as a causal, decayed matrix product on the matrix cores, across
+ * blocks by passing the state.  The block is 64 tokens whatever `chunk_size`
+ * is: any block length gives the same map (the state entering a block is the
+ * decayed sum of everything before it), so `chunk_size` (64, 128 or 256, the
+ * chunk lengths of the pages' chunked form) is validated and otherwise does
+ * not change the computation; results are identical for every accepted value.
  *
  *   x, z, y : (batch, seqlen, nheads, headdim)  act dtype (z NULL for no gate)
  *   dt      : (batch, seqlen, nheads)           delta dtype
@@ -217,7 +221,7 @@ int ssd_chunk_scan_fwd(const void* x, const void* dt, const float* A, const void
  * formed once and shared by the group's heads), plus, when the (batch, head)
  * pairs are too few to fill the device and the sequence is split into time
  * chunks, the chunk states carried on the device.  Zero only for seqlen 0.
- * Depends on the current device. */
+ * chunk_size does not change it.  Depends on the current device. */
 size_t ssd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                            int64_t ngroups, int64_t dstate, int64_t chunk_size);
 
@@ -395,6 +399,12 @@ const char* ssm_status_string(int status);
 
 /* Detail for the calling thread's most recent failure ("" if none). */
 const char* ssm_last_error(void);
+
+/* SHA-256, as 64 lowercase hex digits, of the sources the library was built
+ * from (every file of its csrc/ directory and every header of include/).  A
+ * loader compares it with the sources beside the library and refuses a build
+ * made from other sources.  Static storage; never NULL. */
+const char* ssm_source_digest(void);
 
 #ifdef __cplusplus
 }

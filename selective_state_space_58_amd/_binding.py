@@ -7,6 +7,8 @@ import threading
 
 import torch
 
+from . import build as _build
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libssm_mi355x.so")
 _lock = threading.Lock()
@@ -33,6 +35,15 @@ def library_path() -> str:
     return _LIB_PATH
 
 
+def check_library(lib_path: str = _LIB_PATH, csrc: str = _build.CSRC, include: str = _build.INCLUDE) -> None:
+    """Raise unless `lib_path` was built from the sources in `csrc` and `include` (the digest the
+    build embeds in the library file must equal the digest of those sources)."""
+    why = _build.stale_reason(lib_path, csrc, include)
+    if why is not None:
+        raise RuntimeError(why + "; rebuild with __graft_entry__.build() or "
+                           "python selective_state_space_58_amd/build.py")
+
+
 def load_library():
     """Load the HIP library; raises if it has not been built (no fallback exists)."""
     global _lib
@@ -42,7 +53,12 @@ def load_library():
         if not os.path.exists(_LIB_PATH):
             raise RuntimeError("libssm_mi355x.so is not built; run __graft_entry__.build() or "
                                "python selective_state_space_58_amd/build.py")
+        check_library(_LIB_PATH)
         lib = ctypes.CDLL(_LIB_PATH)
+        lib.ssm_source_digest.argtypes = []
+        lib.ssm_source_digest.restype = ctypes.c_char_p
+        if lib.ssm_source_digest().decode() != _build.source_digest():
+            raise RuntimeError("%s reports another source digest than its file holds" % _LIB_PATH)
         lib.ssm_scan_fwd.argtypes = [_P] * 8 + [_I, _P, _P, _P] + [_I64] * 4 + [_I, _I, _P, _SZ, _P]
         lib.ssm_scan_fwd.restype = _I
         lib.ssm_scan_fwd_ex.argtypes = [_P] * 8 + [_I, _P, _P, _P] + [_I64] * 4 + [_I, _I, _I, _P, _SZ, _P]

@@ -136,6 +136,15 @@ const char* ssm_status_string(int status) {
 
 const char* ssm_last_error(void) { return g_last_error.c_str(); }
 
+#ifndef SSM_SOURCE_DIGEST
+#define SSM_SOURCE_DIGEST "0000000000000000000000000000000000000000000000000000000000000000"
+#endif
+// The marker lets a loader find the digest in the library file without loading it.
+static const char kSourceDigest[] = "ssm-source-sha256:" SSM_SOURCE_DIGEST;
+static_assert(sizeof(kSourceDigest) == 18 + 64 + 1, "the source digest is 64 hex digits");
+
+const char* ssm_source_digest(void) { return kSourceDigest + 18; }
+
 size_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int final_state_only) {
   if (batch <= 0 || seqlen <= 0 || dim <= 0 || dstate <= 0 || dstate > 256) return 0;
   return plan_scan(batch, seqlen, dim, dstate, final_state_only != 0, device_cu_count()).ws_bytes;

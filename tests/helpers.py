@@ -19,27 +19,49 @@ def rel_err(got, ref) -> float:
     return float(np.max(np.abs(got - ref) / (np.abs(ref) + scale + 1e-300)))
 
 
+def err_report(got, ref, block=1 << 22) -> dict:
+    """Three relative-error figures of `got` against `ref`, computed in blocks so that arrays of
+    hundreds of millions of elements need no full-size temporaries:
+      bar   max_i |d_i| / (|ref_i| + rms(ref))    (the parity metric, compared with TOL)
+      inf   max_i |d_i| / max_i |ref_i|           (inf-norm relative error)
+      floor max_i |d_i| / max(|ref_i|, 1e-3 rms)  (per-element relative error, 1e-3 rms floor)
+    plus the element count and rms(ref).  NaN anywhere in `got` makes every figure NaN."""
+    g = np.asarray(got).reshape(-1)
+    r = np.asarray(ref).reshape(-1)
+    if g.shape != r.shape:
+        raise ValueError("shape mismatch %s vs %s" % (np.shape(got), np.shape(ref)))
+    n = r.size
+    if n == 0:
+        return dict(bar=0.0, inf=0.0, floor=0.0, n=0, rms=0.0)
+    ss, amax = 0.0, 0.0
+    for i in range(0, n, block):
+        rb = np.asarray(r[i:i + block], dtype=np.float64)
+        ss += float(np.dot(rb, rb))
+        amax = max(amax, float(np.max(np.abs(rb))))
+    rms = (ss / n) ** 0.5
+    bar = dmax = floor = 0.0
+    for i in range(0, n, block):
+        rb = np.asarray(r[i:i + block], dtype=np.float64)
+        d = np.abs(np.asarray(g[i:i + block], dtype=np.float64) - rb)
+        if np.isnan(d).any():
+            return dict(bar=float("nan"), inf=float("nan"), floor=float("nan"), n=n, rms=rms)
+        a = np.abs(rb)
+        bar = max(bar, float(np.max(d / (a + rms + 1e-300))))
+        floor = max(floor, float(np.max(d / np.maximum(a, 1e-3 * rms + 1e-300))))
+        dmax = max(dmax, float(np.max(d)))
+    return dict(bar=bar, inf=dmax / (amax + 1e-300), floor=floor, n=n, rms=rms)
+
+
+def fmt_report(name, rep) -> str:
+    return "%s: %d elements, bar %.3g, inf-norm %.3g, per-element (1e-3 rms floor) %.3g" % (
+        name, rep["n"], rep["bar"], rep["inf"], rep["floor"])
+
+
 def oracle_scan(inp, want_y=True, threads=None):
     f = workloads.to_f64(inp)
     return oracle.selective_scan(f["x"], f["delta"], f["A"], f["B"], f["C"], Dskip=f["D"], z=f["z"],
                                  delta_bias=f["delta_bias"], delta_softplus=inp["meta"]["softplus"], h0=f["h0"],
                                  want_y=want_y, threads=threads)
-
-
-def oracle_scan_slices(inp, slices, threads=None):
-    """Oracle outputs for a list of (b, d) slices: y (len, L) and h_final (len, N)."""
-    f = workloads.to_f64(inp)
-    ys, hs = [], []
-    for b, d in slices:
-        sl = lambda a: None if a is None else a[b:b + 1, :, d:d + 1]
-        y, h = oracle.selective_scan(sl(f["x"]), sl(f["delta"]), f["A"][d:d + 1], f["B"][b:b + 1], f["C"][b:b + 1],
-                                     Dskip=None if f["D"] is None else f["D"][d:d + 1], z=sl(f["z"]),
-                                     delta_bias=None if f["delta_bias"] is None else f["delta_bias"][d:d + 1],
-                                     delta_softplus=inp["meta"]["softplus"],
-                                     h0=None if f["h0"] is None else f["h0"][b:b + 1, d:d + 1], threads=1)
-        ys.append(y[0, :, 0])
-        hs.append(h[0, 0])
-    return np.stack(ys), np.stack(hs)
 
 
 def oracle_ssd(inp, want_y=True, threads=None):

@@ -12,9 +12,8 @@ HEADER = os.path.join(ROOT, "include", "ssm_mi355x.h")
 
 def _lib():
     from selective_state_space_58_amd import _binding
-    if not os.path.exists(_binding.library_path()):
-        import __graft_entry__
-        __graft_entry__.build()
+    import __graft_entry__
+    __graft_entry__._ensure_built()
     return _binding.load_library()
 
 

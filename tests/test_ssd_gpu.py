@@ -4,7 +4,7 @@ import pytest
 import torch
 
 import workloads
-from tests.helpers import TOL, oracle_ssd, rel_err
+from tests.helpers import TOL, err_report, fmt_report, oracle_ssd, rel_err
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -64,7 +64,9 @@ def test_chunk_size_invariance(ssm):
     y_ref, h_ref = oracle_ssd(inp)
     for y, hf in outs:
         assert rel_err(y, y_ref) <= TOL["bf16"] and rel_err(hf, h_ref) <= TOL["bf16"]
-    assert rel_err(outs[0][0], outs[2][0]) <= TOL["bf16"]
+    # the kernel passes the state every 64 tokens whatever chunk_size is: identical results
+    for y, hf in outs[1:]:
+        assert np.array_equal(y, outs[0][0]) and np.array_equal(hf, outs[0][1])
 
 
 @pytest.mark.parametrize("N,G,L", [(128, 2, 3000), (64, 1, 2077)])
@@ -109,20 +111,15 @@ def test_empty_and_single_token(ssm, P):
     check(ssm, inp1, "single token P=%d" % P)
 
 
-def test_full_size_workload_sampled_heads(ssm):
+def test_full_size_workload_every_element(ssm):
+    # b2 x 64 heads x 8192 tokens: every y and every h_final element against the oracle
     inp, cfg = workloads.config_inputs(4)
-    print("case", cfg["name"], flush=True)
+    print("case", cfg["name"], "(GPU run)", flush=True)
     y, hf = run(ssm, inp, cfg["chunk"])
-    assert np.all(np.isfinite(y))
-    # oracle on a few (batch, head) slices: slice the head axis (ngroups = 1 keeps B, C whole)
-    for b, h in [(0, 0), (1, 37), (0, 63)]:
-        sub = {k: v for k, v in inp.items()}
-        sub["x"] = inp["x"][b:b + 1, :, h:h + 1]
-        sub["dt"] = inp["dt"][b:b + 1, :, h:h + 1]
-        sub["A"] = inp["A"][h:h + 1]
-        sub["B"] = inp["B"][b:b + 1]
-        sub["C"] = inp["C"][b:b + 1]
-        y_ref, h_ref = oracle_ssd(sub, threads=1)
-        ey, eh = rel_err(y[b:b + 1, :, h:h + 1], y_ref), rel_err(hf[b:b + 1, h:h + 1], h_ref)
-        print("  head (%d, %d): y rel err %.3g  h_final rel err %.3g" % (b, h, ey, eh))
-        assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
+    assert np.all(np.isfinite(y)) and np.all(np.isfinite(hf))
+    print("  oracle (recurrent form) on all (batch, head) slices", flush=True)
+    y_ref, h_ref = oracle_ssd(inp)
+    for name, got, ref in (("y", y, y_ref), ("h_final", hf, h_ref)):
+        rep = err_report(got, ref)
+        print("  " + fmt_report(name, rep), flush=True)
+        assert rep["bar"] <= TOL["bf16"], (name, rep)
