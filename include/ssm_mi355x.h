@@ -100,6 +100,31 @@ int ssm_scan_fwd(const void* x, const void* delta, const float* A, const void* B
                  int act_dtype, int delta_dtype,
                  void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * ssm_scan_fwd that allocates nothing, for callers that cannot allocate
+ * device memory while they run: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Arguments, layouts, ownership and
+ * errors are those of ssm_scan_fwd without the workspace: the caller still
+ * passes every input and output, and the time-split chunk states live in a
+ * fixed device array of ssm_scan_fwd_noalloc_max_workspace_bytes() bytes
+ * (32 MiB) that the library holds on each GPU it runs on until the process
+ * ends.  Shapes whose workspace (ssm_scan_workspace_bytes(..., 0)) exceeds it
+ * return SSM_ERR_WORKSPACE before anything is enqueued.  The call makes no
+ * hipMalloc, hipFree or other allocating call (its first call on a device
+ * looks the array's address up once).  Every call on one GPU shares that
+ * GPU's array: calls that overlap on one GPU (other streams, other host
+ * threads) race and must be ordered by the caller; calls on one stream are
+ * ordered by the stream.  Nothing in the array needs to start at zero.
+ */
+int ssm_scan_fwd_noalloc(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                         const float* Dskip, const void* z, const float* delta_bias, int delta_softplus,
+                         const float* h0, void* y, float* h_final,
+                         int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                         int act_dtype, int delta_dtype, void* stream);
+
+/* Size of ssm_scan_fwd_noalloc's fixed per-GPU workspace in bytes. */
+size_t ssm_scan_fwd_noalloc_max_workspace_bytes(void);
+
 /* flag bits of ssm_scan_fwd_ex */
 enum ssm_scan_flag {
   SSM_SCAN_REVERSE = 1,         /* run the recurrence from the last token to the first */

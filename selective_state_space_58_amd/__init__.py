@@ -26,6 +26,8 @@ from ._binding import (  # noqa: F401
     ssm_scan_final_state,
     ssm_scan_fwd,
     ssm_scan_fwd_ex,
+    ssm_scan_fwd_noalloc,
+    ssm_scan_fwd_noalloc_max_workspace_bytes,
     ssm_scan_fwd_train,
     ssm_scan_train_states_bytes,
     ssm_state_update,

@@ -61,6 +61,10 @@ def load_library():
             raise RuntimeError("%s reports another source digest than its file holds" % _LIB_PATH)
         lib.ssm_scan_fwd.argtypes = [_P] * 8 + [_I, _P, _P, _P] + [_I64] * 4 + [_I, _I, _P, _SZ, _P]
         lib.ssm_scan_fwd.restype = _I
+        lib.ssm_scan_fwd_noalloc.argtypes = [_P] * 8 + [_I, _P, _P, _P] + [_I64] * 4 + [_I, _I, _P]
+        lib.ssm_scan_fwd_noalloc.restype = _I
+        lib.ssm_scan_fwd_noalloc_max_workspace_bytes.argtypes = []
+        lib.ssm_scan_fwd_noalloc_max_workspace_bytes.restype = _SZ
         lib.ssm_scan_fwd_ex.argtypes = [_P] * 8 + [_I, _P, _P, _P] + [_I64] * 4 + [_I, _I, _I, _P, _SZ, _P]
         lib.ssm_scan_fwd_ex.restype = _I
         lib.ssm_scan_fwd_train.argtypes = [_P] * 8 + [_I, _P, _P, _P] + [_I64] * 4 + [_I, _I, _I, _P, _P, _SZ, _P]
@@ -162,6 +166,19 @@ def ssm_scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softp
                      workspace, None)
 
 
+def ssm_scan_fwd_noalloc(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False, h0=None,
+                         return_final_state=False, y=None, h_final=None):
+    """ssm_scan_fwd whose library call allocates nothing: the time-split chunk states live in the
+    library's fixed per-GPU workspace (ssm_scan_fwd_noalloc_max_workspace_bytes()).  Outputs not
+    passed are allocated here, by torch, before the call."""
+    return _scan_fwd(x, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, return_final_state, y, h_final,
+                     None, None, noalloc=True)
+
+
+def ssm_scan_fwd_noalloc_max_workspace_bytes() -> int:
+    return int(load_library().ssm_scan_fwd_noalloc_max_workspace_bytes())
+
+
 def ssm_scan_fwd_ex(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False, h0=None,
                     return_final_state=False, y=None, h_final=None, workspace=None, reverse=False, euler=False):
     """ssm_scan_fwd with the variant flags: reverse (scan from the last token to the first),
@@ -198,7 +215,7 @@ def ssm_scan_train_states_bytes(batch, seqlen, dim, dstate) -> int:
 
 
 def _scan_fwd(x, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, return_final_state, y, h_final, workspace,
-              flags, states=None):
+              flags, states=None, noalloc=False):
     lib = load_library()
     dev = x.device
     _need(x, "x", device=dev)
@@ -226,7 +243,10 @@ def _scan_fwd(x, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, return_fi
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = (_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
             int(bool(delta_softplus)), _ptr(h0), _ptr(y), _ptr(h_final), batch, seqlen, dim, dstate, act, dcode)
-    if states is not None:
+    if noalloc:
+        rc = lib.ssm_scan_fwd_noalloc(*args, _stream(dev))
+        _check(lib, "ssm_scan_fwd_noalloc", rc)
+    elif states is not None:
         rc = lib.ssm_scan_fwd_train(*args, int(flags), _ptr(states), _ptr(workspace), wsb, _stream(dev))
         _check(lib, "ssm_scan_fwd_train", rc)
     elif flags is None:

@@ -155,7 +155,7 @@ static int scan_common(const void* x, const void* delta, const float* A, const v
                        const float* h0, void* y, float* h_final, int64_t batch, int64_t seqlen, int64_t dim,
                        int64_t dstate, int act_dtype, int delta_dtype, void* workspace, size_t workspace_bytes,
                        void* stream, bool final_only, int flags = 0, float* save_states = nullptr,
-                       bool want_save = false) {
+                       bool want_save = false, bool no_alloc = false) {
   g_last_error.clear();
   if ((flags & ~(SSM_SCAN_REVERSE | SSM_SCAN_EULER | SSM_SCAN_DELTA_PER_TOKEN)) != 0)
     return fail(SSM_ERR_UNSUPPORTED, "unknown scan flag bits");
@@ -170,7 +170,8 @@ static int scan_common(const void* x, const void* delta, const float* A, const v
   hipStream_t st = (hipStream_t)stream;
   Scratch own;
   void* ws = nullptr;
-  rc = get_workspace(workspace, workspace_bytes, seqlen > 0 ? p.ws_bytes : 0, st, &own, &ws);
+  if (no_alloc) rc = noalloc_scratch(seqlen > 0 ? p.ws_bytes : 0, &ws);
+  else rc = get_workspace(workspace, workspace_bytes, seqlen > 0 ? p.ws_bytes : 0, st, &own, &ws);
   if (rc != SSM_OK) return rc;
   ScanArgs a{};
   a.x = x; a.delta = delta; a.A = A; a.B = B; a.C = final_only ? nullptr : C;
@@ -206,6 +207,16 @@ int ssm_scan_fwd(const void* x, const void* delta, const float* A, const void* B
   return scan_common(x, delta, A, B, C, Dskip, z, delta_bias, delta_softplus, h0, y, h_final, batch, seqlen, dim,
                      dstate, act_dtype, delta_dtype, workspace, workspace_bytes, stream, false);
 }
+
+int ssm_scan_fwd_noalloc(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                         const float* Dskip, const void* z, const float* delta_bias, int delta_softplus,
+                         const float* h0, void* y, float* h_final, int64_t batch, int64_t seqlen, int64_t dim,
+                         int64_t dstate, int act_dtype, int delta_dtype, void* stream) {
+  return scan_common(x, delta, A, B, C, Dskip, z, delta_bias, delta_softplus, h0, y, h_final, batch, seqlen, dim,
+                     dstate, act_dtype, delta_dtype, nullptr, 0, stream, false, 0, nullptr, false, true);
+}
+
+size_t ssm_scan_fwd_noalloc_max_workspace_bytes(void) { return kNoAllocScratchBytes; }
 
 int ssm_scan_fwd_ex(const void* x, const void* delta, const float* A, const void* B, const void* C,
                     const float* Dskip, const void* z, const float* delta_bias, int delta_softplus,

@@ -3,10 +3,47 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
+#include <string>
 
 #include "ssm_internal.h"
 
+// Workspace of ssm_scan_fwd_noalloc (time-split chunk states and step sums):
+// one array per GPU, held until the process ends.  Host code never passes the
+// array's name to a kernel or a copy: on the host that name is only a stand-in
+// for the symbol, so its device address is looked up per device with
+// hipGetSymbolAddress (noalloc_scratch below) and that address is used.
+static __device__ __align__(256) unsigned char scratch[ssm::kNoAllocScratchBytes];
+
 namespace ssm {
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+int noalloc_scratch(size_t need, void** out) {
+  *out = nullptr;
+  if (need > kNoAllocScratchBytes)
+    return fail(5, "the no-allocation scan needs " + std::to_string(need) + " bytes of workspace for these shapes; "
+                   "its fixed workspace holds " + std::to_string(kNoAllocScratchBytes));
+  if (need == 0) return 0;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(6, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(4, "device index beyond the no-allocation scan's table");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(6, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return 0;
+}
 
 #define SSM_DECL(R, XB, DB, S)                                                                         \
   hipError_t launch_scan_r##R##_x##XB##_d##DB##_s##S(int mode, const ScanArgs& a, dim3 grid, int64_t gpb, \

@@ -64,6 +64,14 @@ ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, b
 // Enqueue the whole selective scan (all phases).  Returns an ssm_status.
 int launch_scan(const ScanArgs& a, const ScanPlan& p, bool final_only, void* stream);
 
+// Workspace of the no-allocation scan entry point: a fixed device array of
+// kNoAllocScratchBytes per GPU, shared by every such call on that GPU.
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+// Device address of the current GPU's array (looked up once per device).
+// Fails with SSM_ERR_WORKSPACE when need exceeds the array, SSM_ERR_HIP on a
+// runtime error.
+int noalloc_scratch(size_t need, void** out);
+
 // ---------------------------------------------------------------- selective scan backward
 struct BwdArgs {
   const void* x;

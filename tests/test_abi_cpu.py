@@ -334,3 +334,36 @@ def test_train_pair_queries():
     assert lib.ssm_scan_bwd_train_workspace_bytes(2, 100, 40, 16, 4) == part + 2 * 100 * 40 * 4
     assert lib.ssm_scan_bwd_train_workspace_bytes(2, 100, 40, 16, 8) == 0
     assert lib.ssm_scan_bwd_train_workspace_bytes(2, 100, 40, 257, 0) == 0
+
+
+def scan_noalloc(lib, **kw):
+    a = dict(x=P, delta=P, A=P, B=P, C=P, D=None, z=None, bias=None, sp=0, h0=None, y=P, hf=None,
+             batch=1, seqlen=4, dim=4, dstate=4, act=1, ddt=1, stream=None)
+    a.update(kw)
+    return lib.ssm_scan_fwd_noalloc(a["x"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"], a["sp"],
+                                    a["h0"], a["y"], a["hf"], a["batch"], a["seqlen"], a["dim"], a["dstate"],
+                                    a["act"], a["ddt"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [(dict(x=None), 1), (dict(y=None), 1), (dict(batch=-1), 2), (dict(dstate=0), 2),
+                                     (dict(act=5), 3), (dict(dstate=257), 4), (dict(x=P + 1), 7)])
+def test_noalloc_scan_argument_errors(kw, code):
+    # the same validation as ssm_scan_fwd, before anything is enqueued
+    lib = _lib()
+    assert scan_noalloc(lib, **kw) == code
+    assert lib.ssm_last_error() != b""
+
+
+def test_noalloc_scan_rejects_shapes_beyond_its_workspace():
+    lib = _lib()
+    cap = lib.ssm_scan_fwd_noalloc_max_workspace_bytes()
+    assert cap == 32 << 20
+    # 256 states on 2048 channels over 131072 tokens: the time split needs more than the fixed array
+    need = lib.ssm_scan_workspace_bytes(1, 131072, 2048, 256, 0)
+    assert need > cap
+    assert scan_noalloc(lib, seqlen=131072, dim=2048, dstate=256) == 5
+    msg = lib.ssm_last_error()
+    assert b"no-allocation" in msg and str(need).encode() in msg
+    # the long-sequence layer (16 states) fits
+    assert 0 < lib.ssm_scan_workspace_bytes(1, 131072, 2048, 16, 0) <= cap
+    assert scan_noalloc(lib, batch=0) == 0
