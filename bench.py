@@ -1,16 +1,18 @@
 """Benchmark of the selective scan on one MI355X.
 
 One step = one full selective-scan forward (discretize + recurrence + readout
-+ skip + gate) over the Mamba-130M-like layer workload: batch 8, 1536
-channels, 2048 tokens, 16 states, bf16 inputs/outputs, fp32 state, softplus dt
-with per-channel bias, silu(z) gate.  Inputs are resident in HBM before the
-timed region; each step reads one of six rotating input copies (1.2 GB, far
-beyond the 256 MB last-level cache) so no step reads another step's inputs
-from cache.
++ skip, final state) over the long-sequence layer workload, the largest of the
+five workloads that fits one GPU: batch 1, 2048 channels, 131072 tokens, 16
+states, bf16 x/delta/B/C/y, fp32 A, skip and state, delta log-uniform in
+[1e-4, 1e-1], h_final returned.  Inputs are resident in HBM before the timed
+region (1.1 GB of x and delta per step, several times the 256 MB last-level
+cache, so every step reads them from HBM).
 
 Prints one JSON line with the headline throughput (token*channels/s), the
-roofline of the scan kernel measured with HIP events on the launch stream, the
-oracle timed on the host cores (rank 0, N=1 only), and the other workloads.
+roofline of the scan measured with HIP events on the launch stream, the oracle
+timed on the host cores (rank 0, N=1 only), and the other workloads (the
+small fp32 layer, the 130M-like and 2.8B-like layers, SSD, decode steps,
+conv1d + SiLU, the backward and the training pair).
 """
 from __future__ import annotations
 
@@ -46,41 +48,52 @@ def parse():
                    help="seconds of untimed launches before the warmup steps (clocks settle)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-others", action="store_true")
-    p.add_argument("--only", choices=["scan-2.8b", "scan-long", "ssd", "step", "ssd-step", "conv", "bwd", "train", "copy",
-                                      "ubench"],
+    p.add_argument("--only", choices=["scan-small", "scan-130m", "scan-2.8b", "scan-long", "ssd", "step", "ssd-step",
+                                      "conv", "bwd", "train", "copy", "ubench"],
                    default=None,
-                   help="time only this other workload (for profiling); skips the headline JSON line")
+                   help="time only this workload (for profiling); skips the headline JSON line")
     return p.parse_args()
 
 
-# Sources that determine the headline scan kernel's code and launch plan, and the
-# committed rocprofv3 counter summary of that kernel on the headline workload.
-SCAN_KERNEL_SOURCES = ["selective_state_space_58_amd/csrc/scan_impl.h",
-                       "selective_state_space_58_amd/csrc/scan_inst.hip",
-                       "selective_state_space_58_amd/csrc/scan_host.hip"]
-SCAN_COUNTER_SUMMARY = "profiles/scan_bf16_b8_d1536_l2048_n16_hbm_counters.md"
+# The headline workload (index into workloads.CONFIGS): the long-sequence layer, the largest single-GPU one.
+HEADLINE = 3
+
+# Committed rocprofv3 summaries that carry HBM byte counters, with the sources of the kernels they cover.
+# A summary's traffic figure is used only while the SHA-256 of those sources still matches the one recorded
+# in it (kernel_sources_sha256_16); otherwise the traffic is reported as null.
+COUNTER_SUMMARIES = {
+    "scan_long": ("profiles/scan_bf16_b1_d2048_l131072_n16_hbm_counters.md",
+                  ["selective_state_space_58_amd/csrc/scan_impl.h", "selective_state_space_58_amd/csrc/scan_inst.hip",
+                   "selective_state_space_58_amd/csrc/scan_host.hip"]),
+    "scan_130m": ("profiles/scan_bf16_b8_d1536_l2048_n16_hbm_counters.md",
+                  ["selective_state_space_58_amd/csrc/scan_impl.h", "selective_state_space_58_amd/csrc/scan_inst.hip",
+                   "selective_state_space_58_amd/csrc/scan_host.hip"]),
+    "ssd": ("profiles/ssd_bf16_b2_h64_p64_n128_l8192_q256_kernel.md",
+            ["selective_state_space_58_amd/csrc/ssd_kernels.hip"]),
+}
 
 
-def scan_kernel_digest():
+def sources_digest(files):
     h = hashlib.sha256()
-    for f in SCAN_KERNEL_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per launch of the headline scan kernel, from the committed counter summary
-    (FETCH_SIZE and WRITE_SIZE scaled by a copy-kernel calibration); None when the summary is
-    missing or the kernel sources changed since the counters were taken."""
+def measured_traffic(key):
+    """HBM bytes per launch from a committed counter summary (FETCH_SIZE and WRITE_SIZE scaled by a
+    copy-kernel calibration); None when the summary is missing or its kernels' sources changed since the
+    counters were taken."""
+    path, files = COUNTER_SUMMARIES[key]
     try:
-        with open(os.path.join(ROOT, SCAN_COUNTER_SUMMARY)) as fh:
+        with open(os.path.join(ROOT, path)) as fh:
             text = fh.read()
     except OSError:
         return None
     d = re.search(r"kernel_sources_sha256_16:\s*([0-9a-f]{16})", text)
     t = re.search(r"traffic_bytes_per_launch:\s*(\d+)", text)
-    if d is None or t is None or d.group(1) != scan_kernel_digest():
+    if d is None or t is None or d.group(1) != sources_digest(files):
         return None
     return int(t.group(1))
 
@@ -106,16 +119,23 @@ def ssd_bytes(cfg):
     return total
 
 
-def ssd_flops(cfg):
-    """Algorithmic matrix FLOPs of the chunked form (causal half of each Q x Q block)."""
-    b, L, H, P, N, G, Q = (cfg["batch"], cfg["seqlen"], cfg["nheads"], cfg["headdim"], cfg["dstate"],
-                           cfg["ngroups"], cfg["chunk"])
-    chunks = L // Q
-    cb = b * chunks * G * Q * Q * N * 2 / 2          # C B^T, lower triangle, once per group
-    diag = b * H * chunks * Q * Q * P * 2 / 2        # (CB^T o L) X, lower triangle
-    states = b * H * chunks * Q * N * P * 2          # chunk states
-    off = b * H * chunks * Q * N * P * 2             # C H^T
+def ssd_flops(cfg, block=None):
+    """Algorithmic matrix FLOPs of the blockwise form with blocks of `block` tokens (the causal half of
+    each block x block product): C B^T once per group, (C B^T o L) X, the block states B^T X and the
+    off-diagonal C H.  block=None uses the workload's chunk size."""
+    b, L, H, P, N, G = cfg["batch"], cfg["seqlen"], cfg["nheads"], cfg["headdim"], cfg["dstate"], cfg["ngroups"]
+    Q = block or cfg["chunk"]
+    blocks = L // Q
+    cb = b * blocks * G * Q * Q * N * 2 / 2          # C B^T, lower triangle, once per group
+    diag = b * H * blocks * Q * Q * P * 2 / 2        # (CB^T o L) X, lower triangle
+    states = b * H * blocks * Q * N * P * 2          # block states
+    off = b * H * blocks * Q * N * P * 2             # C H
     return cb + diag + states + off
+
+
+# The SSD kernel passes the state every 64 tokens whatever chunk_size is (a block decomposition gives the
+# same map for any block length), so its own algorithmic FLOPs are those of 64-token blocks.
+SSD_BLOCK = 64
 
 
 def step_bytes(cfg):
@@ -200,27 +220,49 @@ def run_microbench(workloads):
     return out
 
 
-def run_other(oi, steps, warmup, ssm, workloads, torch, dev):
-    """Time one of the non-headline workloads through the C ABI; returns a result dict."""
-    oinp, ocfg = workloads.config_inputs(oi)
-    t = workloads.to_device(oinp, dev)
-    if ocfg["kind"] == "scan":
-        y = torch.empty_like(t["x"])
-        hf = torch.empty((ocfg["batch"], ocfg["dim"], ocfg["dstate"]), dtype=torch.float32, device=dev)
-        nb = ssm.ssm_scan_workspace_bytes(ocfg["batch"], ocfg["seqlen"], ocfg["dim"], ocfg["dstate"])
-        ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
-        sp = oinp["meta"]["softplus"]
+def _pct(per, q, np):
+    return round(float(np.percentile(per, q)), 5)
 
-        def ostep(i):
-            ssm.ssm_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
-                             delta_bias=t["delta_bias"], delta_softplus=sp, y=y, h_final=hf, workspace=ws)
-        tot, _ = time_calls(ostep, steps, warmup, torch)
-        oms = tot / steps
-        otc = ocfg["batch"] * ocfg["seqlen"] * ocfg["dim"]
-        ob = scan_bytes(ocfg)
-        return {"name": ocfg["name"], "ms": round(oms, 4), "Gtc_s": round(otc / (oms * 1e-3) / 1e9, 2),
-                "hbm_frac": round(ob / (oms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                "valu_frac": round(otc * ocfg["dstate"] * SLOTS_PER_ELEMENT / (oms * 1e-3) / 1e12 / VALU_PEAK_TSLOTS, 4)}
+
+def run_scan(oi, steps, warmup, ssm, workloads, torch, dev, np, ncopy=1):
+    """Time ssm_scan_fwd on scan workload `oi` through the C ABI (outputs and workspace preallocated, `ncopy`
+    rotating input copies).  Returns the per-call event times and the derived rates."""
+    inp, cfg = workloads.config_inputs(oi)
+    copies = [workloads.to_device(inp, dev) for _ in range(ncopy)]
+    del inp
+    y = torch.empty_like(copies[0]["x"])
+    hf = torch.empty((cfg["batch"], cfg["dim"], cfg["dstate"]), dtype=torch.float32, device=dev)
+    nb = ssm.ssm_scan_workspace_bytes(cfg["batch"], cfg["seqlen"], cfg["dim"], cfg["dstate"])
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+    sp = copies[0]["meta"]["softplus"]
+    want_hf = bool(cfg.get("final_state"))
+
+    def fn(i):
+        t = copies[i % ncopy]
+        ssm.ssm_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], delta_bias=t["delta_bias"],
+                         delta_softplus=sp, y=y, h_final=hf if want_hf else None, workspace=ws)
+    tot, per = time_calls(fn, steps, warmup, torch)
+    ms = tot / steps
+    kern_ms = float(np.mean(per))
+    tc = cfg["batch"] * cfg["seqlen"] * cfg["dim"]
+    elems = tc * cfg["dstate"]
+    nbytes = scan_bytes(cfg)
+    slots = elems * SLOTS_PER_ELEMENT / (kern_ms * 1e-3) / 1e12
+    res = {"name": cfg["name"], "ms": round(ms, 5), "Gtc_s": round(tc / (ms * 1e-3) / 1e9, 2),
+           "kernel_ms": round(kern_ms, 5), "kernel_ms_p10": _pct(per, 10, np), "kernel_ms_p50": _pct(per, 50, np),
+           "kernel_ms_p90": _pct(per, 90, np), "steps": steps,
+           "hbm_frac": round(nbytes / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "valu_frac": round(slots / VALU_PEAK_TSLOTS, 4), "algorithmic_bytes": nbytes, "elements": elems,
+           "workspace_bytes": nb}
+    del copies, y, hf, ws
+    torch.cuda.empty_cache()
+    return res, cfg
+
+
+def run_ssd(steps, warmup, ssm, workloads, torch, dev, np):
+    """Time ssd_chunk_scan_fwd on the Mamba-2 workload; HBM and MFMA rooflines of the call."""
+    oinp, ocfg = workloads.config_inputs(4)
+    t = workloads.to_device(oinp, dev)
     y = torch.empty_like(t["x"])
     hf = torch.empty((ocfg["batch"], ocfg["nheads"], ocfg["headdim"], ocfg["dstate"]), dtype=torch.float32, device=dev)
     nb = ssm.ssd_workspace_bytes(ocfg["batch"], ocfg["seqlen"], ocfg["nheads"], ocfg["headdim"], ocfg["ngroups"],
@@ -230,12 +272,28 @@ def run_other(oi, steps, warmup, ssm, workloads, torch, dev):
     def sstep(i):
         ssm.ssd_chunk_scan_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], chunk_size=ocfg["chunk"], y=y, h_final=hf,
                                workspace=ws)
-    tot, _ = time_calls(sstep, steps, warmup, torch)
+    tot, per = time_calls(sstep, steps, warmup, torch)
     oms = tot / steps
+    kern_ms = float(np.mean(per))
     otc = ocfg["batch"] * ocfg["seqlen"] * ocfg["nheads"] * ocfg["headdim"]
-    return {"name": ocfg["name"], "ms": round(oms, 4), "Gtc_s": round(otc / (oms * 1e-3) / 1e9, 2),
-            "hbm_frac": round(ssd_bytes(ocfg) / (oms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "mfma_frac_algorithmic": round(ssd_flops(ocfg) / (oms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    nbytes = ssd_bytes(ocfg)
+    fl64 = ssd_flops(ocfg, SSD_BLOCK)
+    flq = ssd_flops(ocfg)
+    hbm = nbytes / (kern_ms * 1e-3) / 1e9
+    tf = fl64 / (kern_ms * 1e-3) / 1e12
+    res = {"name": ocfg["name"], "ms": round(oms, 5), "Gtc_s": round(otc / (oms * 1e-3) / 1e9, 2),
+           "kernel_ms": round(kern_ms, 5), "kernel_ms_p50": _pct(per, 50, np), "steps": steps,
+           "roofline_hbm": {"bound": "hbm", "achieved": round(hbm, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": round(hbm / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes,
+                            "traffic": measured_traffic("ssd")},
+           "roofline_mfma": {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                             "unit": "TFLOP/s (bf16 dense; algorithmic FLOPs of the 64-token blocks the kernel runs)",
+                             "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "algorithmic_flops": fl64,
+                             "frac_if_counted_as_256_token_chunks": round(
+                                 flq / (kern_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                             "flops_256_token_chunks": flq},
+           "note": "one call = the C B^T pre-pass and the fused SSD kernel"}
+    return res
 
 
 def run_step(si, steps, warmup, ssm, workloads, torch, dev):
@@ -378,32 +436,24 @@ def main():
         si = {"step": 0, "ssd-step": 1}[args.only]
         print(json.dumps({"only": args.only, **run_step(si, steps, warmup, ssm, workloads, torch, dev)}), flush=True)
         return
+    if args.only == "ssd":
+        print(json.dumps({"only": "ssd", **run_ssd(steps, warmup, ssm, workloads, torch, dev, np)}), flush=True)
+        return
     if args.only is not None:
-        oi = {"scan-2.8b": 2, "scan-long": 3, "ssd": 4}[args.only]
-        print(json.dumps({"only": args.only, **run_other(oi, steps, warmup, ssm, workloads, torch, dev)}), flush=True)
+        oi = {"scan-small": 0, "scan-130m": 1, "scan-2.8b": 2, "scan-long": 3}[args.only]
+        # the 130M-like layer rotates six input copies (1.2 GB, beyond the 256 MB last-level cache)
+        res, _ = run_scan(oi, steps, warmup, ssm, workloads, torch, dev, np, ncopy=6 if oi == 1 else 1)
+        print(json.dumps({"only": args.only, **res}), flush=True)
         return
 
     # ---------------------------------------------------------------- headline workload
-    idx = 1
-    inp, cfg = workloads.config_inputs(idx)
-    ncopy = 6
-    copies = [workloads.to_device(inp, dev) for _ in range(ncopy)]
-    ys = [torch.empty_like(c["x"]) for c in copies]
-
-    def step(i):
-        t = copies[i % ncopy]
-        ssm.ssm_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], delta_bias=t["delta_bias"],
-                         delta_softplus=True, y=ys[i % ncopy])
-
-    total_ms, per = time_calls(step, steps, warmup, torch)
-    ms = total_ms / steps
-    kern_ms = float(np.mean(per))
+    res, cfg = run_scan(HEADLINE, steps, warmup, ssm, workloads, torch, dev, np)
+    ms, kern_ms = res["ms"], res["kernel_ms"]
     tc = cfg["batch"] * cfg["seqlen"] * cfg["dim"]
-    elems = tc * cfg["dstate"]
     value = tc / (ms * 1e-3) / 1e9
-    nbytes = scan_bytes(cfg)
+    nbytes = res["algorithmic_bytes"]
     hbm_gbs = nbytes / (kern_ms * 1e-3) / 1e9
-    slots = elems * SLOTS_PER_ELEMENT / (kern_ms * 1e-3) / 1e12
+    slots = res["elements"] * SLOTS_PER_ELEMENT / (kern_ms * 1e-3) / 1e12
     out = {
         "metric": "selective-scan Gtoken*channel/s at 1 MI355X + % of HBM roofline",
         "value": round(value, 3),
@@ -415,76 +465,98 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": cfg["name"], "batch": cfg["batch"], "dim": cfg["dim"], "seqlen": cfg["seqlen"],
-                   "dstate": cfg["dstate"], "io_dtype": "bf16", "state_dtype": "f32", "softplus_dt": True,
-                   "gate": True, "skip": True},
+                   "dstate": cfg["dstate"], "io_dtype": "bf16", "state_dtype": "f32", "delta": "log-uniform [1e-4, 1e-1]",
+                   "softplus_dt": False, "gate": False, "skip": True, "final_state": True},
         "hbm": {"algorithmic_bytes": nbytes, "achieved_GBs": round(hbm_gbs, 1), "peak_GBs": HBM_PEAK_GBS,
                 "frac": round(hbm_gbs / HBM_PEAK_GBS, 4)},
-        "timing": {"kernel_ms_p10": round(float(np.percentile(per, 10)), 5),
-                   "kernel_ms_p50": round(float(np.percentile(per, 50)), 5),
-                   "kernel_ms_p90": round(float(np.percentile(per, 90)), 5), "input_copies": ncopy},
+        "timing": {"call_ms_p10": res["kernel_ms_p10"], "call_ms_p50": res["kernel_ms_p50"],
+                   "call_ms_p90": res["kernel_ms_p90"], "input_copies": 1,
+                   "workspace_bytes": res["workspace_bytes"]},
         "roofline": {"bound": "alu", "achieved": round(slots, 3), "peak": round(VALU_PEAK_TSLOTS, 3),
                      "unit": "T VALU lane-slots/s (algorithmic: 8 per state element)",
-                     "frac": round(slots / VALU_PEAK_TSLOTS, 4), "traffic": measured_traffic(),
-                     "kernel_ms": round(kern_ms, 5)},
+                     "frac": round(slots / VALU_PEAK_TSLOTS, 4), "traffic": measured_traffic("scan_long"),
+                     "kernel_ms": round(kern_ms, 5),
+                     "timed": "HIP events around each ssm_scan_fwd call on its stream (all of the call's kernels)"},
     }
 
     # ---------------------------------------------------------------- other workloads
-    others = {}
     if not args.no_others:
-        del copies, ys
+        others = {}
         torch.cuda.empty_cache()
-        for oi in (2, 3, 4):
-            res = run_other(oi, 5, 2, ssm, workloads, torch, dev)
-            others[res.pop("name")] = res
-            torch.cuda.empty_cache()
+        for oi in (0, 1, 2):
+            r, _ = run_scan(oi, 20, 5, ssm, workloads, torch, dev, np, ncopy=6 if oi == 1 else 1)
+            others[r.pop("name")] = r
+        r = run_ssd(20, 5, ssm, workloads, torch, dev, np)
+        others[r.pop("name")] = r
+        torch.cuda.empty_cache()
         for si in range(len(workloads.STEP_CONFIGS)):
-            res = run_step(si, 20, 5, ssm, workloads, torch, dev)
-            others[res.pop("name")] = res
+            r = run_step(si, 20, 5, ssm, workloads, torch, dev)
+            others[r.pop("name")] = r
             torch.cuda.empty_cache()
         for ci in range(len(workloads.CONV_CONFIGS)):
-            res = run_conv(ci, 20, 5, ssm, workloads, torch, dev)
-            others[res.pop("name")] = res
+            r = run_conv(ci, 20, 5, ssm, workloads, torch, dev)
+            others[r.pop("name")] = r
             torch.cuda.empty_cache()
-        res = run_bwd(5, 2, ssm, workloads, torch, dev, np)
-        others[res.pop("name")] = res
+        r = run_bwd(20, 5, ssm, workloads, torch, dev, np)
+        others[r.pop("name")] = r
         torch.cuda.empty_cache()
-        res = run_train(5, 2, ssm, workloads, torch, dev, np)
-        others[res.pop("name")] = res
+        r = run_train(20, 5, ssm, workloads, torch, dev, np)
+        others[r.pop("name")] = r
         torch.cuda.empty_cache()
         out["other_workloads"] = others
 
     # ---------------------------------------------------------------- CPU baseline (oracle)
     if not args.no_cpu_baseline:
-        import oracle
-        threads = oracle.default_threads()
-        f = workloads.to_f64(inp)
-        t0 = time.perf_counter()
-        oracle.selective_scan(f["x"], f["delta"], f["A"], f["B"], f["C"], Dskip=f["D"], z=f["z"],
-                              delta_bias=f["delta_bias"], delta_softplus=True, threads=threads)
-        sec = time.perf_counter() - t0
-        # one thread on batch row 0 (2048 x 1536 token-channels)
-        sl = lambda a: None if a is None else a[:1]
-        t1 = time.perf_counter()
-        oracle.selective_scan(sl(f["x"]), sl(f["delta"]), f["A"], sl(f["B"]), sl(f["C"]), Dskip=f["D"], z=sl(f["z"]),
-                              delta_bias=f["delta_bias"], delta_softplus=True, threads=1)
-        sec1 = time.perf_counter() - t1
-        model = ""
-        try:
-            with open("/proc/cpuinfo") as fh:
-                model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
-        except OSError:
-            pass
-        out["cpu_baseline"] = {"value": round(tc / sec / 1e9, 5), "unit": "Gtoken*channel/s", "cores": threads,
-                               "kind": "oracle",
-                               "sample": "the whole workload (8 x 2048 x 1536 token-channels, 16 states), fp64, "
-                                         "%.1f s wall" % sec,
-                               "value_1_thread": round(tc / 8 / sec1 / 1e9, 5),
-                               "sample_1_thread": "batch row 0 (2048 x 1536 token-channels), %.2f s wall" % sec1,
-                               "host": {"cpu_model": model, "cpu_count": os.cpu_count()}}
+        out["cpu_baseline"] = cpu_baseline(workloads, np)
     print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(workloads, np):
+    """The fp64 oracle timed on the host cores: the headline workload in full (every one of its 4.3e9
+    state updates), the per-workload wall times of all five workloads, and one-thread figures for the
+    two smallest scan workloads."""
+    import oracle
+    from tests.helpers import oracle_scan, oracle_ssd
+    threads = oracle.default_threads()
+    per = {}
+    head = None
+    for i, cfg in enumerate(workloads.CONFIGS):
+        inp, cfg = workloads.config_inputs(i)
+        t0 = time.perf_counter()
+        if cfg["kind"] == "ssd":
+            oracle_ssd(inp, threads=threads)
+            tc = cfg["batch"] * cfg["seqlen"] * cfg["nheads"] * cfg["headdim"]
+        else:
+            oracle_scan(inp, threads=threads)
+            tc = cfg["batch"] * cfg["seqlen"] * cfg["dim"]
+        sec = time.perf_counter() - t0
+        per[cfg["name"]] = {"seconds": round(sec, 3), "Gtc_s": round(tc / sec / 1e9, 5), "threads": threads}
+        if i == HEADLINE:
+            head = (tc, sec)
+        if i in (0, 1):
+            # one thread: the whole small layer, batch row 0 of the 130M-like layer
+            sub = inp if i == 0 else {k: (v[:1] if k in ("x", "delta", "z", "B", "C") else v) for k, v in inp.items()}
+            t1 = time.perf_counter()
+            oracle_scan(sub, threads=1)
+            s1 = time.perf_counter() - t1
+            tc1 = tc if i == 0 else tc // cfg["batch"]
+            per[cfg["name"]]["one_thread"] = {"seconds": round(s1, 3), "Gtc_s": round(tc1 / s1 / 1e9, 5),
+                                              "sample": "whole workload" if i == 0 else "batch row 0"}
+        del inp
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
+    except OSError:
+        pass
+    tc, sec = head
+    return {"value": round(tc / sec / 1e9, 5), "unit": "Gtoken*channel/s", "cores": threads, "kind": "oracle",
+            "sample": "the whole headline workload (1 x 131072 x 2048 token-channels, 16 states, 4.3e9 state "
+                      "updates), fp64, %.1f s wall" % sec,
+            "per_workload": per, "host": {"cpu_model": model, "cpu_count": os.cpu_count()}}
 
 
 if __name__ == "__main__":

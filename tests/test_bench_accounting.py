@@ -41,6 +41,24 @@ def test_ssd_flops_causal_triangle():
     assert abs(bench.ssd_flops(cfg) / (b * L * H * P) - (Q + 4 * N + Q * N / (H * P))) < 1e-9
 
 
+def test_ssd_flops_of_the_64_token_blocks_the_kernel_runs():
+    # the kernel passes the state every 64 tokens: its own algorithmic FLOPs are those of 64-token blocks,
+    # 612 FLOP per token*channel (Q + 4N + Q N / (H P) with Q = 64), against 776 for 256-token chunks
+    cfg = workloads.CONFIGS[4]
+    b, L, H, P, N, Q = 2, 8192, 64, 64, 128, 64
+    per_tc = Q + 4 * N + Q * N / (H * P)
+    assert abs(bench.ssd_flops(cfg, bench.SSD_BLOCK) / (b * L * H * P) - per_tc) < 1e-9
+    assert bench.ssd_flops(cfg, 64) < bench.ssd_flops(cfg)
+
+
+def test_headline_is_the_largest_single_gpu_workload():
+    # by token*channel work and by algorithmic bytes
+    scans = [c for c in workloads.CONFIGS if c["kind"] == "scan"]
+    big = max(range(len(workloads.CONFIGS)), key=lambda i: bench.scan_bytes(workloads.CONFIGS[i])
+              if workloads.CONFIGS[i]["kind"] == "scan" else bench.ssd_bytes(workloads.CONFIGS[i]))
+    assert big == bench.HEADLINE and workloads.CONFIGS[big] in scans
+
+
 def test_valu_peak_from_unit_counts():
     # 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
     assert abs(bench.VALU_PEAK_TSLOTS - 39.3216) < 1e-9

@@ -28,7 +28,7 @@ def test_bench_line_contract_and_cache_flush(capsys, monkeypatch):
     rl = d["roofline"]
     assert rl["bound"] == "alu" and 0 < rl["frac"] <= 1 and abs(rl["achieved"] / rl["peak"] - rl["frac"]) < 1e-3
     mb = run_bench(capsys, monkeypatch, "--only", "ubench")
-    # six rotating input copies: the achieved algorithmic bandwidth cannot exceed a plain HBM copy's
+    # the headline's 1.1 GB of inputs per step: the achieved algorithmic bandwidth cannot exceed a plain HBM copy's
     assert d["hbm"]["achieved_GBs"] < mb["copy_GBs_read_plus_write"]
     # measured rates below the published unit peaks, exp at about half the FMA rate
     assert 0 < mb["fma_T_lane_ops_s"] <= mb["published"]["valu_T_lane_slots_s"] * 1.02
