@@ -90,8 +90,12 @@ enum ssm_status {
  *   y              : required output
  *   h_final        : (batch, dim, dstate) fp32 output or NULL
  *   dstate         : 1..256 (129..256 run 8 rows of 32 states per wave)
- * Long sequences with few (batch, channel) slices are split into time chunks
- * whose carries are combined on the device (needs workspace).
+ * Long sequences with few (batch, channel) slices need time parallelism.
+ * With 16 states, whole groups of 8 channels, 16-byte aligned x, delta, z, y,
+ * B and C, and at least one such group per compute unit, the lanes of a wave
+ * split the time axis and combine their partial states in registers (one
+ * pass, no workspace).  Otherwise the sequence is split into time chunks whose
+ * states are computed in a first pass and combined on the device (workspace).
  */
 int ssm_scan_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
                  const float* Dskip, const void* z, const float* delta_bias, int delta_softplus,
@@ -199,8 +203,11 @@ int ssm_scan_final_state(const void* x, const void* delta, const float* A, const
                          int act_dtype, int delta_dtype,
                          void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace needed by ssm_scan_fwd / ssm_scan_final_state for these shapes
- * (0 when the unsplit path is taken).  Depends on the current device. */
+/* Workspace enough for ssm_scan_fwd / ssm_scan_final_state (and their
+ * variants) on these shapes: 0 when no time split is planned.  It does not
+ * depend on dtypes, flags or alignment, so it is an upper bound: a call whose
+ * arguments take the one-pass long-sequence kernel needs none.  Depends on
+ * the current device. */
 size_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
                                 int final_state_only);
 

@@ -166,13 +166,9 @@ static int scan_common(const void* x, const void* delta, const float* A, const v
     return fail(SSM_ERR_NULL, "states is required");
   if (!aligned(save_states, 4)) return fail(SSM_ERR_ALIGNMENT, "states must be 4-byte aligned");
   if (batch == 0 || dim == 0) return SSM_OK;
-  ScanPlan p = plan_scan(batch, seqlen, dim, dstate, final_only, device_cu_count());
+  const int cus = device_cu_count();
+  ScanPlan p = plan_scan(batch, seqlen, dim, dstate, final_only, cus);
   hipStream_t st = (hipStream_t)stream;
-  Scratch own;
-  void* ws = nullptr;
-  if (no_alloc) rc = noalloc_scratch(seqlen > 0 ? p.ws_bytes : 0, &ws);
-  else rc = get_workspace(workspace, workspace_bytes, seqlen > 0 ? p.ws_bytes : 0, st, &own, &ws);
-  if (rc != SSM_OK) return rc;
   ScanArgs a{};
   a.x = x; a.delta = delta; a.A = A; a.B = B; a.C = final_only ? nullptr : C;
   a.Dskip = final_only ? nullptr : Dskip;
@@ -191,6 +187,18 @@ static int scan_common(const void* x, const void* delta, const float* A, const v
   // vector tile I/O: 16-byte aligned tensors (delta, when it is per channel, in either dtype)
   a.vec_io = aligned16(x) && (a.delta_per_token || aligned16(delta)) && aligned16(B) &&
              (final_only || aligned16(C)) && (final_only || aligned16(z));
+  // A sequence the plan would split into time chunks runs in one pass with
+  // time-split lanes instead when that kernel takes the arguments; it needs
+  // no workspace.
+  if (!final_only && p.nchunks > 1 && scan_long_applies(a, cus)) {
+    p.long_path = true;
+    p.ws_bytes = 0;
+  }
+  Scratch own;
+  void* ws = nullptr;
+  if (no_alloc) rc = noalloc_scratch(seqlen > 0 ? p.ws_bytes : 0, &ws);
+  else rc = get_workspace(workspace, workspace_bytes, seqlen > 0 ? p.ws_bytes : 0, st, &own, &ws);
+  if (rc != SSM_OK) return rc;
   if (ws != nullptr) {
     const size_t st_bytes = (size_t)p.nchunks * (size_t)(batch * dim * dstate) * sizeof(float);
     a.ws_state = (float*)ws;

@@ -33,6 +33,7 @@
 
 #include <type_traits>
 
+#include "device_common.h"
 #include "scan_impl.h"
 #include "ssm_internal.h"
 
@@ -236,9 +237,9 @@ __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64
   float h = (a.h0 != nullptr && nok) ? a.h0[hidx] : 0.f;
   for (int k = 0; k < (a.saved != nullptr ? 0 : ntile); ++k) {
     if (nok) a.ws_ckpt[(int64_t)k * slice + cidx] = h;
-    __syncthreads();
+    lds_sync();
     stage(k, false);
-    __syncthreads();
+    lds_sync();
 #pragma unroll 4
     for (int tl = 0; tl < BT; ++tl) {
       const float2 dx = sm.dx[tl * BWC + wc];
@@ -256,9 +257,9 @@ __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64
   const int64_t per_group = a.batch * L * BR;
   for (int k = ntile - 1; k >= 0; --k) {
     const int64_t t0 = (int64_t)k * BT;
-    __syncthreads();
+    lds_sync();
     stage(k, true);
-    __syncthreads();
+    lds_sync();
     // recompute the tile's states and decays (into LDS) and its readout; y gives dz and dy
     const float hstart = !nok ? 0.f
                                : (a.saved != nullptr ? a.saved[((int64_t)k * a.batch + b) * dim * N + ch * N + n0 + r]
@@ -294,7 +295,7 @@ __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64
         sm.dy[e] = dy;
       }
     }
-    __syncthreads();
+    lds_sync();
     // adjoint, tokens in reverse, in groups of 4 for the row reductions; the
     // state before token t is the state after token t-1, carried to the next
     // (earlier) token instead of read again
@@ -343,7 +344,7 @@ __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64
       dbacc += dv;
     }
     }
-    __syncthreads();
+    lds_sync();
     // dB, dC partial of this workgroup: sum of the 4 waves
     {
       const int tl = tid / BR, n = tid % BR;

@@ -214,6 +214,7 @@ int launch_scan(const ScanArgs& a0, const ScanPlan& p, bool final_only, void* st
     }
     return 0;
   }
+  if (p.long_path) return launch_scan_long(a, stream);
   const int64_t gpb = ceil_div(a.dim, 64 / p.R);
   const int64_t nb = a.batch * gpb;
   if (nb > 0x7fffffffLL || p.nchunks > 65535) return fail(4, "grid too large");

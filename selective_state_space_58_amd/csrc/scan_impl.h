@@ -38,6 +38,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include "device_common.h"
 #include "ssm_internal.h"
 
 namespace ssm {
@@ -493,9 +494,9 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
   };
   fetch(t_begin);
   for (int64_t t0 = t_begin; t0 < t_stop; t0 += T) {
-    __syncthreads();
+    lds_sync();
     stage(t0);
-    __syncthreads();
+    lds_sync();
     if (t0 + T < t_stop) fetch(t0 + T);
     const int64_t nvalid = t_stop - t0;
     TX* yb = gy + (b * L + grow0(t0)) * dim + ch0;   // uniform

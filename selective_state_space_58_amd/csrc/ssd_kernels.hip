@@ -39,6 +39,7 @@
 // of the decay exponentials of a 256-token block.
 #include <hip/hip_runtime.h>
 
+#include "device_common.h"
 #include "ssm_internal.h"
 
 namespace ssm {
@@ -353,7 +354,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
       if (l == 0) decayS = exp_f(cend);
       dsum += cend;
     }
-    __syncthreads();
+    lds_sync();
 
     // ---------------- phase A: x*w, Y_off, mask
     const f32x4 cb_cur0 = rcb0, cb_cur1 = rcb1;
@@ -415,7 +416,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
       mask_tile(cb0, cb_cur0);
       if (cb1 >= 0) mask_tile(cb1, cb_cur1);
     }
-    __syncthreads();   // M and x*w complete; every wave has finished reading Hs/Hl
+    lds_sync();   // M and x*w complete; every wave has finished reading Hs/Hl
 
     // ---------------- phase B: state slices; Y_diag and the outputs
     if (has_st) {
@@ -474,7 +475,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
       }
     }
     if (FULL) store_state_split();   // the state entering the next block
-    __syncthreads();
+    lds_sync();
   }
 
   float* hout = FULL ? (chunk == a.nchunks - 1 ? a.h_final : nullptr) : a.ws_state + chunk * slice;

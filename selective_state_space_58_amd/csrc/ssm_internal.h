@@ -56,6 +56,7 @@ struct ScanPlan {
   int64_t nchunks;
   int64_t chunk_len;
   size_t ws_bytes;
+  bool long_path;     // one pass with time-split lanes (scan_long.hip) instead of chunks
 };
 
 ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, bool final_only,
@@ -63,6 +64,13 @@ ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, b
 
 // Enqueue the whole selective scan (all phases).  Returns an ssm_status.
 int launch_scan(const ScanArgs& a, const ScanPlan& p, bool final_only, void* stream);
+
+// Long sequences on few slices in one pass, the lanes of a wave splitting the
+// time axis (scan_long.hip).  scan_long_applies: the arguments fit that kernel
+// (16 states, whole 8-channel groups, 16-byte aligned rows, no variant flags,
+// enough channel groups for every CU); launch_scan_long returns an ssm_status.
+bool scan_long_applies(const ScanArgs& a, int num_cus);
+int launch_scan_long(const ScanArgs& a, void* stream);
 
 // Workspace of the no-allocation scan entry point: a fixed device array of
 // kNoAllocScratchBytes per GPU, shared by every such call on that GPU.

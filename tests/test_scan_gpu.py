@@ -231,6 +231,75 @@ def test_explicit_workspace(ssm):
         ssm.ssm_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], workspace=small)
 
 
+# ------------------------------------------------------------------ long sequences in one pass
+# Few (batch, channel) slices and a long sequence: with 16 states, whole groups of 8 channels and aligned
+# rows the lanes of a wave split the time axis (one pass, no workspace); otherwise the sequence is split
+# into chunks computed in a first pass (workspace).  A one-byte workspace is therefore accepted only by the
+# one-pass kernel, which shows which path ran.
+LONG_CASES = [((1, 3000, 2048), "bf16", "bf16", True), ((2, 1100, 1024), "f32", "f32", True),
+              ((4, 777, 512), "bf16", "f32", False), ((1, 2048, 4096), "bf16", "bf16", False),
+              ((1, 513, 2048), "f32", "bf16", True)]
+
+
+def _call_ws(ssm, t, inp, ws):
+    y, hf = ssm.ssm_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                             delta_bias=t["delta_bias"], delta_softplus=inp["meta"]["softplus"], h0=t["h0"],
+                             return_final_state=True, workspace=ws)
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy(), hf.cpu().numpy()
+
+
+@pytest.mark.parametrize("shape,dtype,ddtype,gate", LONG_CASES)
+def test_long_sequence_one_pass(ssm, shape, dtype, ddtype, gate):
+    b, L, D = shape
+    print("case one-pass long scan", shape, dtype, ddtype, "gate" if gate else "", flush=True)
+    inp = workloads.scan_inputs(b, L, D, 16, dtype=dtype, delta_dtype=ddtype, seed=L + D + b,
+                                dt="softplus_bias" if gate else "loguniform", dt_lo=1e-4, gate=gate, softplus=gate,
+                                skip=True, h0=True)
+    assert ssm.ssm_scan_workspace_bytes(b, L, D, 16) > 0     # the chunked split would need workspace
+    t = workloads.to_device(inp, DEV)
+    y, hf = _call_ws(ssm, t, inp, torch.empty(1, dtype=torch.uint8, device=DEV))
+    y_ref, h_ref = oracle_scan(inp)
+    ry, rh = err_report(y, y_ref), err_report(hf, h_ref)
+    print("  " + fmt_report("y", ry) + "\n  " + fmt_report("h_final", rh), flush=True)
+    assert ry["bar"] <= TOL[dtype] and rh["bar"] <= TOL[dtype]
+
+
+def test_long_sequence_one_pass_matches_chunked_path(ssm):
+    # the same inputs through both paths: a view two bytes off 16-byte alignment takes the chunked split
+    b, L, D = 1, 1500, 2048
+    inp = workloads.scan_inputs(b, L, D, 16, dtype="bf16", seed=77, dt="softplus_bias", gate=True, softplus=True,
+                                skip=True, h0=True)
+    t = workloads.to_device(inp, DEV)
+    y1, h1 = _call_ws(ssm, t, inp, torch.empty(1, dtype=torch.uint8, device=DEV))
+    xs = torch.empty(t["x"].numel() + 8, dtype=t["x"].dtype, device=DEV)
+    xv = xs[1:1 + t["x"].numel()].view(t["x"].shape)
+    xv.copy_(t["x"])
+    t2 = dict(t)
+    t2["x"] = xv
+    with pytest.raises(ssm.SSMError):   # the chunked split needs its workspace
+        _call_ws(ssm, t2, inp, torch.empty(1, dtype=torch.uint8, device=DEV))
+    y2, h2 = _call_ws(ssm, t2, inp, None)
+    y_ref, h_ref = oracle_scan(inp)
+    for y, hf in ((y1, h1), (y2, h2)):
+        assert rel_err(y, y_ref) <= TOL["bf16"] and rel_err(hf, h_ref) <= TOL["bf16"]
+    assert rel_err(h1, h2) <= 1e-5
+
+
+def test_long_sequence_one_pass_special_values(ssm):
+    # a = 0 and tiny |a| (the series form of the gain), and dt = 1e3 bursts (memoryless steps)
+    inp = workloads.scan_inputs(1, 1200, 2048, 16, dtype="bf16", seed=501, h0=True)
+    inp["A"][::3, 5] = 0.0
+    inp["A"][7, :] = -1e-4
+    inp["delta"][:, 300:310, :] = 1e3
+    t = workloads.to_device(inp, DEV)
+    y, hf = _call_ws(ssm, t, inp, torch.empty(1, dtype=torch.uint8, device=DEV))
+    y_ref, h_ref = oracle_scan(inp)
+    ey, eh = rel_err(y, y_ref), rel_err(hf, h_ref)
+    print("case one-pass special values: y %.3g h_final %.3g" % (ey, eh), flush=True)
+    assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
+
+
 # ------------------------------------------------------------------ full-size workloads, every element
 def _full_compare(label, got, ref, tol):
     rep = err_report(got, ref)
