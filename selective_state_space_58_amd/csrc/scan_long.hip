@@ -66,6 +66,35 @@ __device__ __forceinline__ float dpp(float old, float v) {
 constexpr int kRowShr = 0x110;        // row_shr:k = kRowShr + k
 constexpr int kRowBcast15 = 0x15F;    // row_newbcast:15
 
+// One level of the inclusive scan along a 16-lane row: lanes g >= K take in
+// the aggregate ending K groups earlier, h <- h + P * h[g - K] and
+// P <- P * P[g - K] (the h updates read P before it changes).  The DPP source
+// operand reads lane g - K of the row; with bound_ctrl off, lanes g < K have
+// no source lane and are not written, so they keep their values.  The s_nop
+// gives the two wait states a DPP read needs after a VALU write of its source.
+template <int K>
+__device__ __forceinline__ void hs_level(float (&h)[4], float (&P)[4]) {
+  static_assert(K == 1 || K == 2 || K == 4 || K == 8, "row shift");
+#define SSM_SHR(K) "row_shr:" #K " row_mask:0xf bank_mask:0xf"
+#define SSM_HS_ASM(SH)                                                              \
+  asm volatile("s_nop 1\n\t"                                                        \
+               "v_fmac_f32_dpp %0, %0, %4 " SH "\n\t"                               \
+               "v_fmac_f32_dpp %1, %1, %5 " SH "\n\t"                               \
+               "v_fmac_f32_dpp %2, %2, %6 " SH "\n\t"                               \
+               "v_fmac_f32_dpp %3, %3, %7 " SH "\n\t"                               \
+               "v_mul_f32_dpp %4, %4, %4 " SH "\n\t"                                \
+               "v_mul_f32_dpp %5, %5, %5 " SH "\n\t"                                \
+               "v_mul_f32_dpp %6, %6, %6 " SH "\n\t"                                \
+               "v_mul_f32_dpp %7, %7, %7 " SH                                        \
+               : "+v"(h[0]), "+v"(h[1]), "+v"(h[2]), "+v"(h[3]), "+v"(P[0]), "+v"(P[1]), "+v"(P[2]), "+v"(P[3]))
+  if constexpr (K == 1) SSM_HS_ASM(SSM_SHR(1));
+  else if constexpr (K == 2) SSM_HS_ASM(SSM_SHR(2));
+  else if constexpr (K == 4) SSM_HS_ASM(SSM_SHR(4));
+  else SSM_HS_ASM(SSM_SHR(8));
+#undef SSM_HS_ASM
+#undef SSM_SHR
+}
+
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
@@ -159,20 +188,22 @@ __device__ __forceinline__ void long_body(const ScanArgs& a, int64_t b, int64_t 
       return __builtin_bit_cast(float, v[e]);
     }
   };
-  auto stage = [&](int64_t t0) {
+  auto stage = [&](int64_t t0, int buf) {
     const bool ok = t0 + trow < L;
     if (xrole) {
+      float2* sdx = s_dx + buf * DX_SLOTS;
+      float* sgz = s_gz + buf * DX_SLOTS;
 #pragma unroll
       for (int e = 0; e < W; ++e) {
         const float v = elem(pd, e, RD{}) + bias[e];
         float dt = a.softplus ? (ACC ? softplus_f(v) : softplus_short(v)) : v;
-        s_dx[ix_dx(trow, e)] = make_float2(ok ? dt : 0.f, elem(px, e, RX{}));
-        if (has_z) s_gz[ix_dx(trow, e)] = silu_f(elem(pz, e, RX{}));
+        sdx[ix_dx(trow, e)] = make_float2(ok ? dt : 0.f, elem(px, e, RX{}));
+        if (has_z) sgz[ix_dx(trow, e)] = silu_f(elem(pz, e, RX{}));
       }
     }
     if (bcrole) {
-      float4* db = reinterpret_cast<float4*>(s_b + ix_bc(trow));
-      float4* dc = reinterpret_cast<float4*>(s_c + ix_bc(trow));
+      float4* db = reinterpret_cast<float4*>(s_b + buf * BC_FLOATS + ix_bc(trow));
+      float4* dc = reinterpret_cast<float4*>(s_c + buf * BC_FLOATS + ix_bc(trow));
 #pragma unroll
       for (int q = 0; q < NS / 4; ++q) {
         db[q] = make_float4(elem(pb, 4 * q, RX{}), elem(pb, 4 * q + 1, RX{}), elem(pb, 4 * q + 2, RX{}),
@@ -183,12 +214,12 @@ __device__ __forceinline__ void long_body(const ScanArgs& a, int64_t b, int64_t 
     }
   };
   // y of the previous tile: LDS -> global, one row of the W channels per thread
-  auto store_y = [&](int64_t t0) {
+  auto store_y = [&](int64_t t0, int buf) {
     for (int t = tid; t < T; t += NT) {
       if (t0 + t < L) {
         unsigned v[XWD];
 #pragma unroll
-        for (int i = 0; i < XWD; ++i) v[i] = reinterpret_cast<const unsigned*>(s_y + t * W)[i];
+        for (int i = 0; i < XWD; ++i) v[i] = reinterpret_cast<const unsigned*>(s_y + buf * T * W + t * W)[i];
         store_words<XWD>((char*)a.y + ((size_t)(b * L + t0 + t) * dim + chw0) * sizeof(TX), v);
       }
     }
@@ -201,24 +232,30 @@ __device__ __forceinline__ void long_body(const ScanArgs& a, int64_t b, int64_t 
     const int n = 4 * r + s;
     carry[s] = (a.h0 != nullptr && n < a.dstate) ? a.h0[(b * dim + ch) * a.dstate + n] : 0.f;
   }
-  const float4* s_b4 = reinterpret_cast<const float4*>(s_b);
-  const float4* s_c4 = reinterpret_cast<const float4*>(s_c);
   const int tg = g * TAU;   // this lane's first token within the tile
 
+  // Tiles are double-buffered in LDS: while the waves compute tile k from one
+  // buffer, the staging threads fill the other with tile k+1 (loaded into
+  // registers one tile earlier) and write tile k-1's y out, so one barrier per
+  // tile suffices.
   fetch(0);
-  for (int64_t t0 = 0; t0 < L; t0 += T) {
-    lds_sync();
-    if (t0 > 0) store_y(t0 - T);
-    stage(t0);
-    lds_sync();
-    if (t0 + T < L) fetch(t0 + T);
+  stage(0, 0);
+  if (T < L) fetch(T);
+  lds_sync();
+  int cur = 0;
+  for (int64_t t0 = 0; t0 < L; t0 += T, cur ^= 1) {
+    const float2* sdx = s_dx + cur * DX_SLOTS;
+    const float* sgz = s_gz + cur * DX_SLOTS;
+    const float4* s_b4 = reinterpret_cast<const float4*>(s_b + cur * BC_FLOATS);
+    const float4* s_c4 = reinterpret_cast<const float4*>(s_c + cur * BC_FLOATS);
+    TX* sy = s_y + cur * T * W;
 
     // 1. the group's tokens from a zero state
     float E[TAU][4], U[TAU][4], h[4] = {0.f, 0.f, 0.f, 0.f};
     float dsum = 0.f;
 #pragma unroll
     for (int j = 0; j < TAU; ++j) {
-      const float2 dx = s_dx[ix_dx(tg + j, w)];
+      const float2 dx = sdx[ix_dx(tg + j, w)];
       const float4 bq = s_b4[(ix_bc(tg + j) >> 2) + r];
       const float bv[4] = {bq.x, bq.y, bq.z, bq.w};
 #pragma unroll
@@ -239,18 +276,10 @@ __device__ __forceinline__ void long_body(const ScanArgs& a, int64_t b, int64_t 
     float P[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) P[s] = hw_exp2(a2[s] * dsum);
-#define SSM_LONG_LEVEL(K)                                            \
-  _Pragma("unroll") for (int s = 0; s < 4; ++s) {                    \
-    const float ho = dpp<kRowShr + (K), true>(0.f, h[s]);            \
-    const float po = dpp<kRowShr + (K), false>(1.f, P[s]);           \
-    h[s] = fmaf(P[s], ho, h[s]);                                     \
-    P[s] *= po;                                                      \
-  }
-    SSM_LONG_LEVEL(1)
-    SSM_LONG_LEVEL(2)
-    SSM_LONG_LEVEL(4)
-    SSM_LONG_LEVEL(8)
-#undef SSM_LONG_LEVEL
+    hs_level<1>(h, P);
+    hs_level<2>(h, P);
+    hs_level<4>(h, P);
+    hs_level<8>(h, P);
     float hin[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -280,14 +309,21 @@ __device__ __forceinline__ void long_body(const ScanArgs& a, int64_t b, int64_t 
       }
       const float tot = reduce_scatter_rows<4>(pr);   // row r: token tg + 4 jq + r
       const int t = tg + 4 * jq + r;
-      const float xv = s_dx[ix_dx(t, w)].y;
+      const float xv = sdx[ix_dx(t, w)].y;
       float yv = fmaf(Dv, xv, tot);
-      if (has_z) yv *= s_gz[ix_dx(t, w)];
-      s_y[t * W + w] = (TX)yv;
+      if (has_z) yv *= sgz[ix_dx(t, w)];
+      sy[t * W + w] = (TX)yv;
     }
+
+    // next tile into the other buffer, the previous tile's y out
+    if (t0 + T < L) {
+      stage(t0 + T, cur ^ 1);
+      if (t0 + 2 * T < L) fetch(t0 + 2 * T);
+    }
+    if (t0 > 0) store_y(t0 - T, cur ^ 1);
+    lds_sync();
   }
-  lds_sync();
-  store_y(((L - 1) / T) * T);
+  store_y(((L - 1) / T) * T, cur ^ 1);
 
   if (a.h_final != nullptr && g == 0) {
 #pragma unroll
@@ -300,11 +336,11 @@ __device__ __forceinline__ void long_body(const ScanArgs& a, int64_t b, int64_t 
 
 template <bool XB, bool DB>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void scan_long_kernel(ScanArgs a) {
-  __shared__ __attribute__((aligned(16))) float2 s_dx[DX_SLOTS];
-  __shared__ __attribute__((aligned(16))) float s_gz[DX_SLOTS];
-  __shared__ __attribute__((aligned(16))) float s_b[BC_FLOATS];
-  __shared__ __attribute__((aligned(16))) float s_c[BC_FLOATS];
-  __shared__ __attribute__((aligned(16))) typename Act<XB>::T s_y[T * W];
+  __shared__ __attribute__((aligned(16))) float2 s_dx[2 * DX_SLOTS];
+  __shared__ __attribute__((aligned(16))) float s_gz[2 * DX_SLOTS];
+  __shared__ __attribute__((aligned(16))) float s_b[2 * BC_FLOATS];
+  __shared__ __attribute__((aligned(16))) float s_c[2 * BC_FLOATS];
+  __shared__ __attribute__((aligned(16))) typename Act<XB>::T s_y[2 * T * W];
 
   // XCD-aware order: dispatch id i runs on XCD i % 8; each XCD takes a
   // contiguous range of channel groups, so the 8 workgroups that read one
