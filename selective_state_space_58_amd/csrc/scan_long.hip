@@ -40,24 +40,33 @@ namespace scan_long {
 
 using namespace scan_dev;
 
-#ifndef SSM_LONG_W
-#define SSM_LONG_W 8
-#endif
-constexpr int W = SSM_LONG_W; // waves (channels) per workgroup
+constexpr int W = 8;          // waves (channels) per workgroup
 constexpr int NT = 64 * W;    // threads per workgroup
 constexpr int G = 16;         // time groups per wave (lane bits 0-3)
 constexpr int TAU = 16;       // tokens per group
 constexpr int T = G * TAU;    // tokens per tile
 constexpr int NS = 16;        // states (4 rows x 4 per lane)
 
-// LDS indexing.  (dt, x) and silu(z) of (token t, channel w): one pad slot
-// per 16 tokens, so the 16 groups of a row read 16 different bank pairs.
-__device__ __forceinline__ int ix_dx(int t, int w) { return t * W + w + (t >> 4); }
-// B and C of token t start at this float index: 4 pad floats per 16 tokens
-// (16-byte aligned rows; the groups' 16-byte reads spread over the banks).
-__device__ __forceinline__ int ix_bc(int t) { return t * NS + ((t >> 4) << 2); }
-constexpr int DX_SLOTS = T * W + T / 16;
-constexpr int BC_FLOATS = T * NS + (T / 16) * 4;
+// LDS layouts, padded so that both access patterns of each array touch
+// distinct banks (32 banks of 4 bytes): the staging threads write rows t,
+// t+1, ... from consecutive lanes, and the compute reads one row per time
+// group, t = 16 g + j, from the 16 lanes of a row.
+// (dt, x) and silu(z) of (token t, channel w): rows of W + 1 slots plus one
+// slot per 16 rows.  As 8-byte words: 18 t + 2 (t >> 4) + 2 w, so consecutive
+// rows land 18 words apart (16 distinct bank pairs) and the 16 groups 2 words
+// apart.
+__device__ __forceinline__ int ix_dx(int t, int w) { return t * (W + 1) + (t >> 4) + w; }
+// B and C of token t start at this float index: rows of 20 floats (16-byte
+// aligned) plus 4 floats per 16 rows; 8 consecutive rows, or the 8 groups of
+// a 16-byte read, start in 8 distinct 4-bank quads.
+__device__ __forceinline__ int ix_bc(int t) { return t * 20 + ((t >> 4) << 2); }
+// y of (token t, channel w), fp32: the 64 lanes writing tokens 16 g + 4 jq + r
+// fall at most two to a bank.
+__device__ __forceinline__ int ix_y(int t, int w) { return t * W + (t >> 4) + w; }
+constexpr int DX_SLOTS = T * (W + 1) + T / 16;
+constexpr int BC_FLOATS = T * 20 + (T / 16) * 4;
+constexpr int Y_FLOATS = T * W + T / 16;
+static_assert(W == 8, "the padded layouts are laid out for 8 channels per workgroup");
 
 template <int CTRL, bool ZERO_FILL>
 __device__ __forceinline__ float dpp(float old, float v) {
@@ -125,11 +134,11 @@ __device__ __forceinline__ void store_words(char* p, const unsigned (&w)[NW]) {
   }
 }
 
-template <bool XB, bool DB, int GAIN>
+template <bool XB, bool DB, bool HASZ, int GAIN>
 __device__ __forceinline__ void long_body(const ScanArgs& a, int64_t b, int64_t chw0, const float (&a2)[4],
                                           const float (&ia)[4], const float (&av)[4], float2* __restrict__ s_dx,
                                           float* __restrict__ s_gz, float* __restrict__ s_b, float* __restrict__ s_c,
-                                          typename Act<XB>::T* __restrict__ s_y) {
+                                          float* __restrict__ s_y) {
   using TX = typename Act<XB>::T;
   using RX = typename Raw<XB>::T;
   using RD = typename Raw<DB>::T;
@@ -143,7 +152,7 @@ __device__ __forceinline__ void long_body(const ScanArgs& a, int64_t b, int64_t 
   const int r = lane / 16, g = lane % 16;
   const int64_t L = a.seqlen, dim = a.dim;
   const int64_t ch = chw0 + w;
-  const bool has_z = a.z != nullptr;
+  constexpr bool has_z = HASZ;
   const float Dv = a.Dskip != nullptr ? a.Dskip[ch] : 0.f;
   const char* gx = (const char*)a.x;
   const char* gd = (const char*)a.delta;
@@ -192,7 +201,7 @@ __device__ __forceinline__ void long_body(const ScanArgs& a, int64_t b, int64_t 
     const bool ok = t0 + trow < L;
     if (xrole) {
       float2* sdx = s_dx + buf * DX_SLOTS;
-      float* sgz = s_gz + buf * DX_SLOTS;
+      float* sgz = s_gz + (HASZ ? buf * DX_SLOTS : 0);
 #pragma unroll
       for (int e = 0; e < W; ++e) {
         const float v = elem(pd, e, RD{}) + bias[e];
@@ -218,8 +227,16 @@ __device__ __forceinline__ void long_body(const ScanArgs& a, int64_t b, int64_t 
     for (int t = tid; t < T; t += NT) {
       if (t0 + t < L) {
         unsigned v[XWD];
+        const float* yr = s_y + buf * Y_FLOATS + ix_y(t, 0);
 #pragma unroll
-        for (int i = 0; i < XWD; ++i) v[i] = reinterpret_cast<const unsigned*>(s_y + buf * T * W + t * W)[i];
+        for (int i = 0; i < XWD; ++i) {
+          if constexpr (sizeof(TX) == 2) {
+            v[i] = (unsigned)__builtin_bit_cast(unsigned short, (TX)yr[2 * i]) |
+                   ((unsigned)__builtin_bit_cast(unsigned short, (TX)yr[2 * i + 1]) << 16);
+          } else {
+            v[i] = __builtin_bit_cast(unsigned, yr[i]);
+          }
+        }
         store_words<XWD>((char*)a.y + ((size_t)(b * L + t0 + t) * dim + chw0) * sizeof(TX), v);
       }
     }
@@ -245,10 +262,10 @@ __device__ __forceinline__ void long_body(const ScanArgs& a, int64_t b, int64_t 
   int cur = 0;
   for (int64_t t0 = 0; t0 < L; t0 += T, cur ^= 1) {
     const float2* sdx = s_dx + cur * DX_SLOTS;
-    const float* sgz = s_gz + cur * DX_SLOTS;
+    const float* sgz = s_gz + (HASZ ? cur * DX_SLOTS : 0);
     const float4* s_b4 = reinterpret_cast<const float4*>(s_b + cur * BC_FLOATS);
     const float4* s_c4 = reinterpret_cast<const float4*>(s_c + cur * BC_FLOATS);
-    TX* sy = s_y + cur * T * W;
+    float* sy = s_y + cur * Y_FLOATS;
 
     // 1. the group's tokens from a zero state
     float E[TAU][4], U[TAU][4], h[4] = {0.f, 0.f, 0.f, 0.f};
@@ -312,7 +329,7 @@ __device__ __forceinline__ void long_body(const ScanArgs& a, int64_t b, int64_t 
       const float xv = sdx[ix_dx(t, w)].y;
       float yv = fmaf(Dv, xv, tot);
       if (has_z) yv *= sgz[ix_dx(t, w)];
-      sy[t * W + w] = (TX)yv;
+      sy[ix_y(t, w)] = yv;
     }
 
     // next tile into the other buffer, the previous tile's y out
@@ -334,13 +351,13 @@ __device__ __forceinline__ void long_body(const ScanArgs& a, int64_t b, int64_t 
   }
 }
 
-template <bool XB, bool DB>
+template <bool XB, bool DB, bool HASZ>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void scan_long_kernel(ScanArgs a) {
   __shared__ __attribute__((aligned(16))) float2 s_dx[2 * DX_SLOTS];
-  __shared__ __attribute__((aligned(16))) float s_gz[2 * DX_SLOTS];
+  __shared__ __attribute__((aligned(16))) float s_gz[HASZ ? 2 * DX_SLOTS : 1];
   __shared__ __attribute__((aligned(16))) float s_b[2 * BC_FLOATS];
   __shared__ __attribute__((aligned(16))) float s_c[2 * BC_FLOATS];
-  __shared__ __attribute__((aligned(16))) typename Act<XB>::T s_y[2 * T * W];
+  __shared__ __attribute__((aligned(16))) float s_y[2 * Y_FLOATS];
 
   // XCD-aware order: dispatch id i runs on XCD i % 8; each XCD takes a
   // contiguous range of channel groups, so the 8 workgroups that read one
@@ -366,9 +383,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void sc
   }
   // one gain form for the whole workgroup (its waves pass the same barriers)
   if (!XB || __syncthreads_or(tiny) != 0)
-    long_body<XB, DB, kGainAccurate>(a, b, chw0, a2, ia, av, s_dx, s_gz, s_b, s_c, s_y);
+    long_body<XB, DB, HASZ, kGainAccurate>(a, b, chw0, a2, ia, av, s_dx, s_gz, s_b, s_c, s_y);
   else
-    long_body<XB, DB, kGainShort>(a, b, chw0, a2, ia, av, s_dx, s_gz, s_b, s_c, s_y);
+    long_body<XB, DB, HASZ, kGainShort>(a, b, chw0, a2, ia, av, s_dx, s_gz, s_b, s_c, s_y);
 }
 
 }  // namespace scan_long
@@ -389,10 +406,21 @@ int launch_scan_long(const ScanArgs& a, void* stream) {
   const int64_t blocks = a.batch * (a.dim / scan_long::W);
   if (blocks > 0x7fffffffLL) return fail(4, "grid too large");
   const dim3 grid((unsigned)blocks);
-  if (a.act_bf16 && a.delta_bf16) scan_long::scan_long_kernel<true, true><<<grid, scan_long::NT, 0, st>>>(a);
-  else if (a.act_bf16) scan_long::scan_long_kernel<true, false><<<grid, scan_long::NT, 0, st>>>(a);
-  else if (a.delta_bf16) scan_long::scan_long_kernel<false, true><<<grid, scan_long::NT, 0, st>>>(a);
-  else scan_long::scan_long_kernel<false, false><<<grid, scan_long::NT, 0, st>>>(a);
+  const bool z = a.z != nullptr;
+  using namespace scan_long;
+  if (a.act_bf16 && a.delta_bf16) {
+    if (z) scan_long_kernel<true, true, true><<<grid, NT, 0, st>>>(a);
+    else scan_long_kernel<true, true, false><<<grid, NT, 0, st>>>(a);
+  } else if (a.act_bf16) {
+    if (z) scan_long_kernel<true, false, true><<<grid, NT, 0, st>>>(a);
+    else scan_long_kernel<true, false, false><<<grid, NT, 0, st>>>(a);
+  } else if (a.delta_bf16) {
+    if (z) scan_long_kernel<false, true, true><<<grid, NT, 0, st>>>(a);
+    else scan_long_kernel<false, true, false><<<grid, NT, 0, st>>>(a);
+  } else {
+    if (z) scan_long_kernel<false, false, true><<<grid, NT, 0, st>>>(a);
+    else scan_long_kernel<false, false, false><<<grid, NT, 0, st>>>(a);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(6, std::string("long-sequence scan kernel launch: ") + hipGetErrorString(e));
   return 0;
