@@ -60,12 +60,13 @@ __device__ __forceinline__ int ix_dx(int t, int w) { return t * (W + 1) + (t >> 
 // aligned) plus 4 floats per 16 rows; 8 consecutive rows, or the 8 groups of
 // a 16-byte read, start in 8 distinct 4-bank quads.
 __device__ __forceinline__ int ix_bc(int t) { return t * 20 + ((t >> 4) << 2); }
-// y of (token t, channel w), fp32: the 64 lanes writing tokens 16 g + 4 jq + r
-// fall at most two to a bank.
-__device__ __forceinline__ int ix_y(int t, int w) { return t * W + (t >> 4) + w; }
+// y of (token t, channel w), fp32: rows of W + 1 floats plus one per 16 rows,
+// so the 64 lanes writing tokens 16 g + 4 jq + r fall at most two to a bank,
+// and so do the threads reading back consecutive rows.
+__device__ __forceinline__ int ix_y(int t, int w) { return t * (W + 1) + (t >> 4) + w; }
 constexpr int DX_SLOTS = T * (W + 1) + T / 16;
 constexpr int BC_FLOATS = T * 20 + (T / 16) * 4;
-constexpr int Y_FLOATS = T * W + T / 16;
+constexpr int Y_FLOATS = T * (W + 1) + T / 16;
 static_assert(W == 8, "the padded layouts are laid out for 8 channels per workgroup");
 
 template <int CTRL, bool ZERO_FILL>
@@ -134,7 +135,7 @@ __device__ __forceinline__ void store_words(char* p, const unsigned (&w)[NW]) {
   }
 }
 
-template <bool XB, bool DB, bool HASZ, int GAIN>
+template <bool XB, bool DB, bool HASZ, bool SP, int GAIN>
 __device__ __forceinline__ void long_body(const ScanArgs& a, int64_t b, int64_t chw0, const float (&a2)[4],
                                           const float (&ia)[4], const float (&av)[4], float2* __restrict__ s_dx,
                                           float* __restrict__ s_gz, float* __restrict__ s_b, float* __restrict__ s_c,
@@ -205,7 +206,7 @@ __device__ __forceinline__ void long_body(const ScanArgs& a, int64_t b, int64_t 
 #pragma unroll
       for (int e = 0; e < W; ++e) {
         const float v = elem(pd, e, RD{}) + bias[e];
-        float dt = a.softplus ? (ACC ? softplus_f(v) : softplus_short(v)) : v;
+        const float dt = SP ? (ACC ? softplus_f(v) : softplus_short(v)) : v;
         sdx[ix_dx(trow, e)] = make_float2(ok ? dt : 0.f, elem(px, e, RX{}));
         if (has_z) sgz[ix_dx(trow, e)] = silu_f(elem(pz, e, RX{}));
       }
@@ -351,7 +352,7 @@ __device__ __forceinline__ void long_body(const ScanArgs& a, int64_t b, int64_t 
   }
 }
 
-template <bool XB, bool DB, bool HASZ>
+template <bool XB, bool DB, bool HASZ, bool SP>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void scan_long_kernel(ScanArgs a) {
   __shared__ __attribute__((aligned(16))) float2 s_dx[2 * DX_SLOTS];
   __shared__ __attribute__((aligned(16))) float s_gz[HASZ ? 2 * DX_SLOTS : 1];
@@ -383,9 +384,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void sc
   }
   // one gain form for the whole workgroup (its waves pass the same barriers)
   if (!XB || __syncthreads_or(tiny) != 0)
-    long_body<XB, DB, HASZ, kGainAccurate>(a, b, chw0, a2, ia, av, s_dx, s_gz, s_b, s_c, s_y);
+    long_body<XB, DB, HASZ, SP, kGainAccurate>(a, b, chw0, a2, ia, av, s_dx, s_gz, s_b, s_c, s_y);
   else
-    long_body<XB, DB, HASZ, kGainShort>(a, b, chw0, a2, ia, av, s_dx, s_gz, s_b, s_c, s_y);
+    long_body<XB, DB, HASZ, SP, kGainShort>(a, b, chw0, a2, ia, av, s_dx, s_gz, s_b, s_c, s_y);
 }
 
 }  // namespace scan_long
@@ -406,21 +407,20 @@ int launch_scan_long(const ScanArgs& a, void* stream) {
   const int64_t blocks = a.batch * (a.dim / scan_long::W);
   if (blocks > 0x7fffffffLL) return fail(4, "grid too large");
   const dim3 grid((unsigned)blocks);
-  const bool z = a.z != nullptr;
   using namespace scan_long;
-  if (a.act_bf16 && a.delta_bf16) {
-    if (z) scan_long_kernel<true, true, true><<<grid, NT, 0, st>>>(a);
-    else scan_long_kernel<true, true, false><<<grid, NT, 0, st>>>(a);
-  } else if (a.act_bf16) {
-    if (z) scan_long_kernel<true, false, true><<<grid, NT, 0, st>>>(a);
-    else scan_long_kernel<true, false, false><<<grid, NT, 0, st>>>(a);
-  } else if (a.delta_bf16) {
-    if (z) scan_long_kernel<false, true, true><<<grid, NT, 0, st>>>(a);
-    else scan_long_kernel<false, true, false><<<grid, NT, 0, st>>>(a);
-  } else {
-    if (z) scan_long_kernel<false, false, true><<<grid, NT, 0, st>>>(a);
-    else scan_long_kernel<false, false, false><<<grid, NT, 0, st>>>(a);
-  }
+  // one kernel per (act dtype, delta dtype, gate, softplus)
+  using K = void (*)(ScanArgs);
+  static const K table[16] = {
+      scan_long_kernel<false, false, false, false>, scan_long_kernel<false, false, false, true>,
+      scan_long_kernel<false, false, true, false>,  scan_long_kernel<false, false, true, true>,
+      scan_long_kernel<false, true, false, false>,  scan_long_kernel<false, true, false, true>,
+      scan_long_kernel<false, true, true, false>,   scan_long_kernel<false, true, true, true>,
+      scan_long_kernel<true, false, false, false>,  scan_long_kernel<true, false, false, true>,
+      scan_long_kernel<true, false, true, false>,   scan_long_kernel<true, false, true, true>,
+      scan_long_kernel<true, true, false, false>,   scan_long_kernel<true, true, false, true>,
+      scan_long_kernel<true, true, true, false>,    scan_long_kernel<true, true, true, true>};
+  const int idx = (a.act_bf16 ? 8 : 0) | (a.delta_bf16 ? 4 : 0) | (a.z != nullptr ? 2 : 0) | (a.softplus ? 1 : 0);
+  hipLaunchKernelGGL(table[idx], grid, dim3(NT), 0, st, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(6, std::string("long-sequence scan kernel launch: ") + hipGetErrorString(e));
   return 0;
