@@ -63,13 +63,13 @@ HEADLINE = 3
 # in it (kernel_sources_sha256_16); otherwise the traffic is reported as null.
 COUNTER_SUMMARIES = {
     "scan_long": ("profiles/scan_bf16_b1_d2048_l131072_n16_hbm_counters.md",
-                  ["selective_state_space_58_amd/csrc/scan_impl.h", "selective_state_space_58_amd/csrc/scan_inst.hip",
-                   "selective_state_space_58_amd/csrc/scan_host.hip"]),
+                  ["selective_state_space_58_amd/csrc/scan_long.hip", "selective_state_space_58_amd/csrc/scan_impl.h",
+                   "selective_state_space_58_amd/csrc/device_common.h"]),
     "scan_130m": ("profiles/scan_bf16_b8_d1536_l2048_n16_hbm_counters.md",
                   ["selective_state_space_58_amd/csrc/scan_impl.h", "selective_state_space_58_amd/csrc/scan_inst.hip",
-                   "selective_state_space_58_amd/csrc/scan_host.hip"]),
+                   "selective_state_space_58_amd/csrc/scan_host.hip", "selective_state_space_58_amd/csrc/device_common.h"]),
     "ssd": ("profiles/ssd_bf16_b2_h64_p64_n128_l8192_q256_kernel.md",
-            ["selective_state_space_58_amd/csrc/ssd_kernels.hip"]),
+            ["selective_state_space_58_amd/csrc/ssd_kernels.hip", "selective_state_space_58_amd/csrc/device_common.h"]),
 }
 
 
