@@ -56,7 +56,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int QB = 64;    // tokens per block
 constexpr int PS = 32;    // head channels per workgroup
-constexpr int NWAVE = 8;  // waves per workgroup
+constexpr int NWAVE = 12; // waves per workgroup of the fused kernel (three per SIMD)
 
 __device__ __forceinline__ float hw_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
 __device__ __forceinline__ float hw_log2(float v) { return __builtin_amdgcn_logf(v); }
@@ -137,6 +137,51 @@ __device__ __forceinline__ u32x4 frag_cols_raw(const u16* base, int k0, int c0, 
   return u32x4{l2[0], l2[1], h2[0], h2[1]};
 }
 
+// The staged B (rows of N bf16) and x (rows of 32 bf16) tiles are filled
+// by direct global-to-LDS loads, which place the 64 lanes' 16-byte pieces of
+// one instruction at 64 consecutive chunk slots.  Their rows are therefore
+// unpadded; instead the CPR 16-byte chunks of row r are stored in the order
+// chunk ^ (r mod CPR), so that the fragment reads of one column from
+// consecutive rows spread over the LDS banks.  Element offset of (row, col):
+template <int CPR>
+__device__ __forceinline__ int swz(int row, int col) {
+  return row * CPR * 8 + (((col >> 3) ^ (row & (CPR - 1))) << 3) + (col & 7);
+}
+// frag_cols_raw on a swizzled tile (each 8-byte piece stays inside its chunk).
+template <int CPR>
+__device__ __forceinline__ u32x4 frag_cols_swz(const u16* base, int k0, int c0, int l16) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const int col = c0 + 4 * (l16 & 3);
+  const u16* p0 = base + swz<CPR>(k0 + (l16 >> 2), col);
+  const u16* p1 = base + swz<CPR>(k0 + 4 + (l16 >> 2), col);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p1);
+  const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+  const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+  return u32x4{l2[0], l2[1], h2[0], h2[1]};
+}
+
+// One direct load of 16 bytes per lane into LDS: lane l's piece lands at
+// lds_chunk0 + l (in 16-byte units); lds_chunk0 is wave-uniform.
+__device__ __forceinline__ void load_to_lds(const u16* g, u16* lds_chunk0) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  typedef __attribute__((address_space(1))) void glb_void;
+  __builtin_amdgcn_global_load_lds((glb_void*)g, (lds_void*)lds_chunk0, 16, 0, 0);
+}
+
+// Two fp32 values as a packed bf16 pair (round to nearest even), and as a
+// high pair plus the pair of their remainders (hi + lo keeps ~16 bits).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ unsigned pack_bf2(float v0, float v1) {
+  return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){v0, v1}, bf16x2));
+}
+// Returns {high pair, low pair}.
+__device__ __forceinline__ u32x2 split_bf2(float v0, float v1) {
+  const unsigned hi = pack_bf2(v0, v1);
+  return u32x2{hi, pack_bf2(v0 - __builtin_bit_cast(float, hi << 16), v1 - __builtin_bit_cast(float, hi & 0xffff0000u))};
+}
+
 __device__ __forceinline__ u16 half_of(const u32x4& v, int q) {
   const unsigned w = v[q >> 1];
   return (u16)(w >> (16 * (q & 1)));
@@ -177,43 +222,66 @@ __global__ __launch_bounds__(64 * NCB) void ssd_cb_kernel(SsdArgs a, int64_t nbl
 // !FULL: the chunk's own state contribution (from a zero state) and its total
 // decay exponent a * sum(dt), for the carry pass; no outputs.
 //
-// Block products use the 32x32x16 MFMA, which reads half the operand bytes
-// per FLOP of the 16x16x32 form.  Waves 0 and 1 each own the 32-channel x
-// 32-token output of half the block (Y_off in phase A, Y_diag added in phase
-// B, both transposed so a lane holds 4 x 4 consecutive channels of one
-// token); waves 2 .. 2 + N/32 - 1 each own a 32-state slice of the state
-// (S^T = B^T (X o w) and the update in phase B); every wave masks one or two
-// of the block's C B^T tiles (from the pre-pass) in phase A, and waves 4-7
-// form x*w.
+// Only the state recurrence H <- e^{cum_end} H + S_blk is sequential from
+// block to block: the mask and x*w of a block need only its dt, and its
+// outputs need only the state entering it.  The loop therefore runs as a
+// software pipeline with one barrier per step.  Step i forms the decay terms
+// of block i+1, the mask M and x*w of block i, the state update with block
+// i-1 (giving the state entering block i) and the outputs of block i-1, while
+// the next blocks' inputs are loaded.  Each LDS array is kept in as many
+// buffers as the steps that touch one block's copy of it at once.
+//
+// Twelve waves, three per SIMD (w):
+//   0, 1       outputs of tokens [32 w, 32 w + 32) of a block (Y_off and Y_diag,
+//              transposed so that a lane holds 4 x 4 consecutive channels of one
+//              token), C read straight into registers one step ahead, y left in
+//              LDS;
+//   2, 3 (6, 7 when N = 128)
+//              one 32-state slice each: S^T = B^T (X o w) and the update of the
+//              fp32 state held in registers;
+//   8 - 11     x*w of a quarter of the block's rows each;
+//   2          also the decay terms;
+//   4, 5       the direct loads of B, x and the gate into LDS, and the stores
+//              of y one step later (so that the only memory operations of waves
+//              0 and 1 are their own loads, which they wait for exactly);
+//   4 - 11     the block's ten causal C B^T tiles (the pre-pass product), masked
+//              and decayed into M: one tile each for waves 4 and 5, the rest
+//              spread over the waves that hold no state slice.
+// The 32x32x16 MFMA is used throughout; the fp32 operands (M, x*w, the state)
+// enter as a bf16 high part plus a bf16 low part.
 template <int N, bool DTB, bool FULL>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void ssd_fused_kernel(SsdArgs a) {
-  constexpr int SN = N + 8;        // row stride of [*][N] LDS arrays (bf16 elements)
-  constexpr int SQ = QB + 8;       // row stride of [*][64] LDS arrays
-  constexpr int SP = PS + 8;       // row stride of the x tiles
+__global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(3))) void ssd_fused_kernel(SsdArgs a) {
+  constexpr int SN = N + 8;        // row stride of the state tiles (bf16 elements)
+  constexpr int SQ = QB + 8;       // row stride of M
+  constexpr int SP = PS + 8;       // row stride of x*w
   constexpr int NQ = N / 32;       // 32-state slices of the state
   constexpr int KS = N / 16;       // 16-deep k-steps over the states
-  constexpr int CPR = N / 8;       // 16-byte chunks per B/C row
-  constexpr int BC_CHUNKS = QB * CPR / (NWAVE * 64);  // B (and C) chunks per thread per block
-  constexpr int X0 = 256;          // threads [X0, X0 + 256) load x and form x*w: waves 4-7
-  static_assert(BC_CHUNKS >= 1 && (QB * CPR) % (NWAVE * 64) == 0 && QB * PS / 8 == 256, "tile shape");
+  constexpr int CPR = N / 8;       // 16-byte chunks per B row
+  constexpr int XCPR = PS / 8;     // 16-byte chunks per x row
+  static_assert(NQ == 2 || NQ == 4, "dstate 64 or 128");
+  static_assert(QB * CPR % 64 == 0 && QB * XCPR % 64 == 0 && QB * XCPR == 4 * 64, "tile shape");
 
-  __shared__ __attribute__((aligned(16))) u16 Cs[QB * SN];   // C block [t][n]
-  __shared__ __attribute__((aligned(16))) u16 Bs[QB * SN];   // B block [s][n]
-  __shared__ __attribute__((aligned(16))) u16 Xs[QB * SP];   // x block [s][p]
-  __shared__ __attribute__((aligned(16))) u16 XWh[QB * SP];  // x_s[p] * w_s [s][p], high part
-  __shared__ __attribute__((aligned(16))) u16 XWl[QB * SP];  // low part
-  __shared__ __attribute__((aligned(16))) u16 Ms[QB * SQ];   // masked decayed C B^T [t][s], high part
-  __shared__ __attribute__((aligned(16))) u16 Ml[QB * SQ];   // low part
-  __shared__ __attribute__((aligned(16))) u16 Hs[PS * SN];   // state [p][n], high part
-  __shared__ __attribute__((aligned(16))) u16 Hl[PS * SN];   // low part
-  __shared__ float cumS[QB], gS[QB], eS[QB], wS[QB];
-  __shared__ float decayS;
+  // Buffers by block: B (read one step after its load) x2, x (read by the
+  // two steps after its load) x3, x*w and M (read one step later) x2, the
+  // state entering a block (read one step later) x2, decay terms x3.
+  __shared__ __attribute__((aligned(16))) u16 Bs2[2][QB * N];     // B block [s][n], swizzled rows
+  __shared__ __attribute__((aligned(16))) u16 Xs3[3][QB * PS];    // x block [s][p], swizzled rows
+  __shared__ __attribute__((aligned(16))) u16 XWh2[2][QB * SP];   // x_s[p] * w_s [s][p], high part
+  __shared__ __attribute__((aligned(16))) u16 XWl2[2][QB * SP];   // low part
+  __shared__ __attribute__((aligned(16))) u16 Ms2[2][QB * SQ];    // masked decayed C B^T [t][s], high part
+  __shared__ __attribute__((aligned(16))) u16 Ml2[2][QB * SQ];    // low part
+  __shared__ __attribute__((aligned(16))) u16 Hs2[2][PS * SN];    // state [p][n], high part
+  __shared__ __attribute__((aligned(16))) u16 Hl2[2][PS * SN];    // low part
+  __shared__ __attribute__((aligned(16))) u16 Zs2[2][QB * PS];    // gate block [t][p], swizzled rows
+  __shared__ __attribute__((aligned(16))) u16 Ys2[2][QB * SP];    // outputs of a block [t][p], bf16
+  __shared__ float decS[3][4][QB];   // per token of a block: cum log2(e), gain, e^cum, w = e^{cum_end - cum} gain
+  __shared__ float decT[3];          // e^{cum_end}
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
   const int l = tid & 63, l16 = l & 15, c32 = l & 31, hk = l >> 5;
   const int c16 = 16 * ((l >> 4) & 1);   // column offset of this lane's 16-lane group within a 32-wide tile
-  const int64_t H = a.nheads, P = a.headdim, L = a.seqlen;
+  const int64_t H = a.nheads, P = a.headdim, L = a.seqlen, G = a.ngroups;
   const int64_t nb = gridDim.x;
   int64_t lin = blockIdx.x;
   if ((nb & 7) == 0) lin = (lin & 7) * (nb >> 3) + (lin >> 3);  // a contiguous range of heads per XCD
@@ -221,7 +289,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   const int ph = (int)(lin % nsl);
   const int64_t h = (lin / nsl) % H;
   const int64_t b = (lin / nsl) / H;
-  const int64_t grp = h / (H / a.ngroups);
+  const int64_t grp = h / (H / G);
   const float av = a.A[h];
   const float bias = a.dt_bias != nullptr ? a.dt_bias[h] : 0.f;
   const float Dv = a.Dskip != nullptr ? a.Dskip[h] : 0.f;
@@ -230,6 +298,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   const int64_t t_begin = chunk * a.tchunk;
   const int64_t t_end = t_begin + a.tchunk < L ? t_begin + a.tchunk : L;
   const int64_t slice = a.batch * H * P * N;     // one state per (batch, head)
+  const int64_t last = L - 1;
+  const int nblk = (int)((t_end - t_begin + QB - 1) / QB);
 
   const u16* gX = (const u16*)a.x;
   const u16* gB = (const u16*)a.B;
@@ -237,17 +307,39 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   const u16* gZ = (const u16*)a.z;
   u16* gY = (u16*)a.y;
 
-  // strictly-upper 16x16 tiles of M are never written by the mask: zero them once
-  for (int i = tid; i < QB * SQ; i += NWAVE * 64) {
-    Ms[i] = 0;
-    Ml[i] = 0;
+  // ---- roles
+  const bool y_wave = FULL && w < 2;
+  const int nq = (w == 2 || w == 3) ? w - 2 : ((NQ == 4 && (w == 6 || w == 7)) ? w - 4 : -1);
+  const bool has_st = nq >= 0;
+  const bool xw_wave = w >= 8;
+  const int xw_unit = 64 * (w - 8) + l;   // row xw_unit / 4, 8 channels from 8 (xw_unit % 4)
+  const bool load_wave = w == 4 || w == 5;
+  const bool d_wave = w == 2;
+  // C B^T tiles (index c = ti (ti + 1) / 2 + tj) of this wave, -1 for none
+  int cb0 = -1, cb1 = -1;
+  if (FULL) {
+    if (w == 4 || w == 5) {
+      cb0 = w - 4;
+    } else if (NQ == 4 && w >= 8) {
+      cb0 = 2 + 2 * (w - 8);
+      cb1 = cb0 + 1;
+    } else if (NQ == 2 && (w == 6 || w == 7)) {
+      cb0 = 2 + 2 * (w - 6);
+      cb1 = cb0 + 1;
+    } else if (NQ == 2 && w >= 8) {
+      cb0 = 6 + (w - 8);
+    }
   }
 
-  // ---- state: wave 2 + q (q < N/32) owns states [32 q, 32 q + 32) of the 32 channels.  Lane l holds
-  // H[p = l % 32][n = 32 q + 8 g + 4 (l / 32) + j] in Hacc[4 g + j], g, j = 0..3.
+  // strictly-upper 16x16 tiles of M are never written by the mask: zero both buffers once
+  for (int i = tid; i < 2 * QB * SQ; i += NWAVE * 64) {
+    (&Ms2[0][0])[i] = 0;
+    (&Ml2[0][0])[i] = 0;
+  }
+
+  // ---- state: wave with slice nq owns states [32 nq, 32 nq + 32) of the 32 channels.  Lane l holds
+  // H[p = l % 32][n = 32 nq + 8 g + 4 (l / 32) + j] in Hacc[4 g + j], g, j = 0..3.
   // FULL: h0, or the carry into this chunk; !FULL: zero.
-  const bool has_st = w >= 2 && w < 2 + NQ;
-  const int nq = w - 2;
   const float* hin = !FULL ? nullptr : (a.nchunks > 1 ? a.ws_state + chunk * slice : a.h0);
   const int64_t hrow = ((b * H + h) * P + p0 + c32) * N;   // this lane's channel row of a state
   f32x16 Hacc = {};
@@ -259,236 +351,319 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
       for (int j = 0; j < 4; ++j) Hacc[4 * g + j] = v[j];
     }
   }
-  auto store_state_split = [&]() {
-    if (!has_st) return;
+  auto store_state_split = [&](int buf) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int idx = c32 * SN + 32 * nq + 8 * g + 4 * hk;
       u32x2 hi, lo;
 #pragma unroll
       for (int j = 0; j < 4; j += 2) {
-        const float v0 = Hacc[4 * g + j], v1 = Hacc[4 * g + j + 1];
-        const u16 h0b = f2bf(v0), h1b = f2bf(v1);
-        hi[j >> 1] = (unsigned)h0b | ((unsigned)h1b << 16);
-        lo[j >> 1] = (unsigned)f2bf(v0 - bf2f(h0b)) | ((unsigned)f2bf(v1 - bf2f(h1b)) << 16);
+        const u32x2 v = split_bf2(Hacc[4 * g + j], Hacc[4 * g + j + 1]);
+        hi[j >> 1] = v[0];
+        lo[j >> 1] = v[1];
       }
-      *reinterpret_cast<u32x2*>(Hs + idx) = hi;
-      *reinterpret_cast<u32x2*>(Hl + idx) = lo;
+      *reinterpret_cast<u32x2*>(&Hs2[buf][idx]) = hi;
+      *reinterpret_cast<u32x2*>(&Hl2[buf][idx]) = lo;
     }
   };
-  if (FULL) store_state_split();   // visible after the first barrier of the block loop
 
-  // ---- this wave's causal C B^T tiles of each block (index c = ti (ti + 1) / 2 + tj): waves 0, 1 and
-  // 4-7 one each, waves 2 and 3 two each
-  const int cb0 = w < 2 ? w : (w < 4 ? 2 + 2 * (w - 2) : w + 2);
-  const int cb1 = (w == 2 || w == 3) ? cb0 + 1 : -1;
+  // ---- direct loads into LDS: a block's B and x tiles are loaded as 16-byte pieces per lane, piece i
+  // filling slots [64 i, 64 i + 64) of the LDS tile (slot q holds row q / CPR, chunk (q mod CPR) ^
+  // (row mod CPR)).  Piece i goes to wave 4 + i % 2.  Waves 4 and 5 read none of these arrays, so the
+  // compiler's waits for the loads (which it cannot tell apart from other LDS writes of the same
+  // array) stay out of the waves that read them; waves 4 and 5 wait for them before the step's
+  // barrier.  Rows past the sequence repeat the last token (their dt is zero, so they change nothing).
+  constexpr int NBI = QB * CPR / 128;      // B pieces per loading wave and block
+  constexpr int NXI = QB * XCPR / 128;     // x (and gate) pieces per loading wave and block
+  const int dw = w - 4;                    // waves 4, 5
+  // (64 rows of G*N or H*P elements fit in 32 bits: the launcher checks it)
+  auto load_b = [&](int64_t t0, int buf) {
+    const int lim = (int)(last - t0 < QB - 1 ? last - t0 : QB - 1);   // last row inside the sequence
+    const u16* base = gB + ((b * L + t0) * G + grp) * N;
+#pragma unroll
+    for (int k = 0; k < NBI; ++k) {
+      const int i = dw + 2 * k, q = 64 * i + l, row = q / CPR;
+      const int rc = row < lim ? row : lim;
+      load_to_lds(base + ((unsigned)(rc * (int)(G * N)) + 8 * ((q % CPR) ^ (row & (CPR - 1)))),
+                  &Bs2[buf][64 * i * 8]);
+    }
+  };
+  // x (src gX, into Xs3) or the gate (src gZ, into Zs2): the same layout
+  auto load_xz = [&](const u16* src, int64_t t0, u16* dst) {
+    const int lim = (int)(last - t0 < QB - 1 ? last - t0 : QB - 1);
+    const u16* base = src + ((b * L + t0) * H + h) * P + p0;
+#pragma unroll
+    for (int k = 0; k < NXI; ++k) {
+      const int i = dw + 2 * k, q = 64 * i + l, row = q / XCPR;
+      const int rc = row < lim ? row : lim;
+      load_to_lds(base + ((unsigned)(rc * (int)(H * P)) + 8 * ((q % XCPR) ^ (row & (XCPR - 1)))),
+                  dst + 64 * i * 8);
+    }
+  };
+  auto load_wait = []() { __builtin_amdgcn_s_waitcnt(0x0F70); };   // vmcnt(0)
+  // y of the block at t0 from Ys2[buf]: 64 rows of four 16-byte pieces, two per lane
+  auto store_y = [&](int64_t t0, int buf) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int u = 128 * k + 64 * dw + l, row = u >> 2, c = u & 3;
+      const int64_t t = t0 + row;
+      if (t < t_end)
+        *reinterpret_cast<u32x4*>(gY + ((b * L + t) * H + h) * P + p0 + 8 * c) =
+            *reinterpret_cast<const u32x4*>(&Ys2[buf][row * SP + 8 * c]);
+    }
+  };
+
+  // ---- per-block register loads one step ahead: dt (wave 2), C B^T tiles, C rows (waves 0, 1)
+  auto load_dt = [&](int64_t t0) -> float {
+    int64_t t = t0 + l;
+    t = t < last ? t : last;
+    const int64_t i = (b * L + t) * H + h;
+    return DTB ? bf2f(((const u16*)a.dt)[i]) : ((const float*)a.dt)[i];
+  };
   const int64_t nblk_total = (L + QB - 1) / QB;
-  const f32x4* gcb = reinterpret_cast<const f32x4*>(a.ws_cb) + ((b * nblk_total) * a.ngroups + grp) * NCB * 64;
-
-  // ---- register prefetch of one block
-  u32x4 rc[BC_CHUNKS], rb[BC_CHUNKS], rx = {0u, 0u, 0u, 0u};
-  f32x4 rcb0 = {0.f, 0.f, 0.f, 0.f}, rcb1 = {0.f, 0.f, 0.f, 0.f};
-  float rdt = 0.f;
-  const int64_t last = L - 1;
-  const bool x_thread = tid >= X0;
-  auto fetch = [&](int64_t t0) {
-    if (FULL) {
-      const f32x4* cbp = gcb + (t0 / QB) * a.ngroups * NCB * 64;
-      rcb0 = cbp[cb0 * 64 + l];
-      if (cb1 >= 0) rcb1 = cbp[cb1 * 64 + l];
-    }
+  const f32x4* gcb = reinterpret_cast<const f32x4*>(a.ws_cb) + ((b * nblk_total) * G + grp) * NCB * 64;
+  auto load_cb = [&](int64_t t0, f32x4& r0, f32x4& r1) {   // waves with a tile
+    const f32x4* cbp = gcb + (t0 / QB) * G * NCB * 64;
+    r0 = cbp[cb0 * 64 + l];
+    if (cb1 >= 0) r1 = cbp[cb1 * 64 + l];
+  };
+  // lane l of wave w < 2: token 32 w + l % 32, states 16 ks + 8 (l / 32) .. +7 for ks < KS
+  auto load_c = [&](int64_t t0, bf16x8 (&r)[KS]) {
+    int64_t t = t0 + 32 * w + c32;
+    t = t < last ? t : last;
+    const u16* row = gC + ((b * L + t) * G + grp) * N + 8 * hk;
 #pragma unroll
-    for (int j = 0; j < BC_CHUNKS; ++j) {
-      const int e = tid + NWAVE * 64 * j;
-      const int row = e / CPR, c8 = e % CPR;
-      int64_t t = t0 + row;
-      t = t < last ? t : last;
-      const int64_t off = ((b * L + t) * a.ngroups + grp) * N + c8 * 8;
-      if (FULL) rc[j] = *reinterpret_cast<const u32x4*>(gC + off);
-      rb[j] = *reinterpret_cast<const u32x4*>(gB + off);
+    for (int ks = 0; ks < KS; ++ks) r[ks] = *reinterpret_cast<const bf16x8*>(row + 16 * ks);
+  };
+
+  // ---- decay terms of the block at t0 into decS[buf] (wave 2; lane l = token t0 + l)
+  float dsum = 0.f;   // a * sum of dt over the chunk
+  auto decay_terms = [&](int64_t t0, float dtraw, int buf) {
+    const float v = dtraw + bias;
+    float dtv = a.softplus ? softplus_f(v) : v;
+    if (t0 + l >= L) dtv = 0.f;   // past the end: no input, no decay
+    const float cum = wave_prefix_sum(dtv * av);
+    const float cend = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cum), 63));
+    const float gv = zoh_gain(dtv, av);
+    const float cl = cum * kLog2e, cel = cend * kLog2e;
+    decS[buf][0][l] = cl;
+    decS[buf][1][l] = gv;
+    decS[buf][2][l] = hw_exp2(cl);
+    decS[buf][3][l] = hw_exp2(cel - cl) * gv;
+    if (l == 0) decT[buf] = hw_exp2(cel);
+    dsum += cend;
+  };
+
+  // ---- mask one C B^T tile of a block: lane (l16, g4) holds M's row t = 16 ti + l16 at s = 16 tj + 4 g4 .. +3
+  auto mask_tile = [&](int c, const f32x4& acc, int db, int mb) {
+    const int ti = cb_tile_row(c), tj = c - ti * (ti + 1) / 2;
+    const int t = ti * 16 + l16;
+    const int s0 = tj * 16 + 4 * (l >> 4);
+    const float ct = decS[db][0][t];
+    const f32x4 cs = *reinterpret_cast<const f32x4*>(&decS[db][0][s0]);
+    const f32x4 gs = *reinterpret_cast<const f32x4*>(&decS[db][1][s0]);
+    float m[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) m[v] = acc[v] * hw_exp2(ct - cs[v]) * gs[v];
+    if (ti == tj) {   // diagonal tile: causal within it (off the diagonal, t > s throughout)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) m[v] = t >= s0 + v ? m[v] : 0.f;
     }
-    if (x_thread) {
-      const int e = tid - X0, row = e >> 2, c8 = e & 3;
-      int64_t t = t0 + row;
-      t = t < last ? t : last;
-      rx = *reinterpret_cast<const u32x4*>(gX + ((b * L + t) * H + h) * P + p0 + c8 * 8);
+    const u32x2 v01 = split_bf2(m[0], m[1]), v23 = split_bf2(m[2], m[3]);
+    const u32x2 hi = {v01[0], v23[0]}, lo = {v01[1], v23[1]};
+    *reinterpret_cast<u32x2*>(&Ms2[mb][t * SQ + s0]) = hi;
+    *reinterpret_cast<u32x2*>(&Ml2[mb][t * SQ + s0]) = lo;
+  };
+
+  // ---- prologue: block 0's decay terms, x and C B^T tiles; the state entering it
+  f32x4 rcb0 = {0.f, 0.f, 0.f, 0.f}, rcb1 = {0.f, 0.f, 0.f, 0.f};
+  float rdt = 0.f;                         // wave 2: raw dt of the block after the next decay terms
+  bf16x8 rc[KS];                           // waves 0, 1: C rows of the block whose outputs are formed next
+  if (FULL && cb0 >= 0) load_cb(t_begin, rcb0, rcb1);
+  if (load_wave) load_xz(gX, t_begin, Xs3[0]);
+  if (d_wave) {
+    decay_terms(t_begin, load_dt(t_begin), 0);
+    if (nblk > 1) rdt = load_dt(t_begin + QB);
+  }
+  if (FULL && has_st) store_state_split(0);
+  if (load_wave) load_wait();
+  lds_sync();
+
+  // Each role runs a loop of its own over the nblk + 1 steps, each step ending at the workgroup barrier
+  // (the same count in every wave).  Separate loops keep one role's registers, and the compiler's waits
+  // for its loads, out of the other roles' code.
+  auto mask_own = [&](int i, int i3) {
+    if constexpr (FULL) {
+      if (cb0 >= 0) mask_tile(cb0, rcb0, i3, i & 1);
+      if (cb1 >= 0) mask_tile(cb1, rcb1, i3, i & 1);
     }
-    if (w == 0) {
-      int64_t t = t0 + l;
-      t = t < last ? t : last;
-      const int64_t i = (b * L + t) * H + h;
-      rdt = DTB ? bf2f(((const u16*)a.dt)[i]) : ((const float*)a.dt)[i];
+  };
+  auto next_cb = [&](int64_t t0n) {
+    if constexpr (FULL) {
+      if (cb0 >= 0) load_cb(t0n, rcb0, rcb1);
     }
   };
 
-  const int nblk = (int)((t_end - t_begin + QB - 1) / QB);
-  float dsum = 0.f;                  // a * sum of dt over the chunk (wave 0)
-  f32x16 yacc = {};                  // waves 0, 1: e^{cum_t} Y_off, then + Y_diag
-  fetch(t_begin);
-  for (int blk = 0; blk < nblk; ++blk) {
-    const int64_t t0 = t_begin + (int64_t)blk * QB;
-    // ---------------- stage the block (natural layouts) and the decay terms
-#pragma unroll
-    for (int j = 0; j < BC_CHUNKS; ++j) {
-      const int e = tid + NWAVE * 64 * j;
-      const int row = e / CPR, c8 = e % CPR;
-      if (FULL) *reinterpret_cast<u32x4*>(Cs + row * SN + c8 * 8) = rc[j];
-      *reinterpret_cast<u32x4*>(Bs + row * SN + c8 * 8) = rb[j];
-    }
-    if (x_thread) {
-      const int e = tid - X0, row = e >> 2, c8 = e & 3;
-      *reinterpret_cast<u32x4*>(Xs + row * SP + c8 * 8) = rx;
-    }
-    if (w == 0) {
-      // lane l = token t0 + l: dt, the inclusive scan of dt*a, gain and decays
-      const float v = rdt + bias;
-      float dtv = a.softplus ? softplus_f(v) : v;
-      if (t0 + l >= L) dtv = 0.f;   // past the end: no input, no decay
-      const float cum = wave_prefix_sum(dtv * av);
-      const float cend = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cum), 63));
-      const float gv = zoh_gain(dtv, av);
-      cumS[l] = cum;
-      gS[l] = gv;
-      eS[l] = exp_f(cum);
-      wS[l] = exp_f(cend - cum) * gv;
-      if (l == 0) decayS = exp_f(cend);
-      dsum += cend;
-    }
-    lds_sync();
-
-    // ---------------- phase A: x*w, Y_off, mask
-    const f32x4 cb_cur0 = rcb0, cb_cur1 = rcb1;
-    if (x_thread) {
-      // x * w for the state product, once per workgroup, from the staged registers
-      const int e = tid - X0, row = e >> 2, c8 = e & 3;
-      const float ws = wS[row];
-      u32x4 hi, lo;
-#pragma unroll
-      for (int q = 0; q < 8; q += 2) {
-        const float f0 = bf2f(half_of(rx, q)) * ws, f1 = bf2f(half_of(rx, q + 1)) * ws;
-        const u16 h0b = f2bf(f0), h1b = f2bf(f1);
-        hi[q >> 1] = (unsigned)h0b | ((unsigned)h1b << 16);
-        lo[q >> 1] = (unsigned)f2bf(f0 - bf2f(h0b)) | ((unsigned)f2bf(f1 - bf2f(h1b)) << 16);
+  if (load_wave) {
+    // x of block i+1, B and the gate of block i into LDS; y of block i-2 out; the mask of block i
+    int i3 = 0;   // step % 3
+    for (int i = 0; i <= nblk; ++i) {
+      const int64_t t0 = t_begin + (int64_t)i * QB;
+      const int i3n = i3 == 2 ? 0 : i3 + 1;
+      if (i + 1 < nblk) load_xz(gX, t0 + QB, Xs3[i3n]);
+      if (FULL && i >= 2) store_y(t0 - 2 * QB, i & 1);
+      if (i < nblk) {
+        load_b(t0, i & 1);
+        if (FULL && a.z != nullptr) load_xz(gZ, t0, Zs2[i & 1]);
+        mask_own(i, i3);
+        if (i + 1 < nblk) next_cb(t0 + QB);
       }
-      *reinterpret_cast<u32x4*>(XWh + row * SP + c8 * 8) = hi;
-      *reinterpret_cast<u32x4*>(XWl + row * SP + c8 * 8) = lo;
+      i3 = i3n;
+      load_wait();
+      lds_sync();
     }
-    if (blk + 1 < nblk) fetch(t0 + QB);
-
-    if constexpr (FULL) {
-      if (w < 2) {
-        // Y_off^T = H C^T for tokens [32 w, 32 w + 32) of the block; H = state entering the block.  Two
-        // accumulation chains (even and odd k-steps).
-        f32x16 ya = {}, yb = {};
+    if (FULL) store_y(t_begin + (int64_t)(nblk - 1) * QB, (nblk - 1) & 1);
+  } else if (y_wave) {
+    // outputs of block i-1: Y^T = diag(e^cum) (H C^T) + X^T M^T for tokens [32 w, 32 w + 32), gated, to
+    // Ys2.  The C rows of block i go into the registers of block i-1's once those are used.
+    int i3 = 0;
+    for (int i = 0; i <= nblk; ++i) {
+      const int64_t t0 = t_begin + (int64_t)i * QB;
+      const int i3p = i3 == 0 ? 2 : i3 - 1;
+      f32x16 yacc = {};
+      if (i > 0) {
+        const int jb = (i - 1) & 1;
+        const u16* Hs = Hs2[jb];
+        const u16* Hl = Hl2[jb];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           const int k0 = 16 * ks + 8 * hk;
-          const bf16x8 cfr = frag_rows(Cs, 32 * w + c32, k0, SN);
-          if (ks & 1) {
-            yb = mfma32(frag_rows(Hs, c32, k0, SN), cfr, yb);
-            yb = mfma32(frag_rows(Hl, c32, k0, SN), cfr, yb);
-          } else {
-            ya = mfma32(frag_rows(Hs, c32, k0, SN), cfr, ya);
-            ya = mfma32(frag_rows(Hl, c32, k0, SN), cfr, ya);
-          }
+          yacc = mfma32(frag_rows(Hs, c32, k0, SN), rc[ks], yacc);
+          yacc = mfma32(frag_rows(Hl, c32, k0, SN), rc[ks], yacc);
         }
-        yacc = (ya + yb) * eS[32 * w + c32];
+        yacc *= decS[i3p][2][32 * w + c32];
       }
-      // mask this wave's C B^T tiles: lane (l16, g4) holds M's row t = 16 ti + l16 at s = 16 tj + 4 g4 .. +3
-      auto mask_tile = [&](int c, const f32x4& acc) {
-        const int ti = cb_tile_row(c), tj = c - ti * (ti + 1) / 2;
-        const int t = ti * 16 + l16;
-        const int s0 = tj * 16 + 4 * (l >> 4);
-        const float ct = cumS[t];
-        u32x2 hi, lo;
-#pragma unroll
-        for (int v = 0; v < 4; v += 2) {
-          const int s = s0 + v;
-          const float m0 = (t >= s) ? acc[v] * exp_f(ct - cumS[s]) * gS[s] : 0.f;
-          const float m1 = (t >= s + 1) ? acc[v + 1] * exp_f(ct - cumS[s + 1]) * gS[s + 1] : 0.f;
-          const u16 h0b = f2bf(m0), h1b = f2bf(m1);
-          hi[v >> 1] = (unsigned)h0b | ((unsigned)h1b << 16);
-          lo[v >> 1] = (unsigned)f2bf(m0 - bf2f(h0b)) | ((unsigned)f2bf(m1 - bf2f(h1b)) << 16);
-        }
-        *reinterpret_cast<u32x2*>(Ms + t * SQ + s0) = hi;
-        *reinterpret_cast<u32x2*>(Ml + t * SQ + s0) = lo;
-      };
-      mask_tile(cb0, cb_cur0);
-      if (cb1 >= 0) mask_tile(cb1, cb_cur1);
-    }
-    lds_sync();   // M and x*w complete; every wave has finished reading Hs/Hl
-
-    // ---------------- phase B: state slices; Y_diag and the outputs
-    if (has_st) {
-      // S^T = B^T (X o w) for states [32 nq, 32 nq + 32); H <- decay H + S
-      f32x16 s = {};
-#pragma unroll
-      for (int ks = 0; ks < QB / 16; ++ks) {
-        const int k0 = 16 * ks + 8 * hk;
-        const bf16x8 bt = __builtin_bit_cast(bf16x8, frag_cols_raw(Bs, k0, 32 * nq + c16, SN, l16));
-        s = mfma32(bt, __builtin_bit_cast(bf16x8, frag_cols_raw(XWh, k0, c16, SP, l16)), s);
-        s = mfma32(bt, __builtin_bit_cast(bf16x8, frag_cols_raw(XWl, k0, c16, SP, l16)), s);
-      }
-      const float dec = decayS;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) Hacc[v] = fmaf(dec, Hacc[v], s[v]);
-    }
-    if constexpr (FULL) {
-      if (w < 2) {
-        // Y_diag^T = X^T M^T for tokens [32 w, 32 w + 32): causal, so s < 32 (w + 1)
+      if (i < nblk) load_c(t0, rc);
+      if (i > 0) {
+        const int jb = (i - 1) & 1;
+        // causal: s < 32 (w + 1)
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
           if (ks < 2 * (w + 1)) {
             const int k0 = 16 * ks + 8 * hk;
-            const bf16x8 xb = __builtin_bit_cast(bf16x8, frag_cols_raw(Xs, k0, c16, SP, l16));
-            yacc = mfma32(xb, frag_rows(Ms, 32 * w + c32, k0, SQ), yacc);
-            yacc = mfma32(xb, frag_rows(Ml, 32 * w + c32, k0, SQ), yacc);
+            const bf16x8 xb = __builtin_bit_cast(bf16x8, frag_cols_swz<XCPR>(Xs3[i3p], k0, c16, l16));
+            yacc = mfma32(xb, frag_rows(Ms2[jb], 32 * w + c32, k0, SQ), yacc);
+            yacc = mfma32(xb, frag_rows(Ml2[jb], 32 * w + c32, k0, SQ), yacc);
           }
         }
-        // lane l: token t0 + 32 w + l % 32, channels 8 g + 4 (l / 32) .. +3 for g = 0..3 (8-byte stores)
+        // lane l: token 32 w + l % 32 of block i-1, channels 8 g + 4 (l / 32) .. +3 for g = 0..3
         const int tl = 32 * w + c32;
-        const int64_t t = t0 + tl;
-        if (t < L) {
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int p = 8 * g + 4 * hk;
-            float yv[4];
+        for (int g = 0; g < 4; ++g) {
+          const int p = 8 * g + 4 * hk;
+          float yv[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) yv[j] = yacc[4 * g + j];
-            const int64_t gi = ((b * L + t) * H + h) * P + p0 + p;
-            if (a.Dskip != nullptr) {
-              const u32x2 xr = *reinterpret_cast<const u32x2*>(Xs + tl * SP + p);
+          for (int j = 0; j < 4; ++j) yv[j] = yacc[4 * g + j];
+          if (a.Dskip != nullptr) {
+            const u32x2 xr = *reinterpret_cast<const u32x2*>(&Xs3[i3p][swz<XCPR>(tl, p)]);
 #pragma unroll
-              for (int j = 0; j < 4; ++j) yv[j] = fmaf(Dv, bf2f((u16)(xr[j >> 1] >> (16 * (j & 1)))), yv[j]);
-            }
-            if (a.z != nullptr) {
-              const u32x2 zr = *reinterpret_cast<const u32x2*>(gZ + gi);
-#pragma unroll
-              for (int j = 0; j < 4; ++j) yv[j] *= silu_f(bf2f((u16)(zr[j >> 1] >> (16 * (j & 1)))));
-            }
-            u32x2 out;
-            out[0] = (unsigned)f2bf(yv[0]) | ((unsigned)f2bf(yv[1]) << 16);
-            out[1] = (unsigned)f2bf(yv[2]) | ((unsigned)f2bf(yv[3]) << 16);
-            *reinterpret_cast<u32x2*>(gY + gi) = out;
+            for (int j = 0; j < 4; ++j) yv[j] = fmaf(Dv, bf2f((u16)(xr[j >> 1] >> (16 * (j & 1)))), yv[j]);
           }
+          if (a.z != nullptr) {
+            const u32x2 zr = *reinterpret_cast<const u32x2*>(&Zs2[jb][swz<XCPR>(tl, p)]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) yv[j] *= silu_f(bf2f((u16)(zr[j >> 1] >> (16 * (j & 1)))));
+          }
+          const u32x2 out = {pack_bf2(yv[0], yv[1]), pack_bf2(yv[2], yv[3])};
+          *reinterpret_cast<u32x2*>(&Ys2[jb][tl * SP + p]) = out;
         }
       }
+      i3 = i3 == 2 ? 0 : i3 + 1;
+      lds_sync();
     }
-    if (FULL) store_state_split();   // the state entering the next block
-    lds_sync();
-  }
-
-  float* hout = FULL ? (chunk == a.nchunks - 1 ? a.h_final : nullptr) : a.ws_state + chunk * slice;
-  if (hout != nullptr && has_st) {
+  } else if (has_st) {
+    // decay terms of block i+1 (wave 2); the state update with block i-1: H_i = e^{cum_end} H_{i-1} +
+    // B^T (X o w), then H_i split for the outputs of block i
+    int i3 = 0;
+    for (int i = 0; i <= nblk; ++i) {
+      const int64_t t0 = t_begin + (int64_t)i * QB;
+      const int i3p = i3 == 0 ? 2 : i3 - 1;
+      if (i < nblk) mask_own(i, i3);   // (none when N = 128)
+      if (d_wave && i + 1 < nblk) {
+        decay_terms(t0 + QB, rdt, i3 == 2 ? 0 : i3 + 1);
+        if (i + 2 < nblk) rdt = load_dt(t0 + 2 * QB);   // the raw dt two blocks ahead
+      }
+      if (i > 0) {
+        const int bb = (i - 1) & 1;
+        // fragment reads issued two k-steps ahead of their products
+        f32x16 s = {}, sl = {};
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      f32x4 v;
+        for (int k2 = 0; k2 < QB / 16; k2 += 2) {
+          u32x4 fb[2], fh[2], fl[2];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = Hacc[4 * g + j];
-      *reinterpret_cast<f32x4*>(hout + hrow + 32 * nq + 8 * g + 4 * hk) = v;
+          for (int j = 0; j < 2; ++j) {
+            const int k0 = 16 * (k2 + j) + 8 * hk;
+            fb[j] = frag_cols_swz<CPR>(Bs2[bb], k0, 32 * nq + c16, l16);
+            fh[j] = frag_cols_raw(XWh2[bb], k0, c16, SP, l16);
+            fl[j] = frag_cols_raw(XWl2[bb], k0, c16, SP, l16);
+          }
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const bf16x8 bt = __builtin_bit_cast(bf16x8, fb[j]);
+            s = mfma32(bt, __builtin_bit_cast(bf16x8, fh[j]), s);
+            sl = mfma32(bt, __builtin_bit_cast(bf16x8, fl[j]), sl);
+          }
+        }
+        s += sl;
+        const float dec = decT[i3p];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) Hacc[v] = fmaf(dec, Hacc[v], s[v]);
+        if (FULL && i < nblk) store_state_split(i & 1);
+      }
+      if (i + 1 < nblk) next_cb(t0 + QB);
+      i3 = i3 == 2 ? 0 : i3 + 1;
+      lds_sync();
+    }
+    // the final state (or this chunk's state and decay sum for the carry pass)
+    float* hout = FULL ? (chunk == a.nchunks - 1 ? a.h_final : nullptr) : a.ws_state + chunk * slice;
+    if (hout != nullptr) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = Hacc[4 * g + j];
+        *reinterpret_cast<f32x4*>(hout + hrow + 32 * nq + 8 * g + 4 * hk) = v;
+      }
+    }
+    if (!FULL && d_wave && l == 0 && ph == 0) a.ws_dsum[chunk * a.batch * H + b * H + h] = dsum;
+  } else {
+    // the mask and x*w of block i.  (Waves with neither, such as waves 0 and 1 of the state-only pass,
+    // only keep the barrier count.)
+    int i3 = 0;
+    for (int i = 0; i <= nblk; ++i) {
+      const int64_t t0 = t_begin + (int64_t)i * QB;
+      if (i < nblk) {
+        mask_own(i, i3);
+        if (i + 1 < nblk) next_cb(t0 + QB);
+      }
+      if (i < nblk && xw_wave) {
+        const int row = xw_unit >> 2, c8 = xw_unit & 3;
+        const float ws = decS[i3][3][row];
+        const u32x4 rx = *reinterpret_cast<const u32x4*>(&Xs3[i3][swz<XCPR>(row, 8 * c8)]);
+        u32x4 hi, lo;
+#pragma unroll
+        for (int q = 0; q < 8; q += 2) {
+          const u32x2 v = split_bf2(bf2f(half_of(rx, q)) * ws, bf2f(half_of(rx, q + 1)) * ws);
+          hi[q >> 1] = v[0];
+          lo[q >> 1] = v[1];
+        }
+        *reinterpret_cast<u32x4*>(&XWh2[i & 1][row * SP + c8 * 8]) = hi;
+        *reinterpret_cast<u32x4*>(&XWl2[i & 1][row * SP + c8 * 8]) = lo;
+      }
+      i3 = i3 == 2 ? 0 : i3 + 1;
+      lds_sync();
     }
   }
-  if (!FULL && w == 0 && l == 0 && ph == 0) a.ws_dsum[chunk * a.batch * H + b * H + h] = dsum;
 }
 
 // Combine the chunk states in order: slot c of ws_state receives the state
@@ -600,6 +775,9 @@ int launch_ssd(const SsdArgs& a0, void* stream) {
   }
   const int64_t nwg = a.batch * a.nheads * (a.headdim / PS);
   if (nwg > 0x7fffffffLL) return fail(4, "grid too large");
+  // the fused kernel keeps a block's row offsets (64 rows of B or x) in 32 bits
+  if (QB * a.ngroups * a.dstate > 0xffffffffLL || QB * a.nheads * a.headdim > 0xffffffffLL)
+    return fail(4, "nheads * headdim or ngroups * dstate too large");
   const SsdPlan p = plan_ssd(a.batch, a.seqlen, a.nheads, a.headdim, a.ngroups, a.dstate, device_cu_count());
   if (p.nchunks > 65535 || a.batch > 65535 || a.ngroups > 65535 || (a.seqlen + QB - 1) / QB > 0x7fffffffLL)
     return fail(4, "grid too large");
