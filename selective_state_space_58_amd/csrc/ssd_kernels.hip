@@ -121,33 +121,30 @@ __device__ __forceinline__ bf16x8 frag_rows(const u16* base, int row, int col, i
   return *reinterpret_cast<const bf16x8*>(base + row * stride + col);
 }
 
-// Transposed fragment: for lane i of each 16-lane group, rows k0 .. k0+7 of
-// column c0 + i of a row-major bf16 LDS matrix.  Two ds_read_b64_tr_b16: lane
-// j of the group loads row k0 + q + j/4, columns c0 + 4*(j%4) .. +3, and the
-// hardware hands lane i element i%4 of the loads of lanes i/4, i/4+4, i/4+8,
-// i/4+12, i.e. rows k0+q .. k0+q+3 of column c0 + i.
-__device__ __forceinline__ u32x4 frag_cols_raw(const u16* base, int k0, int c0, int stride, int l16) {
-  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-  const u16* p0 = base + (k0 + (l16 >> 2)) * stride + c0 + 4 * (l16 & 3);
-  const u16* p1 = p0 + 4 * stride;
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p1);
-  const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
-  const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
-  return u32x4{l2[0], l2[1], h2[0], h2[1]};
-}
-
 // The staged B (rows of N bf16) and x (rows of 32 bf16) tiles are filled
 // by direct global-to-LDS loads, which place the 64 lanes' 16-byte pieces of
-// one instruction at 64 consecutive chunk slots.  Their rows are therefore
-// unpadded; instead the CPR 16-byte chunks of row r are stored in the order
-// chunk ^ (r mod CPR), so that the fragment reads of one column from
-// consecutive rows spread over the LDS banks.  Element offset of (row, col):
+// one instruction at 64 consecutive chunk slots; x*w, the gate and y use the
+// x layout.  The rows are unpadded; instead the CPR 16-byte chunks of row r
+// are stored permuted, chunk ^ key(r), so that a transposed fragment read
+// (four consecutive rows, the same columns) touches every LDS bank at most
+// twice per 64 lanes: key = r mod 4 for 4-chunk rows; for B, whose 32-state
+// slices span four chunks of a row, key = 4 (r mod 4) for 16-chunk rows and
+// 4 ((r / 2) mod 2) for 8-chunk rows (measured free of bank conflicts, where
+// key = r mod CPR on B costs 4x, resp. 2x).  Element offset of (row, col):
+template <int CPR>
+__device__ __forceinline__ int swz_key(int row) {
+  return CPR == 4 ? (row & 3) : (CPR == 16 ? 4 * (row & 3) : 4 * ((row >> 1) & 1));
+}
 template <int CPR>
 __device__ __forceinline__ int swz(int row, int col) {
-  return row * CPR * 8 + (((col >> 3) ^ (row & (CPR - 1))) << 3) + (col & 7);
+  return row * CPR * 8 + (((col >> 3) ^ swz_key<CPR>(row)) << 3) + (col & 7);
 }
-// frag_cols_raw on a swizzled tile (each 8-byte piece stays inside its chunk).
+// Transposed fragment: for lane i of each 16-lane group, rows k0 .. k0+7 of
+// column c0 + i of a swizzled bf16 LDS tile.  Two ds_read_b64_tr_b16: lane j
+// of the group loads row k0 + q + j/4, columns c0 + 4*(j%4) .. +3 (an 8-byte
+// piece, which stays inside its 16-byte chunk), and the hardware hands lane i
+// element i%4 of the loads of lanes i/4, i/4+4, i/4+8, i/4+12, i.e. rows
+// k0+q .. k0+q+3 of column c0 + i.
 template <int CPR>
 __device__ __forceinline__ u32x4 frag_cols_swz(const u16* base, int k0, int c0, int l16) {
   typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -253,7 +250,6 @@ template <int N, bool DTB, bool FULL>
 __global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(3))) void ssd_fused_kernel(SsdArgs a) {
   constexpr int SN = N + 8;        // row stride of the state tiles (bf16 elements)
   constexpr int SQ = QB + 8;       // row stride of M
-  constexpr int SP = PS + 8;       // row stride of x*w
   constexpr int NQ = N / 32;       // 32-state slices of the state
   constexpr int KS = N / 16;       // 16-deep k-steps over the states
   constexpr int CPR = N / 8;       // 16-byte chunks per B row
@@ -266,14 +262,14 @@ __global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(3)))
   // state entering a block (read one step later) x2, decay terms x3.
   __shared__ __attribute__((aligned(16))) u16 Bs2[2][QB * N];     // B block [s][n], swizzled rows
   __shared__ __attribute__((aligned(16))) u16 Xs3[3][QB * PS];    // x block [s][p], swizzled rows
-  __shared__ __attribute__((aligned(16))) u16 XWh2[2][QB * SP];   // x_s[p] * w_s [s][p], high part
-  __shared__ __attribute__((aligned(16))) u16 XWl2[2][QB * SP];   // low part
+  __shared__ __attribute__((aligned(16))) u16 XWh2[2][QB * PS];   // x_s[p] * w_s [s][p], high part, swizzled rows
+  __shared__ __attribute__((aligned(16))) u16 XWl2[2][QB * PS];   // low part
   __shared__ __attribute__((aligned(16))) u16 Ms2[2][QB * SQ];    // masked decayed C B^T [t][s], high part
   __shared__ __attribute__((aligned(16))) u16 Ml2[2][QB * SQ];    // low part
   __shared__ __attribute__((aligned(16))) u16 Hs2[2][PS * SN];    // state [p][n], high part
   __shared__ __attribute__((aligned(16))) u16 Hl2[2][PS * SN];    // low part
   __shared__ __attribute__((aligned(16))) u16 Zs2[2][QB * PS];    // gate block [t][p], swizzled rows
-  __shared__ __attribute__((aligned(16))) u16 Ys2[2][QB * SP];    // outputs of a block [t][p], bf16
+  __shared__ __attribute__((aligned(16))) u16 Ys2[2][QB * PS];    // outputs of a block [t][p], bf16, swizzled rows
   __shared__ float decS[3][4][QB];   // per token of a block: cum log2(e), gain, e^cum, w = e^{cum_end - cum} gain
   __shared__ float decT[3];          // e^{cum_end}
 
@@ -384,7 +380,7 @@ __global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(3)))
     for (int k = 0; k < NBI; ++k) {
       const int i = dw + 2 * k, q = 64 * i + l, row = q / CPR;
       const int rc = row < lim ? row : lim;
-      load_to_lds(base + ((unsigned)(rc * (int)(G * N)) + 8 * ((q % CPR) ^ (row & (CPR - 1)))),
+      load_to_lds(base + ((unsigned)(rc * (int)(G * N)) + 8 * ((q % CPR) ^ swz_key<CPR>(row))),
                   &Bs2[buf][64 * i * 8]);
     }
   };
@@ -409,7 +405,7 @@ __global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(3)))
       const int64_t t = t0 + row;
       if (t < t_end)
         *reinterpret_cast<u32x4*>(gY + ((b * L + t) * H + h) * P + p0 + 8 * c) =
-            *reinterpret_cast<const u32x4*>(&Ys2[buf][row * SP + 8 * c]);
+            *reinterpret_cast<const u32x4*>(&Ys2[buf][swz<XCPR>(row, 8 * c)]);
     }
   };
 
@@ -505,21 +501,26 @@ __global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(3)))
   };
 
   if (load_wave) {
-    // x of block i+1, B and the gate of block i into LDS; y of block i-2 out; the mask of block i
+    // x of block i+1, B and the gate of block i into LDS; y of block i-2 out; the mask of block i.  A
+    // wave keeps about a dozen vector loads in flight and further ones wait for the oldest, so the next
+    // block's C B^T tile is requested first, ahead of the direct loads and stores.
     int i3 = 0;   // step % 3
     for (int i = 0; i <= nblk; ++i) {
       const int64_t t0 = t_begin + (int64_t)i * QB;
       const int i3n = i3 == 2 ? 0 : i3 + 1;
+      f32x4 rcbn0 = rcb0, rcbn1 = rcb1;
+      if (FULL && cb0 >= 0 && i + 1 < nblk) load_cb(t0 + QB, rcbn0, rcbn1);
       if (i + 1 < nblk) load_xz(gX, t0 + QB, Xs3[i3n]);
       if (FULL && i >= 2) store_y(t0 - 2 * QB, i & 1);
       if (i < nblk) {
         load_b(t0, i & 1);
         if (FULL && a.z != nullptr) load_xz(gZ, t0, Zs2[i & 1]);
         mask_own(i, i3);
-        if (i + 1 < nblk) next_cb(t0 + QB);
       }
       i3 = i3n;
       load_wait();
+      rcb0 = rcbn0;
+      rcb1 = rcbn1;
       lds_sync();
     }
     if (FULL) store_y(t_begin + (int64_t)(nblk - 1) * QB, (nblk - 1) & 1);
@@ -575,7 +576,7 @@ __global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(3)))
             for (int j = 0; j < 4; ++j) yv[j] *= silu_f(bf2f((u16)(zr[j >> 1] >> (16 * (j & 1)))));
           }
           const u32x2 out = {pack_bf2(yv[0], yv[1]), pack_bf2(yv[2], yv[3])};
-          *reinterpret_cast<u32x2*>(&Ys2[jb][tl * SP + p]) = out;
+          *reinterpret_cast<u32x2*>(&Ys2[jb][swz<XCPR>(tl, p)]) = out;
         }
       }
       i3 = i3 == 2 ? 0 : i3 + 1;
@@ -604,8 +605,8 @@ __global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(3)))
           for (int j = 0; j < 2; ++j) {
             const int k0 = 16 * (k2 + j) + 8 * hk;
             fb[j] = frag_cols_swz<CPR>(Bs2[bb], k0, 32 * nq + c16, l16);
-            fh[j] = frag_cols_raw(XWh2[bb], k0, c16, SP, l16);
-            fl[j] = frag_cols_raw(XWl2[bb], k0, c16, SP, l16);
+            fh[j] = frag_cols_swz<XCPR>(XWh2[bb], k0, c16, l16);
+            fl[j] = frag_cols_swz<XCPR>(XWl2[bb], k0, c16, l16);
           }
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
@@ -657,8 +658,8 @@ __global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(3)))
           hi[q >> 1] = v[0];
           lo[q >> 1] = v[1];
         }
-        *reinterpret_cast<u32x4*>(&XWh2[i & 1][row * SP + c8 * 8]) = hi;
-        *reinterpret_cast<u32x4*>(&XWl2[i & 1][row * SP + c8 * 8]) = lo;
+        *reinterpret_cast<u32x4*>(&XWh2[i & 1][swz<XCPR>(row, 8 * c8)]) = hi;
+        *reinterpret_cast<u32x4*>(&XWl2[i & 1][swz<XCPR>(row, 8 * c8)]) = lo;
       }
       i3 = i3 == 2 ? 0 : i3 + 1;
       lds_sync();
