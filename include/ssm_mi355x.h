@@ -222,6 +222,7 @@ size_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int6
  *   S[p][n] = exp(dt*A[h]) S[p][n] + (exp(dt*A[h]) - 1)/A[h] * B[b,t,g,n] * x[b,t,h,p]
  *   y[b,t,h,p] = (sum_n C[b,t,g,n] S[p][n] + Dskip[h] x[b,t,h,p]) * silu(z[b,t,h,p])
  *
+ * With bf16 activations, headdim 64 or 128 and dstate 64 or 128 it is
  * computed blockwise ([ssd] block decomposition): within a block of 64
  * tokens as a causal, decayed matrix product on the matrix cores, across
  * blocks by passing the state.  The block is 64 tokens whatever `chunk_size`
@@ -229,6 +230,10 @@ size_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int6
  * decayed sum of everything before it), so `chunk_size` (64, 128 or 256, the
  * chunk lengths of the pages' chunked form) is validated and otherwise does
  * not change the computation; results are identical for every accepted value.
+ * Every other call (fp32 activations, or other head or state sizes) runs the
+ * same map as its recurrence over tokens ([ssd] the SSM side of the duality),
+ * one token after another per (batch, head), with no workspace: slower on
+ * long sequences with few heads, and exact to fp32 rounding.
  *
  *   x, z, y : (batch, seqlen, nheads, headdim)  act dtype (z NULL for no gate)
  *   dt      : (batch, seqlen, nheads)           delta dtype
@@ -236,9 +241,9 @@ size_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int6
  *   B, C    : (batch, seqlen, ngroups, dstate)  act dtype
  *   Dskip, dt_bias : (nheads) fp32 or NULL
  *   h0, h_final    : (batch, nheads, headdim, dstate) fp32 or NULL
- * Supported: act_dtype SSM_BF16, headdim in {64, 128}, dstate in {64, 128},
- * chunk_size in {64, 128, 256}, nheads % ngroups == 0.  Other valid shapes
- * return SSM_ERR_UNSUPPORTED.
+ * Supported: act_dtype SSM_F32 or SSM_BF16, any headdim, dstate 1 .. 256,
+ * chunk_size in {64, 128, 256}, nheads % ngroups == 0.  dstate above 256
+ * returns SSM_ERR_UNSUPPORTED.
  */
 int ssd_chunk_scan_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C,
                        const float* Dskip, const void* z, const float* dt_bias, int dt_softplus,
@@ -248,12 +253,15 @@ int ssd_chunk_scan_fwd(const void* x, const void* dt, const float* A, const void
                        int act_dtype, int dt_dtype,
                        void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace needed by ssd_chunk_scan_fwd for these shapes: the C_t . B_s
- * products of every 64-token block and group (10 causal 16x16 fp32 tiles,
- * formed once and shared by the group's heads), plus, when the (batch, head)
- * pairs are too few to fill the device and the sequence is split into time
- * chunks, the chunk states carried on the device.  Zero only for seqlen 0.
- * chunk_size does not change it.  Depends on the current device. */
+/* Workspace needed by ssd_chunk_scan_fwd for these shapes: for the blocked
+ * form (headdim 64 or 128, dstate 64 or 128), the C_t . B_s products of every
+ * 64-token block and group (10 causal 16x16 fp32 tiles, formed once and
+ * shared by the group's heads), plus, when the (batch, head) pairs are too
+ * few to fill the device and the sequence is split into time chunks, the
+ * chunk states carried on the device; zero for other shapes and for seqlen 0.
+ * It does not depend on the dtypes, so it is an upper bound: fp32
+ * activations need none.  chunk_size does not change it.  Depends on the
+ * current device. */
 size_t ssd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                            int64_t ngroups, int64_t dstate, int64_t chunk_size);
 

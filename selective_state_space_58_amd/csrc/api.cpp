@@ -262,6 +262,8 @@ size_t ssd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads, int64_
                            int64_t dstate, int64_t chunk_size) {
   if (batch <= 0 || seqlen <= 0 || nheads <= 0 || headdim <= 0 || ngroups <= 0 || dstate <= 0 || chunk_size <= 0)
     return 0;
+  // (the recurrent form needs none; bf16 activations on these shapes take the blocked kernel)
+  if (!ssd_blocked_applies(true, headdim, dstate)) return 0;
   return ssd_ws_bytes(batch, seqlen, nheads, headdim, ngroups, dstate, chunk_size);
 }
 
@@ -287,9 +289,7 @@ int ssd_chunk_scan_fwd(const void* x, const void* dt, const float* A, const void
   if (!elems_ok({batch, seqlen, nheads, headdim}) || !elems_ok({batch, seqlen, ngroups, dstate}) ||
       !elems_ok({batch, nheads, headdim, dstate}))
     return fail(SSM_ERR_SHAPE, "sizes overflow 64-bit indexing");
-  if (act_dtype != SSM_BF16) return fail(SSM_ERR_UNSUPPORTED, "SSD supports bf16 activations only");
-  if (headdim != 64 && headdim != 128) return fail(SSM_ERR_UNSUPPORTED, "SSD supports headdim 64 or 128");
-  if (dstate != 64 && dstate != 128) return fail(SSM_ERR_UNSUPPORTED, "SSD supports dstate 64 or 128");
+  if (dstate > kSsdRecMaxState) return fail(SSM_ERR_UNSUPPORTED, "SSD supports dstate up to 256");
   if (chunk_size != 64 && chunk_size != 128 && chunk_size != 256)
     return fail(SSM_ERR_UNSUPPORTED, "SSD supports chunk_size 64, 128 or 256");
   const size_t ds = dsize(dt_dtype);
@@ -299,9 +299,10 @@ int ssd_chunk_scan_fwd(const void* x, const void* dt, const float* A, const void
     return fail(SSM_ERR_ALIGNMENT, "SSD needs 16-byte aligned x/B/C/z/y/h0/h_final and element-aligned dt");
   if (batch == 0) return SSM_OK;
   hipStream_t st = (hipStream_t)stream;
+  const bool blocked = ssd_blocked_applies(act_dtype == SSM_BF16, headdim, dstate);
   Scratch own;
   void* ws = nullptr;
-  const size_t need = ssd_ws_bytes(batch, seqlen, nheads, headdim, ngroups, dstate, chunk_size);
+  const size_t need = blocked ? ssd_ws_bytes(batch, seqlen, nheads, headdim, ngroups, dstate, chunk_size) : 0;
   int rc = get_workspace(workspace, workspace_bytes, seqlen > 0 ? need : 0, st, &own, &ws);
   if (rc != SSM_OK) return rc;
   SsdArgs a{};
@@ -310,7 +311,7 @@ int ssd_chunk_scan_fwd(const void* x, const void* dt, const float* A, const void
   a.batch = batch; a.seqlen = seqlen; a.nheads = nheads; a.headdim = headdim; a.ngroups = ngroups;
   a.dstate = dstate; a.chunk = chunk_size; a.softplus = dt_softplus; a.dt_bf16 = dt_dtype == SSM_BF16;
   a.ws = ws;
-  return launch_ssd(a, stream);
+  return blocked ? launch_ssd(a, stream) : launch_ssd_rec(a, act_dtype == SSM_F32, stream);
 }
 
 static int step_common(const void* x, const void* delta, const float* A, const void* B, const void* C,

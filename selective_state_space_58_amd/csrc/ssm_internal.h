@@ -160,6 +160,15 @@ SsdPlan plan_ssd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
 size_t ssd_ws_bytes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t ngroups,
                     int64_t dstate, int64_t chunk);
 int launch_ssd(const SsdArgs& a, void* stream);
+// The blocked kernel (matrix cores) takes bf16 activations with headdim 64 or
+// 128 and dstate 64 or 128; every other call runs the SSD as its recurrence
+// (ssd_rec.hip: fp32 or bf16, any headdim, dstate up to kSsdRecMaxState, no
+// workspace).
+inline bool ssd_blocked_applies(bool act_bf16, int64_t headdim, int64_t dstate) {
+  return act_bf16 && (headdim == 64 || headdim == 128) && (dstate == 64 || dstate == 128);
+}
+constexpr int64_t kSsdRecMaxState = 256;
+int launch_ssd_rec(const SsdArgs& a, bool act_f32, void* stream);
 
 // ---------------------------------------------------------------- single-token state update
 // Channel d of batch b belongs to head d / headdim (headdim 1: every channel is

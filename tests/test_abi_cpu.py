@@ -133,8 +133,7 @@ def ssd(lib, **kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(x=None), 1), (dict(y=None), 1), (dict(nheads=3, ngroups=2), 2), (dict(headdim=-1), 2),
-    (dict(act=7), 3), (dict(act=0), 4), (dict(headdim=32), 4), (dict(headdim=96), 4), (dict(headdim=256), 4),
-    (dict(dstate=96), 4), (dict(chunk=100), 4),
+    (dict(act=7), 3), (dict(dstate=257), 4), (dict(dstate=1024, act=0), 4), (dict(chunk=100), 4),
     (dict(x=P + 2), 7),
 ])
 def test_ssd_argument_errors(kw, code):
@@ -160,6 +159,9 @@ def test_workspace_queries():
     assert lib.ssd_workspace_bytes(1, 3000, 4, 64, 1, 128, 256) == 5 * 4 * 64 * 128 * 4 + 256 + 47 * cb
     assert lib.ssd_workspace_bytes(1, 500, 4, 64, 1, 128, 256) == 8 * cb   # chunks would be shorter than 8 blocks
     assert lib.ssd_workspace_bytes(1, 0, 4, 64, 1, 128, 256) == 0
+    # shapes the blocked kernel does not take run the recurrence, which needs none
+    assert lib.ssd_workspace_bytes(2, 8192, 64, 32, 1, 128, 256) == 0
+    assert lib.ssd_workspace_bytes(2, 8192, 64, 64, 1, 16, 256) == 0
 
 
 def step(lib, **kw):
