@@ -67,7 +67,6 @@ __device__ __forceinline__ float bf2f(u16 v) {
   const unsigned u = (unsigned)v << 16;
   return __builtin_bit_cast(float, u);
 }
-__device__ __forceinline__ u16 f2bf(float f) { return __builtin_bit_cast(u16, (__bf16)f); }
 
 __device__ __forceinline__ float softplus_f(float v) {
   const float e = hw_exp2(-fabsf(v) * kLog2e);

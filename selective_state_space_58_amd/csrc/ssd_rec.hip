@@ -110,7 +110,6 @@ __global__ __launch_bounds__(64 * RW) void ssd_rec_kernel(SsdArgs a) {
 
     // ---- the tile's tokens
     const int nt = (int)(L - t0 < RT ? L - t0 : RT);
-#pragma unroll 4
     for (int t = 0; t < nt; ++t) {
       const float e = sE[t];
       const float xv = sX[t * RC + cw];
