@@ -73,6 +73,10 @@ COUNTER_SUMMARIES = {
 }
 
 
+# workloads whose scan line carries the counter summary's traffic
+SCAN_SUMMARY_KEYS = {"scan_bf16_b8_d1536_l2048_n16": "scan_130m", "scan_bf16_b1_d2048_l131072_n16": "scan_long"}
+
+
 def sources_digest(files):
     h = hashlib.sha256()
     for f in files:
@@ -254,6 +258,8 @@ def run_scan(oi, steps, warmup, ssm, workloads, torch, dev, np, ncopy=1):
            "hbm_frac": round(nbytes / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
            "valu_frac": round(slots / VALU_PEAK_TSLOTS, 4), "algorithmic_bytes": nbytes, "elements": elems,
            "workspace_bytes": nb}
+    if cfg["name"] in SCAN_SUMMARY_KEYS:
+        res["traffic"] = measured_traffic(SCAN_SUMMARY_KEYS[cfg["name"]])
     del copies, y, hf, ws
     torch.cuda.empty_cache()
     return res, cfg
