@@ -8,12 +8,12 @@
 //   y_t    = (sum_n C_t,n h_t,n + Dskip_d x_t) * silu(z_t)
 // ("Mamba / SSM complete guide", sec. 5, selective_scan and the block's gate).
 //
-// Mapping to CDNA4.  One wavefront per workgroup.  The 64 lanes are R rows of
-// 64/R columns (R = 4, 8 or 16): lane (row r, column c) holds states
-// [r*S, r*S+S) of channel ch0+c in VGPRs for the whole sequence, so the state
-// never touches memory.  More rows give fewer channels per wave and so more
-// waves for a given layer: the host picks R so that every SIMD gets waves to
-// interleave.  The work per (t, d, n) element is 6 VALU ops plus one
+// Mapping to CDNA4.  The 64 lanes of a wave are R rows of 64/R columns (R = 4,
+// 8 or 16): lane (row r, column c) holds states [r*S, r*S+S) of channel ch0+c
+// in VGPRs for the whole sequence, so the state never touches memory.  (With
+// 16 rows the four lanes of a quad are one channel's rows, see TileShape.)
+// More rows give fewer channels per wave and so more waves for a given layer:
+// the host picks R so that every SIMD gets waves to interleave.  The work per (t, d, n) element is 6 VALU ops plus one
 // v_exp_f32; the per-(t, d) work (softplus, silu, skip, bf16 conversion,
 // stores) is done once, not per state.
 //   * Per time tile (T tokens) the wave stages (dt, x) and silu(z) per
@@ -21,9 +21,10 @@
 //     loads for the next tile are issued before the current tile is scanned.
 //   * The readout sum over n is split over the R rows; every R tokens a
 //     reduce-scatter over the rows (v_permlane32_swap / v_permlane16_swap for
-//     lanes 32 and 16 apart, a DPP row rotation or a swizzle for 8 and 4)
-//     leaves row r with the full sum for token Rk + r, and that lane applies
-//     the skip and gate and stores y for that token.
+//     lanes 32 and 16 apart, a DPP row rotation or a swizzle for 8 and 4, DPP
+//     quad permutations for 2 and 1) leaves row r with the full sum for token
+//     Rk + r, and that lane applies the skip and gate and stores y for that
+//     token.
 //   * Lanes whose channel is past `dim` load from a clamped (valid) address
 //     and compute values that are never stored; a column never mixes with
 //     another column, so nothing leaks.  Tokens past the end of the slice get
@@ -37,6 +38,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <utility>
 
 #include "device_common.h"
 #include "ssm_internal.h"
@@ -79,10 +82,10 @@ struct Raw<false> {
 
 // log(1 + e^v) without overflow.  Short form: log1p(e^-|v|) as log2(1 + e)*ln2,
 // whose absolute error (< 6e-8) is far below bf16 resolution of the output.
+// For v > 17, 1 + e rounds to 1 and the result is v itself; max(v, 0) is a median of three.
 __device__ __forceinline__ float softplus_short(float v) {
   const float e = hw_exp2(-fabsf(v) * kLog2e);
-  const float r = fmaxf(v, 0.f) + hw_log2(1.f + e) * kLn2;
-  return v > 20.f ? v : r;
+  return __builtin_amdgcn_fmed3f(v, 0.f, __builtin_inff()) + hw_log2(1.f + e) * kLn2;
 }
 
 // Accurate form: log1p(e^-|v|) by its series when e^-|v| < 1/16.
@@ -109,7 +112,7 @@ __device__ __forceinline__ float bits_f(unsigned u) { return __builtin_bit_cast(
 __device__ __forceinline__ unsigned f_bits(float f) { return __builtin_bit_cast(unsigned, f); }
 
 // One level of the row reduce-scatter: lanes whose bit `D` (a lane distance
-// of 32, 16, 8 or 4) is clear end with a + a(lane ^ D), the others with
+// of 32, 16, 8, 4, 2 or 1) is clear end with a + a(lane ^ D), the others with
 // b + b(lane ^ D).
 template <int D>
 __device__ __forceinline__ float pair_sum(float a, float b) {
@@ -127,12 +130,33 @@ __device__ __forceinline__ float pair_sum(float a, float b) {
     int other;
     if constexpr (D == 8) {
       other = __builtin_amdgcn_update_dpp(0, (int)f_bits(send), 0x128, 0xf, 0xf, false);  // row_ror:8 = lane ^ 8
+    } else if constexpr (D == 2) {
+      other = __builtin_amdgcn_mov_dpp((int)f_bits(send), 0x4E, 0xf, 0xf, true);   // quad_perm [2,3,0,1]
+    } else if constexpr (D == 1) {
+      other = __builtin_amdgcn_mov_dpp((int)f_bits(send), 0xB1, 0xf, 0xf, true);   // quad_perm [1,0,3,2]
     } else {
       static_assert(D == 4, "row distance");
       other = __builtin_amdgcn_ds_swizzle((int)f_bits(send), 0x101f);  // bit mode: xor 4 within 32 lanes
     }
     return keep + bits_f((unsigned)other);
   }
+}
+
+// Value J of each quad of lanes in all four lanes of the quad (DPP quad_perm [J,J,J,J]).  As the
+// operand of a VALU op the broadcast folds into the op itself.
+template <int J>
+__device__ __forceinline__ float quad_bcast(float v) {
+  return bits_f((unsigned)__builtin_amdgcn_mov_dpp((int)f_bits(v), J * 0x55, 0xf, 0xf, true));
+}
+
+// Calls f(std::integral_constant<int, J>) for J = 0 .. N-1 (indices usable as template arguments).
+template <int... J, class F>
+__device__ __forceinline__ void static_for_impl(std::integer_sequence<int, J...>, F&& f) {
+  (f(std::integral_constant<int, J>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(std::make_integer_sequence<int, N>{}, f);
 }
 
 // Lanes are R rows of 64/R (row = lane / (64/R)).  p[j] holds, in every lane,
@@ -157,6 +181,19 @@ __device__ __forceinline__ float reduce_scatter_rows(const float (&p)[R]) {
     }
   }
   return v[0];
+}
+
+// The same for the 16-row quad layout (row = 4 * lane bits 4-5 + lane bits 0-1): the levels run over
+// lane bits 5, 4, 1 and 0, which leaves row r with token r's sum as above.
+__device__ __forceinline__ float reduce_scatter_quad16(const float (&p)[16]) {
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = pair_sum<32>(p[i], p[i + 8]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = pair_sum<16>(v[i], v[i + 4]);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) v[i] = pair_sum<2>(v[i], v[i + 2]);
+  return pair_sum<1>(v[0], v[1]);
 }
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -187,6 +224,21 @@ struct TileShape {
   static constexpr int T = R == 4 ? 32 : (S >= 16 ? 16 : 64);   // tokens per LDS tile
   static constexpr int KX = T / R;                 // (token, channel) items per lane per tile
   static constexpr int KB = T * NP / 64;           // B (and C) items per lane per tile
+  // lane -> (row, column).  4 and 8 rows: lane = row * CH + column.  16 rows (4 channels, one
+  // state per lane): the column is lane bits 2-3 and the row 4 * (lane bits 4-5) + lane bits 0-1,
+  // so that the four lanes of a quad belong to one channel.
+  static __device__ __forceinline__ int row_of(int lane) { return R == 16 ? ((lane >> 4) << 2) | (lane & 3) : lane / CH; }
+  static __device__ __forceinline__ int col_of(int lane) { return R == 16 ? (lane >> 2) & 3 : lane % CH; }
+  // Row stride (in pairs) of the staged (dt, x) tile of a W-wave workgroup, and of the gate tile
+  // unless GZ2.  The 16-row layout reads four token rows at once (one per quad lane): rows of 20
+  // pairs put those reads on distinct LDS banks, where rows of 16 pairs would share them.
+  template <int W>
+  static constexpr int xs() { return CH * W + (R == 16 ? 4 : 0); }
+  // The 16-row layout's gate tile holds (D x, silu z) pairs, read once per 16 tokens by the
+  // readout (sixteen rows at once, on distinct banks with rows of 20 pairs as well).
+  static constexpr bool GZ2 = R == 16;
+  template <int W>
+  static constexpr int gz_floats() { return (GZ2 ? 2 : 1) * T * xs<W>(); }
 };
 
 // GAIN: kGainShort (e^q - 1)/a, kGainAccurate (series near q = 0), kGainEuler dt.
@@ -210,10 +262,12 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
   // h' = E*h + ((E - 1)/a)*B*x; the scale is undone when the state is stored.
   constexpr bool SCALED = !FULL && GAIN == kGainShort;
   static_assert(VEC || W == 1, "the scalar tile path runs one wave per workgroup");
-  constexpr int WCH = W * CH;                 // channels per workgroup (LDS row width)
+  constexpr int WCH = W * CH;                 // channels per workgroup
+  constexpr int XS = TS::template xs<W>();    // LDS row stride of s_dx (and s_gz, in pairs when GZ2)
+  constexpr bool GZ2 = TS::GZ2;
   const int tid = threadIdx.x;                // thread in the workgroup
   const int lane = tid % 64;
-  const int r = lane / CH, c = lane % CH;
+  const int r = TS::row_of(lane), c = TS::col_of(lane);
   const int wc = w * CH + c;                  // this lane's channel within the workgroup
   const int64_t L = a.seqlen, dim = a.dim, N = a.dstate;
   const int64_t ch = ch0 + c;
@@ -305,8 +359,13 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
       const float v = Raw<DB>::f32(pd[k]) + bias;
       float dt = a.softplus ? (ACC ? softplus_f(v) : softplus_short(v)) : v;
       dt = (t < nvalid) ? dt : 0.f;
-      s_dx[t * WCH + wc] = make_float2(dt, Raw<XB>::f32(px[k]));
-      if (FULL) s_gz[t * WCH + wc] = has_z ? silu_f(Raw<XB>::f32(pz[k])) : 1.f;
+      const float xv = Raw<XB>::f32(px[k]);
+      s_dx[t * XS + wc] = make_float2(dt, xv);
+      if (FULL) {
+        const float gv = has_z ? silu_f(Raw<XB>::f32(pz[k])) : 1.f;
+        if constexpr (GZ2) reinterpret_cast<float2*>(s_gz)[t * XS + wc] = make_float2(Dv * xv, gv);
+        else s_gz[t * XS + wc] = gv;
+      }
     }
 #pragma unroll
     for (int j = 0; j < KB; ++j) {
@@ -357,9 +416,12 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
   VTB vb[CBN], vc[CBN];
   const int vc0 = (tid % XROW) * EX;                        // this thread's first workgroup channel
   const int64_t chw0 = ch0 - (int64_t)w * CH;               // first channel of the workgroup
-  float vbias[EX];
+  float vbias[EX], vDs[EX];
 #pragma unroll
-  for (int e = 0; e < EX; ++e) vbias[e] = (VEC && a.delta_bias != nullptr) ? a.delta_bias[chw0 + vc0 + e] : 0.f;
+  for (int e = 0; e < EX; ++e) {
+    vbias[e] = (VEC && a.delta_bias != nullptr) ? a.delta_bias[chw0 + vc0 + e] : 0.f;
+    vDs[e] = (VEC && GZ2 && FULL && a.Dskip != nullptr) ? a.Dskip[chw0 + vc0 + e] : 0.f;
+  }
   // (the element is copied to a scalar first: bit-casting a vector-element
   // lvalue directly reads element 0 with this compiler)
   auto raw_elem = [](const auto& v, int e) -> float {
@@ -421,40 +483,73 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
       if (FULL) vc[q] = *reinterpret_cast<const VTB*>(cb + off);
     }
   };
-  auto stage_vec = [&](int64_t t0) {
-    const int64_t nvalid = t_stop - t0;
+  // (delta per token, gate, softplus) are uniform over the call: each combination stages through
+  // code of its own, without per-item selects between the forms
+  auto stage_vec_x = [&](int64_t nvalid, auto tokc, auto gatec, auto spc) {
+    constexpr bool TOK = decltype(tokc)::value, GATE = decltype(gatec)::value, SP = decltype(spc)::value;
 #pragma unroll
     for (int q = 0; q < CXN; ++q) {
       const int k = tid + NT * q;
       const int tl = k / XROW;
-      const bool ok = tl < nvalid;
       float dxv[2 * EX];
       const unsigned dtok_bits = vd[q][0][0];
 #pragma unroll
       for (int e = 0; e < EX; ++e) {
-        const float v = (tok_delta ? __builtin_bit_cast(float, dtok_bits) : raw_delta(vd[q], e)) + vbias[e];
-        float dt = a.softplus ? (ACC ? softplus_f(v) : softplus_short(v)) : v;
-        dxv[2 * e] = ok ? dt : 0.f;
+        const float v = (TOK ? __builtin_bit_cast(float, dtok_bits) : raw_delta(vd[q], e)) + vbias[e];
+        dxv[2 * e] = SP ? (ACC ? softplus_f(v) : softplus_short(v)) : v;
         dxv[2 * e + 1] = raw_elem(vx[q], e);
       }
-      float4* dst = reinterpret_cast<float4*>(s_dx + tl * WCH + vc0);
+      float4* dst = reinterpret_cast<float4*>(s_dx + tl * XS + vc0);
 #pragma unroll
       for (int e = 0; e < EX / 2; ++e) dst[e] = make_float4(dxv[4 * e], dxv[4 * e + 1], dxv[4 * e + 2], dxv[4 * e + 3]);
+      // tokens past the end of the slice: dt = 0 (the same thread overwrites what it just wrote)
+      if (nvalid < T && tl >= nvalid) {
+#pragma unroll
+        for (int e = 0; e < EX; ++e) s_dx[tl * XS + vc0 + e].x = 0.f;
+      }
       if (FULL) {
         float gzv[EX];
 #pragma unroll
-        for (int e = 0; e < EX; ++e) gzv[e] = has_z ? silu_f(raw_elem(vz[q], e)) : 1.f;
-        if constexpr (EX % 4 == 0) {
-          float4* gd4 = reinterpret_cast<float4*>(s_gz + tl * WCH + vc0);
+        for (int e = 0; e < EX; ++e) gzv[e] = GATE ? silu_f(raw_elem(vz[q], e)) : 1.f;
+        if constexpr (GZ2) {
+          // (D x, silu z) pairs
+          float4* gd4 = reinterpret_cast<float4*>(s_gz + 2 * (tl * XS + vc0));
+#pragma unroll
+          for (int e = 0; e < EX / 2; ++e)
+            gd4[e] = make_float4(vDs[2 * e] * dxv[4 * e + 1], gzv[2 * e], vDs[2 * e + 1] * dxv[4 * e + 3], gzv[2 * e + 1]);
+        } else if constexpr (EX % 4 == 0) {
+          float4* gd4 = reinterpret_cast<float4*>(s_gz + tl * XS + vc0);
 #pragma unroll
           for (int e = 0; e < EX / 4; ++e)
             gd4[e] = make_float4(gzv[4 * e], gzv[4 * e + 1], gzv[4 * e + 2], gzv[4 * e + 3]);
         } else {
           // two channels per chunk (fp32, 8 rows of 32 states): 8-byte writes
-          float2* gd2 = reinterpret_cast<float2*>(s_gz + tl * WCH + vc0);
+          float2* gd2 = reinterpret_cast<float2*>(s_gz + tl * XS + vc0);
 #pragma unroll
           for (int e = 0; e < EX / 2; ++e) gd2[e] = make_float2(gzv[2 * e], gzv[2 * e + 1]);
         }
+      }
+    }
+  };
+  auto stage_vec = [&](int64_t t0) {
+    const int64_t nvalid = t_stop - t0;
+    const std::true_type Y;
+    const std::false_type N;
+    if (tok_delta) {
+      if (has_z) {
+        if (a.softplus) stage_vec_x(nvalid, Y, Y, Y);
+        else stage_vec_x(nvalid, Y, Y, N);
+      } else {
+        if (a.softplus) stage_vec_x(nvalid, Y, N, Y);
+        else stage_vec_x(nvalid, Y, N, N);
+      }
+    } else {
+      if (has_z) {
+        if (a.softplus) stage_vec_x(nvalid, N, Y, Y);
+        else stage_vec_x(nvalid, N, Y, N);
+      } else {
+        if (a.softplus) stage_vec_x(nvalid, N, N, Y);
+        else stage_vec_x(nvalid, N, N, N);
       }
     }
 #pragma unroll
@@ -504,13 +599,95 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
     const int nval32 = nvalid < T ? (int)nvalid : T;
     // Readout of the group of R tokens starting at tg: row r gets token tg + r.
     auto emit = [&](int tg, const float (&pr)[R]) {
-      const float tot = reduce_scatter_rows<R>(pr);
+      float tot;
+      if constexpr (R == 16 && S == 1) tot = reduce_scatter_quad16(pr);
+      else tot = reduce_scatter_rows<R>(pr);
       const int tl = tg + r;
-      const float xv = s_dx[tl * WCH + wc].y;
-      const float yv = fmaf(Dv, xv, tot) * s_gz[tl * WCH + wc];
+      const float xv = s_dx[tl * XS + wc].y;
+      const float yv = fmaf(Dv, xv, tot) * s_gz[tl * XS + wc];
       if (full_tile || (ch_ok && tl < nval32)) yb[urow(tl) * dim32 + (uint32_t)c] = (TX)yv;
     };
-    if constexpr (S < 16) {
+    if constexpr (R == 16 && S == 1) {
+      // 16 rows of one state, quads of lanes on one channel.  Per step of U = 4 tokens a lane
+      // reads the (dt, x) pair of one of them, token tb + lane % 4; the multiplies that use a
+      // token's dt and x take it from that quad lane by a DPP broadcast folded into the
+      // instruction, so the (dt, x) tile is read once per quad rather than once per lane.
+      // Each lane reads its row's (B, C) pair per token.  Every 16 tokens end with the
+      // reduce-scatter over the rows; the y values wait in registers for the tile's end.
+      constexpr int U = 4;
+      const int q4 = lane & 3;
+      struct Step16 {
+        float2 dx;
+        float2 bc[U];
+      };
+      auto load16 = [&](int tb, Step16& g) {
+        g.dx = s_dx[(tb + q4) * XS + wc];
+#pragma unroll
+        for (int j = 0; j < U; ++j) g.bc[j] = *reinterpret_cast<const float2*>(s_bc + ((tb + j) * R + r) * 2);
+      };
+      // exp(dt*a) one step ahead, as in the general path below
+      auto exp16 = [&](const Step16& g, float (&E)[U]) {
+        static_for<U>([&](auto jc) {
+          constexpr int j = decltype(jc)::value;
+          E[j] = hw_exp2(quad_bcast<j>(g.dx.x) * a2[0]);
+        });
+      };
+      Step16 cur, nxt;
+      float Ecur[U], Enxt[U];
+      load16(0, cur);
+      exp16(cur, Ecur);
+      float pr[16];
+      float yq[T / 16];   // y of token 16 g + r
+      constexpr int kStepUnroll = T / U;
+#pragma unroll kStepUnroll
+      for (int tb = 0; tb < T; tb += U) {
+        if (tb + U < T) {
+          load16(tb + U, nxt);
+          exp16(nxt, Enxt);
+        }
+        if (SAVE && tb % kSaveTile == 0) save_state(t0 + tb);
+        static_for<U>([&](auto jc) {
+          constexpr int j = decltype(jc)::value;
+          const float E = Ecur[j];
+          const float u = quad_bcast<j>(cur.dx.y) * cur.bc[j].x;   // B x
+          if constexpr (SCALED) {
+            h[0] = fmaf(E, h[0], fmaf(E, u, -u));
+          } else {
+            float g;
+            if constexpr (GAIN == kGainShort) {
+              g = fmaf(E, ia[0], -ia[0]);
+            } else {
+              const float dt = quad_bcast<j>(cur.dx.x);
+              g = GAIN == kGainEuler ? dt : zoh_gain_accurate(E, dt, av[0], ia[0]);
+            }
+            h[0] = fmaf(E, h[0], g * u);
+          }
+          if (FULL) pr[(tb + j) % 16] = cur.bc[j].y * h[0];
+        });
+        if (!FULL) dsum += cur.dx.x;   // this lane's token of the step (the quad adds up at the end)
+        if (FULL && (tb + U) % 16 == 0) {
+          const int tl = tb + U - 16 + r;
+          const float2 e = reinterpret_cast<const float2*>(s_gz)[tl * XS + wc];   // (D x, silu z)
+          yq[tb / 16] = (reduce_scatter_quad16(pr) + e.x) * e.y;
+        }
+        if (tb + U < T) {
+          cur = nxt;
+#pragma unroll
+          for (int j = 0; j < U; ++j) Ecur[j] = Enxt[j];
+        }
+      }
+      // the tile's stores after its loop, which then has no branches
+      if (FULL) {
+        if (full_tile) {
+#pragma unroll
+          for (int g = 0; g < T / 16; ++g) yb[urow(16 * g + r) * dim32 + (uint32_t)c] = (TX)yq[g];
+        } else {
+#pragma unroll
+          for (int g = 0; g < T / 16; ++g)
+            if (ch_ok && 16 * g + r < nval32) yb[urow(16 * g + r) * dim32 + (uint32_t)c] = (TX)yq[g];
+        }
+      }
+    } else if constexpr (S < 16) {
     // Operands of one step of U = 4 tokens: (dt, x) and this row's B/C
     // slices.  The next step's operands are read from LDS while the current
     // step is computed, so LDS latency overlaps the VALU work; a group of R
@@ -525,7 +702,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
 #pragma unroll
       for (int j = 0; j < U; ++j) {
         const int tt = tb + j;
-        g.dx[j] = s_dx[tt * WCH + wc];
+        g.dx[j] = s_dx[tt * XS + wc];
         const float* bc = s_bc + ((tt * R + r) * 2) * S;
         if constexpr (S >= 4) {
 #pragma unroll
@@ -607,7 +784,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
         for (int j = 0; j < R; ++j) {
           const int tt = tb + j;
           if (SAVE && (tt % kSaveTile) == 0) save_state(t0 + tt);
-          const float2 dx = s_dx[tt * WCH + wc];
+          const float2 dx = s_dx[tt * XS + wc];
           const float4* bc4 = reinterpret_cast<const float4*>(s_bc + ((tt * R + r) * 2) * S);
           float acc = 0.f;
 #pragma unroll
@@ -655,6 +832,11 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
       if (n < N) hout[(b * dim + ch) * N + n] = h[s];
     }
   }
+  if constexpr (!FULL && R == 16 && S == 1) {
+    // each lane summed the dt of the tokens it read (one in four): add up the quad
+    dsum += bits_f((unsigned)__builtin_amdgcn_mov_dpp((int)f_bits(dsum), 0xB1, 0xf, 0xf, true));
+    dsum += bits_f((unsigned)__builtin_amdgcn_mov_dpp((int)f_bits(dsum), 0x4E, 0xf, 0xf, true));
+  }
   if (!FULL && a.nchunks > 1 && r == 0 && ch_ok) a.ws_dsum[chunk * a.batch * dim + b * dim + ch] = dsum;
 }
 
@@ -673,8 +855,9 @@ template <int RR, bool XB, bool DB, int S, int MODE, bool VEC, int W>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(scan_waves_per_simd<RR, S>())))
 void scan_kernel(ScanArgs a, int64_t groups_per_batch) {
   using TS = TileShape<RR, S>;
-  __shared__ __attribute__((aligned(16))) float2 s_dx[TS::T * TS::CH * W];
-  __shared__ __attribute__((aligned(16))) float s_gz[TS::T * TS::CH * W];
+  constexpr int XS = TS::template xs<W>();
+  __shared__ __attribute__((aligned(16))) float2 s_dx[TS::T * XS];
+  __shared__ __attribute__((aligned(16))) float s_gz[TS::template gz_floats<W>()];
   __shared__ __attribute__((aligned(16))) float s_bc[TS::T * TS::R * 2 * S];
 
   // XCD-aware order: dispatch id i runs on XCD i % 8; give each XCD a contiguous
@@ -689,7 +872,7 @@ void scan_kernel(ScanArgs a, int64_t groups_per_batch) {
   const int64_t chunk = blockIdx.y;
 
   const int lane = threadIdx.x % 64;
-  const int r = lane / TS::CH, c = lane % TS::CH;
+  const int r = TS::row_of(lane), c = TS::col_of(lane);
   const int64_t ch = ch0 + c;
   float a2[S], ia[S], av[S];
   bool tiny = false;
