@@ -56,16 +56,19 @@ constexpr int NS = 16;        // states (4 rows x 4 per lane)
 // rows land 18 words apart (16 distinct bank pairs) and the 16 groups 2 words
 // apart.
 __device__ __forceinline__ int ix_dx(int t, int w) { return t * (W + 1) + (t >> 4) + w; }
-// B and C of token t start at this float index: rows of 20 floats (16-byte
-// aligned) plus 4 floats per 16 rows; 8 consecutive rows, or the 8 groups of
-// a 16-byte read, start in 8 distinct 4-bank quads.
-__device__ __forceinline__ int ix_bc(int t) { return t * 20 + ((t >> 4) << 2); }
+// B and C of token t = 16 g + j, states 4 r .. 4 r + 3: 16-byte slot
+// (4 j + r) * 16 + g.  The compute reads of token j of every group (lane
+// (r, g) reads slot (4 j + r) 16 + g) are then one contiguous 1 KB block, and
+// the staging threads, which take the tile's tokens in the transposed order
+// t = 16 (k mod 16) + k / 16, write 16 consecutive slots per 16 lanes.  (Rows
+// of 20 floats, read a token per group, cost twice the LDS cycles.)
+__device__ __forceinline__ int ix_b4(int j, int r, int g) { return (j * 4 + r) * 16 + g; }
 // y of (token t, channel w), fp32: rows of W + 1 floats plus one per 16 rows,
 // so the 64 lanes writing tokens 16 g + 4 jq + r fall at most two to a bank,
 // and so do the threads reading back consecutive rows.
 __device__ __forceinline__ int ix_y(int t, int w) { return t * (W + 1) + (t >> 4) + w; }
 constexpr int DX_SLOTS = T * (W + 1) + T / 16;
-constexpr int BC_FLOATS = T * 20 + (T / 16) * 4;
+constexpr int BC_FLOATS = T * NS;
 constexpr int Y_FLOATS = T * (W + 1) + T / 16;
 static_assert(W == 8, "the padded layouts are laid out for 8 channels per workgroup");
 
@@ -169,6 +172,7 @@ __device__ __forceinline__ void long_body(const ScanArgs& a, int64_t b, int64_t 
   const bool xrole = NT == T || tid < T;
   const bool bcrole = NT == T || tid >= T;
   const int trow = tid % T;
+  const int brow = 16 * (trow & 15) + (trow >> 4);   // the B/C row this thread stages (see ix_b4)
   float bias[W];
 #pragma unroll
   for (int e = 0; e < W; ++e) bias[e] = (xrole && a.delta_bias != nullptr) ? a.delta_bias[chw0 + e] : 0.f;
@@ -176,6 +180,8 @@ __device__ __forceinline__ void long_body(const ScanArgs& a, int64_t b, int64_t 
   auto fetch = [&](int64_t t0) {
     int64_t row = t0 + trow;
     row = row < L ? row : L - 1;   // the tail loads a valid row; its tokens get dt = 0
+    int64_t rowb = t0 + brow;
+    rowb = rowb < L ? rowb : L - 1;
     if (xrole) {
       const size_t ox = (size_t)(b * L + row) * rowx + (size_t)chw0 * sizeof(RX);
       const size_t od = (size_t)(b * L + row) * rowd + (size_t)chw0 * sizeof(RD);
@@ -184,7 +190,7 @@ __device__ __forceinline__ void long_body(const ScanArgs& a, int64_t b, int64_t 
       if (has_z) load_words<XWD>(pz, gz + ox);
     }
     if (bcrole) {
-      const size_t ob = (size_t)(b * L + row) * NS * sizeof(RX);
+      const size_t ob = (size_t)(b * L + rowb) * NS * sizeof(RX);
       load_words<BWD>(pb, gB + ob);
       load_words<BWD>(pc, gC + ob);
     }
@@ -212,13 +218,14 @@ __device__ __forceinline__ void long_body(const ScanArgs& a, int64_t b, int64_t 
       }
     }
     if (bcrole) {
-      float4* db = reinterpret_cast<float4*>(s_b + buf * BC_FLOATS + ix_bc(trow));
-      float4* dc = reinterpret_cast<float4*>(s_c + buf * BC_FLOATS + ix_bc(trow));
+      float4* db = reinterpret_cast<float4*>(s_b + buf * BC_FLOATS);
+      float4* dc = reinterpret_cast<float4*>(s_c + buf * BC_FLOATS);
 #pragma unroll
       for (int q = 0; q < NS / 4; ++q) {
-        db[q] = make_float4(elem(pb, 4 * q, RX{}), elem(pb, 4 * q + 1, RX{}), elem(pb, 4 * q + 2, RX{}),
+        const int o = ix_b4(brow & 15, q, brow >> 4);
+        db[o] = make_float4(elem(pb, 4 * q, RX{}), elem(pb, 4 * q + 1, RX{}), elem(pb, 4 * q + 2, RX{}),
                             elem(pb, 4 * q + 3, RX{}));
-        dc[q] = make_float4(elem(pc, 4 * q, RX{}), elem(pc, 4 * q + 1, RX{}), elem(pc, 4 * q + 2, RX{}),
+        dc[o] = make_float4(elem(pc, 4 * q, RX{}), elem(pc, 4 * q + 1, RX{}), elem(pc, 4 * q + 2, RX{}),
                             elem(pc, 4 * q + 3, RX{}));
       }
     }
@@ -274,7 +281,7 @@ __device__ __forceinline__ void long_body(const ScanArgs& a, int64_t b, int64_t 
 #pragma unroll
     for (int j = 0; j < TAU; ++j) {
       const float2 dx = sdx[ix_dx(tg + j, w)];
-      const float4 bq = s_b4[(ix_bc(tg + j) >> 2) + r];
+      const float4 bq = s_b4[ix_b4(j, r, g)];
       const float bv[4] = {bq.x, bq.y, bq.z, bq.w};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -315,7 +322,7 @@ __device__ __forceinline__ void long_body(const ScanArgs& a, int64_t b, int64_t 
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int j = 4 * jq + jj;
-        const float4 cq = s_c4[(ix_bc(tg + j) >> 2) + r];
+        const float4 cq = s_c4[ix_b4(j, r, g)];
         const float cv[4] = {cq.x, cq.y, cq.z, cq.w};
         float acc = 0.f;
 #pragma unroll
