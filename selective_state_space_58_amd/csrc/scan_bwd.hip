@@ -182,32 +182,52 @@ __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64
   const RX* gB = (const RX*)a.B;
   const RX* gC = (const RX*)a.C;
 
-  // Stage tile k: per (token, channel) one item per thread, per (token, state) one item per thread.
-  auto stage = [&](int k, bool full) {
+  // Staging of tile k: per (token, channel) one item per thread, per (token, state) one item per
+  // thread.  fetch() loads a tile's items into registers one tile ahead of put_tile(), which converts
+  // them and writes them to LDS, so the loads' latency overlaps the previous tile's work.
+  const int s_tl = tid / BWC, s_cc = tid % BWC;             // (token, channel) item of this thread
+  const int64_t s_chl = chw0 + s_cc < dim ? chw0 + s_cc : dim - 1;
+  const float s_bias = a.delta_bias != nullptr ? a.delta_bias[s_chl] : 0.f;
+  const int b_tl = tid / BR, b_n = tid % BR;                // (token, state) item of this thread
+  RD pre_d;
+  RX pre_x, pre_do, pre_z, pre_b, pre_c;
+  auto fetch = [&](int k, bool full) {
     const int64_t t0 = (int64_t)k * BT;
     {
-      const int tl = tid / BWC, cc = tid % BWC;
-      const int64_t t = t0 + tl;
-      const int64_t chl = chw0 + cc < dim ? chw0 + cc : dim - 1;
-      const bool ok = t < L && chw0 + cc < dim;
+      const int64_t t = t0 + s_tl;
       const int64_t row = b * L + grow(t < L ? t : L - 1);
-      const int64_t i = row * dim + chl;
-      const float v = Raw<DB>::f32(gd[a.tok_delta ? row : i]) + ((a.delta_bias != nullptr) ? a.delta_bias[chl] : 0.f);
-      const float dt = ok ? (a.softplus ? softplus_f(v) : v) : 0.f;
-      sm.dx[tid] = make_float2(dt, Raw<XB>::f32(gx[i]));
+      const int64_t i = row * dim + s_chl;
+      pre_d = gd[a.tok_delta ? row : i];
+      pre_x = gx[i];
       if (full) {
-        sm.v[tid] = v;
-        sm.dout[tid] = ok ? Raw<XB>::f32(gdo[i]) : 0.f;
-        sm.z[tid] = (a.z != nullptr) ? Raw<XB>::f32(gz[i]) : 0.f;
+        pre_do = gdo[i];
+        if (a.z != nullptr) pre_z = gz[i];
       }
     }
     {
-      const int tl = tid / BR, n = tid % BR;
-      const int64_t t = t0 + tl;
-      const bool ok = t < L && n0 + n < N;
-      const int64_t i = (b * L + grow(t < L ? t : L - 1)) * N + (n0 + n < N ? n0 + n : 0);
-      sm.bc[(tl * BR + n) * 2] = ok ? Raw<XB>::f32(gB[i]) : 0.f;
-      if (full) sm.bc[(tl * BR + n) * 2 + 1] = ok ? Raw<XB>::f32(gC[i]) : 0.f;
+      const int64_t t = t0 + b_tl;
+      const int64_t i = (b * L + grow(t < L ? t : L - 1)) * N + (n0 + b_n < N ? n0 + b_n : 0);
+      pre_b = gB[i];
+      if (full) pre_c = gC[i];
+    }
+  };
+  auto put_tile = [&](int k, bool full) {
+    const int64_t t0 = (int64_t)k * BT;
+    {
+      const bool ok = t0 + s_tl < L && chw0 + s_cc < dim;
+      const float v = Raw<DB>::f32(pre_d) + s_bias;
+      const float dt = ok ? (a.softplus ? softplus_f(v) : v) : 0.f;
+      sm.dx[tid] = make_float2(dt, Raw<XB>::f32(pre_x));
+      if (full) {
+        sm.v[tid] = v;
+        sm.dout[tid] = ok ? Raw<XB>::f32(pre_do) : 0.f;
+        sm.z[tid] = (a.z != nullptr) ? Raw<XB>::f32(pre_z) : 0.f;
+      }
+    }
+    {
+      const bool ok = t0 + b_tl < L && n0 + b_n < N;
+      sm.bc[(b_tl * BR + b_n) * 2] = ok ? Raw<XB>::f32(pre_b) : 0.f;
+      if (full) sm.bc[(b_tl * BR + b_n) * 2 + 1] = ok ? Raw<XB>::f32(pre_c) : 0.f;
     }
   };
   // Per (token, channel) gradient k (0 dx, 1 ddelta, 2 dz) at element i: written
@@ -235,11 +255,14 @@ __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64
   // ---- forward: the state at the start of every tile into the workspace (unless the forward pass
   // already stored the states at every tile start)
   float h = (a.h0 != nullptr && nok) ? a.h0[hidx] : 0.f;
-  for (int k = 0; k < (a.saved != nullptr ? 0 : ntile); ++k) {
+  const int nck = a.saved != nullptr ? 0 : ntile;
+  if (nck > 0) fetch(0, false);
+  for (int k = 0; k < nck; ++k) {
     if (nok) a.ws_ckpt[(int64_t)k * slice + cidx] = h;
     lds_sync();
-    stage(k, false);
+    put_tile(k, false);
     lds_sync();
+    if (k + 1 < nck) fetch(k + 1, false);
 #pragma unroll 4
     for (int tl = 0; tl < BT; ++tl) {
       const float2 dx = sm.dx[tl * BWC + wc];
@@ -255,11 +278,13 @@ __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64
   float* hw = sm.h + w * BT * 64;
   float* rw = sm.red + w * BT * BR * 2;
   const int64_t per_group = a.batch * L * BR;
+  if (ntile > 0) fetch(ntile - 1, true);
   for (int k = ntile - 1; k >= 0; --k) {
     const int64_t t0 = (int64_t)k * BT;
     lds_sync();
-    stage(k, true);
+    put_tile(k, true);
     lds_sync();
+    if (k > 0) fetch(k - 1, true);
     // recompute the tile's states and decays (into LDS) and its readout; y gives dz and dy
     const float hstart = !nok ? 0.f
                                : (a.saved != nullptr ? a.saved[((int64_t)k * a.batch + b) * dim * N + ch * N + n0 + r]
