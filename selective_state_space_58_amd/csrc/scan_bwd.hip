@@ -279,16 +279,29 @@ __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64
   float* rw = sm.red + w * BT * BR * 2;
   const int64_t per_group = a.batch * L * BR;
   if (ntile > 0) fetch(ntile - 1, true);
+  // the state entering tile k (stored by the forward or by the pass above), also one tile ahead
+  float pre_h = 0.f;
+  auto fetch_h = [&](int k) {
+    pre_h = !nok ? 0.f
+                 : (a.saved != nullptr ? a.saved[((int64_t)k * a.batch + b) * dim * N + ch * N + n0 + r]
+                                       : a.ws_ckpt[(int64_t)k * slice + cidx]);
+  };
+  if (ntile > 0) fetch_h(ntile - 1);
+  // Barriers of a reverse tile: one after the staging (its items go to every wave) and one after
+  // the adjoint (the dB/dC partials add the four waves' sums).  The recompute's states, dy and
+  // readout, and the adjoint's partial sums, are per wave and need none; the barrier after the
+  // adjoint also orders the next tile's staging after every wave's reads of this tile.
+  lds_sync();
   for (int k = ntile - 1; k >= 0; --k) {
     const int64_t t0 = (int64_t)k * BT;
-    lds_sync();
     put_tile(k, true);
     lds_sync();
-    if (k > 0) fetch(k - 1, true);
+    const float hstart = pre_h;
+    if (k > 0) {
+      fetch(k - 1, true);
+      fetch_h(k - 1);
+    }
     // recompute the tile's states and decays (into LDS) and its readout; y gives dz and dy
-    const float hstart = !nok ? 0.f
-                               : (a.saved != nullptr ? a.saved[((int64_t)k * a.batch + b) * dim * N + ch * N + n0 + r]
-                                                     : a.ws_ckpt[(int64_t)k * slice + cidx]);
     float hs = hstart;
 #pragma unroll
     for (int tb = 0; tb < BT; tb += BG) {
@@ -320,7 +333,6 @@ __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64
         sm.dy[e] = dy;
       }
     }
-    lds_sync();
     // adjoint, tokens in reverse, in groups of 4 for the row reductions; the
     // state before token t is the state after token t-1, carried to the next
     // (earlier) token instead of read again
