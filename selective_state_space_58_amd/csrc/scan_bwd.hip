@@ -93,13 +93,16 @@ __device__ __forceinline__ float reduce4_rows(const float (&p)[4]) {
 }
 
 // Sum over the 4 lanes of a quad (the 4 channels of a row); every lane gets it.
-// The empty asm hides where v came from, so the compiler cannot fuse the
-// product that feeds v into the first add (an FMA cannot take a DPP source):
-// each level stays one v_add_f32 with a DPP source.
+// The empty asm statements hide where v came from, so the compiler cannot fuse
+// the product that feeds v into the first add (an FMA cannot take a DPP
+// source), and keep the second add out of a branch that only some lanes take
+// (its DPP source must then be a separate move): each level stays one
+// v_add_f32 with a DPP source.
 __device__ __forceinline__ float quad_sum(float v) {
   asm("" : "+v"(v));
   v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xf, 0xf, true));
   v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xf, 0xf, true));
+  asm("" : "+v"(v));
   return v;
 }
 
