@@ -278,6 +278,9 @@ __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64
   // ---- reverse
   float lam = (a.dh_final != nullptr && nok) ? a.dh_final[hidx] : 0.f;
   float dA = 0.f, dDacc = 0.f, dbacc = 0.f;
+  // short ZOH gain: dg/da = (dt E - g) / a, so the gain part of dA is summed without the 1/a and
+  // scaled once at the end
+  float dAg = 0.f;
   float* hw = sm.h + w * BT * 64;
   float* rw = sm.red + w * BT * BR * 2;
   const int64_t per_group = a.batch * L * BR;
@@ -367,7 +370,14 @@ __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64
       pdx[j] = lam * g * Bn;
       // dg/ddt is E for ZOH and 1 for Euler; dg/da is zero for Euler
       pdt[j] = fmaf(dE * E, av, EULER ? dg : dg * E);
-      dA = EULER ? fmaf(dE * E, dx.x, dA) : fmaf(dE * E, dx.x, fmaf(dg, gain_da<ACC>(dx.x, av, ia, E, g), dA));
+      if constexpr (EULER) {
+        dA = fmaf(dE * E, dx.x, dA);
+      } else if constexpr (ACC) {
+        dA = fmaf(dE * E, dx.x, fmaf(dg, gain_da<ACC>(dx.x, av, ia, E, g), dA));
+      } else {
+        dA = fmaf(dE * E, dx.x, dA);
+        dAg = fmaf(dg, fmaf(dx.x, E, -g), dAg);
+      }
       lam *= E;
     }
     const float tdx = reduce4_rows(pdx);
@@ -405,7 +415,7 @@ __device__ __forceinline__ void scan_bwd_body(const BwdArgs& a, int64_t b, int64
   // ---- per-wave sums: dh0, dA per lane; Dskip and bias gradients summed over the 16 rows
   if (nok) {
     if (a.dh0 != nullptr) a.dh0[hidx] = lam;
-    atomicAdd(a.dA + ch * N + n0 + r, dA);
+    atomicAdd(a.dA + ch * N + n0 + r, (EULER || ACC) ? dA : fmaf(dAg, ia, dA));   // (1/a is infinite at a = 0)
   }
 #pragma unroll
   for (int o = 4; o < 64; o <<= 1) {

@@ -669,6 +669,11 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
           const int tl = tb + U - 16 + r;
           const float2 e = reinterpret_cast<const float2*>(s_gz)[tl * XS + wc];   // (D x, silu z)
           yq[tb / 16] = (reduce_scatter_quad16(pr) + e.x) * e.y;
+          // the one-wave tile path stores at once: its prefetch registers leave no room for four
+          // held y values
+          if constexpr (!VEC) {
+            if (ch_ok && tl < nval32) yb[urow(tl) * dim32 + (uint32_t)c] = (TX)yq[tb / 16];
+          }
         }
         if (tb + U < T) {
           cur = nxt;
@@ -676,8 +681,8 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
           for (int j = 0; j < U; ++j) Ecur[j] = Enxt[j];
         }
       }
-      // the tile's stores after its loop, which then has no branches
-      if (FULL) {
+      // the tile's stores after its loop, which then has no branches (vector path)
+      if (FULL && VEC) {
         if (full_tile) {
 #pragma unroll
           for (int g = 0; g < T / 16; ++g) yb[urow(16 * g + r) * dim32 + (uint32_t)c] = (TX)yq[g];
