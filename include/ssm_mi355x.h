@@ -112,7 +112,7 @@ int ssm_scan_fwd(const void* x, const void* delta, const float* A, const void* B
  * passes every input and output, and the time-split chunk states live in a
  * fixed device array of ssm_scan_fwd_noalloc_max_workspace_bytes() bytes
  * (32 MiB) that the library holds on each GPU it runs on until the process
- * ends.  Shapes whose workspace (ssm_scan_workspace_bytes(..., 0)) exceeds it
+ * ends.  Shapes whose workspace (ssm_scan_workspace_bytes()) exceeds it
  * return SSM_ERR_WORKSPACE before anything is enqueued.  The call makes no
  * hipMalloc, hipFree or other allocating call (its first call on a device
  * looks the array's address up once).  Every call on one GPU shares that
@@ -208,8 +208,7 @@ int ssm_scan_final_state(const void* x, const void* delta, const float* A, const
  * depend on dtypes, flags or alignment, so it is an upper bound: a call whose
  * arguments take the one-pass long-sequence kernel needs none.  Depends on
  * the current device. */
-size_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
-                                int final_state_only);
+size_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
 
 /*
  * Mamba-2 SSD forward ([ssd] "Basic idea" and "Linear and quadratic forms";

@@ -75,7 +75,7 @@ def load_library():
         lib.ssm_scan_final_state.restype = _I
         lib.ssd_chunk_scan_fwd.argtypes = [_P] * 8 + [_I, _P, _P, _P] + [_I64] * 7 + [_I, _I, _P, _SZ, _P]
         lib.ssd_chunk_scan_fwd.restype = _I
-        lib.ssm_scan_workspace_bytes.argtypes = [_I64] * 4 + [_I]
+        lib.ssm_scan_workspace_bytes.argtypes = [_I64] * 4
         lib.ssm_scan_workspace_bytes.restype = _SZ
         lib.ssd_workspace_bytes.argtypes = [_I64] * 7
         lib.ssd_workspace_bytes.restype = _SZ
@@ -143,8 +143,8 @@ def _act_code(t, name):
     return _DT[t.dtype]
 
 
-def ssm_scan_workspace_bytes(batch, seqlen, dim, dstate, final_state_only=False) -> int:
-    return int(load_library().ssm_scan_workspace_bytes(batch, seqlen, dim, dstate, int(final_state_only)))
+def ssm_scan_workspace_bytes(batch, seqlen, dim, dstate) -> int:
+    return int(load_library().ssm_scan_workspace_bytes(batch, seqlen, dim, dstate))
 
 
 def ssd_workspace_bytes(batch, seqlen, nheads, headdim, ngroups, dstate, chunk_size) -> int:

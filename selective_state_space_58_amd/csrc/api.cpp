@@ -145,9 +145,9 @@ static_assert(sizeof(kSourceDigest) == 18 + 64 + 1, "the source digest is 64 hex
 
 const char* ssm_source_digest(void) { return kSourceDigest + 18; }
 
-size_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int final_state_only) {
+size_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
   if (batch <= 0 || seqlen <= 0 || dim <= 0 || dstate <= 0 || dstate > 256) return 0;
-  return plan_scan(batch, seqlen, dim, dstate, final_state_only != 0, device_cu_count()).ws_bytes;
+  return plan_scan(batch, seqlen, dim, dstate, device_cu_count()).ws_bytes;
 }
 
 static int scan_common(const void* x, const void* delta, const float* A, const void* B, const void* C,
@@ -167,7 +167,7 @@ static int scan_common(const void* x, const void* delta, const float* A, const v
   if (!aligned(save_states, 4)) return fail(SSM_ERR_ALIGNMENT, "states must be 4-byte aligned");
   if (batch == 0 || dim == 0) return SSM_OK;
   const int cus = device_cu_count();
-  ScanPlan p = plan_scan(batch, seqlen, dim, dstate, final_only, cus);
+  ScanPlan p = plan_scan(batch, seqlen, dim, dstate, cus);
   hipStream_t st = (hipStream_t)stream;
   ScanArgs a{};
   a.x = x; a.delta = delta; a.A = A; a.B = B; a.C = final_only ? nullptr : C;

@@ -136,8 +136,7 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 }  // namespace
 
-ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, bool final_only, int num_cus) {
-  (void)final_only;
+ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int num_cus) {
   ScanPlan p{};
   const int64_t simds = 4LL * (num_cus > 0 ? num_cus : 256);
   // Rows per wave.  Four rows of 16 channels run one wave per SIMD at best

@@ -59,8 +59,7 @@ struct ScanPlan {
   bool long_path;     // one pass with time-split lanes (scan_long.hip) instead of chunks
 };
 
-ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, bool final_only,
-                   int num_cus);
+ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int num_cus);
 
 // Enqueue the whole selective scan (all phases).  Returns an ssm_status.
 int launch_scan(const ScanArgs& a, const ScanPlan& p, bool final_only, void* stream);

@@ -143,13 +143,13 @@ def test_ssd_argument_errors(kw, code):
 
 def test_workspace_queries():
     lib = _lib()
-    assert lib.ssm_scan_workspace_bytes(0, 10, 10, 16, 0) == 0
+    assert lib.ssm_scan_workspace_bytes(0, 10, 10, 16) == 0
     # few slices, long sequence: the time-split path needs workspace
-    assert lib.ssm_scan_workspace_bytes(1, 131072, 2048, 16, 0) > 0
-    assert lib.ssm_scan_workspace_bytes(8, 2048, 1536, 16, 0) == 0
+    assert lib.ssm_scan_workspace_bytes(1, 131072, 2048, 16) > 0
+    assert lib.ssm_scan_workspace_bytes(8, 2048, 1536, 16) == 0
     # 129..256 states run 8 rows of 32 states per wave; 257 is unsupported
-    assert lib.ssm_scan_workspace_bytes(1, 65536, 64, 256, 0) > 0
-    assert lib.ssm_scan_workspace_bytes(1, 65536, 64, 257, 0) == 0
+    assert lib.ssm_scan_workspace_bytes(1, 65536, 64, 256) > 0
+    assert lib.ssm_scan_workspace_bytes(1, 65536, 64, 257) == 0
     # SSD: every call keeps the C B^T products of each (batch, 64-token block, group): 10 causal 16 x 16 fp32
     # tiles.  The b2 x 64-head layer fills the CUs (no split); 1 x 4 heads x 3000 tokens splits into 5 chunks
     # of 640 tokens: 5 fp32 states of 4 x 64 x 128, then 5 x 4 decay sums, each part 256-byte aligned
@@ -361,11 +361,11 @@ def test_noalloc_scan_rejects_shapes_beyond_its_workspace():
     cap = lib.ssm_scan_fwd_noalloc_max_workspace_bytes()
     assert cap == 32 << 20
     # 256 states on 2048 channels over 131072 tokens: the time split needs more than the fixed array
-    need = lib.ssm_scan_workspace_bytes(1, 131072, 2048, 256, 0)
+    need = lib.ssm_scan_workspace_bytes(1, 131072, 2048, 256)
     assert need > cap
     assert scan_noalloc(lib, seqlen=131072, dim=2048, dstate=256) == 5
     msg = lib.ssm_last_error()
     assert b"no-allocation" in msg and str(need).encode() in msg
     # the long-sequence layer (16 states) fits
-    assert 0 < lib.ssm_scan_workspace_bytes(1, 131072, 2048, 16, 0) <= cap
+    assert 0 < lib.ssm_scan_workspace_bytes(1, 131072, 2048, 16) <= cap
     assert scan_noalloc(lib, batch=0) == 0
