@@ -276,8 +276,8 @@ __device__ __forceinline__ void long_body(const ScanArgs& a, int64_t b, int64_t 
     float* sy = s_y + cur * Y_FLOATS;
 
     // 1. the group's tokens from a zero state
-    float E[TAU][4], U[TAU][4], h[4] = {0.f, 0.f, 0.f, 0.f};
-    float dsum = 0.f;
+    float E[TAU][4], U[TAU][4], h[4];
+    float dsum;
 #pragma unroll
     for (int j = 0; j < TAU; ++j) {
       const float2 dx = sdx[ix_dx(tg + j, w)];
@@ -290,11 +290,11 @@ __device__ __forceinline__ void long_body(const ScanArgs& a, int64_t b, int64_t 
                          : GAIN == kGainAccurate ? zoh_gain_accurate(e, dx.x, av[s], ia[s])
                                                  : fmaf(e, ia[s], -ia[s]);
         const float u = gn * (bv[s] * dx.y);
-        h[s] = fmaf(e, h[s], u);
+        h[s] = j == 0 ? u : fmaf(e, h[s], u);   // from a zero state
         E[j][s] = e;
         U[j][s] = u;
       }
-      dsum += dx.x;
+      dsum = j == 0 ? dx.x : dsum + dx.x;
     }
 
     // 2. inclusive scan of the groups' (decay, state) aggregates along the row
