@@ -260,9 +260,14 @@ __device__ __forceinline__ void long_body(const ScanArgs& a, int64_t b, int64_t 
   const int tg = g * TAU;   // this lane's first token within the tile
 
   // Tiles are double-buffered in LDS: while the waves compute tile k from one
-  // buffer, the staging threads fill the other with tile k+1 (loaded into
-  // registers one tile earlier) and write tile k-1's y out, so one barrier per
-  // tile suffices.
+  // buffer, the staging threads write tile k-1's y out (first, so that its LDS
+  // reads and stores overlap the scan's own LDS reads instead of delaying the
+  // barrier) and at the end fill the other buffer with tile k+1 (loaded into
+  // registers one tile earlier), so one barrier per tile suffices.  The scan's
+  // LDS reads are issued two tokens ahead of their use; the scheduling
+  // barriers keep the compiler from sinking them back next to their first use,
+  // where each read's latency was exposed (bf16 rows; the fp32 variants have
+  // no registers to spare for it).
   fetch(0);
   stage(0, 0);
   if (T < L) fetch(T);
@@ -274,14 +279,36 @@ __device__ __forceinline__ void long_body(const ScanArgs& a, int64_t b, int64_t 
     const float4* s_b4 = reinterpret_cast<const float4*>(s_b + cur * BC_FLOATS);
     const float4* s_c4 = reinterpret_cast<const float4*>(s_c + cur * BC_FLOATS);
     float* sy = s_y + cur * Y_FLOATS;
+    if (t0 > 0) store_y(t0 - T, cur ^ 1);   // the previous tile's y (written before the last barrier) out
 
     // 1. the group's tokens from a zero state
     float E[TAU][4], U[TAU][4], h[4];
     float dsum;
+    constexpr int KD = XB ? 2 : 0;   // tokens of (dt, x) and B read ahead
+    float2 dpre[2];
+    float4 bpre[2];
+    if (KD > 0) {
+      dpre[0] = sdx[ix_dx(tg, w)];
+      dpre[1] = sdx[ix_dx(tg + 1, w)];
+      bpre[0] = s_b4[ix_b4(0, r, g)];
+      bpre[1] = s_b4[ix_b4(1, r, g)];
+    }
 #pragma unroll
     for (int j = 0; j < TAU; ++j) {
-      const float2 dx = sdx[ix_dx(tg + j, w)];
-      const float4 bq = s_b4[ix_b4(j, r, g)];
+      float2 dx;
+      float4 bq;
+      if (KD > 0) {
+        dx = dpre[j & 1];
+        bq = bpre[j & 1];
+        if (j + 2 < TAU) {
+          dpre[j & 1] = sdx[ix_dx(tg + j + 2, w)];
+          bpre[j & 1] = s_b4[ix_b4(j + 2, r, g)];
+        }
+        if (j & 1) __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of these tokens' work
+      } else {
+        dx = sdx[ix_dx(tg + j, w)];
+        bq = s_b4[ix_b4(j, r, g)];
+      }
       const float bv[4] = {bq.x, bq.y, bq.z, bq.w};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -295,6 +322,15 @@ __device__ __forceinline__ void long_body(const ScanArgs& a, int64_t b, int64_t 
         U[j][s] = u;
       }
       dsum = j == 0 ? dx.x : dsum + dx.x;
+    }
+
+    // C of the replay's first two tokens, read ahead of the scan (the replay
+    // reads each token's C two tokens ahead of its use)
+    constexpr int KC = XB ? 2 : 0;
+    float4 cpre[2];
+    if (KC > 0) {
+      cpre[0] = s_c4[ix_b4(0, r, g)];
+      cpre[1] = s_c4[ix_b4(1, r, g)];
     }
 
     // 2. inclusive scan of the groups' (decay, state) aggregates along the row
@@ -318,11 +354,20 @@ __device__ __forceinline__ void long_body(const ScanArgs& a, int64_t b, int64_t 
     for (int s = 0; s < 4; ++s) h[s] = hin[s];
 #pragma unroll
     for (int jq = 0; jq < TAU / 4; ++jq) {
+      const int t = tg + 4 * jq + r;   // the token whose y this lane forms
+      const float xv = sdx[ix_dx(t, w)].y;
       float pr[4];
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int j = 4 * jq + jj;
-        const float4 cq = s_c4[ix_b4(j, r, g)];
+        float4 cq;
+        if (KC > 0) {
+          cq = cpre[jj & 1];
+          if (j + 2 < TAU) cpre[jj & 1] = s_c4[ix_b4(j + 2, r, g)];
+          if (jj & 1) __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of these tokens' work
+        } else {
+          cq = s_c4[ix_b4(j, r, g)];
+        }
         const float cv[4] = {cq.x, cq.y, cq.z, cq.w};
         float acc = 0.f;
 #pragma unroll
@@ -333,8 +378,6 @@ __device__ __forceinline__ void long_body(const ScanArgs& a, int64_t b, int64_t 
         pr[jj] = acc;
       }
       const float tot = reduce_scatter_rows<4>(pr);   // row r: token tg + 4 jq + r
-      const int t = tg + 4 * jq + r;
-      const float xv = sdx[ix_dx(t, w)].y;
       float yv = fmaf(Dv, xv, tot);
       if (has_z) yv *= sgz[ix_dx(t, w)];
       sy[ix_y(t, w)] = yv;
@@ -345,7 +388,6 @@ __device__ __forceinline__ void long_body(const ScanArgs& a, int64_t b, int64_t 
       stage(t0 + T, cur ^ 1);
       if (t0 + 2 * T < L) fetch(t0 + 2 * T);
     }
-    if (t0 > 0) store_y(t0 - T, cur ^ 1);
     lds_sync();
   }
   store_y(((L - 1) / T) * T, cur ^ 1);
