@@ -259,11 +259,12 @@ __device__ __forceinline__ void long_body(const ScanArgs& a, int64_t b, int64_t 
   }
   const int tg = g * TAU;   // this lane's first token within the tile
 
-  // Tiles are double-buffered in LDS: while the waves compute tile k from one
-  // buffer, the staging threads write tile k-1's y out (first, so that its LDS
-  // reads and stores overlap the scan's own LDS reads instead of delaying the
-  // barrier) and at the end fill the other buffer with tile k+1 (loaded into
-  // registers one tile earlier), so one barrier per tile suffices.  The scan's
+  // Tiles are double-buffered in LDS: at the start of tile k, the staging
+  // threads write tile k-1's y out and fill the other buffer with tile k+1
+  // (loaded into registers one tile earlier), then issue the loads of tile
+  // k+2, and all waves compute tile k from its buffer; one barrier per tile
+  // suffices.  (Staging at the start rather than just before the barrier lets
+  // its LDS traffic overlap the scan instead of delaying the barrier.)  The scan's
   // LDS reads are issued two tokens ahead of their use; the scheduling
   // barriers keep the compiler from sinking them back next to their first use,
   // where each read's latency was exposed (bf16 rows; the fp32 variants have
@@ -280,6 +281,10 @@ __device__ __forceinline__ void long_body(const ScanArgs& a, int64_t b, int64_t 
     const float4* s_c4 = reinterpret_cast<const float4*>(s_c + cur * BC_FLOATS);
     float* sy = s_y + cur * Y_FLOATS;
     if (t0 > 0) store_y(t0 - T, cur ^ 1);   // the previous tile's y (written before the last barrier) out
+    if (t0 + T < L) {   // the next tile into the other buffer, which no wave reads in this tile
+      stage(t0 + T, cur ^ 1);
+      if (t0 + 2 * T < L) fetch(t0 + 2 * T);
+    }
 
     // 1. the group's tokens from a zero state
     float E[TAU][4], U[TAU][4], h[4];
@@ -383,11 +388,6 @@ __device__ __forceinline__ void long_body(const ScanArgs& a, int64_t b, int64_t 
       sy[ix_y(t, w)] = yv;
     }
 
-    // next tile into the other buffer, the previous tile's y out
-    if (t0 + T < L) {
-      stage(t0 + T, cur ^ 1);
-      if (t0 + 2 * T < L) fetch(t0 + 2 * T);
-    }
     lds_sync();
   }
   store_y(((L - 1) / T) * T, cur ^ 1);
