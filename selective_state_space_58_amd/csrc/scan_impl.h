@@ -591,8 +591,8 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
   for (int64_t t0 = t_begin; t0 < t_stop; t0 += T) {
     lds_sync();
     stage(t0);
+    if (t0 + T < t_stop) fetch(t0 + T);   // the staged registers are free again: next tile's loads before the barrier
     lds_sync();
-    if (t0 + T < t_stop) fetch(t0 + T);
     const int64_t nvalid = t_stop - t0;
     TX* yb = gy + (b * L + grow0(t0)) * dim + ch0;   // uniform
     const bool full_tile = ch_ok && nvalid >= T;       // uniform on the vector path
