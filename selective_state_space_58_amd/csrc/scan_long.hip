@@ -259,16 +259,19 @@ __device__ __forceinline__ void long_body(const ScanArgs& a, int64_t b, int64_t 
   }
   const int tg = g * TAU;   // this lane's first token within the tile
 
-  // Tiles are double-buffered in LDS: at the start of tile k, the staging
-  // threads write tile k-1's y out and fill the other buffer with tile k+1
-  // (loaded into registers one tile earlier), then issue the loads of tile
-  // k+2, and all waves compute tile k from its buffer; one barrier per tile
-  // suffices.  (Staging at the start rather than just before the barrier lets
-  // its LDS traffic overlap the scan instead of delaying the barrier.)  The scan's
-  // LDS reads are issued two tokens ahead of their use; the scheduling
-  // barriers keep the compiler from sinking them back next to their first use,
-  // where each read's latency was exposed (bf16 rows; the fp32 variants have
-  // no registers to spare for it).
+  // Tiles are double-buffered in LDS, one barrier per tile: while all waves
+  // compute tile k from one buffer, the staging threads fill the other with
+  // tile k+1 (loaded into registers one tile earlier), issue the loads of tile
+  // k+2 and write tile k-1's y out.  The B/C staging waves do their part at
+  // the start of the tile and the (dt, x) staging waves theirs, with the y
+  // stores, at its end.  Each SIMD holds one wave of each kind, so the two
+  // run their latency-bound stretches (the start of the scan, the aggregate
+  // scan, the replay's end) out of step, and each covers the other's waits;
+  // staging all at the start or all at the end measured 5-7% slower.  The
+  // scan's LDS reads are issued two tokens ahead of their use; the scheduling
+  // barriers keep the compiler from sinking them back next to their first
+  // use, where each read's latency was exposed (bf16 rows; the fp32 variants
+  // have no registers to spare for it).
   fetch(0);
   stage(0, 0);
   if (T < L) fetch(T);
@@ -280,8 +283,7 @@ __device__ __forceinline__ void long_body(const ScanArgs& a, int64_t b, int64_t 
     const float4* s_b4 = reinterpret_cast<const float4*>(s_b + cur * BC_FLOATS);
     const float4* s_c4 = reinterpret_cast<const float4*>(s_c + cur * BC_FLOATS);
     float* sy = s_y + cur * Y_FLOATS;
-    if (t0 > 0) store_y(t0 - T, cur ^ 1);   // the previous tile's y (written before the last barrier) out
-    if (t0 + T < L) {   // the next tile into the other buffer, which no wave reads in this tile
+    if (!xrole && t0 + T < L) {   // B/C of the next tile into the other buffer, which no wave reads in this tile
       stage(t0 + T, cur ^ 1);
       if (t0 + 2 * T < L) fetch(t0 + 2 * T);
     }
@@ -388,6 +390,11 @@ __device__ __forceinline__ void long_body(const ScanArgs& a, int64_t b, int64_t 
       sy[ix_y(t, w)] = yv;
     }
 
+    if (xrole && t0 + T < L) {   // (dt, x) of the next tile
+      stage(t0 + T, cur ^ 1);
+      if (t0 + 2 * T < L) fetch(t0 + 2 * T);
+    }
+    if (t0 > 0) store_y(t0 - T, cur ^ 1);   // the previous tile's y (written before the last barrier)
     lds_sync();
   }
   store_y(((L - 1) / T) * T, cur ^ 1);
