@@ -645,6 +645,9 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
           load16(tb + U, nxt);
           exp16(nxt, Enxt);
         }
+        // keep the next step's LDS reads and exponentials ahead of this step's work (the compiler
+        // otherwise moves reads next to their use; 2.8B-like layer 0.495 -> 0.488 ms)
+        __builtin_amdgcn_sched_barrier(0);
         if (SAVE && tb % kSaveTile == 0) save_state(t0 + tb);
         static_for<U>([&](auto jc) {
           constexpr int j = decltype(jc)::value;
