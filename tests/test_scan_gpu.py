@@ -238,7 +238,9 @@ def test_explicit_workspace(ssm):
 # one-pass kernel, which shows which path ran.
 LONG_CASES = [((1, 3000, 2048), "bf16", "bf16", True), ((2, 1100, 1024), "f32", "f32", True),
               ((4, 777, 512), "bf16", "f32", False), ((1, 2048, 4096), "bf16", "bf16", False),
-              ((1, 513, 2048), "f32", "bf16", True)]
+              ((1, 513, 2048), "f32", "bf16", True),
+              # exactly two tiles over two batch rows; whole tiles only
+              ((2, 512, 2048), "bf16", "bf16", True), ((1, 1024, 2048), "bf16", "bf16", False)]
 
 
 def _call_ws(ssm, t, inp, ws):
