@@ -161,6 +161,35 @@ def step_bytes(cfg):
 SETTLE_S = 0.5
 
 
+def graph_call_ms(fn, torch, reps=50, replays=5):
+    """GPU time per call of fn with `reps` calls recorded once in a HIP graph and replayed, so that no host
+    launch gap sits between the kernels (the eager timing of a kernel of a few tens of microseconds includes
+    the binding's host work per call).  The calls must allocate nothing and record no memset."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(3):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(reps):
+            fn(i)
+    g.replay()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (replays * reps)
+    del g
+    return ms
+
+
 def time_calls(fn, steps, warmup, torch, settle_s=None):
     """Run fn(i) for settle_s seconds of wall time and then warmup times, untimed; then `steps` times
     bracketed by events.  Returns (total_ms, [per-call ms]).  The settle phase is there because the GPU's
@@ -260,6 +289,8 @@ def run_scan(oi, steps, warmup, ssm, workloads, torch, dev, np, ncopy=1):
            "workspace_bytes": nb}
     if cfg["name"] in SCAN_SUMMARY_KEYS:
         res["traffic"] = measured_traffic(SCAN_SUMMARY_KEYS[cfg["name"]])
+    if kern_ms < 0.1:   # launch-bound when called eagerly: also the time per call inside a graph
+        res["graph_ms"] = round(graph_call_ms(fn, torch), 5)
     del copies, y, hf, ws
     torch.cuda.empty_cache()
     return res, cfg
@@ -321,8 +352,10 @@ def run_step(si, steps, warmup, ssm, workloads, torch, dev):
     tot, _ = time_calls(fn, steps, warmup, torch)
     ms = tot / steps
     nb = step_bytes(cfg)
+    gms = graph_call_ms(fn, torch)
     return {"name": cfg["name"], "us": round(ms * 1e3, 2), "Gchannel_steps_s": round(chans / (ms * 1e-3) / 1e9, 2),
-            "hbm_GBs": round(nb / (ms * 1e-3) / 1e9, 1), "hbm_frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            "hbm_GBs": round(nb / (ms * 1e-3) / 1e9, 1), "hbm_frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "graph_us": round(gms * 1e3, 2), "graph_hbm_frac": round(nb / (gms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def run_conv(ci, steps, warmup, ssm, workloads, torch, dev):
@@ -339,8 +372,10 @@ def run_conv(ci, steps, warmup, ssm, workloads, torch, dev):
     e = 2 if cfg["dtype"] == "bf16" else 4
     tc = cfg["batch"] * cfg["seqlen"] * cfg["dim"]
     nb = 2 * tc * e + cfg["dim"] * (cfg["width"] + 1) * 4
+    gms = graph_call_ms(fn, torch)
     return {"name": cfg["name"], "us": round(ms * 1e3, 2), "Gtc_s": round(tc / (ms * 1e-3) / 1e9, 2),
-            "hbm_GBs": round(nb / (ms * 1e-3) / 1e9, 1), "hbm_frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            "hbm_GBs": round(nb / (ms * 1e-3) / 1e9, 1), "hbm_frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "graph_us": round(gms * 1e3, 2), "graph_hbm_frac": round(nb / (gms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def run_bwd(steps, warmup, ssm, workloads, torch, dev, np):
