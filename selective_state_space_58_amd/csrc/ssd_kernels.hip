@@ -230,15 +230,18 @@ __global__ __launch_bounds__(64 * NCB) void ssd_cb_kernel(SsdArgs a, int64_t nbl
 // Twelve waves, three per SIMD (w):
 //   0, 1       outputs of tokens [32 w, 32 w + 32) of a block (Y_off and Y_diag,
 //              transposed so that a lane holds 4 x 4 consecutive channels of one
-//              token), C read straight into registers one step ahead, y left in
-//              LDS;
+//              token), C read straight into registers one step ahead; the
+//              epilogue (skip, gate, bf16 into an LDS tile) of a block runs at
+//              the start of the next step, ahead of its products, so that these
+//              waves issue VALU work while the others start on LDS reads
+//              (0.191 -> 0.183 ms);
 //   2, 3 (6, 7 when N = 128)
 //              one 32-state slice each: S^T = B^T (X o w) and the update of the
 //              fp32 state held in registers;
 //   8 - 11     x*w of a quarter of the block's rows each;
 //   2          also the decay terms;
 //   4, 5       the direct loads of B, x and the gate into LDS, and the stores
-//              of y one step later (so that the only memory operations of waves
+//              of y one step after its epilogue (so that the only memory operations of waves
 //              0 and 1 are their own loads, which they wait for exactly);
 //   4 - 11     the block's ten causal C B^T tiles (the pre-pass product), masked
 //              and decayed into M: with 128 states, one tile each for state
@@ -515,7 +518,7 @@ __global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(3)))
       f32x4 rcbn0 = rcb0, rcbn1 = rcb1;
       if (FULL && cb0 >= 0 && i + 1 < nblk) load_cb(t0 + QB, rcbn0, rcbn1);
       if (i + 1 < nblk) load_xz(gX, t0 + QB, Xs3[i3n]);
-      if (FULL && i >= 2) store_y(t0 - 2 * QB, i & 1);
+      if (FULL && i >= 3) store_y(t0 - 3 * QB, (i + 1) & 1);
       if (i < nblk) {
         load_b(t0, i & 1);
         if (FULL && a.z != nullptr) load_xz(gZ, t0, Zs2[i & 1]);
@@ -527,14 +530,45 @@ __global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(3)))
       rcb1 = rcbn1;
       lds_sync();
     }
+    if (FULL && nblk >= 2) store_y(t_begin + (int64_t)(nblk - 2) * QB, nblk & 1);
+    lds_sync();   // the output waves' epilogue of the last block
     if (FULL) store_y(t_begin + (int64_t)(nblk - 1) * QB, (nblk - 1) & 1);
   } else if (y_wave) {
-    // outputs of block i-1: Y^T = diag(e^cum) (H C^T) + X^T M^T for tokens [32 w, 32 w + 32), gated, to
-    // Ys2.  The C rows of block i go into the registers of block i-1's once those are used.
+    // outputs of block i-1: Y^T = diag(e^cum) (H C^T) + X^T M^T for tokens [32 w, 32 w + 32).  The C
+    // rows of block i go into the registers of block i-1's once those are used.  The epilogue (skip,
+    // gate, bf16 into Ys2) of a block runs at the start of the next step, ahead of that step's products,
+    // so that these waves do VALU work while the others start on their LDS reads.
+    f32x16 ypend = {};
+    u32x2 xpend[4] = {}, zpend[4] = {};
+    int pend_jb = 0;
+    bool have_pend = false;
+    // lane l: token 32 w + l % 32 of the block, channels 8 g + 4 (l / 32) .. +3 for g = 0..3
+    auto epilogue = [&]() {
+      const int tl = 32 * w + c32;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int p = 8 * g + 4 * hk;
+        float yv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) yv[j] = ypend[4 * g + j];
+        if (a.Dskip != nullptr) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) yv[j] = fmaf(Dv, bf2f((u16)(xpend[g][j >> 1] >> (16 * (j & 1)))), yv[j]);
+        }
+        if (a.z != nullptr) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) yv[j] *= silu_f(bf2f((u16)(zpend[g][j >> 1] >> (16 * (j & 1)))));
+        }
+        const u32x2 out = {pack_bf2(yv[0], yv[1]), pack_bf2(yv[2], yv[3])};
+        *reinterpret_cast<u32x2*>(&Ys2[pend_jb][swz<XCPR>(tl, p)]) = out;
+      }
+      have_pend = false;
+    };
     int i3 = 0;
     for (int i = 0; i <= nblk; ++i) {
       const int64_t t0 = t_begin + (int64_t)i * QB;
       const int i3p = i3 == 0 ? 2 : i3 - 1;
+      if (have_pend) epilogue();   // block i-2
       f32x16 yacc = {};
       if (i > 0) {
         const int jb = (i - 1) & 1;
@@ -561,31 +595,23 @@ __global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(3)))
             yacc = mfma32(xb, frag_rows(Ml2[jb], 32 * w + c32, k0, SQ), yacc);
           }
         }
-        // lane l: token 32 w + l % 32 of block i-1, channels 8 g + 4 (l / 32) .. +3 for g = 0..3
+        // the block's x (skip) and gate values, read now: their buffers take later blocks next step
         const int tl = 32 * w + c32;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int p = 8 * g + 4 * hk;
-          float yv[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) yv[j] = yacc[4 * g + j];
-          if (a.Dskip != nullptr) {
-            const u32x2 xr = *reinterpret_cast<const u32x2*>(&Xs3[i3p][swz<XCPR>(tl, p)]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) yv[j] = fmaf(Dv, bf2f((u16)(xr[j >> 1] >> (16 * (j & 1)))), yv[j]);
-          }
-          if (a.z != nullptr) {
-            const u32x2 zr = *reinterpret_cast<const u32x2*>(&Zs2[jb][swz<XCPR>(tl, p)]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) yv[j] *= silu_f(bf2f((u16)(zr[j >> 1] >> (16 * (j & 1)))));
-          }
-          const u32x2 out = {pack_bf2(yv[0], yv[1]), pack_bf2(yv[2], yv[3])};
-          *reinterpret_cast<u32x2*>(&Ys2[jb][swz<XCPR>(tl, p)]) = out;
+          if (a.Dskip != nullptr) xpend[g] = *reinterpret_cast<const u32x2*>(&Xs3[i3p][swz<XCPR>(tl, p)]);
+          if (a.z != nullptr) zpend[g] = *reinterpret_cast<const u32x2*>(&Zs2[jb][swz<XCPR>(tl, p)]);
         }
+        ypend = yacc;
+        pend_jb = jb;
+        have_pend = true;
       }
       i3 = i3 == 2 ? 0 : i3 + 1;
       lds_sync();
     }
+    if (have_pend) epilogue();
+    lds_sync();   // the last block's y, for the loading waves
   } else if (has_st) {
     // decay terms of block i+1 (wave 2); the state update with block i-1: H_i = e^{cum_end} H_{i-1} +
     // B^T (X o w), then H_i split for the outputs of block i
@@ -629,6 +655,7 @@ __global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(3)))
       i3 = i3 == 2 ? 0 : i3 + 1;
       lds_sync();
     }
+    lds_sync();   // (the output waves' last epilogue)
     // the final state (or this chunk's state and decay sum for the carry pass)
     float* hout = FULL ? (chunk == a.nchunks - 1 ? a.h_final : nullptr) : a.ws_state + chunk * slice;
     if (hout != nullptr) {
@@ -668,6 +695,7 @@ __global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(3)))
       i3 = i3 == 2 ? 0 : i3 + 1;
       lds_sync();
     }
+    lds_sync();   // (the output waves' last epilogue)
   }
 }
 
