@@ -15,7 +15,7 @@
 //
 // Mapping.  C B^T does not depend on the head, so a pre-pass forms it once
 // per (batch, 64-token block, group).  The main kernel runs one workgroup of
-// 8 waves per (batch, head, 32-channel slice of the head): 256 workgroups for
+// 12 waves per (batch, head, 32-channel slice of the head): 256 workgroups for
 // the 2-batch, 64-head, 64-channel workload, one per CU.  The workgroup walks the
 // sequence in 64-token blocks; the fp32 state H (32 x dstate) stays in
 // registers for the whole sequence and is never written to HBM.  The block
@@ -27,9 +27,10 @@
 // transposed copies are made.  The fp32 operands (M, x*w and the state)
 // enter as a bf16 high part plus a bf16 low part, keeping ~16 bits instead
 // of 8: a single bf16 copy of the state loses accuracy where C.H cancels over
-// the states.  The block's decay prefix sum is a DPP scan in one wave during
-// staging; the next block's B, C, x, dt and C B^T tiles are loaded into
-// registers while the current one computes.
+// the states.  The block's decay prefix sum is a DPP scan in one wave; the
+// block loop is a software pipeline over the waves' roles (below), with the
+// next blocks' B, x, gate, C, dt and C B^T tiles loaded while the current
+// ones are computed.
 //
 // Block size.  Any chunk length that is a multiple of 64 gives the same map
 // (the state entering a 64-token block is the decayed sum of everything
