@@ -569,17 +569,33 @@ __global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(3)))
     for (int i = 0; i <= nblk; ++i) {
       const int64_t t0 = t_begin + (int64_t)i * QB;
       const int i3p = i3 == 0 ? 2 : i3 - 1;
+      // the first 4 k-steps' state fragments are read before the epilogue, and each later one 4
+      // k-steps ahead of its products, so that the reads' latency overlaps other work
+      constexpr int KA = 4;
+      bf16x8 fhs[KA], fhl[KA];
+      const int jbh = (i - 1) & 1;
+      if (i > 0) {
+#pragma unroll
+        for (int ks = 0; ks < KA; ++ks) {
+          const int k0 = 16 * ks + 8 * hk;
+          fhs[ks] = frag_rows(Hs2[jbh], c32, k0, SN);
+          fhl[ks] = frag_rows(Hl2[jbh], c32, k0, SN);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
       if (have_pend) epilogue();   // block i-2
       f32x16 yacc = {};
       if (i > 0) {
-        const int jb = (i - 1) & 1;
-        const u16* Hs = Hs2[jb];
-        const u16* Hl = Hl2[jb];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const int k0 = 16 * ks + 8 * hk;
-          yacc = mfma32(frag_rows(Hs, c32, k0, SN), rc[ks], yacc);
-          yacc = mfma32(frag_rows(Hl, c32, k0, SN), rc[ks], yacc);
+          const bf16x8 hs = fhs[ks % KA], hl = fhl[ks % KA];
+          if (ks + KA < KS) {
+            const int k0 = 16 * (ks + KA) + 8 * hk;
+            fhs[ks % KA] = frag_rows(Hs2[jbh], c32, k0, SN);
+            fhl[ks % KA] = frag_rows(Hl2[jbh], c32, k0, SN);
+          }
+          yacc = mfma32(hs, rc[ks], yacc);
+          yacc = mfma32(hl, rc[ks], yacc);
         }
         yacc *= decS[i3p][2][32 * w + c32];
       }
