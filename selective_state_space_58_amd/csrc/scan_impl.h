@@ -636,8 +636,22 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
       float Ecur[U], Enxt[U];
       load16(0, cur);
       exp16(cur, Ecur);
-      float pr[16];
+      // readout products of the 16 tokens of a group, two groups' worth: on the vector path a group's
+      // reduce-scatter runs after the first step of the next group, so that its exchange chain
+      // overlaps that step's independent work
+      constexpr bool DEFER_RS = VEC;
+      float pr2[DEFER_RS ? 2 : 1][16];
       float yq[T / 16];   // y of token 16 g + r
+      auto readout16 = [&](int gq) {
+        const int tl = 16 * gq + r;
+        const float2 e = reinterpret_cast<const float2*>(s_gz)[tl * XS + wc];   // (D x, silu z)
+        yq[gq] = (reduce_scatter_quad16(pr2[DEFER_RS ? (gq & 1) : 0]) + e.x) * e.y;
+        // the one-wave tile path stores at once: its prefetch registers leave no room for four
+        // held y values
+        if constexpr (!VEC) {
+          if (ch_ok && tl < nval32) yb[urow(tl) * dim32 + (uint32_t)c] = (TX)yq[gq];
+        }
+      };
       constexpr int kStepUnroll = T / U;
 #pragma unroll kStepUnroll
       for (int tb = 0; tb < T; tb += U) {
@@ -665,17 +679,14 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
             }
             h[0] = fmaf(E, h[0], g * u);
           }
-          if (FULL) pr[(tb + j) % 16] = cur.bc[j].y * h[0];
+          if (FULL) pr2[DEFER_RS ? ((tb / 16) & 1) : 0][(tb + j) % 16] = cur.bc[j].y * h[0];
         });
         if (!FULL) dsum += cur.dx.x;   // this lane's token of the step (the quad adds up at the end)
-        if (FULL && (tb + U) % 16 == 0) {
-          const int tl = tb + U - 16 + r;
-          const float2 e = reinterpret_cast<const float2*>(s_gz)[tl * XS + wc];   // (D x, silu z)
-          yq[tb / 16] = (reduce_scatter_quad16(pr) + e.x) * e.y;
-          // the one-wave tile path stores at once: its prefetch registers leave no room for four
-          // held y values
-          if constexpr (!VEC) {
-            if (ch_ok && tl < nval32) yb[urow(tl) * dim32 + (uint32_t)c] = (TX)yq[tb / 16];
+        if (FULL) {
+          if (DEFER_RS) {
+            if (tb % 16 == 0 && tb >= 16) readout16(tb / 16 - 1);
+          } else if ((tb + U) % 16 == 0) {
+            readout16(tb / 16);
           }
         }
         if (tb + U < T) {
@@ -684,6 +695,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
           for (int j = 0; j < U; ++j) Ecur[j] = Enxt[j];
         }
       }
+      if (FULL && DEFER_RS) readout16(T / 16 - 1);
       // the tile's stores after its loop, which then has no branches (vector path)
       if (FULL && VEC) {
         if (full_tile) {
