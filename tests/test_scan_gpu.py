@@ -324,7 +324,7 @@ def test_full_size_layer_workloads_every_element(ssm, index):
 
 
 def test_full_size_long_sequence_every_element(ssm):
-    # the 131072-token layer (time split with chunk carries): the workload's own check -- every 4096th
+    # the 131072-token layer (one pass with time-split lanes): the workload's own check -- every 4096th
     # output of all 2048 channels plus the whole final state -- and every other output as well
     inp, cfg = workloads.config_inputs(3)
     print("case", cfg["name"], "(GPU run)", flush=True)
