@@ -353,7 +353,8 @@ __device__ __forceinline__ void long_body(const ScanArgs& a, int64_t b, int64_t 
     for (int s = 0; s < 4; ++s) {
       const float end_true = fmaf(P[s], carry[s], h[s]);           // state after this lane's group
       hin[s] = dpp<kRowShr + 1, false>(carry[s], end_true);          // group 0 starts from the carry
-      carry[s] = dpp<kRowBcast15, false>(0.f, end_true);             // state after the tile (group 15)
+      // state after the tile (group 15); every lane has a source lane, so no old value is needed
+      carry[s] = bits_f((unsigned)__builtin_amdgcn_mov_dpp((int)f_bits(end_true), kRowBcast15, 0xf, 0xf, false));
     }
 
     // 3. replay from the true starting state; readout summed over the rows
