@@ -18,11 +18,11 @@
 //      ("Paper explainer: Mamba", hardware-aware parallel scan; "Mamba / SSM
 //      complete guide", sec. 5, with the corrected combine), by DPP row shifts
 //      of 1, 2, 4 and 8 lanes; the tile's carried-in state then gives every
-//      group its true starting state, and row_newbcast carries the tile's end
-//      state to the next tile;
+//      group its true starting state;
 //   3. every lane replays its 16 tokens from that state (one fma per element
 //      with the stored E and U) and forms the readout, which is summed over
-//      the 4 rows by a reduce-scatter.
+//      the 4 rows by a reduce-scatter; row_newbcast hands the replayed state
+//      of group 15, the tile's end state, to the whole row for the next tile.
 // Per (t, d, n) element this costs one fma more than the serial scan, instead
 // of the second pass over the sequence that a split into independently
 // computed time chunks needs.  A workgroup holds 8 waves = 8 consecutive
@@ -353,8 +353,6 @@ __device__ __forceinline__ void long_body(const ScanArgs& a, int64_t b, int64_t 
     for (int s = 0; s < 4; ++s) {
       const float end_true = fmaf(P[s], carry[s], h[s]);           // state after this lane's group
       hin[s] = dpp<kRowShr + 1, false>(carry[s], end_true);          // group 0 starts from the carry
-      // state after the tile (group 15); every lane has a source lane, so no old value is needed
-      carry[s] = bits_f((unsigned)__builtin_amdgcn_mov_dpp((int)f_bits(end_true), kRowBcast15, 0xf, 0xf, false));
     }
 
     // 3. replay from the true starting state; readout summed over the rows
@@ -390,6 +388,12 @@ __device__ __forceinline__ void long_body(const ScanArgs& a, int64_t b, int64_t 
       if (has_z) yv *= sgz[ix_dx(t, w)];
       sy[ix_y(t, w)] = yv;
     }
+    // the state after the tile: the replayed state of group 15, in every lane of its row (each lane
+    // has a source lane, so no old value is needed; carry, hin and the replayed state then share
+    // registers, with no copies between tiles)
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      carry[s] = bits_f((unsigned)__builtin_amdgcn_mov_dpp((int)f_bits(h[s]), kRowBcast15, 0xf, 0xf, false));
 
     if (xrole && t0 + T < L) {   // (dt, x) of the next tile
       stage(t0 + T, cur ^ 1);
