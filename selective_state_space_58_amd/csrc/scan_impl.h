@@ -216,12 +216,14 @@ struct VecOf<1> {
   using T = u32x1;
 };
 
-template <int R_, int S>
+// V: the vector tile path (the one-wave tile path of the 16-row layout takes 32-token tiles, whose
+// prefetched items fit its registers; 64-token ones spilled)
+template <int R_, int S, bool V = true>
 struct TileShape {
   static constexpr int R = R_;
   static constexpr int CH = 64 / R;                // channels per wave
   static constexpr int NP = R * S;                 // padded state count of the wave
-  static constexpr int T = R == 4 ? 32 : (S >= 16 ? 16 : 64);   // tokens per LDS tile
+  static constexpr int T = R == 4 ? 32 : (S >= 16 ? 16 : (R == 16 && !V ? 32 : 64));   // tokens per LDS tile
   static constexpr int KX = T / R;                 // (token, channel) items per lane per tile
   static constexpr int KB = T * NP / 64;           // B (and C) items per lane per tile
   // lane -> (row, column).  4 and 8 rows: lane = row * CH + column.  16 rows (4 channels, one
@@ -249,7 +251,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int64_t b, int64_t 
                                           const float (&a2)[S], const float (&ia)[S], const float (&av)[S],
                                           float2* __restrict__ s_dx, float* __restrict__ s_gz,
                                           float* __restrict__ s_bc) {
-  using TS = TileShape<RR, S>;
+  using TS = TileShape<RR, S, VEC>;
   using TX = typename Act<XB>::T;
   using TD = typename Act<DB>::T;
   constexpr int R = TS::R, CH = TS::CH, NP = TS::NP, T = TS::T, KX = TS::KX, KB = TS::KB;
@@ -874,7 +876,7 @@ constexpr int scan_waves_per_simd() {
 template <int RR, bool XB, bool DB, int S, int MODE, bool VEC, int W>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(scan_waves_per_simd<RR, S>())))
 void scan_kernel(ScanArgs a, int64_t groups_per_batch) {
-  using TS = TileShape<RR, S>;
+  using TS = TileShape<RR, S, VEC>;
   constexpr int XS = TS::template xs<W>();
   __shared__ __attribute__((aligned(16))) float2 s_dx[TS::T * XS];
   __shared__ __attribute__((aligned(16))) float s_gz[TS::template gz_floats<W>()];
