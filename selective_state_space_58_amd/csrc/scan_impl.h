@@ -216,14 +216,14 @@ struct VecOf<1> {
   using T = u32x1;
 };
 
-// V: the vector tile path (the one-wave tile path of the 16-row layout takes 32-token tiles, whose
-// prefetched items fit its registers; 64-token ones spilled)
+// V: the vector tile path (the one-wave tile paths of the 8- and 16-row layouts take 32-token tiles,
+// whose prefetched items fit their registers; 64-token ones spilled)
 template <int R_, int S, bool V = true>
 struct TileShape {
   static constexpr int R = R_;
   static constexpr int CH = 64 / R;                // channels per wave
   static constexpr int NP = R * S;                 // padded state count of the wave
-  static constexpr int T = R == 4 ? 32 : (S >= 16 ? 16 : (R == 16 && !V ? 32 : 64));   // tokens per LDS tile
+  static constexpr int T = R == 4 ? 32 : (S >= 16 ? 16 : (!V ? 32 : 64));   // tokens per LDS tile
   static constexpr int KX = T / R;                 // (token, channel) items per lane per tile
   static constexpr int KB = T * NP / 64;           // B (and C) items per lane per tile
   // lane -> (row, column).  4 and 8 rows: lane = row * CH + column.  16 rows (4 channels, one
